@@ -1,0 +1,180 @@
+"""Pins of the oracle's kernel halving (brute force, closed forms, invariants)."""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from oracle import kernel_halving as khm
+from oracle import philox
+
+
+def _points(rng, N, E=4, D=3, scale_k=0.7):
+    return rng.standard_normal((N, E)) * scale_k, rng.standard_normal((N, D))
+
+
+def _kap_scalar(kx, vx, ky, vy, s):
+    """kappa by explicit loops over the coordinates (no matrix products)."""
+    dk = 0.0
+    for a, b in zip(kx, ky):
+        dk += a * b
+    dv = 0.0
+    for a, b in zip(vx, vy):
+        dv += a * b
+    return math.exp(s * dk) * (dv + 1.0)
+
+
+@pytest.mark.parametrize("N,seed", [(2, 0), (4, 1), (8, 2), (12, 3), (16, 4), (16, 5)])
+def test_every_step_by_brute_force(N, seed):
+    """Recompute b, alpha, a, sigma, p of every pair from pointwise kernel sums."""
+    rng = np.random.default_rng(seed)
+    K, V = _points(rng, N)
+    s, delta, unit, bin_id, tag = 0.9, 0.5, 3, 17, philox.TAG_COMPRESS
+    keep, margins = khm.kernel_halving(K, V, s, delta, seed, unit, bin_id, tag)
+    P = N // 2
+    c = math.sqrt(2 * math.log(2 * N / delta))
+    kap = lambda i, j: _kap_scalar(K[i], V[i], K[j], V[j], s)
+    eta = []
+    sigma2 = 0.0
+    for i in range(P):
+        x, xp = 2 * i, 2 * i + 1
+        b2 = kap(x, x) + kap(xp, xp) - 2 * kap(x, xp)
+        # psi_{i-1}(x) - psi_{i-1}(x'), psi = sum_j eta_j (kappa(x_2j, .) - kappa(x_2j+1, .))
+        alpha = 0.0
+        for j in range(i):
+            alpha += eta[j] * (kap(2 * j, x) - kap(2 * j + 1, x) - kap(2 * j, xp) + kap(2 * j + 1, xp))
+        b = math.sqrt(max(b2, 0.0))
+        a = max(b * math.sqrt(sigma2) * c, b2)
+        pt = 0.5 * (1 - alpha / a) if a > 0 else 0.5
+        u = philox.uniform(i, bin_id, unit, tag, seed)
+        assert abs(margins[i] - abs(u - pt)) <= 1e-9 * max(1.0, abs(pt))
+        e = 1.0 if u < min(max(pt, 0.0), 1.0) else -1.0
+        assert keep[i] == (e > 0)
+        eta.append(e)
+        if a > 0:
+            sigma2 = sigma2 + b2 * max(0.0, 1 + (b2 - 2 * a) * sigma2 / a ** 2)
+
+
+@pytest.mark.parametrize("N,seed", [(4, 0), (8, 1), (16, 2), (32, 3)])
+def test_mmd_identity(N, seed):
+    """||mean(kept) - mean(all)||^2 from direct kernel sums equals eta^T G eta / (4 P^2)."""
+    rng = np.random.default_rng(100 + seed)
+    K, V = _points(rng, N)
+    s = 0.8
+    keep, _ = khm.kernel_halving(K, V, s, 0.5, seed, 0, 0, 0)
+    P = N // 2
+    kept = khm.kept_positions(keep)
+    kap = lambda i, j: _kap_scalar(K[i], V[i], K[j], V[j], s)
+    allp = range(N)
+    mmd2 = (sum(kap(i, j) for i in kept for j in kept) / P ** 2
+            - 2 * sum(kap(i, j) for i in kept for j in allp) / (P * N)
+            + sum(kap(i, j) for i in allp for j in allp) / N ** 2)
+    G = khm.pair_gram(K, V, s)
+    eta = np.where(keep, 1.0, -1.0)
+    assert mmd2 == pytest.approx(eta @ G @ eta / (4 * P ** 2), rel=1e-9, abs=1e-12)
+
+
+def test_enumerate_all_sign_vectors_report_rank():
+    """All 2^P outcomes of a tiny bin: both MMD formulas agree for every one.
+
+    The rank of the chosen outcome is reported, not asserted: the walk is
+    randomised and is not a minimiser.
+    """
+    rng = np.random.default_rng(7)
+    N = 12
+    K, V = _points(rng, N)
+    s = 1.0
+    G = khm.pair_gram(K, V, s)
+    P = N // 2
+    kap = khm.kappa_matrix(K, V, K, V, s)
+    vals = []
+    for signs in itertools.product((1.0, -1.0), repeat=P):
+        eta = np.array(signs)
+        kept = [2 * i if e > 0 else 2 * i + 1 for i, e in enumerate(eta)]
+        direct = (kap[np.ix_(kept, kept)].sum() / P ** 2
+                  - 2 * kap[kept, :].sum() / (P * N) + kap.sum() / N ** 2)
+        quad = eta @ G @ eta / (4 * P ** 2)
+        assert direct == pytest.approx(quad, rel=1e-8, abs=1e-12)
+        vals.append(quad)
+    keep, _ = khm.kernel_halving(K, V, s, 0.5, 0, 0, 0, 0)
+    chosen = np.where(keep, 1.0, -1.0) @ G @ np.where(keep, 1.0, -1.0) / (4 * P ** 2)
+    rank = int((np.array(vals) < chosen - 1e-15).sum())
+    print(f"kernel halving outcome rank {rank} of {len(vals)}")
+
+
+def test_forced_decisions_follow_the_walk_sign():
+    """|alpha| > a clips p to 0 or 1: the second pair must oppose the first."""
+    G = np.array([[1.0, 5.0], [5.0, 1.0]])
+    dummy = np.zeros((4, 1))
+    for seed in range(200):
+        keep, margins = khm.kernel_halving(dummy, dummy, 1.0, 0.5, seed, 0, 0, 0, G=G)
+        assert keep[1] != keep[0]
+        assert margins[1] > 0.5  # p~ lies outside [0, 1]
+
+
+def test_degenerate_pair_is_a_fair_coin():
+    """b = 0 (identical points) gives p = 1/2 exactly: keep first iff u < 1/2."""
+    K = np.zeros((2, 3)); V = np.ones((2, 2))
+    for seed in range(100):
+        keep, margins = khm.kernel_halving(K, V, 1.0, 0.5, seed, 5, 9, 1)
+        u = philox.uniform(0, 9, 5, 1, seed)
+        assert keep[0] == (u < 0.5)
+        assert margins[0] == abs(u - 0.5)
+
+
+@pytest.mark.parametrize("k", [-6, -2, 2, 4, 10])
+def test_scale_invariance_of_decisions(k):
+    """kappa -> 4^k kappa changes no decision (bit-identical)."""
+    rng = np.random.default_rng(11)
+    K, V = _points(rng, 64)
+    G = khm.pair_gram(K, V, 0.9)
+    a, _ = khm.kernel_halving(K, V, 0.9, 0.5, 3, 1, 2, 0, G=G)
+    b, _ = khm.kernel_halving(K, V, 0.9, 0.5, 3, 1, 2, 0, G=G * (4.0 ** k))
+    assert np.array_equal(a, b)
+
+
+def test_kernel_gram_symmetric_psd():
+    rng = np.random.default_rng(5)
+    K, V = _points(rng, 40, E=8, D=8)
+    kap = khm.kappa_matrix(K, V, K, V, 0.5)
+    assert np.allclose(kap, kap.T, rtol=0, atol=1e-12 * np.abs(kap).max())
+    assert np.linalg.eigvalsh(kap).min() >= -1e-12 * np.trace(kap)
+    G = khm.pair_gram(K, V, 0.5)
+    assert np.all(np.diag(G) >= 0)
+    assert np.linalg.eigvalsh(G).min() >= -1e-12 * np.trace(G)
+
+
+def test_halving_beats_random_halving():
+    """The walk keeps the kept half's mean close to the full mean.
+
+    Keeping a uniformly random point of every pair gives E[eta^T G eta] =
+    trace G.  On low-dimensional points (where the kernel's effective rank is
+    small) the walk stays far below that; a sign error in alpha or p makes it
+    grow far above it instead (about 60x trace G on this data).
+    """
+    rng = np.random.default_rng(21)
+    ratios = []
+    for seed in range(6):
+        K, V = _points(rng, 512, E=1, D=1, scale_k=0.5)
+        G = khm.pair_gram(K, V, 1.0)
+        keep, _ = khm.kernel_halving(K, V, 1.0, 0.5, seed, 0, 0, 0, G=G)
+        eta = np.where(keep, 1.0, -1.0)
+        ratios.append((eta @ G @ eta) / np.trace(G))
+    assert np.mean(ratios) < 0.5, ratios
+
+
+def test_replay_counts_flips():
+    rng = np.random.default_rng(2)
+    K, V = _points(rng, 32)
+    keep, margins = khm.kernel_halving(K, V, 1.0, 0.5, 0, 0, 0, 0)
+    flipped = keep.copy()
+    flipped[3] = not flipped[3]
+    st = khm.HalvingStats()
+    keep2, _ = khm.kernel_halving(K, V, 1.0, 0.5, 0, 0, 0, 0, override=flipped, stats=st)
+    assert np.array_equal(keep2, flipped)
+    assert st.decisions == 16
+    if margins[3] < 1e-6:
+        assert st.near_ties == 1 and st.fails == 0
+    else:
+        assert st.fails == 1 and st.near_ties == 0
