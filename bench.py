@@ -1,0 +1,281 @@
+"""Benchmark of the thinned-attention hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one thin_attn_forward call (thinning + coreset attention) on one
+batch of seeded synthetic input already resident in HBM.  The default
+workload is the 56x56-token ViT token-mixing layer (B=64, S=3136, fp32).
+Prints ONE JSON line with the throughput in effective queries*keys per
+second (the pairs exact attention would evaluate), the per-kernel launch
+times measured with HIP events on the launch stream over the timed region,
+the roofline of the dominant kernel, the exact-attention comparators on the
+same GPU and the float64 CPU oracle's rate on a bounded sample.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "thinned-attention queries·keys/sec & ms/call vs exact attn; HBM GB/s, MFMA %"
+PEAK = {"hbm_GBs": 8000.0, "f32": 157.3, "bf16": 2500.0, "f64": 78.6}   # MI355X: HBM GB/s, dense TFLOP/s
+
+WORKLOADS = {
+    # name: (generator kwargs, causal, H, H_kv, E, D)
+    "unmasked_small": (dict(), False, 1, 1, 64, 64),
+    "vit_token_mixing": (dict(), False, 1, 1, 64, 64),
+    "biggan_self_attention": (dict(), False, 1, 1, 64, 256),
+    "causal_prefill": (dict(), True, 32, 32, 128, 128),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="vit_token_mixing", choices=sorted(WORKLOADS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-exact", action="store_true")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work (what the definition needs, not what a kernel happens to do)
+# ---------------------------------------------------------------------------
+def compress_depth(S, g=0):
+    j = 0
+    while S % (4 ** (j + 1)) == 0 and S // (4 ** (j + 1)) >= 4 ** g:
+        j += 1
+    return j, S // (4 ** j)
+
+
+def express_visible_total(S, n):
+    """Sum over queries t of |visible set| under the Express schedule (per unit)."""
+    total = 0
+    for beta in range((S + n - 1) // n):
+        rows = min(n, S - beta * n)
+        raw = rows * (rows + 1) // 2
+        if beta < 4:
+            total += rows * beta * n + raw
+            continue
+        E = 1
+        while 4 ** (E + 1) <= beta:
+            E += 1
+        m = 4 ** E
+        since = beta - m
+        state = n + (since // m) * n + ((since % m) * 2 * n) // m
+        total += rows * state + raw
+    return total
+
+
+def express_gram_entries(S, n):
+    """Point-Gram entries N(N+1)/2 of every halving (batch and both HALVE passes), per unit."""
+    nblk = S // n
+    halves = 0
+    while 4 ** (halves + 1) <= nblk:
+        halves += 1
+    done = 0
+    e = 1
+    while 4 ** e < nblk:
+        for j in range(3):
+            if 4 ** e * (2 + j) <= nblk:
+                done += 1
+        e += 1
+    tri = lambda N: N * (N + 1) // 2
+    return halves * (tri(4 * n) + tri(2 * n)) + done * tri(2 * n)
+
+
+def work_model(name, B, T, S, H, Hkv, E, D, causal, elt):
+    """Per-forward algorithmic flops / bytes of each kernel label."""
+    units = B * Hkv
+    if not causal:
+        j, s0 = compress_depth(S)
+        n_out = S >> j
+        gram_entries = sum((S // (s0 * 4 ** l)) * (s0 * 2 ** (l + 1)) * (s0 * 2 ** (l + 1) + 1) // 2
+                           for l in range(1, j + 1))
+        keys = n_out
+        pairs_eff = B * H * T * S
+        visible = B * H * T * keys
+        attn_bytes = (B * T * H * (E + D) + units * n_out * (E + D)) * elt
+    else:
+        n_out = 2
+        while n_out * n_out < S:
+            n_out *= 2
+        gram_entries = express_gram_entries(S, n_out)
+        pairs_eff = B * H * T * (T + 1) // 2
+        visible = B * H * express_visible_total(S, n_out)
+        attn_bytes = (B * T * H * E + units * S * (E + D) + B * T * H * D) * elt
+    return dict(
+        n_out=n_out,
+        pairs_eff=pairs_eff,
+        attention=dict(flops=2.0 * visible * (E + D), bytes=attn_bytes),
+        pair_gram=dict(flops=2.0 * (E + D) * gram_entries * units, bytes=None),
+    )
+
+
+# ---------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(every (batch, KV head) unit is independent; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sub_quadratic_attention_amd import inputs
+    from sub_quadratic_attention_amd.binding import ThinAttention
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gen_kw, causal, H, Hkv, E, D = WORKLOADS[args.workload]
+    d = inputs.workload(args.workload, seed=0, **gen_kw)
+    dt = d["dtype"]
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    elt = 4 if dt == "f32" else 2
+    q, k, v = (torch.from_numpy(d[x]).to(tdt).cuda() for x in ("q", "k", "v"))
+    B, T = q.shape[:2]
+    S = k.shape[1]
+    ta = ThinAttention(E, D, H, Hkv, tdt)
+    ws = ta.workspace(B, T, S, causal)
+    out = torch.empty((B, T, H, D), dtype=tdt, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ta.forward(q, k, v, causal=causal, seed=0, workspace=ws, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ta.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    recs = ta.timing_records()
+    ta.set_timing(False)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    wm = work_model(args.workload, B, T, S, H, Hkv, E, D, causal, elt)
+    per_kernel = {}
+    for label, ms in recs:
+        r = per_kernel.setdefault(label, dict(launches=0, total_ms=0.0))
+        r["launches"] += 1
+        r["total_ms"] += ms
+    for label, r in per_kernel.items():
+        r["avg_ms"] = r["total_ms"] / r["launches"]
+        r["ms_per_step"] = r["total_ms"] / args.steps
+        r["launches_per_step"] = r["launches"] / args.steps
+    dom = max(per_kernel, key=lambda l: per_kernel[l]["total_ms"])
+
+    def roof(label):
+        r = per_kernel[label]
+        w = wm.get(label)
+        if not w:
+            return None
+        per_launch_flops = w["flops"] / r["launches_per_step"]
+        peak_key = "f64" if label == "pair_gram" else dt
+        achieved = per_launch_flops / (r["avg_ms"] * 1e-3) / 1e12
+        res = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK[peak_key], "unit": "TFLOP/s",
+               "frac": round(achieved / PEAK[peak_key], 4), "traffic": None, "kernel": label,
+               "work_per_launch_flops": per_launch_flops, "avg_launch_ms": r["avg_ms"],
+               "dtype": peak_key}
+        if w.get("bytes"):
+            gbs = w["bytes"] / r["launches_per_step"] / (r["avg_ms"] * 1e-3) / 1e9
+            res["hbm_GBs"] = round(gbs, 1)
+            res["hbm_frac"] = round(gbs / PEAK["hbm_GBs"], 4)
+        return res
+
+    roofline = roof(dom) if wm.get(dom) else None
+    rooflines = {l: roof(l) for l in per_kernel if wm.get(l)}
+
+    # exact comparators on the same GPU
+    exact = {}
+    if not args.no_exact:
+        qt, kt, vt = (x.permute(0, 2, 1, 3).contiguous() for x in (q, k, v))
+        if Hkv != H:
+            kt = kt.repeat_interleave(H // Hkv, dim=1)
+            vt = vt.repeat_interleave(H // Hkv, dim=1)
+        f = torch.nn.functional.scaled_dot_product_attention
+        for _ in range(2):
+            f(qt, kt, vt, is_causal=causal)
+        torch.cuda.synchronize()
+        n_ex = max(3, min(args.steps, 10))
+        a = time.perf_counter()
+        for _ in range(n_ex):
+            f(qt, kt, vt, is_causal=causal)
+        torch.cuda.synchronize()
+        exact["sdpa_ms"] = (time.perf_counter() - a) * 1e3 / n_ex
+        del qt, kt, vt
+        if not causal:
+            ex = ThinAttention(E, D, H, Hkv, tdt)
+            for _ in range(2):
+                ex.coreset_attention(q, k, v, out=out)
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            for _ in range(n_ex):
+                ex.coreset_attention(q, k, v, out=out)
+            torch.cuda.synchronize()
+            exact["own_exact_kernel_ms"] = (time.perf_counter() - a) * 1e3 / n_ex
+        exact["speedup_vs_sdpa"] = exact["sdpa_ms"] / ms_per_step
+
+    # float64 CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import forward as ofwd
+        if causal:
+            heads = min(H, 2)
+            rows = np.array([[0, t, h] for h in range(heads) for t in range(0, T, 64)])
+            sub = {x: d[x][:, :, :heads] for x in ("q", "k", "v")}
+            pairs = sum(t + 1 for _, t, _ in rows)
+            desc = f"{heads} of {H} heads (thinning in full), {len(rows)} sampled queries"
+            with threadpool_limits(1):
+                a = time.perf_counter()
+                ofwd.forward(sub["q"], sub["k"], sub["v"], causal=True, queries=rows)
+                sec = time.perf_counter() - a
+        else:
+            nb = B if args.workload != "biggan_self_attention" else min(B, 8)
+            sub = {x: d[x][:nb] for x in ("q", "k", "v")}
+            pairs = nb * H * T * S
+            desc = f"{nb} of {B} batch entries, every query (thinning + attention)"
+            with threadpool_limits(1):
+                a = time.perf_counter()
+                ofwd.forward(sub["q"], sub["k"], sub["v"], causal=False)
+                sec = time.perf_counter() - a
+        cpu = {"value": pairs / sec, "unit": "queries·keys/s", "cores": 1, "kind": "oracle",
+               "sample": desc, "seconds": round(sec, 3)}
+
+    line = {
+        "metric": METRIC,
+        "value": wm["pairs_eff"] / (ms_per_step * 1e-3),
+        "unit": "queries·keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "H_kv": Hkv, "T": T, "S": S, "E": E, "D": D,
+                   "causal": causal, "n_out": wm["n_out"], "seed": 0},
+        "kernels": {l: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
+                    for l, r in per_kernel.items()},
+        "roofline": roofline,
+        "rooflines": rooflines,
+        "exact": exact,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * thin_attn.h - C ABI of the MI355X (gfx950) Thinformer / Thinformer Express
+ * attention library.
+ *
+ * What is computed.  For every batch entry b and KV head h (a "unit") the S
+ * key-value pairs x_j = (k_j, v_j) are thinned to a small weighted coreset
+ * by kernel halving under the key-value attention kernel
+ *     kappa((k, v), (k', v')) = exp(s <k, k'>) (<v, v'> + 1),
+ * and every query attends to that coreset:
+ *     out(q) = sum_j w_j exp(s <q, k_j>) v_j / sum_j w_j exp(s <q, k_j>).
+ * Sources: the "Thinformer" README (introduction and "Getting Started":
+ * Thinformer for unmasked attention, Thinformer Express for causal attention,
+ * the (query, key, value, causal) call and its shapes) and "Express Language
+ * Modeling" (sections "The EXPRESS Meta-Procedure" and "Thinformer Express":
+ * the exact / thin / HALVE weighted cache, kernel halving, kappa_att).
+ *
+ * Conventions shared by every call.
+ *  - Tensors are dense, row-major, on the device: query [B, T, H, E],
+ *    key [B, S, H_kv, E], value [B, S, H_kv, D], output [B, T, H, D], all of
+ *    the configured dtype (float32, or bfloat16 as raw 16-bit patterns).
+ *    Query head h reads KV head h / (H / H_kv).
+ *  - The caller owns every device buffer (inputs, outputs, workspace); the
+ *    library owns only the host-side handle.  No call allocates device
+ *    memory.  Work is enqueued asynchronously on `stream` (a hipStream_t,
+ *    NULL = the default stream); device faults surface at the caller's next
+ *    synchronisation.
+ *  - Return value 0 (THIN_OK) on success, a negative THIN_E* code otherwise.
+ *    Argument errors are detected before anything is enqueued; the message
+ *    is kept in the handle (thin_attn_last_error).
+ *  - Same inputs, seed and configuration give bit-identical results.
+ *  - One handle must not be used from two host threads at once.
+ */
+#ifndef THIN_ATTN_H
+#define THIN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum thin_dtype { THIN_F32 = 0, THIN_BF16 = 1 };
+
+enum thin_status {
+  THIN_OK = 0,
+  THIN_EINVAL = -1,   /* bad argument: null pointer, shape, dtype, layout */
+  THIN_ENOTSUP = -2,  /* valid but not built: head dims, schedule range    */
+  THIN_ENOMEM = -3,   /* workspace smaller than thin_attn_workspace_size   */
+  THIN_EHIP = -4      /* a HIP launch reported an error                    */
+};
+
+typedef struct thin_attn_config {
+  int32_t dtype;   /* THIN_F32 or THIN_BF16 (query, key, value, output)              */
+  int32_t E;       /* query / key head dim: 64 or 128                                  */
+  int32_t D;       /* value head dim: 64, 128 or 256 (see thin_attn_create)            */
+  int32_t H;       /* query heads                                                      */
+  int32_t H_kv;    /* key / value heads, H % H_kv == 0                                 */
+  int32_t g;       /* unmasked oversampling: base blocks of size >= 4^g; 4^g >= S
+                      disables thinning (exact attention)                              */
+  int32_t n_out;   /* causal cache size and block length, a power of two >= 2;
+                      0 = smallest power of two p with p*p >= S; n_out >= S disables
+                      thinning (exact causal attention)                                */
+  double delta;    /* kernel-halving failure parameter; <= 0 means 0.5                */
+  float scale;     /* softmax scale s; 0 means 1/sqrt(E)                              */
+  uint32_t flags;  /* reserved, must be 0                                             */
+} thin_attn_config;
+
+typedef struct thin_attn thin_attn_t;
+
+/* Create a handle.  Supported head dims: float32 E=64 with D=64 or 128, E=128
+ * with D=128; bfloat16 E=64 with D=64, 128 or 256, E=128 with D=64 or 128.
+ * Returns THIN_EINVAL for inconsistent values, THIN_ENOTSUP for other dims.
+ * *out is set only on success. */
+int thin_attn_create(const thin_attn_config* cfg, thin_attn_t** out);
+
+/* Destroy a handle (NULL is accepted).  Work already enqueued is unaffected. */
+int thin_attn_destroy(thin_attn_t* h);
+
+/* Last error message of the handle ("" if none); NULL gives the message of
+ * the last failed thin_attn_create.  Valid until the next call on h. */
+const char* thin_attn_last_error(const thin_attn_t* h);
+
+/* Coreset size of one unit.  Unmasked: n_out = S / 2^j with
+ * j = max{ j : 4^j | S and S / 4^j >= 4^g } (each point of weight 2^j).
+ * Causal: the cache size n_out (the configured value or the default rule).
+ * Returns a negative status on invalid arguments. */
+int64_t thin_attn_coreset_size(const thin_attn_t* h, int64_t S, int causal);
+
+/* Entries per unit of the optional coreset arrays of thin_attn_forward:
+ * unmasked n_out; causal 6 * n_out (the cache bound of EXPRESS). */
+int64_t thin_attn_coreset_capacity(const thin_attn_t* h, int64_t S, int causal);
+
+/* Number of kernel-halving decisions per unit (bytes per unit of the
+ * optional decision log). */
+int64_t thin_attn_decision_count(const thin_attn_t* h, int64_t S, int causal);
+
+/* Workspace bytes thin_attn_forward needs for these sizes (0 if invalid). */
+size_t thin_attn_workspace_size(const thin_attn_t* h, int64_t B, int64_t T, int64_t S, int causal);
+
+/*
+ * Thinned attention forward.
+ *
+ * causal = 0 (Thinformer): each unit's S pairs are thinned by a recursive
+ * four-way Compress: base blocks of s0 = S / 4^j consecutive tokens; every
+ * merge concatenates four compressed quarters and applies one kernel halving
+ * (Philox stream: pair, (level << 20) | block, unit, tag 0).  Every query
+ * attends to the unit's n_out points (weight 2^j each).
+ *
+ * causal = 1 (Thinformer Express, requires T == S): tokens are ingested in
+ * blocks of n_out.  While m = 1 blocks enter the cache unchanged (exact
+ * phase).  While m >= 4 every aligned group of r = m / 2 tokens contributes
+ * one Philox-chosen representative of weight r (uniform subsampling); each
+ * 2 n_out representatives are halved to n_out points of weight m that join
+ * the cache (thin phase).  When the cache holds 4 n_out points it is halved
+ * twice back to n_out and m becomes 4 m (HALVE).  A query at token t in block
+ * beta attends to the cache and buffer left by blocks 0 .. beta-1 plus the raw
+ * tokens beta n_out .. t (weight 1).  Supported while m / 2 <= n_out for
+ * every block (t < 2 n_out^2), else THIN_ENOTSUP.
+ *
+ * Arguments: q, k, v, out as described above (out must not alias inputs);
+ * seed keys the Philox4x64-10 stream; optional outputs (NULL to skip):
+ *   coreset_idx [B * H_kv, capacity] int32 token indices, ascending, padded -1;
+ *   coreset_w   [B * H_kv, capacity] float32 weights, padded 0;
+ *   coreset_len [B * H_kv] int32 entries used (causal: final cache, buffer and
+ *               trailing partial block; weights sum to S);
+ *   decisions   [B * H_kv, decision_count] uint8, 1 = first point of the pair
+ *               kept, in the order: unmasked by level, block, pair; causal by
+ *               the chronological order of the halvings.
+ * workspace must hold thin_attn_workspace_size bytes (256-byte aligned).
+ */
+int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* v,
+                      int64_t B, int64_t T, int64_t S, int causal, uint64_t seed,
+                      void* out, int32_t* coreset_idx, float* coreset_w,
+                      int32_t* coreset_len, uint8_t* decisions,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Weighted-coreset attention alone (no thinning): every query of unit
+ * (b, h_kv) attends to the n keys idx[unit * n + j] (token indices into k / v,
+ * each in [0, S)) with weights w[unit * n + j] > 0 (w may be NULL: weight 1).
+ * idx may be NULL with n == S: exact attention over all keys.
+ */
+int thin_attn_coreset_attention(thin_attn_t* h, const void* q, const void* k, const void* v,
+                                int64_t B, int64_t T, int64_t S, const int32_t* idx,
+                                const float* w, int64_t n, void* out, void* stream);
+
+/*
+ * One kernel halving per unit, on a given point list (the base halving of
+ * both paths, exposed on its own).  points [B * H_kv, N] int32 token indices
+ * in [0, S) (N even, 2 <= N <= 2048) name each unit's list x_0 .. x_{N-1};
+ * pairs are (x_2i, x_2i+1).  The Philox stream is (pair, bin, unit, tag).
+ * Outputs: kept [B * H_kv, N/2] the kept token of every pair; decisions
+ * (optional) [B * H_kv, N/2], 1 = first point kept; gram [B * H_kv, N/2, N/2]
+ * float64 receives the pair Gram G_ij = <h_i, h_j>, h_i = kappa(x_2i, .) -
+ * kappa(x_2i+1, .) (lower triangle) and is also the kernel's scratch.
+ */
+int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, int64_t S,
+                      const int32_t* points, int64_t N, uint64_t seed, uint32_t tag, uint64_t bin,
+                      int32_t* kept, uint8_t* decisions, double* gram, void* stream);
+
+/* Philox4x64-10 block for n counters (device arrays, 4 words each) under key
+ * (seed, 0); out receives 4 words per counter.  Exposes the generator the
+ * halving and subsampling steps draw from. */
+int thin_attn_philox(const uint64_t* counters, int64_t n, uint64_t seed, uint64_t* out, void* stream);
+
+/* Launch timing.  thin_attn_set_timing(h, 1) starts a fresh list of records:
+ * from then on every kernel launch of thin_attn_forward is bracketed by two
+ * HIP events on the caller's stream.  thin_attn_timing_count gives the number
+ * of records; thin_attn_timing_read(i) waits for record i, copies its kernel
+ * label (NUL-terminated, at most label_len bytes) and its duration in
+ * milliseconds.  set_timing(h, 0) stops recording and frees the events. */
+int thin_attn_set_timing(thin_attn_t* h, int enable);
+int64_t thin_attn_timing_count(const thin_attn_t* h);
+int thin_attn_timing_read(thin_attn_t* h, int64_t i, char* label, size_t label_len, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* THIN_ATTN_H */

@@ -1,0 +1,118 @@
+// Internal launch interfaces of the thin-attention library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace thin {
+
+// Random-stream tags (fourth counter word).
+enum : uint32_t {
+  kTagCompress = 0,
+  kTagBatch = 1,
+  kTagHalveFirst = 2,
+  kTagHalveSecond = 3,
+  kTagSubsample = 4,
+};
+
+
+// Where the points of one unit (batch entry b, KV head h) live:
+// key [B, S, H_kv, E] and value [B, S, H_kv, D], row-major, fp32 or bf16.
+struct PointSource {
+  const void* k;
+  const void* v;
+  int64_t S;
+  int H_kv;
+  int E;
+  int D;
+  int bf16;
+};
+
+// Pair Gram of many bins at once.  Bin z holds N points whose token indices
+// are idx[z * idx_stride + 0 .. N); its pairs are (2i, 2i+1).  The launch
+// writes G[z][i][j] = <h_i, h_j> for the lower triangle (row-major P x P,
+// P = N / 2), h_i = kappa(x_2i, .) - kappa(x_2i+1, .).
+struct GramLaunch {
+  PointSource src;
+  const int32_t* idx;       // bin (u, j) list at idx + u * idx_unit_stride + j * idx_stride
+  int64_t idx_stride;
+  int64_t idx_unit_stride;
+  int N;
+  int nbins;
+  int bins_per_unit;
+  double scale;
+  double* G;
+};
+
+// Kernel-halving decisions of many bins at once (one workgroup per bin).
+struct SweepLaunch {
+  const double* G;          // from GramLaunch, P x P per bin
+  int N;
+  int nbins;
+  int bins_per_unit;
+  const int32_t* idx_in;    // the bins' point lists (as in GramLaunch)
+  int64_t in_stride;
+  int64_t in_unit_stride;
+  int32_t* idx_out;         // kept token indices, P per bin
+  int64_t out_stride;
+  uint8_t* dec;             // optional decision log (1 = first point kept)
+  int64_t dec_per_unit;
+  int64_t dec_base;         // offset of this launch's first bin inside a unit's log
+  int dec_mode;             // 0: dec_base + bin * P;  1: Express batch order
+  uint64_t seed;
+  uint32_t tag;
+  uint64_t bin_base;        // Philox bin id = bin_base + bin-in-unit
+  double delta;
+};
+
+// Express schedule view used by the causal attention kernel and helpers.
+struct ExpressView {
+  int n;                 // cache size n_out = block size
+  int nblk;              // full blocks in the sequence
+  int n_batches_done;    // batch halvings that complete inside the sequence
+  int n_batches_alloc;   // batches with at least one representative
+  int n_halves;          // HALVEs inside the sequence
+  const int32_t* halve_out;  // [units][n_halves][n]
+  const int32_t* batch_out;  // [units][n_batches_done][n]
+  const int32_t* reps;       // [units][n_batches_alloc][2n]
+};
+
+struct AttnLaunch {
+  const void* q;        // [B, T, H, E]
+  const void* k;        // [B, S, H_kv, E]
+  const void* v;        // [B, S, H_kv, D]
+  void* out;            // [B, T, H, D]
+  int B, T, S, H, H_kv;
+  float scale;          // softmax scale s
+  int causal;           // 0: one index segment per unit; 1: Express view
+  // unmasked coreset (per unit: cs_n entries at unit * cs_stride)
+  const int32_t* cs_idx;   // nullptr => all S keys in order
+  const float* cs_w;       // nullptr => common log-weight cs_lnw
+  int cs_n;
+  int64_t cs_stride;
+  float cs_lnw;
+  ExpressView ev;
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s);
+hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s);
+hipError_t launch_iota(int32_t* out, int64_t units, int64_t n, int64_t stride, hipStream_t s);
+hipError_t launch_express_reps(const ExpressView& ev, int units, uint64_t seed, int32_t* reps, hipStream_t s);
+hipError_t launch_halve_input(const ExpressView& ev, int units, int e, int32_t* halve_in, hipStream_t s);
+hipError_t launch_express_final(const ExpressView& ev, int units, int S, int32_t* idx, float* w,
+                                int32_t* len, int64_t cap, hipStream_t s);
+hipError_t launch_fill_coreset(const int32_t* src, int64_t src_stride, int units, int n, float w,
+                               int32_t* idx, float* wout, int32_t* len, hipStream_t s);
+hipError_t launch_attention(const AttnLaunch& a, int bf16, int E, int D, hipStream_t s);
+hipError_t launch_philox_words(const uint64_t* ctr, int64_t n, uint64_t seed, uint64_t* out, hipStream_t s);
+
+// Host mirror of the Express schedule (r <= n_out range only).
+struct ExpressSchedule {
+  int n, nblk, n_batches_done, n_batches_alloc, n_halves;
+  int64_t decisions;     // per unit
+};
+ExpressSchedule express_schedule(int64_t S, int n);
+bool attention_supported(int bf16, int E, int D);
+
+}  // namespace thin

@@ -1,0 +1,111 @@
+"""End-to-end GPU parity of thin_attn_forward against the float64 oracle (replay protocol)."""
+
+import numpy as np
+import pytest
+import torch
+
+from sub_quadratic_attention_amd import inputs
+from tests.parity import run_and_compare, sample_queries, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sub_quadratic_attention_amd import binding
+    binding.load_library()
+
+
+# ---- unmasked (Thinformer) ------------------------------------------------
+
+def test_unmasked_small_full():
+    """B=1, H=1, S=256, fp32: every output, coreset and decision."""
+    d = inputs.unmasked_small(seed=0)
+    run_and_compare("unmasked S=256", d, False, 1, 1, 64, 64)
+
+
+def test_unmasked_small_unit_scale():
+    d = inputs.unmasked_small(seed=0)
+    run_and_compare("unmasked S=256 scale=1", d, False, 1, 1, 64, 64, scale=1.0)
+
+
+def test_unmasked_disabled_is_exact():
+    d = inputs.unmasked_small(seed=1)
+    s = run_and_compare("unmasked g=4 (no thinning)", d, False, 1, 1, 64, 64, g=4)
+    assert s["decisions"] == 0
+
+
+def test_unmasked_ragged_and_gqa():
+    """S = 4^2 * 13 (base blocks of 13), T ragged, 2 query heads per KV head, bf16."""
+    rng = np.random.default_rng(3)
+    B, T, S, H, Hkv = 2, 83, 208, 4, 2
+    d = dict(q=inputs.bf16_round(rng.standard_normal((B, T, H, 64)) * 0.5),
+             k=inputs.bf16_round(rng.standard_normal((B, S, Hkv, 64)) * 0.5),
+             v=inputs.bf16_round(rng.standard_normal((B, S, Hkv, 128))), dtype="bf16")
+    run_and_compare("unmasked S=208 GQA", d, False, H, Hkv, 64, 128)
+
+
+def test_vit_token_mixing_reduced():
+    """56x56 ViT tokens (S=3136, n_out=392), two batch entries, sampled outputs."""
+    d = inputs.vit_token_mixing(seed=0, B=2)
+    qs = sample_queries(2, 3136, 1, 400, always=[(0, 0, 0), (1, 3135, 0)])
+    run_and_compare("vit B=2", d, False, 1, 1, 64, 64, queries=qs)
+
+
+def test_biggan_reduced():
+    d = inputs.biggan_self_attention(seed=0, B=2)
+    qs = sample_queries(2, 4096, 1, 400, always=[(1, 4095, 0)])
+    run_and_compare("biggan B=2", d, False, 1, 1, 64, 256, queries=qs)
+
+
+# ---- causal (Thinformer Express) -------------------------------------------
+
+def test_causal_three_halves_ragged():
+    """n_out=64: exact phase, three HALVEs, six batches, ragged tail; every output."""
+    d = inputs.causal_prefill(seed=0, H=2, S=4096 + 64 * 3 + 37)
+    run_and_compare("causal S=4325 n=64", d, True, 2, 2, 128, 128, n_out=64)
+
+
+def test_causal_small_cache_tiles_span_blocks():
+    """n_out=16 < query tile: tiles see several blocks' states."""
+    d = inputs.causal_prefill(seed=1, H=1, S=500, E=64, D=64)
+    run_and_compare("causal S=500 n=16", d, True, 1, 1, 64, 64, n_out=16)
+
+
+def test_causal_gqa_fp32():
+    rng = np.random.default_rng(4)
+    S, H, Hkv = 1100, 4, 2
+    d = dict(q=rng.standard_normal((1, S, H, 64)).astype(np.float32),
+             k=rng.standard_normal((1, S, Hkv, 64)).astype(np.float32),
+             v=rng.standard_normal((1, S, Hkv, 64)).astype(np.float32), dtype="f32")
+    run_and_compare("causal fp32 GQA S=1100 n=32", d, True, H, Hkv, 64, 64, n_out=32)
+
+
+def test_causal_disabled_is_exact():
+    d = inputs.causal_prefill(seed=2, H=1, S=300)
+    s = run_and_compare("causal n_out>=S", d, True, 1, 1, 128, 128, n_out=512)
+    assert s["decisions"] == 0
+
+
+def test_causal_prefill_reduced():
+    """The 32k-token prefill shape on two heads, sampled outputs."""
+    d = inputs.causal_prefill(seed=0, H=2, S=32768)
+    qs = sample_queries(1, 32768, 2, 300, always=[(0, 32767, 1), (0, 0, 0), (0, 16384, 0)])
+    run_and_compare("causal S=32768 H=2", d, True, 2, 2, 128, 128, queries=qs)
+
+
+def test_determinism_and_seed():
+    from sub_quadratic_attention_amd.binding import ThinAttention
+    from tests.parity import to_gpu
+    d = inputs.causal_prefill(seed=3, H=2, S=2048)
+    ta = ThinAttention(128, 128, 2, 2, torch.bfloat16, n_out=32)
+    q, k, v = (to_gpu(d[x], "bf16") for x in "qkv")
+    a, ea = ta.forward(q, k, v, causal=True, seed=5, return_coreset=True)
+    b, eb = ta.forward(q, k, v, causal=True, seed=5, return_coreset=True)
+    c, ec = ta.forward(q, k, v, causal=True, seed=6, return_coreset=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(ea["coreset_idx"], eb["coreset_idx"])
+    assert not torch.equal(ea["coreset_idx"], ec["coreset_idx"])
+    say("[determinism] ok")
