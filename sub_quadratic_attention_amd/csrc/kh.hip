@@ -132,12 +132,12 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
     }
   }
 
-  // accumulator element i of lane l is (row 4 (l / 16) + i, column l % 16)
+  // fp64 16x16x4 accumulator element i of lane l is (row l / 16 + 4 i, column l % 16)
   double* G = a.G + static_cast<int64_t>(z) * P * P;
   const int col = 32 * tc + 16 * wc + (lane & 15);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = 32 * tr + 16 * wr + 4 * kq + i;
+    const int row = 32 * tr + 16 * wr + kq + 4 * i;
     const double kee = exp(a.scale * acc[0][0][i]) * (acc[1][0][i] + 1.0);
     const double keo = exp(a.scale * acc[0][1][i]) * (acc[1][1][i] + 1.0);
     const double koe = exp(a.scale * acc[0][2][i]) * (acc[1][2][i] + 1.0);
