@@ -109,63 +109,85 @@ struct Attn {
 
   __device__ __forceinline__ int key_token(const Seg& s, int j) const { return s.idx ? s.idx[s.start + j] : s.start + j; }
 
-  // Stage keys [c0, c0 + nk) of segment s in LDS.
-  __device__ void stage(const Seg& s, int c0, int nk) {
+  // A chunk of 32 keys travels global -> registers -> LDS, so that the next
+  // chunk's loads are in flight while the current one is consumed.
+  static constexpr int KPT = BF16 ? (kKC * E / 8 + 255) / 256 : (kKC * E / 4 + 255) / 256;   // 16-byte pieces / thread
+  static constexpr int VPT = BF16 ? (kKC * D / 8 + 255) / 256 : (kKC * D / 4 + 255) / 256;
+  struct Chunk {
+    uint4 k[KPT];
+    uint4 v[VPT];
+    int pos;
+    float l2;
+  };
+
+  __device__ __forceinline__ void load(const Seg& s, int c0, int nk, Chunk& ch) const {
     const int tid = threadIdx.x;
     const int64_t kv_base = static_cast<int64_t>(b) * a.S;
-    if constexpr (BF16) {
-      constexpr int KP = E / 8, VP = D / 8;
-      for (int p = tid; p < kKC * KP; p += 256) {
-        const int r = p / KP, c8 = p % KP;
-        uint4 val = {0, 0, 0, 0};
-        if (r < nk) {
-          const int64_t row = (kv_base + key_token(s, c0 + r)) * a.H_kv + hk;
-          val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + row * E + c8 * 8);
-        }
-        *reinterpret_cast<uint4*>(&sm.k[r][c8 * 8]) = val;
-      }
-      for (int p = tid; p < kKC * VP; p += 256) {
-        const int r = p / VP, c8 = p % VP;
-        uint4 val = {0, 0, 0, 0};
-        if (r < nk) {
-          const int64_t row = (kv_base + key_token(s, c0 + r)) * a.H_kv + hk;
-          val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + row * D + c8 * 8);
-        }
-        const int slot = bf16_slot(r);
-        const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+    constexpr int KP = BF16 ? E / 8 : E / 4;
+    constexpr int VP = BF16 ? D / 8 : D / 4;
+    constexpr int ELT = BF16 ? 2 : 4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sm.vt[c8 * 8 + 2 * j][slot] = static_cast<uint16_t>(wv[j] & 0xffffu);
-          sm.vt[c8 * 8 + 2 * j + 1][slot] = static_cast<uint16_t>(wv[j] >> 16);
-        }
+    for (int j = 0; j < KPT; ++j) {
+      const int p = tid + 256 * j;
+      const int r = p / KP, c = p % KP;
+      ch.k[j] = uint4{0, 0, 0, 0};
+      if (p < kKC * KP && r < nk) {
+        const int64_t row = (kv_base + key_token(s, c0 + r)) * a.H_kv + hk;
+        ch.k[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k) + (row * E + c * (16 / ELT)) * ELT);
       }
-    } else {
-      constexpr int KP = E / 4, VP = D / 4;
-      for (int p = tid; p < kKC * KP; p += 256) {
-        const int r = p / KP, c4 = p % KP;
-        float4 val = {0.f, 0.f, 0.f, 0.f};
-        if (r < nk) {
-          const int64_t row = (kv_base + key_token(s, c0 + r)) * a.H_kv + hk;
-          val = *reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + row * E + c4 * 4);
-        }
-        *reinterpret_cast<float4*>(&sm.k[r][c4 * 4]) = val;
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int p = tid + 256 * j;
+      const int r = p / VP, c = p % VP;
+      ch.v[j] = uint4{0, 0, 0, 0};
+      if (p < kKC * VP && r < nk) {
+        const int64_t row = (kv_base + key_token(s, c0 + r)) * a.H_kv + hk;
+        ch.v[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) + (row * D + c * (16 / ELT)) * ELT);
       }
-      for (int p = tid; p < kKC * VP; p += 256) {
-        const int r = p / VP, c4 = p % VP;
-        float4 val = {0.f, 0.f, 0.f, 0.f};
-        if (r < nk) {
-          const int64_t row = (kv_base + key_token(s, c0 + r)) * a.H_kv + hk;
-          val = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + row * D + c4 * 4);
+    }
+    ch.pos = 0x7fffffff;
+    ch.l2 = -INFINITY;
+    if (tid < kKC && tid < nk) {
+      ch.pos = key_token(s, c0 + tid);
+      ch.l2 = s.w ? log2f(s.w[s.start + c0 + tid]) : s.lnw2;
+    }
+  }
+
+  __device__ __forceinline__ void store(const Chunk& ch) {
+    const int tid = threadIdx.x;
+    constexpr int KP = BF16 ? E / 8 : E / 4;
+    constexpr int VP = BF16 ? D / 8 : D / 4;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int p = tid + 256 * j;
+      if (p >= kKC * KP) break;
+      const int r = p / KP, c = p % KP;
+      if constexpr (BF16)
+        *reinterpret_cast<uint4*>(&sm.k[r][c * 8]) = ch.k[j];
+      else
+        *reinterpret_cast<uint4*>(&sm.k[r][c * 4]) = ch.k[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int p = tid + 256 * j;
+      if (p >= kKC * VP) break;
+      const int r = p / VP, c = p % VP;
+      if constexpr (BF16) {
+        const int slot = bf16_slot(r);
+        const uint32_t wv[4] = {ch.v[j].x, ch.v[j].y, ch.v[j].z, ch.v[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sm.vt[c * 8 + 2 * q][slot] = static_cast<uint16_t>(wv[q] & 0xffffu);
+          sm.vt[c * 8 + 2 * q + 1][slot] = static_cast<uint16_t>(wv[q] >> 16);
         }
-        *reinterpret_cast<float4*>(&sm.v[r][c4 * 4]) = val;
+      } else {
+        *reinterpret_cast<uint4*>(&sm.v[r][c * 4]) = ch.v[j];
       }
     }
     if (tid < kKC) {
-      const bool valid = tid < nk;
-      sm.pos[tid] = valid ? key_token(s, c0 + tid) : 0x7fffffff;
-      float l2 = -INFINITY;
-      if (valid) l2 = s.w ? log2f(s.w[s.start + c0 + tid]) : s.lnw2;
-      sm.lnw2[tid] = l2;
+      sm.pos[tid] = ch.pos;
+      sm.lnw2[tid] = ch.l2;
     }
   }
 
@@ -247,11 +269,14 @@ struct Attn {
     }
   }
 
-  __device__ void run_segment(const Seg& s, bool row_ok) {
+  __device__ void run_segment(const Seg s, bool row_ok) {
+    if (s.count <= 0) return;
+    Chunk ch;
+    load(s, 0, min(kKC, s.count), ch);
     for (int c0 = 0; c0 < s.count; c0 += kKC) {
-      const int nk = min(kKC, s.count - c0);
-      stage(s, c0, nk);
+      store(ch);
       __syncthreads();
+      if (c0 + kKC < s.count) load(s, c0 + kKC, min(kKC, s.count - c0 - kKC), ch);
       consume(s, row_ok);
       __syncthreads();
     }
@@ -277,14 +302,15 @@ struct Attn {
   }
 };
 
-// State of the Express cache after beta blocks, as index segments.
-__device__ int express_segments(const ExpressView& ev, int unit, int beta, int S, int key_end, Seg* segs) {
-  int n = 0;
-  const int bn = beta * ev.n;
-  if (beta < 4) {
-    // exact phase: everything before the block plus the block itself, weight 1
-    segs[n++] = Seg{nullptr, 0, min(key_end, S), 0.f, nullptr, 1};
-    return n;
+// Attend to the Express state after beta blocks, then to the raw causal block.
+// Segments: HALVE output (weight m), completed batches of the epoch (m),
+// representatives of the current batch (m / 2), raw tokens (1, causal).
+template <class A>
+__device__ void express_block(A& at, const ExpressView& ev, int beta, int S, int key_end, bool row_ok) {
+  const int unit = at.unit;
+  if (beta < 4) {   // exact phase: every earlier token and the block itself, weight 1
+    at.run_segment(Seg{nullptr, 0, min(key_end, S), 0.f, nullptr, 1}, row_ok);
+    return;
   }
   int E = 1;
   while ((1LL << (2 * (E + 1))) <= beta) ++E;
@@ -293,16 +319,20 @@ __device__ int express_segments(const ExpressView& ev, int unit, int beta, int S
   const int nbc = since / m;
   const int rem = since % m;
   const float lm = static_cast<float>(2 * E);        // log2 m
-  segs[n++] = Seg{ev.halve_out + (static_cast<int64_t>(unit) * ev.n_halves + (E - 1)) * ev.n, 0, ev.n, lm, nullptr, 0};
+  at.run_segment(Seg{ev.halve_out + (static_cast<int64_t>(unit) * ev.n_halves + (E - 1)) * ev.n, 0, ev.n, lm,
+                     nullptr, 0},
+                 row_ok);
   if (nbc > 0)
-    segs[n++] = Seg{ev.batch_out + (static_cast<int64_t>(unit) * ev.n_batches_done + 3 * (E - 1)) * ev.n, 0,
-                    nbc * ev.n, lm, nullptr, 0};
+    at.run_segment(Seg{ev.batch_out + (static_cast<int64_t>(unit) * ev.n_batches_done + 3 * (E - 1)) * ev.n, 0,
+                       nbc * ev.n, lm, nullptr, 0},
+                   row_ok);
   const int n_rep = static_cast<int>((static_cast<int64_t>(rem) * 2 * ev.n) / m);
   if (n_rep > 0)
-    segs[n++] = Seg{ev.reps + (static_cast<int64_t>(unit) * ev.n_batches_alloc + 3 * (E - 1) + nbc) * 2 * ev.n, 0,
-                    n_rep, lm - 1.0f, nullptr, 0};
-  segs[n++] = Seg{nullptr, bn, min(key_end, S) - bn, 0.f, nullptr, 1};
-  return n;
+    at.run_segment(Seg{ev.reps + (static_cast<int64_t>(unit) * ev.n_batches_alloc + 3 * (E - 1) + nbc) * 2 * ev.n, 0,
+                       n_rep, lm - 1.0f, nullptr, 0},
+                   row_ok);
+  const int bn = beta * ev.n;
+  at.run_segment(Seg{nullptr, bn, min(key_end, S) - bn, 0.f, nullptr, 1}, row_ok);
 }
 
 template <bool BF16, int E, int D>
@@ -314,24 +344,19 @@ __global__ __launch_bounds__(256) void seg_attention_kernel(AttnLaunch a) {
     const int bh = blockIdx.y;
     const int b = bh / a.H, hk = (bh % a.H) / (a.H / a.H_kv);
     const int unit = b * a.H_kv + hk;
-    Seg s;
-    if (a.cs_idx) {
-      s = Seg{a.cs_idx + unit * a.cs_stride, 0, a.cs_n, a.cs_lnw * kLog2e,
-              a.cs_w ? a.cs_w + unit * a.cs_stride : nullptr, 0};
-    } else {
-      s = Seg{nullptr, 0, a.S, a.cs_lnw * kLog2e, nullptr, 0};
-    }
-    at.run_segment(s, true);
+    if (a.cs_idx)
+      at.run_segment(Seg{a.cs_idx + unit * a.cs_stride, 0, a.cs_n, a.cs_lnw * kLog2e,
+                         a.cs_w ? a.cs_w + unit * a.cs_stride : nullptr, 0},
+                     true);
+    else
+      at.run_segment(Seg{nullptr, 0, a.S, a.cs_lnw * kLog2e, nullptr, 0}, true);
   } else {
     const int n = a.ev.n;
     const int q_last = min(q0 + kQT - 1, a.T - 1);
     const int beta_lo = q0 / n, beta_hi = q_last / n;
     for (int beta = beta_lo; beta <= beta_hi; ++beta) {
-      Seg segs[4];
       const int key_end = min(q_last + 1, (beta + 1) * n);
-      const int ns = express_segments(a.ev, at.unit, beta, a.S, key_end, segs);
-      const bool row_ok = (at.qr / n) == beta;
-      for (int i = 0; i < ns; ++i) at.run_segment(segs[i], row_ok);
+      express_block(at, a.ev, beta, a.S, key_end, (at.qr / n) == beta);
     }
   }
   at.store();

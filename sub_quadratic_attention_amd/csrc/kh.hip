@@ -51,24 +51,34 @@ __device__ __forceinline__ void load4(const void* base, int64_t off, double out[
   }
 }
 
+// Tiles.  Bins get the lower-triangular 32 x 32 pair tiles of their own
+// P x P Gram, except bins with P dividing 32 (P < 32), which are packed: a unit's bins
+// are consecutive in its point list, so one diagonal tile of 32 pairs covers
+// 32 / P whole bins and only entries of equal bin are kept.  Blocks lying
+// entirely above the diagonal are skipped (the walk reads j <= i only).
 template <bool BF16>
 __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
-  // blockIdx.x = bin * tiles_per_bin + lower-triangular tile (tr >= tc)
   const int P = a.N / 2;
-  const int nt = (P + 31) / 32;
-  const int tiles = nt * (nt + 1) / 2;
-  const int z = static_cast<int>(blockIdx.x / tiles);
-  const int t = static_cast<int>(blockIdx.x % tiles);
-  int tr = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
-  while (tr * (tr + 1) / 2 > t) --tr;
-  while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
-  const int tc = t - tr * (tr + 1) / 2;
-
-  const int unit = z / a.bins_per_unit;
+  const bool packed = P < 32 && (32 % P) == 0;   // whole bins per tile
+  int unit, tr, tc, z;
+  if (packed) {
+    const int tiles = (a.bins_per_unit * P + 31) / 32;
+    unit = static_cast<int>(blockIdx.x / tiles);
+    tr = tc = static_cast<int>(blockIdx.x % tiles);
+    z = -1;
+  } else {
+    const int nt = (P + 31) / 32;
+    const int tiles = nt * (nt + 1) / 2;
+    z = static_cast<int>(blockIdx.x / tiles);
+    const int t = static_cast<int>(blockIdx.x % tiles);
+    tr = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
+    while (tr * (tr + 1) / 2 > t) --tr;
+    while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
+    tc = t - tr * (tr + 1) / 2;
+    unit = z / a.bins_per_unit;
+  }
   const int b = unit / a.src.H_kv;
   const int h = unit % a.src.H_kv;
-  const int32_t* idx = a.idx + static_cast<int64_t>(unit) * a.idx_unit_stride +
-                       static_cast<int64_t>(z % a.bins_per_unit) * a.idx_stride;
 
   __shared__ double rowF[64][kPad];
   __shared__ double colF[64][kPad];
@@ -81,12 +91,29 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
   // loader role: point lp of the row / column sets, features lf .. lf+3
   const int lp = tid >> 2;
   const int lf = (tid & 3) * 4;
-  const int rp = 64 * tr + lp;
-  const int cp = 64 * tc + lp;
-  const bool rvalid = rp < a.N;
-  const bool cvalid = cp < a.N;
-  const int64_t rrow = rvalid ? (static_cast<int64_t>(b) * a.src.S + idx[rp]) * a.src.H_kv + h : 0;
-  const int64_t crow = cvalid ? (static_cast<int64_t>(b) * a.src.S + idx[cp]) * a.src.H_kv + h : 0;
+  const int64_t ubase = static_cast<int64_t>(unit) * a.idx_unit_stride;
+  auto token = [&](int q) -> int {   // q-th point of the tile's range; -1 if none
+    if (packed) {
+      const int bin = q / a.N;
+      if (bin >= a.bins_per_unit) return -1;
+      return a.idx[ubase + static_cast<int64_t>(bin) * a.idx_stride + q % a.N];
+    }
+    if (q >= a.N) return -1;
+    return a.idx[ubase + static_cast<int64_t>(z % a.bins_per_unit) * a.idx_stride + q];
+  };
+  const int rtok = token(64 * tr + lp);
+  const int ctok = token(64 * tc + lp);
+  const bool rvalid = rtok >= 0;
+  const bool cvalid = ctok >= 0;
+  const int64_t rrow = rvalid ? (static_cast<int64_t>(b) * a.src.S + rtok) * a.src.H_kv + h : 0;
+  const int64_t crow = cvalid ? (static_cast<int64_t>(b) * a.src.S + ctok) * a.src.H_kv + h : 0;
+
+  // does this wave's 16 x 16 pair block hold anything the walk reads?
+  const int r0 = 32 * tr + 16 * wr;    // first pair row of the block
+  const int c0 = 32 * tc + 16 * wc;    // first pair column
+  bool active = r0 + 15 >= c0;          // not entirely above the diagonal
+  if (packed && active && wr != wc) active = (r0 % P) != 0;   // a bin straddles the two halves
+  if (!packed && (r0 >= P || c0 >= P)) active = false;
 
   f64x4_t acc[2][4];
 #pragma unroll
@@ -116,33 +143,42 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
         if (rvalid) load4<BF16>(base, rrow * F + f0 + kChunk + lf, nr);
         if (cvalid) load4<BF16>(base, crow * F + f0 + kChunk + lf, nc);
       }
+      if (active) {
 #pragma unroll
-      for (int kk = 0; kk < kChunk / 4; ++kk) {
-        const int kf = kk * 4 + kq;
-        const double Ae = rowF[2 * pr][kf];
-        const double Ao = rowF[2 * pr + 1][kf];
-        const double Be = colF[2 * pc][kf];
-        const double Bo = colF[2 * pc + 1][kf];
-        acc[pass][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ae, Be, acc[pass][0], 0, 0, 0);
-        acc[pass][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ae, Bo, acc[pass][1], 0, 0, 0);
-        acc[pass][2] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ao, Be, acc[pass][2], 0, 0, 0);
-        acc[pass][3] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ao, Bo, acc[pass][3], 0, 0, 0);
+        for (int kk = 0; kk < kChunk / 4; ++kk) {
+          const int kf = kk * 4 + kq;
+          const double Ae = rowF[2 * pr][kf];
+          const double Ao = rowF[2 * pr + 1][kf];
+          const double Be = colF[2 * pc][kf];
+          const double Bo = colF[2 * pc + 1][kf];
+          acc[pass][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ae, Be, acc[pass][0], 0, 0, 0);
+          acc[pass][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ae, Bo, acc[pass][1], 0, 0, 0);
+          acc[pass][2] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ao, Be, acc[pass][2], 0, 0, 0);
+          acc[pass][3] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ao, Bo, acc[pass][3], 0, 0, 0);
+        }
       }
       __syncthreads();
     }
   }
+  if (!active) return;
 
   // fp64 16x16x4 accumulator element i of lane l is (row l / 16 + 4 i, column l % 16)
-  double* G = a.G + static_cast<int64_t>(z) * P * P;
-  const int col = 32 * tc + 16 * wc + (lane & 15);
+  const int col = c0 + (lane & 15);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = 32 * tr + 16 * wr + kq + 4 * i;
+    const int row = r0 + kq + 4 * i;
     const double kee = exp(a.scale * acc[0][0][i]) * (acc[1][0][i] + 1.0);
     const double keo = exp(a.scale * acc[0][1][i]) * (acc[1][1][i] + 1.0);
     const double koe = exp(a.scale * acc[0][2][i]) * (acc[1][2][i] + 1.0);
     const double koo = exp(a.scale * acc[0][3][i]) * (acc[1][3][i] + 1.0);
-    if (row < P && col < P) G[static_cast<int64_t>(row) * P + col] = (kee - keo) - (koe - koo);
+    const double gv = (kee - keo) - (koe - koo);
+    if (packed) {
+      const int bin = row / P;
+      if (bin == col / P && bin < a.bins_per_unit && col <= row)
+        a.G[(static_cast<int64_t>(unit) * a.bins_per_unit + bin) * P * P + (row % P) * P + (col % P)] = gv;
+    } else if (row < P && col < P) {
+      a.G[static_cast<int64_t>(z) * P * P + static_cast<int64_t>(row) * P + col] = gv;
+    }
   }
 }
 
@@ -153,11 +189,23 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
 // c_N = sqrt(2 ln(2N / delta)), and the first point is kept iff
 // u_i < (1 - alpha_i / a_i) / 2, i.e. iff alpha_i < a_i (1 - 2 u_i)
 // (a_i = 0: iff u_i < 1/2).  a_i and sigma_i depend only on the b's, so the
-// thresholds thr_i = a_i (1 - 2 u_i) are computed first; alpha_i =
-// sum_{j<i} eta_j G_ij is then swept panel by panel: the contribution of
-// earlier panels is a matrix-vector product spread over the workgroup, and
-// the 64 decisions inside a panel are taken by one wave, lane i holding
-// alpha_i and its row of the panel's G block, one ballot per decision.
+// thresholds thr_i = a_i (1 - 2 u_i) can be computed ahead of the walk.
+//
+// The walk runs in panels of 64 pairs.  alpha_i = sum_{j<i} eta_j G_ij is
+// kept for every pair in LDS.  For panel p:
+//   wave 0   takes the 64 decisions: lane l holds alpha of pair p0+l and its
+//            row of the panel's diagonal block; one ballot per decision;
+//   wave 1-2 stage the next panel's diagonal block (double buffered);
+//   wave 3   runs the sigma recursion for the next panel's thresholds;
+// then all waves add the panel's contribution eta_p G[:, p] to the alpha of
+// every later pair (independent row loads, many in flight).
+//
+// sigma recursion without a division: with sigma = sqrt(sigma^2),
+//   if b sigma c >= b^2 (a = b sigma c):
+//     sigma^2 += max(0, b^2 (1 + 1/c^2) - 2 sigma b / c)
+//   else (a = b^2):  sigma^2 = max(sigma^2, b^2)
+// which is the published update b^2 max(0, 1 + (b^2 - 2a) sigma^2 / a^2)
+// written out for the two cases of a.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t dec_offset(const SweepLaunch& a, int lb, int P) {
   if (a.dec_mode == 1) {   // Express batch k = lb: HALVE 0, then (3 batches, HALVE) per epoch
@@ -167,6 +215,30 @@ __device__ __forceinline__ int64_t dec_offset(const SweepLaunch& a, int lb, int 
   return a.dec_base + static_cast<int64_t>(lb) * P;
 }
 
+struct SigmaState {
+  double s2;
+};
+
+// thresholds of pairs [i0, i1) (s_thr holds u on entry)
+__device__ __forceinline__ void sigma_chain(SigmaState& st, const double* s_b2, double* s_thr, int i0, int i1,
+                                            double c, double k1, double k2) {
+  double s2 = st.s2;
+  for (int i = i0; i < i1; ++i) {
+    const double b2 = s_b2[i];
+    const double bb = sqrt(b2);
+    const double sg = sqrt(s2);
+    const double bsc = bb * sg * c;
+    const double aa = fmax(bsc, b2);
+    const double u = s_thr[i];
+    s_thr[i] = aa > 0.0 ? aa * (1.0 - 2.0 * u) : (u < 0.5 ? INFINITY : -INFINITY);
+    if (bsc >= b2)
+      s2 = s2 + fmax(0.0, b2 * k1 - k2 * sg * bb);
+    else
+      s2 = fmax(s2, b2);
+  }
+  st.s2 = s2;
+}
+
 __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
   extern __shared__ double smem[];
   const int z = blockIdx.x;
@@ -174,62 +246,49 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
   const int unit = z / a.bins_per_unit;
   const int lb = z % a.bins_per_unit;
   const double* G = a.G + static_cast<int64_t>(z) * P * P;
-  double* s_thr = smem;               // P
+  double* s_thr = smem;               // P   (u, then thresholds)
   double* s_b2 = s_thr + P;           // P
-  double* s_eta = s_b2 + P;           // P
-  double* s_alpha = s_eta + P;        // 64
-  double* s_G = s_alpha + 64;         // 64 x 65
+  double* s_alpha = s_b2 + P;         // P
+  double* s_eta = s_alpha + P;        // P   (+1 / -1)
+  double* s_G = s_eta + P;            // 2 x 64 x 65
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const double c = sqrt(2.0 * log(2.0 * a.N / a.delta));
+  const double k1 = 1.0 + 1.0 / (c * c);
+  const double k2 = 2.0 / c;
 
   for (int i = tid; i < P; i += 256) {
     s_thr[i] = philox_uniform(static_cast<uint64_t>(i), a.bin_base + lb, static_cast<uint64_t>(unit), a.tag,
                               a.seed);
     s_b2[i] = fmax(G[static_cast<int64_t>(i) * P + i], 0.0);
+    s_alpha[i] = 0.0;
   }
   __syncthreads();
-  if (tid == 0) {
-    const double c = sqrt(2.0 * log(2.0 * a.N / a.delta));
-    double s2 = 0.0;
-    for (int i = 0; i < P; ++i) {
-      const double b2 = s_b2[i];
-      const double bb = sqrt(b2);
-      const double aa = fmax(bb * sqrt(s2) * c, b2);
-      const double u = s_thr[i];
-      s_thr[i] = aa > 0.0 ? aa * (1.0 - 2.0 * u) : (u < 0.5 ? INFINITY : -INFINITY);
-      if (aa > 0.0) s2 = s2 + b2 * fmax(0.0, 1.0 + (b2 - 2.0 * aa) * s2 / (aa * aa));
-    }
+  SigmaState sig{0.0};
+  const int np = (P + 63) / 64;
+  // panel 0: thresholds and diagonal block
+  if (tid == 192) sigma_chain(sig, s_b2, s_thr, 0, min(64, P), c, k1, k2);
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int r = e >> 6, cc = e & 63;
+    s_G[r * 65 + cc] = (r < P && cc <= r) ? G[static_cast<int64_t>(r) * P + cc] : 0.0;
   }
   __syncthreads();
 
   const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
   int32_t* out = a.idx_out + static_cast<int64_t>(z) * a.out_stride;
-  for (int p0 = 0; p0 < P; p0 += 64) {
+  uint8_t* dec = a.dec ? a.dec + static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) : nullptr;
+  for (int p = 0; p < np; ++p) {
+    const int p0 = 64 * p;
     const int rows = min(64, P - p0);
-    // contribution of the decided panels
-    for (int r = w * 16; r < w * 16 + 16; ++r) {
-      double part = 0.0;
-      if (r < rows) {
-        const double* g = G + static_cast<int64_t>(p0 + r) * P;
-        for (int j = lane; j < p0; j += 64) part += s_eta[j] * g[j];
-      }
-      part = wave_sum(part);
-      if (lane == 0) s_alpha[r] = part;
-    }
-    // this panel's block (lower triangle)
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int r = e >> 6, c = e & 63;
-      s_G[r * 65 + c] = (r < rows && c <= r) ? G[static_cast<int64_t>(p0 + r) * P + p0 + c] : 0.0;
-    }
-    __syncthreads();
+    const double* blk = s_G + (p & 1) * 64 * 65;
     if (w == 0) {
-      double alpha = s_alpha[lane];
+      double alpha = s_alpha[p0 + lane < P ? p0 + lane : 0];
       const double thr = lane < rows ? s_thr[p0 + lane] : 0.0;
       double g[64];
 #pragma unroll
-      for (int c = 0; c < 64; ++c) g[c] = s_G[lane * 65 + c];
+      for (int cc = 0; cc < 64; ++cc) g[cc] = blk[lane * 65 + cc];
       uint64_t bits = 0;
 #pragma unroll
       for (int j = 0; j < 64; ++j) {
@@ -243,10 +302,34 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
         const bool first = (bits >> lane) & 1ull;
         s_eta[i] = first ? 1.0 : -1.0;
         out[i] = in[2 * i + (first ? 0 : 1)];
-        if (a.dec) a.dec[static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) + i] = first ? 1 : 0;
+        if (dec) dec[i] = first ? 1 : 0;
+      }
+    } else if (w == 3) {
+      if (lane == 0 && p + 1 < np) sigma_chain(sig, s_b2, s_thr, p0 + 64, min(p0 + 128, P), c, k1, k2);
+    } else if (p + 1 < np) {
+      // waves 1 and 2 stage the next diagonal block
+      double* nb = s_G + ((p + 1) & 1) * 64 * 65;
+      const int q0 = p0 + 64;
+      for (int e = tid - 64; e < 64 * 64; e += 128) {
+        const int r = e >> 6, cc = e & 63;
+        nb[r * 65 + cc] = (q0 + r < P && cc <= r) ? G[static_cast<int64_t>(q0 + r) * P + q0 + cc] : 0.0;
       }
     }
     __syncthreads();
+    // the panel's contribution to every later pair
+    if (p + 1 < np) {
+      for (int i = p0 + 64 + tid; i < P; i += 256) {
+        const double* row = G + static_cast<int64_t>(i) * P + p0;
+        double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll 16
+        for (int j = 0; j < 64; j += 2) {   // full panel: rows == 64 here
+          acc0 += s_eta[p0 + j] * row[j];
+          acc1 += s_eta[p0 + j + 1] * row[j + 1];
+        }
+        s_alpha[i] += acc0 + acc1;
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -394,8 +477,15 @@ inline unsigned grid1d(int64_t n, int block) { return static_cast<unsigned>((n +
 
 hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s) {
   const int P = a.N / 2;
-  const int nt = (P + 31) / 32;
-  dim3 grid(static_cast<unsigned>(static_cast<int64_t>(nt) * (nt + 1) / 2 * a.nbins));
+  int64_t blocks;
+  if (P < 32 && (32 % P) == 0) {
+    blocks = static_cast<int64_t>(a.nbins / a.bins_per_unit) * ((a.bins_per_unit * P + 31) / 32);
+  } else {
+    const int nt = (P + 31) / 32;
+    blocks = static_cast<int64_t>(nt) * (nt + 1) / 2 * a.nbins;
+  }
+  if (blocks == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(blocks));
   if (a.src.bf16)
     hipLaunchKernelGGL(pair_gram_kernel<true>, grid, dim3(256), 0, s, a);
   else
@@ -403,10 +493,16 @@ hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t sweep_lds_bytes(int N) { return (3 * static_cast<size_t>(N / 2) + 64 + 64 * 65) * sizeof(double); }
+size_t sweep_lds_bytes(int N) { return (4 * static_cast<size_t>(N / 2) + 2 * 64 * 65) * sizeof(double); }
 
 hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s) {
-  hipLaunchKernelGGL(halving_sweep_kernel, dim3(a.nbins), dim3(256), sweep_lds_bytes(a.N), s, a);
+  const size_t lds = sweep_lds_bytes(a.N);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(halving_sweep_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(halving_sweep_kernel, dim3(a.nbins), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
