@@ -30,6 +30,7 @@ WORKLOADS = {
     "vit_token_mixing": (dict(), False, 1, 1, 64, 64),
     "biggan_self_attention": (dict(), False, 1, 1, 64, 256),
     "causal_prefill": (dict(), True, 32, 32, 128, 128),
+    "kv_decode": (dict(), True, 32, 8, 128, 128),
 }
 
 
@@ -119,6 +120,130 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt):
 
 
 # ---------------------------------------------------------------------------
+def decode_main(args):
+    """KV-cache thinning + decode: one step = ingest the 131k-token history into a
+    fresh Express state (thinned once), then 1024 one-token decode steps."""
+    import torch
+    from sub_quadratic_attention_amd import inputs
+    from sub_quadratic_attention_amd.binding import KVState, ThinAttention
+
+    _, _, H, Hkv, E, D = WORKLOADS["kv_decode"]
+    d = inputs.kv_decode(seed=0)
+    kh, vh = (torch.from_numpy(d[x]).to(torch.bfloat16).cuda() for x in ("k_hist", "v_hist"))
+    qs, ks, vs = (torch.from_numpy(d[x]).to(torch.bfloat16).cuda() for x in ("q_steps", "k_steps", "v_steps"))
+    B, S0 = kh.shape[:2]
+    steps_dec = qs.shape[1]
+    n_out = 2
+    while n_out * n_out < S0:
+        n_out *= 2
+    ta = ThinAttention(E, D, H, Hkv, torch.bfloat16)
+    st = KVState(ta, B, n_out)
+    st._workspace(S0)
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def one_pass(timing=False):
+        nonlocal st
+        st = KVState(ta, B, n_out)
+        st._ws = ws
+        st.append(kh, vh, stream=stream)
+        for i in range(steps_dec):
+            st.decode(qs[:, i], ks[:, i], vs[:, i], out=out, stream=stream)
+
+    ws = torch.empty(max(int(ta.lib.thin_attn_kv_workspace_size(st.kv, S0)), 256), dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    ta.set_timing(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_pass()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    recs = ta.timing_records()
+    ta.set_timing(False)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_kernel = {}
+    for label, ms in recs:
+        r = per_kernel.setdefault(label, dict(launches=0, total_ms=0.0))
+        r["launches"] += 1
+        r["total_ms"] += ms
+    for r in per_kernel.values():
+        r["avg_ms"] = r["total_ms"] / r["launches"]
+        r["ms_per_step"] = r["total_ms"] / args.steps
+        r["launches_per_step"] = r["launches"] / args.steps
+    # decode-only timing of the 1024 steps (state ingested once, outside the region)
+    st = KVState(ta, B, n_out)
+    st._ws = ws
+    st.append(kh, vh, stream=stream)
+    torch.cuda.synchronize()
+    a = time.perf_counter()
+    for i in range(steps_dec):
+        st.decode(qs[:, i], ks[:, i], vs[:, i], out=out, stream=stream)
+    torch.cuda.synchronize()
+    decode_us = (time.perf_counter() - a) * 1e6 / steps_dec
+    pairs = sum(H * (S0 + i + 1) for i in range(steps_dec))
+    # visible rows per step (algorithmic bytes of the decode attention): cache + buffer + raw block
+    vis = 0
+    tmp = KVState(ta, B, n_out)
+    tmp._ws = ws
+    tmp.append(kh, vh, stream=stream)
+    torch.cuda.synchronize()
+    _, _, ln = tmp.coreset()
+    vis_rows = int(ln.sum().item())
+    dec_bytes = vis_rows * (E + D) * 2 + B * H * (E + D) * 2
+    kd = per_kernel.get("kv_decode", {})
+    roof = None
+    if kd:
+        gbs = dec_bytes / (kd["avg_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK["hbm_GBs"], "unit": "GB/s",
+                "frac": round(gbs / PEAK["hbm_GBs"], 4), "traffic": None, "kernel": "kv_decode",
+                "work_per_launch_bytes": dec_bytes, "avg_launch_ms": kd["avg_ms"]}
+    exact = {}
+    if not args.no_exact:
+        # exact decode over the full cache (GQA by repeating KV heads), one step
+        kt = torch.cat([kh, ks], dim=1).permute(0, 2, 1, 3).repeat_interleave(H // Hkv, dim=1).contiguous()
+        vt = torch.cat([vh, vs], dim=1).permute(0, 2, 1, 3).repeat_interleave(H // Hkv, dim=1).contiguous()
+        f = torch.nn.functional.scaled_dot_product_attention
+        qq = qs[:, -1].reshape(B, H, 1, E)
+        for _ in range(3):
+            f(qq, kt, vt)
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        for _ in range(50):
+            f(qq, kt, vt)
+        torch.cuda.synchronize()
+        exact["sdpa_decode_step_us"] = (time.perf_counter() - a) * 1e6 / 50
+        exact["decode_speedup_vs_sdpa"] = exact["sdpa_decode_step_us"] / decode_us
+        del kt, vt
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import forward as ofwd
+        sub = dict(k_hist=d["k_hist"][:, :, :1], v_hist=d["v_hist"][:, :, :1], q_steps=d["q_steps"][:, :256, :H // Hkv],
+                   k_steps=d["k_steps"][:, :256, :1], v_steps=d["v_steps"][:, :256, :1])
+        with threadpool_limits(1):
+            a = time.perf_counter()
+            ofwd.decode(sub["k_hist"], sub["v_hist"], sub["q_steps"], sub["k_steps"], sub["v_steps"], n_out=n_out)
+            sec = time.perf_counter() - a
+        cpair = sum((H // Hkv) * (S0 + i + 1) for i in range(256))
+        cpu = {"value": cpair / sec, "unit": "queries·keys/s", "cores": 1, "kind": "oracle",
+               "sample": f"1 of {Hkv} KV heads with its {H // Hkv} query heads: ingest + 256 of {steps_dec} steps",
+               "seconds": round(sec, 3)}
+    line = {
+        "metric": METRIC, "value": pairs / (ms_per_step * 1e-3), "unit": "queries·keys/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "kv_decode", "B": B, "H": H, "H_kv": Hkv, "S0": S0, "decode_steps": steps_dec,
+                   "E": E, "D": D, "n_out": n_out, "seed": 0},
+        "decode_us_per_token": decode_us,
+        "kernels": {l: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
+                    for l, r in per_kernel.items()},
+        "roofline": roof, "exact": exact, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -132,6 +257,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload == "kv_decode":
+        return decode_main(args)
     gen_kw, causal, H, Hkv, E, D = WORKLOADS[args.workload]
     d = inputs.workload(args.workload, seed=0, **gen_kw)
     dt = d["dtype"]

@@ -164,6 +164,69 @@ int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, i
  * halving and subsampling steps draw from. */
 int thin_attn_philox(const uint64_t* counters, int64_t n, uint64_t seed, uint64_t* out, void* stream);
 
+/*
+ * Streaming Express state for decoding (KV-cache thinning).
+ *
+ * A state summarises the tokens streamed into it for every unit with the
+ * causal schedule of thin_attn_forward (same blocks of n_out tokens, same
+ * representatives, halvings and Philox streams, keyed by `seed`), and keeps
+ * compact copies of the rows it needs: cache (<= 4 n_out rows), buffer
+ * (< 2 n_out) and the block being streamed (< n_out).  Its size does not
+ * depend on the stream length ("Express Language Modeling", "The EXPRESS
+ * Meta-Procedure": the cache stays within 6 n_out).  Decode queries see
+ * exactly what a causal forward query at the same position sees.
+ *
+ * The caller allocates the device state buffer (thin_attn_kv_state_size
+ * bytes, 256-byte aligned) and the per-call workspace; the returned host
+ * handle holds the counters and must be destroyed with thin_attn_kv_destroy
+ * before the thin_attn handle it was created from.  Supported while every
+ * subsampling group lies in one block (stream length < 2 n_out^2).
+ */
+typedef struct thin_kv thin_kv_t;
+
+/* Device bytes of the state of B batch entries (all H_kv heads). 0 if invalid. */
+size_t thin_attn_kv_state_size(const thin_attn_t* h, int64_t B, int64_t n_out);
+
+/* Create an empty state over `state` (n_out 0 = the handle's n_out). */
+int thin_attn_kv_create(thin_attn_t* h, void* state, size_t state_bytes, int64_t B, int64_t n_out,
+                        uint64_t seed, thin_kv_t** out);
+int thin_attn_kv_destroy(thin_kv_t* kv);
+
+/* Tokens streamed so far. */
+int64_t thin_attn_kv_tokens(const thin_kv_t* kv);
+
+/* Halving decisions per unit that appending n_new tokens will make (decode = 1). */
+int64_t thin_attn_kv_decision_count(const thin_kv_t* kv, int64_t n_new);
+
+/* Workspace bytes of an append of n_new tokens or of a decode step (n_new = 1). */
+size_t thin_attn_kv_workspace_size(const thin_kv_t* kv, int64_t n_new);
+
+/* Append n_new tokens: k [B, n_new, H_kv, E], v [B, n_new, H_kv, D].  From an
+ * empty state with n_new >= n_out the whole chunk is thinned at once (batch
+ * halvings in parallel, then the HALVE chain); otherwise block by block.
+ * decisions (optional) [B * H_kv, thin_attn_kv_decision_count] receives the
+ * decisions of this call in chronological order. */
+int thin_attn_kv_append(thin_kv_t* kv, const void* k, const void* v, int64_t n_new, uint8_t* decisions,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step: the new token (k1 [B, H_kv, E], v1 [B, H_kv, D]) is
+ * appended and its queries q [B, H, E] attend to the state plus the token
+ * itself; out [B, H, D].  decisions as for append (n_new = 1). */
+int thin_attn_kv_decode(thin_kv_t* kv, const void* q, const void* k1, const void* v1, void* out,
+                        uint8_t* decisions, void* workspace, size_t workspace_bytes, void* stream);
+
+/* What the next query would see: token indices [B * H_kv, 7 n_out] (padded
+ * -1), weights (padded 0) and lengths [B * H_kv]; weights sum to the tokens
+ * streamed. */
+int thin_attn_kv_coreset(thin_kv_t* kv, int32_t* idx, float* w, int32_t* len, void* stream);
+
+/* Checkpoint of the host counters (the device state is the caller's buffer:
+ * copy it alongside).  export with host == NULL returns the bytes needed;
+ * import restores the counters into a state created with the same B, heads,
+ * n_out and seed. */
+int64_t thin_attn_kv_export(const thin_kv_t* kv, void* host, size_t bytes);
+int thin_attn_kv_import(thin_kv_t* kv, const void* host, size_t bytes);
+
 /* Launch timing.  thin_attn_set_timing(h, 1) starts a fresh list of records:
  * from then on every kernel launch of thin_attn_forward is bracketed by two
  * HIP events on the caller's stream.  thin_attn_timing_count gives the number

@@ -53,6 +53,19 @@ _SIGNATURES = {
                           + [ctypes.c_void_p] * 4),
     "thin_attn_philox": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p,
                                         ctypes.c_void_p]),
+    "thin_attn_kv_state_size": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64]),
+    "thin_attn_kv_create": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_uint64, ctypes.POINTER(ctypes.c_void_p)]),
+    "thin_attn_kv_destroy": (ctypes.c_int, [ctypes.c_void_p]),
+    "thin_attn_kv_tokens": (ctypes.c_int64, [ctypes.c_void_p]),
+    "thin_attn_kv_decision_count": (ctypes.c_int64, [ctypes.c_void_p, ctypes.c_int64]),
+    "thin_attn_kv_workspace_size": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int64]),
+    "thin_attn_kv_append": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int64] + [ctypes.c_void_p] * 2
+                            + [ctypes.c_size_t, ctypes.c_void_p]),
+    "thin_attn_kv_decode": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "thin_attn_kv_coreset": (ctypes.c_int, [ctypes.c_void_p] * 5),
+    "thin_attn_kv_export": (ctypes.c_int64, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]),
+    "thin_attn_kv_import": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]),
     "thin_attn_set_timing": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
     "thin_attn_timing_count": (ctypes.c_int64, [ctypes.c_void_p]),
     "thin_attn_timing_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_char_p, ctypes.c_size_t,
@@ -250,3 +263,94 @@ def philox(counters, seed, stream=None):
     if rc != 0:
         raise ThinAttnError(rc, "philox launch failed")
     return out
+
+
+class KVState:
+    """Streaming Express state for decoding, backed by a caller-owned device buffer.
+
+    append(k [B, n, H_kv, E], v) streams tokens in; decode(q [B, H, E],
+    k1 [B, H_kv, E], v1) appends one token and returns its attention output
+    [B, H, D].  Both can return the halving decisions they made.
+    """
+
+    def __init__(self, attn, B, n_out, seed=0, device="cuda"):
+        self.attn = attn
+        self.lib = attn.lib
+        self.B = B
+        self.n_out = n_out
+        nbytes = int(self.lib.thin_attn_kv_state_size(attn.h, B, n_out))
+        if nbytes == 0:
+            raise ValueError("invalid state size arguments")
+        self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        h = ctypes.c_void_p()
+        attn._check(self.lib.thin_attn_kv_create(attn.h, _ptr(self.buffer), nbytes, B, n_out, ctypes.c_uint64(seed),
+                                                 ctypes.byref(h)))
+        self.kv = h
+        self._ws = None
+
+    def __del__(self):
+        if getattr(self, "kv", None) is not None and _lib is not None:
+            _lib.thin_attn_kv_destroy(self.kv)
+            self.kv = None
+
+    @property
+    def tokens(self):
+        return int(self.lib.thin_attn_kv_tokens(self.kv))
+
+    def decision_count(self, n_new):
+        n = int(self.lib.thin_attn_kv_decision_count(self.kv, n_new))
+        if n < 0:
+            self.attn._check(n)
+        return n
+
+    def _workspace(self, n_new):
+        need = max(int(self.lib.thin_attn_kv_workspace_size(self.kv, n_new)), 256)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.buffer.device)
+        return self._ws
+
+    def _decisions(self, n_new, want):
+        if not want:
+            return None
+        return torch.zeros((self.B * self.attn.H_kv, max(self.decision_count(n_new), 1)), dtype=torch.uint8,
+                           device=self.buffer.device)
+
+    def append(self, k, v, return_decisions=False, stream=None):
+        k, v = k.contiguous(), v.contiguous()
+        n_new = k.shape[1]
+        dec = self._decisions(n_new, return_decisions)
+        cnt = self.decision_count(n_new) if return_decisions else 0
+        ws = self._workspace(n_new)
+        self.attn._check(self.lib.thin_attn_kv_append(self.kv, _ptr(k), _ptr(v), n_new, _ptr(dec), _ptr(ws),
+                                                      ws.numel(), _stream(stream)))
+        return dec[:, :cnt] if return_decisions else None
+
+    def decode(self, q, k1, v1, out=None, return_decisions=False, stream=None):
+        q, k1, v1 = q.contiguous(), k1.contiguous(), v1.contiguous()
+        if out is None:
+            out = torch.empty((self.B, self.attn.H, self.attn.D), dtype=self.attn.dtype, device=q.device)
+        dec = self._decisions(1, return_decisions)
+        cnt = self.decision_count(1) if return_decisions else 0
+        ws = self._workspace(1)
+        self.attn._check(self.lib.thin_attn_kv_decode(self.kv, _ptr(q), _ptr(k1), _ptr(v1), _ptr(out), _ptr(dec),
+                                                      _ptr(ws), ws.numel(), _stream(stream)))
+        return (out, dec[:, :cnt]) if return_decisions else out
+
+    def coreset(self, stream=None):
+        units = self.B * self.attn.H_kv
+        cap = 7 * self.n_out
+        idx = torch.empty((units, cap), dtype=torch.int32, device=self.buffer.device)
+        w = torch.empty((units, cap), dtype=torch.float32, device=self.buffer.device)
+        ln = torch.empty((units,), dtype=torch.int32, device=self.buffer.device)
+        self.attn._check(self.lib.thin_attn_kv_coreset(self.kv, _ptr(idx), _ptr(w), _ptr(ln), _stream(stream)))
+        return idx, w, ln
+
+    def export_meta(self):
+        n = int(self.lib.thin_attn_kv_export(self.kv, None, 0))
+        buf = ctypes.create_string_buffer(n)
+        self.attn._check(0 if self.lib.thin_attn_kv_export(self.kv, buf, n) == n else -1)
+        return bytes(buf.raw)
+
+    def import_meta(self, meta):
+        buf = ctypes.create_string_buffer(meta, len(meta))
+        self.attn._check(self.lib.thin_attn_kv_import(self.kv, buf, len(meta)))

@@ -94,6 +94,41 @@ struct AttnLaunch {
   ExpressView ev;
 };
 
+// Row moves into / inside the streaming Express state (see kv.hip).
+struct KvRowsLaunch {
+  void* state_k;               // [units][slots][E]
+  void* state_v;               // [units][slots][D]
+  const int32_t* state_tok;    // token of every slot (read side of state moves)
+  int32_t* state_tok_out;      // token of every slot (write side)
+  int units, slots, E, D, elt;
+  int cnt;                     // rows per unit
+  int dst_first;               // first destination slot
+  const int32_t* src_list;     // state-to-state: source slots [units][list_stride]
+  int64_t list_stride;
+  const void* src_k;           // token source [B, S_src, H_kv, E] (when src_list == nullptr)
+  const void* src_v;
+  int64_t S_src;
+  int H_kv;
+  int64_t src_first;           // first token of the source range (tok_list == nullptr)
+  const int32_t* tok_list;     // or explicit token list [units][list_stride]
+  int64_t tok_base;            // stream position of source token 0
+};
+
+struct KvDecodeLaunch {
+  const void* q;        // [B, H, E] (one token)
+  const void* k1;       // [B, H_kv, E]
+  const void* v1;       // [B, H_kv, D]
+  void* out;            // [B, H, D]
+  const void* state_k;
+  const void* state_v;
+  int units, slots, n, H, H_kv;
+  int nC, nBf, nRaw;    // visible cache, buffer and raw rows (before the new token)
+  float lw_c, lw_b;     // log2 weights of cache and buffer rows
+  float scale_log2;     // softmax scale * log2(e)
+  float* partial;       // [units][splits][G][D + 2]
+  int splits;
+};
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s);
 hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s);
@@ -113,6 +148,14 @@ struct ExpressSchedule {
   int64_t decisions;     // per unit
 };
 ExpressSchedule express_schedule(int64_t S, int n);
+hipError_t launch_kv_rows(const KvRowsLaunch& a, hipStream_t s);
+hipError_t launch_kv_block_reps(int units, int n, int64_t t0, int log2r, uint64_t seed, int32_t* list, hipStream_t s);
+hipError_t launch_kv_iota(int32_t* out, int units, int cnt, int first, hipStream_t s);
+hipError_t launch_kv_decode(const KvDecodeLaunch& a, int bf16, int E, int D, int G, hipStream_t s);
+bool kv_decode_supported(int bf16, int E, int D, int G);
+hipError_t launch_kv_summary(const int32_t* tok, int units, int slots, int n, int nC, int nBf, int nRaw, float wc,
+                             float wb, int32_t* idx, float* w, int32_t* len, int cap, hipStream_t s);
+int kv_decode_splits(int n);
 bool attention_supported(int bf16, int E, int D);
 
 }  // namespace thin

@@ -1,0 +1,348 @@
+// Streaming Express state for decoding (gfx950).
+//
+// The state of a unit holds compact copies of the rows it summarises, so its
+// size does not grow with the sequence ("Express Language Modeling",
+// "The EXPRESS Meta-Procedure": the cache stays within 6 n_out whatever n):
+//
+//   slots [0, 4n)    cache C   (weight m)
+//   slots [4n, 6n)   buffer Bf (weight m / 2, representatives of the batch)
+//   slots [6n, 7n)   raw block (weight 1, tokens of the block being streamed)
+//
+// K rows [units][7n][E], V rows [units][7n][D] (input dtype) and the token
+// index of every slot [units][7n] live in the caller's state buffer.  Block
+// ingest, batch halving and HALVE move rows between these regions; the
+// halvings themselves run the pair-Gram and walk kernels on slot lists.
+
+#include <math.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace thin {
+
+namespace {
+
+inline unsigned grid1d(int64_t n, int block) { return static_cast<unsigned>((n + block - 1) / block); }
+
+// Copy rows of `cnt` entries per unit.  Source row of entry j of unit u:
+//   src_list == nullptr: token src_first + j of a [B, S_src, H_kv, *] tensor (unit = b * H_kv + h)
+//   src_list != nullptr: slot src_list[u * list_stride + j] of the state (state-to-state move)
+// Destination: state slot dst_first + j.  One 16-byte piece per thread.
+__global__ void kv_rows_kernel(KvRowsLaunch a) {
+  const int ke = a.E * a.elt / 16, ve = a.D * a.elt / 16;   // 16-byte pieces per row
+  const int per_row = ke + ve + 1;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.units) * a.cnt * per_row;
+  if (i >= total) return;
+  const int piece = static_cast<int>(i % per_row);
+  const int64_t e = i / per_row;
+  const int j = static_cast<int>(e % a.cnt);
+  const int u = static_cast<int>(e / a.cnt);
+  const int64_t dslot = static_cast<int64_t>(u) * a.slots + a.dst_first + j;
+  const char* sk;
+  const char* sv;
+  int32_t tok;
+  if (a.src_list) {
+    const int32_t slot = a.src_list[static_cast<int64_t>(u) * a.list_stride + j];
+    const int64_t s = static_cast<int64_t>(u) * a.slots + slot;
+    sk = static_cast<const char*>(a.state_k) + s * a.E * a.elt;
+    sv = static_cast<const char*>(a.state_v) + s * a.D * a.elt;
+    tok = a.state_tok[s];
+  } else {
+    const int b = u / a.H_kv, h = u % a.H_kv;
+    const int64_t tk = a.tok_list ? a.tok_list[static_cast<int64_t>(u) * a.list_stride + j] : a.src_first + j;
+    const int64_t row = (static_cast<int64_t>(b) * a.S_src + tk) * a.H_kv + h;
+    sk = static_cast<const char*>(a.src_k) + row * a.E * a.elt;
+    sv = static_cast<const char*>(a.src_v) + row * a.D * a.elt;
+    tok = static_cast<int32_t>(a.tok_base + tk);
+  }
+  if (piece < ke) {
+    reinterpret_cast<uint4*>(static_cast<char*>(a.state_k) + dslot * a.E * a.elt)[piece] =
+        reinterpret_cast<const uint4*>(sk)[piece];
+  } else if (piece < ke + ve) {
+    reinterpret_cast<uint4*>(static_cast<char*>(a.state_v) + dslot * a.D * a.elt)[piece - ke] =
+        reinterpret_cast<const uint4*>(sv)[piece - ke];
+  } else {
+    a.state_tok_out[dslot] = tok;
+  }
+}
+
+// Slots of the representatives of the block starting at token t0 (groups of
+// r <= n tokens; each contributes the token at offset floor(u r) of its group,
+// u from counter (group, log2 r, unit, subsample tag)).
+__global__ void kv_block_reps_kernel(int units, int n, int64_t t0, int log2r, uint64_t seed, int32_t* list) {
+  const int per = n >> log2r;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(units) * per) return;
+  const int u = static_cast<int>(i / per);
+  const int k = static_cast<int>(i % per);
+  const int64_t g = (t0 >> log2r) + k;
+  const uint64_t word = philox_word0(static_cast<uint64_t>(g), static_cast<uint64_t>(log2r), static_cast<uint64_t>(u),
+                                     kTagSubsample, seed);
+  const int64_t off = log2r ? static_cast<int64_t>(word >> (64 - log2r)) : 0;
+  list[i] = static_cast<int32_t>(6 * n + ((g << log2r) + off - t0));
+}
+
+__global__ void kv_iota_kernel(int32_t* out, int units, int cnt, int first) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(units) * cnt) return;
+  out[i] = first + static_cast<int>(i % cnt);
+}
+
+// Token indices and weights of what the next query would see (cache, buffer,
+// raw block), padded with -1 / 0 up to cap.
+__global__ void kv_summary_kernel(const int32_t* tok, int slots, int n, int nC, int nBf, int nRaw, float wc, float wb,
+                                  int32_t* idx, float* w, int32_t* len, int cap) {
+  const int u = blockIdx.x;
+  const int total = nC + nBf + nRaw;
+  for (int j = threadIdx.x; j < cap; j += blockDim.x) {
+    int32_t id = -1;
+    float wt = 0.f;
+    if (j < nC) {
+      id = tok[static_cast<int64_t>(u) * slots + j];
+      wt = wc;
+    } else if (j < nC + nBf) {
+      id = tok[static_cast<int64_t>(u) * slots + 4 * n + (j - nC)];
+      wt = wb;
+    } else if (j < total) {
+      id = tok[static_cast<int64_t>(u) * slots + 6 * n + (j - nC - nBf)];
+      wt = 1.f;
+    }
+    if (idx) idx[static_cast<int64_t>(u) * cap + j] = id;
+    if (w) w[static_cast<int64_t>(u) * cap + j] = wt;
+  }
+  if (len && threadIdx.x == 0) len[u] = total;
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention: one query token, G = H / H_kv query heads per unit.
+// Visible keys = cache slots [0, nC) (log2 weight lw_c), buffer slots
+// [4n, 4n + nBf) (lw_b), raw slots [6n, 6n + nRaw) (weight 1) and the new
+// token itself (read from the caller's k1 / v1).  The key range is split
+// across workgroups; each writes a partial (max, sum, unnormalised output)
+// per query head, merged by kv_combine_kernel.
+// ---------------------------------------------------------------------------
+constexpr int kSplitKeys = 128;   // keys per workgroup (2 per lane... 32 per wave)
+
+template <bool BF16, int E, int D, int G>
+__global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
+  const int u = blockIdx.y;
+  const int split = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = u / a.H_kv, hk = u % a.H_kv;
+  const int total = a.nC + a.nBf + a.nRaw + 1;
+  const int k0 = split * kSplitKeys;
+  const int k1 = min(total, k0 + kSplitKeys);
+  constexpr int ELT = BF16 ? 2 : 4;
+
+  __shared__ float sq[G][E];
+  __shared__ float sp[G][kSplitKeys];
+  __shared__ float red[4][G];
+  __shared__ float smax[G];
+
+  // queries of the group
+  for (int x = tid; x < G * E; x += 256) {
+    const int gh = x / E, e = x % E;
+    const int64_t off = (static_cast<int64_t>(b) * a.H + hk * G + gh) * E + e;
+    sq[gh][e] = BF16 ? bf16_bits_to_float(static_cast<const uint16_t*>(a.q)[off]) : static_cast<const float*>(a.q)[off];
+  }
+  __syncthreads();
+
+  // logits: one key per thread (threads beyond the range idle)
+  const int kk = k0 + tid;
+  float logit[G];
+  const bool live = tid < kSplitKeys && kk < k1;
+  if (live) {
+    const char* krow;
+    float lw;
+    if (kk < a.nC) {
+      krow = static_cast<const char*>(a.state_k) + (static_cast<int64_t>(u) * a.slots + kk) * E * ELT;
+      lw = a.lw_c;
+    } else if (kk < a.nC + a.nBf) {
+      krow = static_cast<const char*>(a.state_k) + (static_cast<int64_t>(u) * a.slots + 4 * a.n + kk - a.nC) * E * ELT;
+      lw = a.lw_b;
+    } else if (kk < total - 1) {
+      krow = static_cast<const char*>(a.state_k) +
+             (static_cast<int64_t>(u) * a.slots + 6 * a.n + kk - a.nC - a.nBf) * E * ELT;
+      lw = 0.f;
+    } else {
+      krow = static_cast<const char*>(a.k1) + (static_cast<int64_t>(b) * a.H_kv + hk) * E * ELT;
+      lw = 0.f;
+    }
+    float acc[G];
+#pragma unroll
+    for (int gh = 0; gh < G; ++gh) acc[gh] = 0.f;
+    for (int e0 = 0; e0 < E; e0 += 16 / ELT) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(krow + e0 * ELT);
+      float kv[16 / ELT];
+      if constexpr (BF16) {
+        const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kv[2 * j] = bf16_bits_to_float(static_cast<uint16_t>(wv[j] & 0xffffu));
+          kv[2 * j + 1] = bf16_bits_to_float(static_cast<uint16_t>(wv[j] >> 16));
+        }
+      } else {
+        kv[0] = __uint_as_float(raw.x);
+        kv[1] = __uint_as_float(raw.y);
+        kv[2] = __uint_as_float(raw.z);
+        kv[3] = __uint_as_float(raw.w);
+      }
+#pragma unroll
+      for (int gh = 0; gh < G; ++gh)
+#pragma unroll
+        for (int j = 0; j < 16 / ELT; ++j) acc[gh] += sq[gh][e0 + j] * kv[j];
+    }
+#pragma unroll
+    for (int gh = 0; gh < G; ++gh) logit[gh] = acc[gh] * a.scale_log2 + lw;
+  } else {
+#pragma unroll
+    for (int gh = 0; gh < G; ++gh) logit[gh] = -INFINITY;
+  }
+  // max over the split
+#pragma unroll
+  for (int gh = 0; gh < G; ++gh) {
+    float m = logit[gh];
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (lane == 0) red[w][gh] = m;
+  }
+  __syncthreads();
+  if (tid < G) smax[tid] = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+  __syncthreads();
+#pragma unroll
+  for (int gh = 0; gh < G; ++gh) {
+    const float p = live ? __builtin_amdgcn_exp2f(logit[gh] - smax[gh]) : 0.f;
+    if (tid < kSplitKeys) sp[gh][tid] = p;
+    float s = p;
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0) red[w][gh] = s;
+  }
+  __syncthreads();
+  // P V: thread = (head, dim); rows read coalesced
+  float* part = a.partial + ((static_cast<int64_t>(u) * gridDim.x + split) * G) * (D + 2);
+  for (int x = tid; x < G * D; x += 256) {
+    const int gh = x / D, d = x % D;
+    float acc = 0.f;
+    for (int j = 0; j < k1 - k0; ++j) {
+      const int key = k0 + j;
+      const char* vrow;
+      if (key < a.nC)
+        vrow = static_cast<const char*>(a.state_v) + (static_cast<int64_t>(u) * a.slots + key) * D * ELT;
+      else if (key < a.nC + a.nBf)
+        vrow = static_cast<const char*>(a.state_v) + (static_cast<int64_t>(u) * a.slots + 4 * a.n + key - a.nC) * D * ELT;
+      else if (key < total - 1)
+        vrow = static_cast<const char*>(a.state_v) +
+               (static_cast<int64_t>(u) * a.slots + 6 * a.n + key - a.nC - a.nBf) * D * ELT;
+      else
+        vrow = static_cast<const char*>(a.v1) + (static_cast<int64_t>(b) * a.H_kv + hk) * D * ELT;
+      const float vv = BF16 ? bf16_bits_to_float(reinterpret_cast<const uint16_t*>(vrow)[d])
+                            : reinterpret_cast<const float*>(vrow)[d];
+      acc += sp[gh][j] * vv;
+    }
+    part[gh * (D + 2) + d] = acc;
+  }
+  if (tid < G) {
+    part[tid * (D + 2) + D] = smax[tid];
+    part[tid * (D + 2) + D + 1] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+  }
+}
+
+template <bool BF16, int D, int G>
+__global__ void kv_combine_kernel(const float* partial, int splits, int H, int H_kv, void* out) {
+  const int u = blockIdx.x;
+  const int b = u / H_kv, hk = u % H_kv;
+  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
+    const int gh = x / D, d = x % D;
+    float m = -INFINITY;
+    for (int s = 0; s < splits; ++s) m = fmaxf(m, partial[((static_cast<int64_t>(u) * splits + s) * G + gh) * (D + 2) + D]);
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float* p = partial + ((static_cast<int64_t>(u) * splits + s) * G + gh) * (D + 2);
+      const float sc = p[D] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(p[D] - m);
+      num += sc * p[d];
+      den += sc * p[D + 1];
+    }
+    const float o = num / den;
+    const int64_t off = (static_cast<int64_t>(b) * H + hk * G + gh) * D + d;
+    if constexpr (BF16)
+      static_cast<uint16_t*>(out)[off] = float_to_bf16_bits(o);
+    else
+      static_cast<float*>(out)[off] = o;
+  }
+}
+
+template <bool BF16, int E, int D, int G>
+hipError_t decode_one(const KvDecodeLaunch& a, int splits, hipStream_t s) {
+  hipLaunchKernelGGL((kv_decode_kernel<BF16, E, D, G>), dim3(splits, a.units), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((kv_combine_kernel<BF16, D, G>), dim3(a.units), dim3(256), 0, s, a.partial, splits, a.H, a.H_kv,
+                     a.out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int kv_decode_splits(int n) { return (7 * n + kSplitKeys) / kSplitKeys; }
+
+hipError_t launch_kv_rows(const KvRowsLaunch& a, hipStream_t s) {
+  const int per_row = (a.E + a.D) * a.elt / 16 + 1;
+  const int64_t total = static_cast<int64_t>(a.units) * a.cnt * per_row;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_rows_kernel, dim3(grid1d(total, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_block_reps(int units, int n, int64_t t0, int log2r, uint64_t seed, int32_t* list, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(units) * (n >> log2r);
+  hipLaunchKernelGGL(kv_block_reps_kernel, dim3(grid1d(total, 256)), dim3(256), 0, s, units, n, t0, log2r, seed, list);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_iota(int32_t* out, int units, int cnt, int first, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(units) * cnt;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_iota_kernel, dim3(grid1d(total, 256)), dim3(256), 0, s, out, units, cnt, first);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_summary(const int32_t* tok, int units, int slots, int n, int nC, int nBf, int nRaw, float wc,
+                             float wb, int32_t* idx, float* w, int32_t* len, int cap, hipStream_t s) {
+  if (units == 0 || (!idx && !w && !len)) return hipSuccess;
+  hipLaunchKernelGGL(kv_summary_kernel, dim3(units), dim3(256), 0, s, tok, slots, n, nC, nBf, nRaw, wc, wb, idx, w, len,
+                     cap);
+  return hipGetLastError();
+}
+
+bool kv_decode_supported(int bf16, int E, int D, int G) {
+  const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
+  return g_ok && ((E == 128 && D == 128) || (E == 64 && D == 64));
+}
+
+hipError_t launch_kv_decode(const KvDecodeLaunch& a, int bf16, int E, int D, int G, hipStream_t s) {
+  const int splits = (a.nC + a.nBf + a.nRaw + 1 + kSplitKeys - 1) / kSplitKeys;
+  KvDecodeLaunch b = a;
+  b.splits = splits;
+#define THIN_KV_CASE(BF, EE, DD, GG) \
+  if (bf16 == BF && E == EE && D == DD && G == GG) return decode_one<BF, EE, DD, GG>(b, splits, s);
+  THIN_KV_CASE(1, 128, 128, 1)
+  THIN_KV_CASE(1, 128, 128, 2)
+  THIN_KV_CASE(1, 128, 128, 4)
+  THIN_KV_CASE(1, 128, 128, 8)
+  THIN_KV_CASE(1, 64, 64, 1)
+  THIN_KV_CASE(1, 64, 64, 2)
+  THIN_KV_CASE(1, 64, 64, 4)
+  THIN_KV_CASE(1, 64, 64, 8)
+  THIN_KV_CASE(0, 128, 128, 1)
+  THIN_KV_CASE(0, 128, 128, 2)
+  THIN_KV_CASE(0, 128, 128, 4)
+  THIN_KV_CASE(0, 128, 128, 8)
+  THIN_KV_CASE(0, 64, 64, 1)
+  THIN_KV_CASE(0, 64, 64, 2)
+  THIN_KV_CASE(0, 64, 64, 4)
+  THIN_KV_CASE(0, 64, 64, 8)
+#undef THIN_KV_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace thin

@@ -1,0 +1,132 @@
+"""GPU parity of the streaming Express state (KV-cache thinning + decode) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as att
+from oracle import express as oexp
+from oracle import forward as fwd
+from sub_quadratic_attention_amd import inputs
+from tests.parity import TOL, say, to_gpu, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sub_quadratic_attention_amd import binding
+    binding.load_library()
+
+
+def _run_stream(d, n, H, Hkv, E, D, seed=0, chunks=None):
+    """Ingest the history (in `chunks` appends, or one bulk append), then decode step by step.
+
+    Returns (outputs [B, steps, H, D] float64, decisions per unit (flat, chronological), state)."""
+    from sub_quadratic_attention_amd.binding import KVState, ThinAttention
+    dt = d["dtype"]
+    ta = ThinAttention(E, D, H, Hkv, torch_dtype(dt))
+    B = d["k_hist"].shape[0]
+    st = KVState(ta, B, n, seed=seed)
+    kh, vh = to_gpu(d["k_hist"], dt), to_gpu(d["v_hist"], dt)
+    decs = []
+    S0 = kh.shape[1]
+    bounds = [0, S0] if chunks is None else chunks
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        decs.append(st.append(kh[:, a:b], vh[:, a:b], return_decisions=True))
+    qs, ks, vs = to_gpu(d["q_steps"], dt), to_gpu(d["k_steps"], dt), to_gpu(d["v_steps"], dt)
+    outs = []
+    for i in range(qs.shape[1]):
+        o, dd = st.decode(qs[:, i], ks[:, i], vs[:, i], return_decisions=True)
+        outs.append(o.float())
+        decs.append(dd)
+    torch.cuda.synchronize()
+    out = torch.stack(outs, dim=1).cpu().numpy().astype(np.float64)
+    dec = torch.cat(decs, dim=1).cpu().numpy()
+    return out, dec, st
+
+
+def _check(name, d, n, H, Hkv, E, D, seed=0, chunks=None):
+    say(f"[decode] {name}")
+    out, dec, st = _run_stream(d, n, H, Hkv, E, D, seed, chunks)
+    units = dec.shape[0]
+    ref, stats, logs = fwd.decode(d["k_hist"], d["v_hist"], d["q_steps"], d["k_steps"], d["v_steps"],
+                                  n_out=n, seed=seed, decisions={u: dec[u] for u in range(units)})
+    say(f"[decode] {name}: decisions={stats.decisions} near_ties={stats.near_ties} fails={stats.fails}")
+    assert stats.decisions == dec.shape[1] * units
+    assert stats.fails == 0 and stats.near_ties <= 0.005 * max(stats.decisions, 1)
+    err = att.max_abs_error(out, ref)
+    say(f"[decode] {name}: max|gpu - oracle| = {err:.3g}")
+    assert err <= TOL[d["dtype"]]
+    # the state's summary equals the oracle's cache / buffer / raw block after the stream
+    idx, w, ln = (x.cpu().numpy() for x in st.coreset())
+    total = d["k_hist"].shape[1] + d["q_steps"].shape[1]
+    for u in range(units):
+        assert w[u, :ln[u]].sum() == total
+    return out
+
+
+def _stream(seed, S0, steps, Hkv, H, E=128, D=128, dtype="bf16"):
+    return inputs.kv_decode(seed=seed, Hkv=Hkv, H=H, S0=S0, steps=steps, E=E, D=D, walk_len=S0 + steps, dtype=dtype)
+
+
+def test_decode_crosses_batch_and_halve():
+    """n=32: bulk history of 1900 tokens, 200 decode steps across a batch halving and a HALVE (token 2048)."""
+    d = _stream(0, 1900, 200, Hkv=2, H=8)
+    _check("bulk 1900 + 200 steps", d, 32, 8, 2, 128, 128)
+
+
+def test_decode_block_path_from_empty():
+    """History streamed in uneven appends from an empty state (block-by-block ingest)."""
+    d = _stream(1, 700, 100, Hkv=2, H=2, E=64, D=64)
+    _check("appends 10/90/300/300 + 100 steps", d, 16, 2, 2, 64, 64, chunks=[0, 10, 100, 400, 700])
+
+
+def test_decode_fp32_gqa8():
+    d = _stream(2, 600, 80, Hkv=1, H=8, dtype="f32")
+    _check("fp32 G=8", d, 32, 8, 1, 128, 128)
+
+
+def test_decode_matches_causal_forward():
+    """A decode step sees what a causal forward query at the same token sees."""
+    from sub_quadratic_attention_amd.binding import ThinAttention
+    d = _stream(3, 1000, 64, Hkv=2, H=2)
+    out, _, _ = _run_stream(d, 32, 2, 2, 128, 128)
+    k = np.concatenate([d["k_hist"], d["k_steps"]], axis=1)
+    v = np.concatenate([d["v_hist"], d["v_steps"]], axis=1)
+    q = np.concatenate([np.zeros((1, 1000, 2, 128), np.float32), d["q_steps"]], axis=1)
+    ta = ThinAttention(128, 128, 2, 2, torch.bfloat16, n_out=32)
+    f = ta.forward(to_gpu(q, "bf16"), to_gpu(k, "bf16"), to_gpu(v, "bf16"), causal=True)
+    torch.cuda.synchronize()
+    fo = f.float().cpu().numpy()[:, 1000:]
+    assert att.max_abs_error(out, fo) <= 2 * TOL["bf16"]
+
+
+def test_checkpoint_round_trip():
+    """Export the counters and copy the device state mid-stream: the resumed stream is bit-identical."""
+    from sub_quadratic_attention_amd.binding import KVState, ThinAttention
+    d = _stream(4, 500, 120, Hkv=2, H=4)
+    ta = ThinAttention(128, 128, 4, 2, torch.bfloat16)
+    qs, ks, vs = (to_gpu(d[x], "bf16") for x in ("q_steps", "k_steps", "v_steps"))
+    a = KVState(ta, 1, 32, seed=9)
+    a.append(to_gpu(d["k_hist"], "bf16"), to_gpu(d["v_hist"], "bf16"))
+    for i in range(50):
+        a.decode(qs[:, i], ks[:, i], vs[:, i])
+    meta = a.export_meta()
+    b = KVState(ta, 1, 32, seed=9)
+    b.buffer.copy_(a.buffer)
+    b.import_meta(meta)
+    assert b.tokens == a.tokens
+    for i in range(50, 120):
+        oa = a.decode(qs[:, i], ks[:, i], vs[:, i])
+        ob = b.decode(qs[:, i], ks[:, i], vs[:, i])
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), i
+
+
+def test_kv_decode_full_size_window():
+    """The 131k-token, 8-KV-head state (n_out 512) and 1024 decode steps; every output checked."""
+    d = inputs.kv_decode(seed=0)
+    _check("kv_decode S0=131072 x 1024 steps", d, 512, 32, 8, 128, 128)
