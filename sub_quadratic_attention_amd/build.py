@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libthin_attn.so")
-SOURCES = ["api.hip", "kvapi.hip", "kh.hip", "attn.hip", "kv.hip"]
+SOURCES = ["api.hip", "kvapi.hip", "kh.hip", "attn.hip", "attn_bf16.hip", "kv.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -36,7 +36,7 @@ def _compile(src):
 def build(verbose=False):
     """Compile every HIP source and link libthin_attn.so next to this file."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 6)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, *FLAGS, "-shared", *objs, "-o", tmp]

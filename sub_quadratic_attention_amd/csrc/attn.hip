@@ -379,11 +379,7 @@ bool attention_supported(int bf16, int E, int D) {
 hipError_t launch_attention(const AttnLaunch& a, int bf16, int E, int D, hipStream_t s) {
   if (a.T == 0 || a.B * a.H == 0) return hipSuccess;
   if (bf16) {
-    if (E == 64 && D == 64) return launch_one<true, 64, 64>(a, s);
-    if (E == 64 && D == 128) return launch_one<true, 64, 128>(a, s);
-    if (E == 64 && D == 256) return launch_one<true, 64, 256>(a, s);
-    if (E == 128 && D == 128) return launch_one<true, 128, 128>(a, s);
-    if (E == 128 && D == 64) return launch_one<true, 128, 64>(a, s);
+    return launch_attention_bf16(a, E, D, s);
   } else {
     if (E == 64 && D == 64) return launch_one<false, 64, 64>(a, s);
     if (E == 64 && D == 128) return launch_one<false, 64, 128>(a, s);
