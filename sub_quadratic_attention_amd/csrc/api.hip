@@ -245,11 +245,12 @@ int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, i
   const hipStream_t st = as_stream(stream);
   thin::PointSource src{k, v, S, c.H_kv, c.E, c.D, c.dtype == THIN_BF16};
   const int n = static_cast<int>(N);
-  THIN_HIP(thin::launch_pair_gram(make_gram(src, points, n, n, units, 1, h->scale64, gram), st));
+  const thin::GramLaunch gl = make_gram(src, points, n, n, units, 1, h->scale64, gram);
+  THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gl, st); }));
   thin::SweepLaunch sl = make_sweep(h, gram, n, units, 1, points, n, kept, seed, tag, bin);
   sl.dec = decisions;
   sl.dec_per_unit = n / 2;
-  THIN_HIP(thin::launch_halving_sweep(sl, st));
+  THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, st); }));
   return THIN_OK;
 }
 

@@ -31,23 +31,34 @@ namespace {
 // combination G = k_ee - k_eo - k_oe + k_oo needs no lane exchange.
 // Pass 0 accumulates <k, k'>, pass 1 <v, v'>.
 // ---------------------------------------------------------------------------
-constexpr int kChunk = 16;             // features staged per step
+constexpr int kChunk = 32;             // features staged per step
 constexpr int kPad = kChunk + 1;
 
+// 8 consecutive features of one point, kept raw until they are staged.
+struct Raw8 {
+  uint4 w[2];   // fp32: two float4; bf16: w[0] only
+};
+
 template <bool BF16>
-__device__ __forceinline__ void load4(const void* base, int64_t off, double out[4]) {
+__device__ __forceinline__ void load8(const void* base, int64_t off, Raw8& r) {
   if constexpr (BF16) {
-    const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
-    out[0] = bf16_bits_to_float(static_cast<uint16_t>(raw.x & 0xffffu));
-    out[1] = bf16_bits_to_float(static_cast<uint16_t>(raw.x >> 16));
-    out[2] = bf16_bits_to_float(static_cast<uint16_t>(raw.y & 0xffffu));
-    out[3] = bf16_bits_to_float(static_cast<uint16_t>(raw.y >> 16));
+    r.w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
   } else {
-    const float4 raw = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    out[0] = raw.x;
-    out[1] = raw.y;
-    out[2] = raw.z;
-    out[3] = raw.w;
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + off);
+    r.w[0] = p[0];
+    r.w[1] = p[1];
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ double raw8_at(const Raw8& r, int j) {
+  if constexpr (BF16) {
+    const uint32_t word = (j < 2 ? r.w[0].x : j < 4 ? r.w[0].y : j < 6 ? r.w[0].z : r.w[0].w);
+    return bf16_bits_to_float(static_cast<uint16_t>((j & 1) ? (word >> 16) : (word & 0xffffu)));
+  } else {
+    const uint4& q = r.w[j >> 2];
+    const uint32_t word = ((j & 3) == 0 ? q.x : (j & 3) == 1 ? q.y : (j & 3) == 2 ? q.z : q.w);
+    return __uint_as_float(word);
   }
 }
 
@@ -88,9 +99,9 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
   const int w = tid >> 6;
   const int wr = w >> 1, wc = w & 1;
 
-  // loader role: point lp of the row / column sets, features lf .. lf+3
+  // loader role: point lp of the row / column sets, features lf .. lf+7
   const int lp = tid >> 2;
-  const int lf = (tid & 3) * 4;
+  const int lf = (tid & 3) * 8;
   const int64_t ubase = static_cast<int64_t>(unit) * a.idx_unit_stride;
   auto token = [&](int q) -> int {   // q-th point of the tile's range; -1 if none
     if (packed) {
@@ -101,12 +112,14 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
     if (q >= a.N) return -1;
     return a.idx[ubase + static_cast<int64_t>(z % a.bins_per_unit) * a.idx_stride + q];
   };
+  const bool diag = tr == tc;          // rows and columns are the same points
   const int rtok = token(64 * tr + lp);
-  const int ctok = token(64 * tc + lp);
+  const int ctok = diag ? rtok : token(64 * tc + lp);
   const bool rvalid = rtok >= 0;
   const bool cvalid = ctok >= 0;
   const int64_t rrow = rvalid ? (static_cast<int64_t>(b) * a.src.S + rtok) * a.src.H_kv + h : 0;
   const int64_t crow = cvalid ? (static_cast<int64_t>(b) * a.src.S + ctok) * a.src.H_kv + h : 0;
+  double (*colS)[kPad] = diag ? rowF : colF;
 
   // does this wave's 16 x 16 pair block hold anything the walk reads?
   const int r0 = 32 * tr + 16 * wr;    // first pair row of the block
@@ -129,19 +142,19 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
   for (int pass = 0; pass < 2; ++pass) {
     const int F = pass ? a.src.D : a.src.E;
     const void* base = pass ? a.src.v : a.src.k;
-    double nr[4] = {0, 0, 0, 0}, nc[4] = {0, 0, 0, 0};
-    if (rvalid) load4<BF16>(base, rrow * F + lf, nr);
-    if (cvalid) load4<BF16>(base, crow * F + lf, nc);
+    Raw8 nr{}, nc{};
+    if (rvalid) load8<BF16>(base, rrow * F + lf, nr);
+    if (cvalid && !diag) load8<BF16>(base, crow * F + lf, nc);
     for (int f0 = 0; f0 < F; f0 += kChunk) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        rowF[lp][lf + j] = nr[j];
-        colF[lp][lf + j] = nc[j];
+      for (int j = 0; j < 8; ++j) {
+        rowF[lp][lf + j] = rvalid ? raw8_at<BF16>(nr, j) : 0.0;
+        if (!diag) colF[lp][lf + j] = cvalid ? raw8_at<BF16>(nc, j) : 0.0;
       }
       __syncthreads();
-      if (f0 + kChunk < F) {     // prefetch the next chunk while this one is used
-        if (rvalid) load4<BF16>(base, rrow * F + f0 + kChunk + lf, nr);
-        if (cvalid) load4<BF16>(base, crow * F + f0 + kChunk + lf, nc);
+      if (f0 + kChunk < F) {     // prefetch the next stage while this one is used
+        if (rvalid) load8<BF16>(base, rrow * F + f0 + kChunk + lf, nr);
+        if (cvalid && !diag) load8<BF16>(base, crow * F + f0 + kChunk + lf, nc);
       }
       if (active) {
 #pragma unroll
@@ -149,8 +162,8 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
           const int kf = kk * 4 + kq;
           const double Ae = rowF[2 * pr][kf];
           const double Ao = rowF[2 * pr + 1][kf];
-          const double Be = colF[2 * pc][kf];
-          const double Bo = colF[2 * pc + 1][kf];
+          const double Be = colS[2 * pc][kf];
+          const double Bo = colS[2 * pc + 1][kf];
           acc[pass][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ae, Be, acc[pass][0], 0, 0, 0);
           acc[pass][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ae, Bo, acc[pass][1], 0, 0, 0);
           acc[pass][2] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ao, Be, acc[pass][2], 0, 0, 0);
@@ -219,23 +232,59 @@ struct SigmaState {
   double s2;
 };
 
-// thresholds of pairs [i0, i1) (s_thr holds u on entry)
-__device__ __forceinline__ void sigma_chain(SigmaState& st, const double* s_b2, double* s_thr, int i0, int i1,
-                                            double c, double k1, double k2) {
+// Rows q0..q0+63, columns q0..q0+63 of a bin's G into LDS (row stride 65),
+// `PER` consecutive doubles per thread, all loads issued before any store.
+// Entries above the diagonal are copied too: a lane only uses row entries
+// left of its own pair, so they never influence a decision.  Rows and
+// columns beyond P read as 0.
+template <int PER>
+__device__ __forceinline__ void stage_block(const double* G, int P, int q0, double* dst, int t) {
+  const int r = (t * PER) >> 6;
+  const int cb = (t * PER) & 63;
+  const bool rok = q0 + r < P;
+  const double* src = G + static_cast<int64_t>(q0 + r) * P + q0 + cb;
+  double v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) v[j] = (rok && q0 + cb + j < P) ? src[j] : 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) dst[r * 65 + cb + j] = v[j];
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int i) {
+  const uint64_t bits = __double_as_longlong(x);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(bits), i);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(bits >> 32), i);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Thresholds of the pairs [i0, i0 + 64) by one wave: lane l holds b^2, b and
+// u of pair i0 + l in registers; the recursion runs on uniform values read
+// with readlane (no memory access on the serial path) and lane i keeps the
+// threshold of pair i0 + i.  The only serial operation besides fma / max is
+// sqrt(sigma^2); the hardware fp64 square root is used (its error is far
+// below the 1e-6 decision margins that matter).
+__device__ __forceinline__ void sigma_chain_wave(SigmaState& st, const double* s_b2, const double* s_b, double* s_thr,
+                                                 int i0, int P, double c, double k1, double k2) {
+  const int lane = threadIdx.x & 63;
+  const int n = min(64, P - i0);
+  const bool mine = lane < n;
+  const double b2l = mine ? s_b2[i0 + lane] : 0.0;
+  const double bl = mine ? s_b[i0 + lane] : 0.0;
+  const double ul = mine ? s_thr[i0 + lane] : 0.0;
   double s2 = st.s2;
-  for (int i = i0; i < i1; ++i) {
-    const double b2 = s_b2[i];
-    const double bb = sqrt(b2);
-    const double sg = sqrt(s2);
+  double thr = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const double b2 = readlane_f64(b2l, i);
+    const double bb = readlane_f64(bl, i);
+    const double u = readlane_f64(ul, i);
+    const double sg = __builtin_amdgcn_sqrt(s2);
     const double bsc = bb * sg * c;
     const double aa = fmax(bsc, b2);
-    const double u = s_thr[i];
-    s_thr[i] = aa > 0.0 ? aa * (1.0 - 2.0 * u) : (u < 0.5 ? INFINITY : -INFINITY);
-    if (bsc >= b2)
-      s2 = s2 + fmax(0.0, b2 * k1 - k2 * sg * bb);
-    else
-      s2 = fmax(s2, b2);
+    const double t = aa > 0.0 ? aa * (1.0 - 2.0 * u) : (u < 0.5 ? INFINITY : -INFINITY);
+    thr = lane == i ? t : thr;
+    s2 = bsc >= b2 ? s2 + fmax(0.0, b2 * k1 - k2 * sg * bb) : fmax(s2, b2);
   }
+  if (mine) s_thr[i0 + lane] = thr;
   st.s2 = s2;
 }
 
@@ -250,7 +299,8 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
   double* s_b2 = s_thr + P;           // P
   double* s_alpha = s_b2 + P;         // P
   double* s_eta = s_alpha + P;        // P   (+1 / -1)
-  double* s_G = s_eta + P;            // 2 x 64 x 65
+  double* s_b = s_eta + P;            // P   (b = sqrt(b^2))
+  double* s_G = s_b + P;              // 2 x 64 x 65
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -263,17 +313,15 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
     s_thr[i] = philox_uniform(static_cast<uint64_t>(i), a.bin_base + lb, static_cast<uint64_t>(unit), a.tag,
                               a.seed);
     s_b2[i] = fmax(G[static_cast<int64_t>(i) * P + i], 0.0);
+    s_b[i] = sqrt(s_b2[i]);
     s_alpha[i] = 0.0;
   }
   __syncthreads();
   SigmaState sig{0.0};
   const int np = (P + 63) / 64;
   // panel 0: thresholds and diagonal block
-  if (tid == 192) sigma_chain(sig, s_b2, s_thr, 0, min(64, P), c, k1, k2);
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int r = e >> 6, cc = e & 63;
-    s_G[r * 65 + cc] = (r < P && cc <= r) ? G[static_cast<int64_t>(r) * P + cc] : 0.0;
-  }
+  if (w == 3) sigma_chain_wave(sig, s_b2, s_b, s_thr, 0, P, c, k1, k2);
+  stage_block<16>(G, P, 0, s_G, tid);
   __syncthreads();
 
   const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
@@ -305,31 +353,88 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
         if (dec) dec[i] = first ? 1 : 0;
       }
     } else if (w == 3) {
-      if (lane == 0 && p + 1 < np) sigma_chain(sig, s_b2, s_thr, p0 + 64, min(p0 + 128, P), c, k1, k2);
+      if (p + 1 < np) sigma_chain_wave(sig, s_b2, s_b, s_thr, p0 + 64, P, c, k1, k2);
     } else if (p + 1 < np) {
       // waves 1 and 2 stage the next diagonal block
-      double* nb = s_G + ((p + 1) & 1) * 64 * 65;
-      const int q0 = p0 + 64;
-      for (int e = tid - 64; e < 64 * 64; e += 128) {
-        const int r = e >> 6, cc = e & 63;
-        nb[r * 65 + cc] = (q0 + r < P && cc <= r) ? G[static_cast<int64_t>(q0 + r) * P + q0 + cc] : 0.0;
-      }
+      stage_block<32>(G, P, p0 + 64, s_G + ((p + 1) & 1) * 64 * 65, tid - 64);
     }
     __syncthreads();
     // the panel's contribution to every later pair
     if (p + 1 < np) {
       for (int i = p0 + 64 + tid; i < P; i += 256) {
         const double* row = G + static_cast<int64_t>(i) * P + p0;
+        double gv[64];                       // full panel: rows == 64 here; all loads in flight
+#pragma unroll
+        for (int j = 0; j < 64; ++j) gv[j] = row[j];
         double acc0 = 0.0, acc1 = 0.0;
-#pragma unroll 16
-        for (int j = 0; j < 64; j += 2) {   // full panel: rows == 64 here
-          acc0 += s_eta[p0 + j] * row[j];
-          acc1 += s_eta[p0 + j + 1] * row[j + 1];
+#pragma unroll
+        for (int j = 0; j < 64; j += 2) {
+          acc0 += s_eta[p0 + j] * gv[j];
+          acc1 += s_eta[p0 + j + 1] * gv[j + 1];
         }
         s_alpha[i] += acc0 + acc1;
       }
       __syncthreads();
     }
+  }
+}
+
+// Bins of at most 64 pairs: one wave per bin, four bins per workgroup.
+// Lane i holds pair i: its threshold, alpha_i and row i of G (lower part)
+// in registers; lane 0 runs the sigma recursion reading b_i from lane i.
+template <int PMAX>
+__global__ __launch_bounds__(256) void halving_sweep_small_kernel(SweepLaunch a) {
+  const int P = a.N / 2;
+  const int lane = threadIdx.x & 63;
+  const int z = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (z >= a.nbins) return;   // whole wave: no barrier in this kernel
+  const int unit = z / a.bins_per_unit;
+  const int lb = z % a.bins_per_unit;
+  const double* G = a.G + static_cast<int64_t>(z) * P * P;
+  const bool mine = lane < P;
+  const double u = mine ? philox_uniform(static_cast<uint64_t>(lane), a.bin_base + lb, static_cast<uint64_t>(unit),
+                                         a.tag, a.seed)
+                        : 0.0;
+  const double b2 = mine ? fmax(G[static_cast<int64_t>(lane) * P + lane], 0.0) : 0.0;
+  const double bb = sqrt(b2);
+  double g[PMAX];
+#pragma unroll
+  for (int j = 0; j < PMAX; ++j) g[j] = (mine && j < lane) ? G[static_cast<int64_t>(lane) * P + j] : 0.0;
+  // thresholds: the recursion runs on uniform values read with readlane
+  const double c = sqrt(2.0 * log(2.0 * a.N / a.delta));
+  const double k1 = 1.0 + 1.0 / (c * c);
+  const double k2 = 2.0 / c;
+  double thr = 0.0;
+  double s2 = 0.0;
+  for (int i = 0; i < P; ++i) {
+    const double b2i = readlane_f64(b2, i);
+    const double bi = readlane_f64(bb, i);
+    const double ui = readlane_f64(u, i);
+    const double sg = __builtin_amdgcn_sqrt(s2);
+    const double bsc = bi * sg * c;
+    const double aa = fmax(bsc, b2i);
+    const double t = aa > 0.0 ? aa * (1.0 - 2.0 * ui) : (ui < 0.5 ? INFINITY : -INFINITY);
+    if (lane == i) thr = t;
+    if (bsc >= b2i)
+      s2 = s2 + fmax(0.0, b2i * k1 - k2 * sg * bi);
+    else
+      s2 = fmax(s2, b2i);
+  }
+  double alpha = 0.0;
+  uint64_t bits = 0;
+#pragma unroll
+  for (int j = 0; j < PMAX; ++j) {
+    if (j >= P) continue;   // uniform: P is the same for the whole wave
+    const uint64_t m = __ballot(alpha < thr);
+    const bool first = (m >> j) & 1ull;
+    bits |= static_cast<uint64_t>(first) << j;
+    alpha += first ? g[j] : -g[j];
+  }
+  if (mine) {
+    const bool first = (bits >> lane) & 1ull;
+    const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
+    a.idx_out[static_cast<int64_t>(z) * a.out_stride + lane] = in[2 * lane + (first ? 0 : 1)];
+    if (a.dec) a.dec[static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) + lane] = first ? 1 : 0;
   }
 }
 
@@ -493,9 +598,17 @@ hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t sweep_lds_bytes(int N) { return (4 * static_cast<size_t>(N / 2) + 2 * 64 * 65) * sizeof(double); }
+size_t sweep_lds_bytes(int N) { return (5 * static_cast<size_t>(N / 2) + 2 * 64 * 65) * sizeof(double); }
 
 hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s) {
+  if (a.N / 2 <= 16) {
+    hipLaunchKernelGGL(halving_sweep_small_kernel<16>, dim3((a.nbins + 3) / 4), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  if (a.N / 2 <= 64) {
+    hipLaunchKernelGGL(halving_sweep_small_kernel<64>, dim3((a.nbins + 3) / 4), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const size_t lds = sweep_lds_bytes(a.N);
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(halving_sweep_kernel),
