@@ -34,6 +34,12 @@ WORKLOADS = {
 }
 
 
+def _traffic(label, workload):
+    """HBM bytes per launch from the committed counter runs, None if absent or the kernel changed since."""
+    from sub_quadratic_attention_amd.profiling import traffic_for
+    return traffic_for(label, workload)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -42,6 +48,8 @@ def parse():
     p.add_argument("--workload", default="vit_token_mixing", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-exact", action="store_true")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -197,7 +205,8 @@ def decode_main(args):
     if kd:
         gbs = dec_bytes / (kd["avg_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK["hbm_GBs"], "unit": "GB/s",
-                "frac": round(gbs / PEAK["hbm_GBs"], 4), "traffic": None, "kernel": "kv_decode",
+                "frac": round(gbs / PEAK["hbm_GBs"], 4), "traffic": _traffic("kv_decode", "kv_decode"),
+                "kernel": "kv_decode",
                 "work_per_launch_bytes": dec_bytes, "avg_launch_ms": kd["avg_ms"]}
     exact = {}
     if not args.no_exact:
@@ -257,6 +266,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
+        return
     if args.workload == "kv_decode":
         return decode_main(args)
     gen_kw, causal, H, Hkv, E, D = WORKLOADS[args.workload]
@@ -320,6 +338,8 @@ def main():
         return res
 
     roofline = roof(dom) if wm.get(dom) else None
+    if roofline:
+        roofline["traffic"] = _traffic(dom, args.workload)
     rooflines = {l: roof(l) for l in per_kernel if wm.get(l)}
 
     # exact comparators on the same GPU
