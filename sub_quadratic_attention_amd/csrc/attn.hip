@@ -81,8 +81,7 @@ struct Attn {
   f32x4_t o[ND];
   float m_run, l_run;
 
-  __device__ Attn(const AttnLaunch& la, Smem<BF16, E, D>& s, int q0) : a(la), sm(s) {
-    const int bh = blockIdx.y;
+  __device__ Attn(const AttnLaunch& la, Smem<BF16, E, D>& s, int q0, int bh) : a(la), sm(s) {
     b = bh / a.H;
     h = bh % a.H;
     hk = h / (a.H / a.H_kv);
@@ -338,10 +337,12 @@ __device__ void express_block(A& at, const ExpressView& ev, int beta, int S, int
 template <bool BF16, int E, int D>
 __global__ __launch_bounds__(256) void seg_attention_kernel(AttnLaunch a) {
   __shared__ Smem<BF16, E, D> sm;
-  const int q0 = blockIdx.x * kQT;
-  Attn<BF16, E, D> at(a, sm, q0);
+  const int64_t tile = xcd_remap(blockIdx.y * static_cast<int64_t>(gridDim.x) + blockIdx.x,
+                                 static_cast<int64_t>(gridDim.x) * gridDim.y);
+  const int q0 = static_cast<int>(tile % gridDim.x) * kQT;
+  const int bh = static_cast<int>(tile / gridDim.x);
+  Attn<BF16, E, D> at(a, sm, q0, bh);
   if (!a.causal) {
-    const int bh = blockIdx.y;
     const int b = bh / a.H, hk = (bh % a.H) / (a.H / a.H_kv);
     const int unit = b * a.H_kv + hk;
     if (a.cs_idx)

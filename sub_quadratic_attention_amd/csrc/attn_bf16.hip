@@ -79,8 +79,7 @@ struct AttnB {
     float l2;
   };
 
-  __device__ AttnB(const AttnLaunch& la, SmemB<E, D>& s, int q0) : a(la), sm(s) {
-    const int bh = blockIdx.y;
+  __device__ AttnB(const AttnLaunch& la, SmemB<E, D>& s, int q0, int bh) : a(la), sm(s) {
     b = bh / a.H;
     h = bh % a.H;
     hk = h / (a.H / a.H_kv);
@@ -314,8 +313,10 @@ __device__ void express_block_b(AttnB<E, D>& at, const ExpressView& ev, int beta
 template <int E, int D>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnLaunch a) {
   __shared__ SmemB<E, D> sm;
-  const int q0 = blockIdx.x * kQ;
-  AttnB<E, D> at(a, sm, q0);
+  const int64_t tile = xcd_remap(blockIdx.y * static_cast<int64_t>(gridDim.x) + blockIdx.x,
+                                 static_cast<int64_t>(gridDim.x) * gridDim.y);
+  const int q0 = static_cast<int>(tile % gridDim.x) * kQ;
+  AttnB<E, D> at(a, sm, q0, static_cast<int>(tile / gridDim.x));
   if (!a.causal) {
     bool ok[NQG];
     for (int qg = 0; qg < NQG; ++qg) ok[qg] = true;

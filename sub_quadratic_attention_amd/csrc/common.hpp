@@ -72,6 +72,17 @@ __device__ __forceinline__ double philox_uniform(uint64_t c0, uint64_t c1, uint6
   return static_cast<double>(philox_word0(c0, c1, c2, c3, seed) >> 11) * 0x1.0p-53;
 }
 
+// The dispatcher hands workgroups to the chip's 8 XCDs round-robin by linear
+// id, and each XCD has its own L2.  Remap the linear id so that every XCD
+// receives one contiguous range of logical ids: neighbouring tiles, which read
+// the same rows, then share one L2 instead of fetching them eight times.
+__device__ __forceinline__ int64_t xcd_remap(int64_t pid, int64_t total) {
+  constexpr int64_t kXcd = 8;
+  const int64_t q = total / kXcd, r = total % kXcd;
+  const int64_t x = pid % kXcd, local = pid / kXcd;
+  return x * q + (x < r ? x : r) + local;
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

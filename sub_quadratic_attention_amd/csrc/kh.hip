@@ -62,6 +62,31 @@ __device__ __forceinline__ double raw8_at(const Raw8& r, int j) {
   }
 }
 
+// e^x in fp64 for finite x: Cody-Waite reduction x = n ln2 + r (ln2 split into
+// a double and its remainder, so r is exact to far below an ulp), |r| <= ln2/2,
+// the Taylor series of e^r through r^13 (truncation < 5e-18 relative), then a
+// scaling by 2^n (overflow gives inf, underflow 0 or a subnormal).
+__device__ __forceinline__ double exp_f64(double x) {
+  const double n = __builtin_rint(x * 1.4426950408889634);
+  double r = fma(-n, 0x1.62e42fefa39efp-1, x);
+  r = fma(-n, 0x1.abc9e3b39803fp-56, r);
+  double p = 1.6059043836821613e-10;
+  p = fma(p, r, 2.08767569878681e-09);
+  p = fma(p, r, 2.505210838544172e-08);
+  p = fma(p, r, 2.755731922398589e-07);
+  p = fma(p, r, 2.7557319223985893e-06);
+  p = fma(p, r, 2.48015873015873e-05);
+  p = fma(p, r, 0.0001984126984126984);
+  p = fma(p, r, 0.001388888888888889);
+  p = fma(p, r, 0.008333333333333333);
+  p = fma(p, r, 0.041666666666666664);
+  p = fma(p, r, 0.16666666666666666);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return __builtin_amdgcn_ldexp(p, static_cast<int>(fmax(fmin(n, 2100.0), -2100.0)));
+}
+
 // Tiles.  Bins get the lower-triangular 32 x 32 pair tiles of their own
 // P x P Gram, except bins with P dividing 32 (P < 32), which are packed: a unit's bins
 // are consecutive in its point list, so one diagonal tile of 32 pairs covers
@@ -71,17 +96,18 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
   const int P = a.N / 2;
   const bool packed = P < 32 && (32 % P) == 0;   // whole bins per tile
+  const int bid = static_cast<int>(xcd_remap(blockIdx.x, gridDim.x));
   int unit, tr, tc, z;
   if (packed) {
     const int tiles = (a.bins_per_unit * P + 31) / 32;
-    unit = static_cast<int>(blockIdx.x / tiles);
-    tr = tc = static_cast<int>(blockIdx.x % tiles);
+    unit = bid / tiles;
+    tr = tc = bid % tiles;
     z = -1;
   } else {
     const int nt = (P + 31) / 32;
     const int tiles = nt * (nt + 1) / 2;
-    z = static_cast<int>(blockIdx.x / tiles);
-    const int t = static_cast<int>(blockIdx.x % tiles);
+    z = bid / tiles;
+    const int t = bid % tiles;
     tr = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
     while (tr * (tr + 1) / 2 > t) --tr;
     while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
@@ -180,10 +206,10 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = r0 + kq + 4 * i;
-    const double kee = exp(a.scale * acc[0][0][i]) * (acc[1][0][i] + 1.0);
-    const double keo = exp(a.scale * acc[0][1][i]) * (acc[1][1][i] + 1.0);
-    const double koe = exp(a.scale * acc[0][2][i]) * (acc[1][2][i] + 1.0);
-    const double koo = exp(a.scale * acc[0][3][i]) * (acc[1][3][i] + 1.0);
+    const double kee = exp_f64(a.scale * acc[0][0][i]) * (acc[1][0][i] + 1.0);
+    const double keo = exp_f64(a.scale * acc[0][1][i]) * (acc[1][1][i] + 1.0);
+    const double koe = exp_f64(a.scale * acc[0][2][i]) * (acc[1][2][i] + 1.0);
+    const double koo = exp_f64(a.scale * acc[0][3][i]) * (acc[1][3][i] + 1.0);
     const double gv = (kee - keo) - (koe - koo);
     if (packed) {
       const int bin = row / P;
