@@ -1,27 +1,33 @@
 // Weighted-coreset / Express attention for bfloat16 inputs on gfx950.
 //
-// Same definition as the fp32 kernel (attn.hip): for every query the
-// visible keys form segments (coreset or cache / buffer index lists with a
-// log-weight, raw token ranges with weight 1, the block being streamed with a
-// causal mask); out = sum w e^{s<q,k>} v / sum w e^{s<q,k>}, ln w folded into
-// the logit, online softmax, fp32 accumulation, MFMA for Q K^T and P V.
+// Same definition as the fp32 kernel (attn.hip): for every query the visible
+// keys are a gathered part (coreset, or cache / buffer index lists of the
+// Express state, each list with its log-weight) followed by a raw token range
+// (weight 1; causal inside the block being streamed);
+// out = sum w e^{s<q,k>} v / sum w e^{s<q,k>}, ln w folded into the logit,
+// online softmax, fp32 accumulation, MFMA (v_mfma_f32_16x16x32_bf16) for
+// Q K^T and P V.
 //
-// Layout for bf16 (MFMA v_mfma_f32_16x16x32_bf16):
-//  * one workgroup = 8 waves x 16 queries of one (b, h), all sharing each
-//    staged key chunk;
-//  * keys are staged 64 at a time in LDS, K and V both row-major (16-byte
-//    global loads and LDS writes); the next chunk is loaded into registers
-//    while the current one is consumed;
+// Layout:
+//  * one workgroup = 4 waves x 16 NQG queries of one (b, h); two workgroups
+//    fit one CU, so one workgroup's MFMA phase overlaps the other's softmax;
+//  * the keys visible to the workgroup form one stream: its token indices
+//    (gathered lists, then the raw tail) are staged in LDS in windows of up to
+//    kIdxCap keys (a stream of only a raw range needs none), then 64-key chunks
+//    of K and V (row-major, 16-byte loads and stores) go through two LDS
+//    buffers with one barrier per chunk; chunk c + 2 is loaded into registers
+//    while chunk c is consumed, and stored when chunk c + 1 is.  Chunk loads
+//    are branch-free, so a thread's loads are all in flight together;
+//  * S^T = K Q^T keeps one query per lane column, so softmax statistics and
+//    the O^T = V^T P^T accumulator of a query share lanes; each K fragment
+//    read from LDS feeds the NQG query groups of the wave;
 //  * the V operand of P V is read with the gfx950 transposing LDS read
 //    (ds_read_tr16_b64): within each 16-lane group, lane j receives element
 //    j % 4 of the 8-byte pieces addressed by lanes j/4 + 4k (k = 0..3), so
 //    lanes addressing V[k0 + i/4][d0 + 4 (i % 4)] deliver V[k0..k0+3][d0 + j]
-//    to lane j: four keys of one dimension, as the MFMA operand wants;
-//  * the index list of a gathered segment is staged in LDS once, so chunk
-//    loads never wait on a dependent global index read;
-//  * S^T = K Q^T keeps one query per lane column, so softmax statistics and
-//    the O^T = V^T P^T accumulator of a query share lanes.
+//    to lane j: four keys of one dimension, as the MFMA operand wants.
 
+#include <limits.h>
 #include <math.h>
 
 #include "common.hpp"
@@ -31,59 +37,87 @@ namespace thin {
 
 namespace {
 
-constexpr int kQ = 128;       // queries per workgroup
-constexpr int kThreads = 512; // 8 waves x 16 queries
-constexpr int NQG = 1;        // 16-query groups per wave
-constexpr int kC = 64;        // keys per chunk
-constexpr int kIdxCap = 1024; // index entries staged per pass
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kC = 64;          // keys per chunk
+constexpr int kIdxCap = 1536;   // gathered indices staged per window
+constexpr int kIdxPT = kIdxCap / kThreads;
 constexpr float kLog2eB = 1.4426950408889634f;
 
-struct SegB {
-  const int32_t* idx;   // nullptr: raw token range
-  int start;
-  int count;
+template <int E, int D>
+constexpr int nqg() { return (E <= 128 && D <= 128) ? 2 : 1; }   // 16-query groups per wave
+
+// Gathered part of a stream: up to three index lists, one after the other.
+// Lists 0 and 1 carry log2-weight lnw2, list 2 half that weight (lnw2 - 1);
+// a single list may instead carry per-entry weights w.
+struct Gather {
+  const int32_t* p[3];
+  int cnt[3];
   float lnw2;
   const float* w;
+};
+
+// Raw part: tokens start .. start + count - 1, log2-weight lnw2, causal mask.
+struct Raw {
+  int start, count;
+  float lnw2;
   int causal;
 };
 
 template <int E, int D>
 struct SmemB {
-  uint16_t k[kC][E + 8];
-  uint16_t v[kC][D + 16];      // row stride D + 16 keeps the transposing reads conflict-free
-  float lnw2[kC];
-  int pos[kC];
+  uint16_t k[2][kC][E + 8];    // row stride E + 8: 16 consecutive rows hit distinct banks
+  uint16_t v[2][kC][D + 16];   // row stride D + 16 keeps the transposing reads conflict-free
+  float lnw2[2][kC];
+  int posc[2][kC];             // key visible to query t iff posc <= t (INT_MIN: always, INT_MAX: never)
   int idx[kIdxCap];
 };
 
-template <int E, int D>
+// RAW: the stream is one raw token range (exact attention), tokens computed;
+// otherwise every token of the stream is staged in sm.idx.
+template <int E, int D, bool RAW>
 struct AttnB {
+  static constexpr int NQG = nqg<E, D>();
   static constexpr int NK = E / 32;   // k-steps of Q K^T
   static constexpr int ND = D / 16;   // 16-dim output blocks
-  static constexpr int KPT = kC * E / 8 / kThreads;   // 16-byte pieces per thread
-  static constexpr int VPT = kC * D / 8 / kThreads;
+  static constexpr int KP = E / 8;    // 16-byte pieces per K row
+  static constexpr int VP = D / 8;
+  static constexpr int KPT = kC * KP / kThreads;   // pieces per thread per chunk
+  static constexpr int VPT = kC * VP / kThreads;
 
   const AttnLaunch& a;
   SmemB<E, D>& sm;
   int b, h, hk, unit, lane, g;
+  // K / V rows of this unit: token t starts at kbase + t * kstride (elements);
+  // offsets stay below 2^30 elements (checked by the host), so they are 32-bit
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  uint32_t kstride, vstride;
   int qr[NQG];
   bool live[NQG];
   bf16x8_t qf[NQG][NK];
   f32x4_t o[NQG][ND];
   float m_run[NQG], l_run[NQG];
 
-  struct Chunk {
-    uint4 k[KPT];
-    uint4 v[VPT];
-    int pos;
-    float l2;
-  };
+  // one chunk in flight
+  uint4 rk[KPT];
+  uint4 rv[VPT];
+  float r_w;   // per-entry weight of the key this thread describes (weighted coreset)
 
-  __device__ AttnB(const AttnLaunch& la, SmemB<E, D>& s, int q0, int bh) : a(la), sm(s) {
+  // the stream: G gathered keys, then raw.count raw ones; current window [w0, w0 + wl)
+  Gather gs;
+  Raw raw;
+  int G, w0, wl;
+
+  __device__ __forceinline__ AttnB(const AttnLaunch& la, SmemB<E, D>& s, int q0, int bh) : a(la), sm(s) {
     b = bh / a.H;
     h = bh % a.H;
     hk = h / (a.H / a.H_kv);
     unit = b * a.H_kv + hk;
+    kstride = static_cast<uint32_t>(a.H_kv * E);
+    vstride = static_cast<uint32_t>(a.H_kv * D);
+    kbase = static_cast<const uint16_t*>(a.k) + (static_cast<int64_t>(b) * a.S * a.H_kv + hk) * E;
+    vbase = static_cast<const uint16_t*>(a.v) + (static_cast<int64_t>(b) * a.S * a.H_kv + hk) * D;
     lane = threadIdx.x & 63;
     g = lane >> 4;
     const int w = threadIdx.x >> 6;
@@ -104,64 +138,65 @@ struct AttnB {
     }
   }
 
-  __device__ __forceinline__ int token(const SegB& s, int base, int j) const {
-    return s.idx ? sm.idx[j] : s.start + base + j;
+  // token of window position r (r < wl)
+  __device__ __forceinline__ int token(int r) const {
+    if constexpr (RAW) return raw.start + w0 + r;
+    else return sm.idx[min(r, kIdxCap - 1)];
   }
 
-  __device__ __forceinline__ void load(const SegB& s, int base, int c0, int nk, Chunk& ch) const {
+  // Chunk c of the window into registers.  Nothing here waits for a load:
+  // rows beyond the window read the unit's first row and are zeroed by
+  // store(), and the per-key values are finished there too.
+  __device__ __forceinline__ void load(int c) {
     const int tid = threadIdx.x;
-    const int64_t kv_base = static_cast<int64_t>(b) * a.S;
-    constexpr int KP = E / 8;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int r = kC * c + (tid + kThreads * j) / KP;
+      const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), kstride) +
+                           static_cast<uint32_t>((tid % KP) * 8);
+      rk[j] = *reinterpret_cast<const uint4*>(kbase + off);
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int r = kC * c + (tid + kThreads * j) / VP;
+      const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), vstride) +
+                           static_cast<uint32_t>((tid % VP) * 8);
+      rv[j] = *reinterpret_cast<const uint4*>(vbase + off);
+    }
+    if (gs.w != nullptr && G > 0 && tid < kC) r_w = gs.w[min(w0 + kC * c + tid, G - 1)];
+  }
+
+  // Chunk c (in registers) into buffer buf, with its per-key visibility and
+  // log2-weight.
+  __device__ __forceinline__ void store(int c, int buf) {
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int p = tid + kThreads * j;
-      const int r = p / KP, c = p % KP;
-      ch.k[j] = uint4{0, 0, 0, 0};
-      if (r < nk) {
-        const int64_t row = (kv_base + token(s, base, c0 + r)) * a.H_kv + hk;
-        ch.k[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + row * E + c * 8);
-      }
+      const bool ok = kC * c + p / KP < wl;
+      *reinterpret_cast<uint4*>(&sm.k[buf][p / KP][(p % KP) * 8]) = ok ? rk[j] : uint4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int p = tid + kThreads * j;
-      const int r = p / (D / 8), c = p % (D / 8);
-      ch.v[j] = uint4{0, 0, 0, 0};
-      if (r < nk) {
-        const int64_t row = (kv_base + token(s, base, c0 + r)) * a.H_kv + hk;
-        ch.v[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + row * D + c * 8);
-      }
-    }
-    ch.pos = 0x7fffffff;
-    ch.l2 = -INFINITY;
-    if (tid < kC && tid < nk) {
-      ch.pos = token(s, base, c0 + tid);
-      ch.l2 = s.w ? log2f(s.w[s.start + base + c0 + tid]) : s.lnw2;
-    }
-  }
-
-  __device__ __forceinline__ void store(const Chunk& ch) {
-    const int tid = threadIdx.x;
-    constexpr int KP = E / 8;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int p = tid + kThreads * j;
-      const int r = p / KP, c = p % KP;
-      *reinterpret_cast<uint4*>(&sm.k[r][c * 8]) = ch.k[j];
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int p = tid + kThreads * j;
-      const int r = p / (D / 8), c = p % (D / 8);
-      *reinterpret_cast<uint4*>(&sm.v[r][c * 8]) = ch.v[j];
+      const bool ok = kC * c + p / VP < wl;
+      *reinterpret_cast<uint4*>(&sm.v[buf][p / VP][(p % VP) * 8]) = ok ? rv[j] : uint4{0, 0, 0, 0};
     }
     if (tid < kC) {
-      sm.pos[tid] = ch.pos;
-      sm.lnw2[tid] = ch.l2;
+      const int r = kC * c + tid;
+      const int pos = w0 + r;   // position in the stream
+      const bool gathered = pos < G;
+      const float lg = gs.w != nullptr ? log2f(r_w) : gs.lnw2 - (pos < gs.cnt[0] + gs.cnt[1] ? 0.f : 1.f);
+      int posc = gathered ? INT_MIN : (raw.causal ? raw.start + (pos - G) : INT_MIN);
+      float lw = gathered ? lg : raw.lnw2;
+      posc = r < wl ? posc : INT_MAX;
+      lw = r < wl ? lw : -INFINITY;
+      sm.posc[buf][tid] = posc;
+      sm.lnw2[buf][tid] = lw;
     }
   }
 
-  __device__ void consume(const SegB& s, const bool row_ok[NQG]) {
+  __device__ __forceinline__ void consume(int buf, const bool row_ok[NQG]) {
     f32x4_t st[NQG][4];
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg)
@@ -171,12 +206,21 @@ struct AttnB {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&sm.k[kb * 16 + (lane & 15)][kk * 32 + 8 * g]);
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&sm.k[buf][kb * 16 + (lane & 15)][kk * 32 + 8 * g]);
 #pragma unroll
         for (int qg = 0; qg < NQG; ++qg)
           st[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qg][kk], st[qg][kb], 0, 0, 0);
       }
     const float sc = a.scale * kLog2eB;
+    int pc[4][4];
+    float lw[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int4 pv = *reinterpret_cast<const int4*>(&sm.posc[buf][kb * 16 + 4 * g]);
+      const float4 lv = *reinterpret_cast<const float4*>(&sm.lnw2[buf][kb * 16 + 4 * g]);
+      pc[kb][0] = pv.x, pc[kb][1] = pv.y, pc[kb][2] = pv.z, pc[kb][3] = pv.w;
+      lw[kb][0] = lv.x, lw[kb][1] = lv.y, lw[kb][2] = lv.z, lw[kb][3] = lv.w;
+    }
     bf16x8_t pb[NQG][2];
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg) {
@@ -186,9 +230,8 @@ struct AttnB {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kk = kb * 16 + 4 * g + i;
-          const bool vis = row_ok[qg] && (!s.causal || sm.pos[kk] <= qr[qg]);
-          const float val = vis ? st[qg][kb][i] * sc + sm.lnw2[kk] : -INFINITY;
+          const bool vis = row_ok[qg] && pc[kb][i] <= qr[qg];
+          const float val = vis ? fmaf(st[qg][kb][i], sc, lw[kb][i]) : -INFINITY;
           x[kb][i] = val;
           mx = fmaxf(mx, val);
         }
@@ -229,9 +272,9 @@ struct AttnB {
       for (int hh = 0; hh < 2; ++hh) {
         typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
         const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)&sm.v[32 * hh + 4 * g + (i16 >> 2)][16 * d + 4 * (i16 & 3)]);
+            (lds_bf16x4*)&sm.v[buf][32 * hh + 4 * g + (i16 >> 2)][16 * d + 4 * (i16 & 3)]);
         const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)&sm.v[32 * hh + 16 + 4 * g + (i16 >> 2)][16 * d + 4 * (i16 & 3)]);
+            (lds_bf16x4*)&sm.v[buf][32 * hh + 16 + 4 * g + (i16 >> 2)][16 * d + 4 * (i16 & 3)]);
         const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int qg = 0; qg < NQG; ++qg)
@@ -239,27 +282,61 @@ struct AttnB {
       }
   }
 
-  __device__ void run_segment(const SegB s, const bool row_ok[NQG]) {
-    for (int base = 0; base < s.count; base += kIdxCap) {
-      const int cnt = min(kIdxCap, s.count - base);
-      if (s.idx) {
-        __syncthreads();
-        for (int j = threadIdx.x; j < cnt; j += kThreads) sm.idx[j] = s.idx[s.start + base + j];
-        __syncthreads();
+  // One window: its tokens are staged (all loads in flight at once), then
+  // its chunks stream through the two buffers.
+  __device__ __forceinline__ void run_window(const bool row_ok[NQG]) {
+    __syncthreads();   // earlier users of sm.idx and of the buffers are done
+    if constexpr (!RAW) {
+      const int c0 = gs.cnt[0], c01 = gs.cnt[0] + gs.cnt[1];
+      int v[kIdxPT];
+#pragma unroll
+      for (int i = 0; i < kIdxPT; ++i) {
+        const int pos = w0 + min(static_cast<int>(threadIdx.x) + kThreads * i, wl - 1);
+        const int32_t* src = pos < c0 ? gs.p[0] + pos : (pos < c01 ? gs.p[1] + (pos - c0) : gs.p[2] + (pos - c01));
+        v[i] = pos < G ? *src : raw.start + (pos - G);
       }
-      Chunk ch;
-      load(s, base, 0, min(kC, cnt), ch);
-      for (int c0 = 0; c0 < cnt; c0 += kC) {
-        __syncthreads();
-        store(ch);
-        __syncthreads();
-        if (c0 + kC < cnt) load(s, base, c0 + kC, min(kC, cnt - c0 - kC), ch);
-        consume(s, row_ok);
+#pragma unroll
+      for (int i = 0; i < kIdxPT; ++i) {
+        const int e = threadIdx.x + kThreads * i;
+        if (e < wl) sm.idx[e] = v[i];
       }
+      __syncthreads();
+    }
+    const int nch = (wl + kC - 1) / kC;
+    load(0);
+    store(0, 0);
+    if (nch > 1) load(1);
+    __syncthreads();
+    for (int c = 0; c < nch; c += 2) {   // unrolled by two: the buffer of each step is a constant
+      step<0>(c, nch, row_ok);
+      if (c + 1 < nch) step<1>(c + 1, nch, row_ok);
     }
   }
 
-  __device__ void finish() {
+  // chunk c sits in buffer B; chunk c + 1 goes from the registers to the other
+  // buffer, chunk c + 2 from memory to the registers
+  template <int B>
+  __device__ __forceinline__ void step(int c, int nch, const bool row_ok[NQG]) {
+    if (c + 1 < nch) store(c + 1, 1 - B);
+    if (c + 2 < nch) load(c + 2);
+    consume(B, row_ok);
+    __syncthreads();
+  }
+
+  // The whole stream, in windows of at most kIdxCap staged tokens.
+  __device__ __forceinline__ void run_stream(const Gather& gather, const Raw& r, const bool row_ok[NQG]) {
+    gs = gather;
+    raw = r;
+    G = gs.cnt[0] + gs.cnt[1] + gs.cnt[2];
+    const int L = G + raw.count;
+    const int cap = RAW ? L : kIdxCap;
+    for (w0 = 0; w0 < L; w0 += cap) {
+      wl = min(cap, L - w0);
+      run_window(row_ok);
+    }
+  }
+
+  __device__ __forceinline__ void finish() {
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg) {
       if (!live[qg]) continue;
@@ -278,13 +355,22 @@ struct AttnB {
   }
 };
 
-template <int E, int D>
-__device__ void express_block_b(AttnB<E, D>& at, const ExpressView& ev, int beta, int S, int key_end) {
-  bool row_ok[NQG];
-  for (int qg = 0; qg < NQG; ++qg) row_ok[qg] = (at.qr[qg] / ev.n) == beta;
-  const int unit = at.unit;
+// Stream of pass `pass` of the workgroup.  Unmasked: one pass (the coreset,
+// or all S keys).  Causal: one pass per block beta met by the workgroup's
+// queries; pass beta covers the queries of block beta (tokens
+// [beta n, (beta + 1) n)) and holds the Express state after blocks
+// 0 .. beta-1, then the block itself up to key_end with the causal mask:
+//   beta < 4: everything before is still exact (raw, weight 1);
+//   else, with E = floor(log4 beta), m = 4^E, since = beta - m:
+//     cache   = HALVE output E-1 and batches 3(E-1) .. 3(E-1) + since/m - 1 (weight m),
+//     buffer  = the first (since % m) 2n / m representatives of batch 3(E-1) + since/m
+//               (weight m/2),
+//   each weight as log2 added to the logit.
+__device__ __forceinline__ void express_pass(const ExpressView& ev, int unit, int beta, int S, int key_end,
+                                             Gather& gs, Raw& raw) {
+  gs = Gather{{nullptr, nullptr, nullptr}, {0, 0, 0}, 0.f, nullptr};
   if (beta < 4) {
-    at.run_segment(SegB{nullptr, 0, min(key_end, S), 0.f, nullptr, 1}, row_ok);
+    raw = Raw{0, min(key_end, S), 0.f, 1};
     return;
   }
   int Ep = 1;
@@ -293,52 +379,61 @@ __device__ void express_block_b(AttnB<E, D>& at, const ExpressView& ev, int beta
   const int since = beta - m;
   const int nbc = since / m;
   const int rem = since % m;
-  const float lm = static_cast<float>(2 * Ep);
-  at.run_segment(SegB{ev.halve_out + (static_cast<int64_t>(unit) * ev.n_halves + (Ep - 1)) * ev.n, 0, ev.n, lm,
-                      nullptr, 0},
-                 row_ok);
-  if (nbc > 0)
-    at.run_segment(SegB{ev.batch_out + (static_cast<int64_t>(unit) * ev.n_batches_done + 3 * (Ep - 1)) * ev.n, 0,
-                        nbc * ev.n, lm, nullptr, 0},
-                   row_ok);
-  const int n_rep = static_cast<int>((static_cast<int64_t>(rem) * 2 * ev.n) / m);
-  if (n_rep > 0)
-    at.run_segment(SegB{ev.reps + (static_cast<int64_t>(unit) * ev.n_batches_alloc + 3 * (Ep - 1) + nbc) * 2 * ev.n,
-                        0, n_rep, lm - 1.0f, nullptr, 0},
-                   row_ok);
+  gs.lnw2 = static_cast<float>(2 * Ep);
+  gs.p[0] = ev.halve_out + (static_cast<int64_t>(unit) * ev.n_halves + (Ep - 1)) * ev.n;
+  gs.cnt[0] = ev.n;
+  gs.p[1] = ev.batch_out + (static_cast<int64_t>(unit) * ev.n_batches_done + 3 * (Ep - 1)) * ev.n;
+  gs.cnt[1] = nbc * ev.n;
+  gs.p[2] = ev.reps + (static_cast<int64_t>(unit) * ev.n_batches_alloc + 3 * (Ep - 1) + nbc) * 2 * ev.n;
+  gs.cnt[2] = static_cast<int>((static_cast<int64_t>(rem) * 2 * ev.n) / m);
   const int bn = beta * ev.n;
-  at.run_segment(SegB{nullptr, bn, min(key_end, S) - bn, 0.f, nullptr, 1}, row_ok);
+  raw = Raw{bn, min(key_end, S) - bn, 0.f, 1};
 }
 
-template <int E, int D>
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnLaunch a) {
+template <int E, int D, bool RAW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(AttnLaunch a) {
+  constexpr int kQ = 16 * nqg<E, D>() * kWaves;
+  constexpr int NQG = AttnB<E, D, RAW>::NQG;
   __shared__ SmemB<E, D> sm;
   const int64_t tile = xcd_remap(blockIdx.y * static_cast<int64_t>(gridDim.x) + blockIdx.x,
                                  static_cast<int64_t>(gridDim.x) * gridDim.y);
   const int q0 = static_cast<int>(tile % gridDim.x) * kQ;
-  AttnB<E, D> at(a, sm, q0, static_cast<int>(tile / gridDim.x));
-  if (!a.causal) {
-    bool ok[NQG];
-    for (int qg = 0; qg < NQG; ++qg) ok[qg] = true;
-    if (a.cs_idx)
-      at.run_segment(SegB{a.cs_idx + at.unit * a.cs_stride, 0, a.cs_n, a.cs_lnw * kLog2eB,
-                          a.cs_w ? a.cs_w + at.unit * a.cs_stride : nullptr, 0},
-                     ok);
-    else
-      at.run_segment(SegB{nullptr, 0, a.S, a.cs_lnw * kLog2eB, nullptr, 0}, ok);
-  } else {
-    const int n = a.ev.n;
-    const int q_last = min(q0 + kQ - 1, a.T - 1);
-    for (int beta = q0 / n; beta <= q_last / n; ++beta)
-      express_block_b(at, a.ev, beta, a.S, min(q_last + 1, (beta + 1) * n));
+  AttnB<E, D, RAW> at(a, sm, q0, static_cast<int>(tile / gridDim.x));
+  const int q_last = min(q0 + kQ - 1, a.T - 1);
+  const int n = a.causal ? a.ev.n : 1;
+  const int beta_lo = a.causal ? q0 / n : 0, beta_hi = a.causal ? q_last / n : 0;
+  for (int beta = beta_lo; beta <= beta_hi; ++beta) {
+    Gather gs;
+    Raw raw;
+    bool row_ok[NQG];
+    if (!a.causal) {
+      gs = Gather{{nullptr, nullptr, nullptr}, {0, 0, 0}, a.cs_lnw * kLog2eB, nullptr};
+      raw = Raw{0, 0, 0.f, 0};
+      if (a.cs_idx) {
+        gs.p[0] = a.cs_idx + at.unit * a.cs_stride;
+        gs.cnt[0] = a.cs_n;
+        gs.w = a.cs_w ? a.cs_w + at.unit * a.cs_stride : nullptr;
+      } else {
+        raw = Raw{0, a.S, a.cs_lnw * kLog2eB, 0};
+      }
+      for (int qg = 0; qg < NQG; ++qg) row_ok[qg] = true;
+    } else {
+      express_pass(a.ev, at.unit, beta, a.S, min(q_last + 1, (beta + 1) * n), gs, raw);
+      for (int qg = 0; qg < NQG; ++qg) row_ok[qg] = (at.qr[qg] / n) == beta;
+    }
+    at.run_stream(gs, raw, row_ok);
   }
   at.finish();
 }
 
 template <int E, int D>
 hipError_t launch_b(const AttnLaunch& a, hipStream_t s) {
+  constexpr int kQ = 16 * nqg<E, D>() * kWaves;
   dim3 grid((a.T + kQ - 1) / kQ, a.B * a.H);
-  hipLaunchKernelGGL((attn_bf16_kernel<E, D>), grid, dim3(kThreads), 0, s, a);
+  if (!a.causal && a.cs_idx == nullptr)   // exact attention: one raw range, nothing staged
+    hipLaunchKernelGGL((attn_bf16_kernel<E, D, true>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<E, D, false>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
