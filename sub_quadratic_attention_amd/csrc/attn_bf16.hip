@@ -14,10 +14,13 @@
 //  * the keys visible to the workgroup form one stream: its token indices
 //    (gathered lists, then the raw tail) are staged in LDS in windows of up to
 //    kIdxCap keys (a stream of only a raw range needs none), then 64-key chunks
-//    of K and V (row-major, 16-byte loads and stores) go through two LDS
-//    buffers with one barrier per chunk; chunk c + 2 is loaded into registers
-//    while chunk c is consumed, and stored when chunk c + 1 is.  Chunk loads
-//    are branch-free, so a thread's loads are all in flight together;
+//    of K and V go through two LDS buffers with one barrier per chunk: chunk
+//    c + 1 is copied from memory straight into LDS (global_load_lds_dwordx4,
+//    16 bytes per lane, no registers) while chunk c is consumed;
+//  * K and V rows sit unpadded in LDS; the 16-byte pieces of row R are stored
+//    permuted (piece q at q ^ f(R)), which the copy does for free by choosing
+//    the global piece each lane fetches, and which makes the MFMA operand
+//    reads hit distinct banks;
 //  * S^T = K Q^T keeps one query per lane column, so softmax statistics and
 //    the O^T = V^T P^T accumulator of a query share lanes; each K fragment
 //    read from LDS feeds the NQG query groups of the wave;
@@ -43,9 +46,23 @@ constexpr int kC = 64;          // keys per chunk
 constexpr int kIdxCap = 1536;   // gathered indices staged per window
 constexpr int kIdxPT = kIdxCap / kThreads;
 constexpr float kLog2eB = 1.4426950408889634f;
+constexpr int kVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters unconstrained
 
 template <int E, int D>
 constexpr int nqg() { return (E <= 128 && D <= 128) ? 2 : 1; }   // 16-query groups per wave
+
+// Piece permutations.  K is read 16 bytes per lane, 16 consecutive rows at one
+// logical piece: 128-element rows take q ^ (R % 16), 64-element rows (two per
+// 256 bytes of banks) q ^ (R / 2 % 8).  V is read 8 bytes per lane by the
+// transposing read, 8 rows x 32 bytes (pieces 2d, 2d + 1) at a time: the
+// permutation keeps the pair together, 2 (R % 8) for rows of 128 or more
+// elements, 2 (R / 2 % 4) for 64.
+typedef __attribute__((address_space(3))) uint16_t lds_u16;   // LDS views of the buffers
+
+template <int E>
+__device__ __forceinline__ int kswz(int R) { return E == 64 ? (R >> 1) & 7 : R & 15; }
+template <int D>
+__device__ __forceinline__ int vswz(int R) { return D == 64 ? 2 * ((R >> 1) & 3) : 2 * (R & 7); }
 
 // Gathered part of a stream: up to three index lists, one after the other.
 // Lists 0 and 1 carry log2-weight lnw2, list 2 half that weight (lnw2 - 1);
@@ -66,8 +83,8 @@ struct Raw {
 
 template <int E, int D>
 struct SmemB {
-  uint16_t k[2][kC][E + 8];    // row stride E + 8: 16 consecutive rows hit distinct banks
-  uint16_t v[2][kC][D + 16];   // row stride D + 16 keeps the transposing reads conflict-free
+  uint16_t k[2][kC][E];        // 16-byte pieces permuted by kswz(row)
+  uint16_t v[2][kC][D];        // 16-byte pieces permuted by vswz(row)
   float lnw2[2][kC];
   int posc[2][kC];             // key visible to query t iff posc <= t (INT_MIN: always, INT_MAX: never)
   int idx[kIdxCap];
@@ -99,10 +116,7 @@ struct AttnB {
   f32x4_t o[NQG][ND];
   float m_run[NQG], l_run[NQG];
 
-  // one chunk in flight
-  uint4 rk[KPT];
-  uint4 rv[VPT];
-  float r_w;   // per-entry weight of the key this thread describes (weighted coreset)
+  float r_w;   // weighted coreset: weight of the key this thread describes in the next chunk
 
   // the stream: G gathered keys, then raw.count raw ones; current window [w0, w0 + wl)
   Gather gs;
@@ -144,49 +158,59 @@ struct AttnB {
     else return sm.idx[min(r, kIdxCap - 1)];
   }
 
-  // Chunk c of the window into registers.  Nothing here waits for a load:
-  // rows beyond the window read the unit's first row and are zeroed by
-  // store(), and the per-key values are finished there too.
-  __device__ __forceinline__ void load(int c) {
-    const int tid = threadIdx.x;
+  // Copy chunk c of the window into buffer buf, memory -> LDS.  Wave w fills
+  // slots [w KPT 64, (w + 1) KPT 64) of K (and likewise of V): slot s is row
+  // s / KP, stored piece s % KP, which holds logical piece (s % KP) ^ kswz(row).
+  // Rows beyond the window copy the unit's first row; zero_tail() clears them.
+  __device__ __forceinline__ void copy(int c, lds_u16* kdst, lds_u16* vdst) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    typedef __attribute__((address_space(1))) const void* gptr;
+    typedef __attribute__((address_space(3))) void* lptr;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int r = kC * c + (tid + kThreads * j) / KP;
+    for (int i = 0; i < KPT; ++i) {
+      const int s = (w * KPT + i) * 64 + lane;
+      const int R = s / KP, P = s % KP;
+      const int r = kC * c + R;
       const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), kstride) +
-                           static_cast<uint32_t>((tid % KP) * 8);
-      rk[j] = *reinterpret_cast<const uint4*>(kbase + off);
+                           static_cast<uint32_t>(8 * (P ^ kswz<E>(R)));
+      __builtin_amdgcn_global_load_lds((gptr)(kbase + off),
+                                       (lptr)(kdst + (w * KPT + i) * 512),
+                                       16, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int r = kC * c + (tid + kThreads * j) / VP;
+    for (int i = 0; i < VPT; ++i) {
+      const int s = (w * VPT + i) * 64 + lane;
+      const int R = s / VP, P = s % VP;
+      const int r = kC * c + R;
       const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), vstride) +
-                           static_cast<uint32_t>((tid % VP) * 8);
-      rv[j] = *reinterpret_cast<const uint4*>(vbase + off);
+                           static_cast<uint32_t>(8 * (P ^ vswz<D>(R)));
+      __builtin_amdgcn_global_load_lds((gptr)(vbase + off),
+                                       (lptr)(vdst + (w * VPT + i) * 512),
+                                       16, 0, 0);
     }
-    if (gs.w != nullptr && G > 0 && tid < kC) r_w = gs.w[min(w0 + kC * c + tid, G - 1)];
   }
 
-  // Chunk c (in registers) into buffer buf, with its per-key visibility and
-  // log2-weight.
-  __device__ __forceinline__ void store(int c, int buf) {
+  // Weighted coreset: entry weight of the key thread tid describes in chunk c.
+  __device__ __forceinline__ float entry_weight(int c) const {
+    return gs.w[min(w0 + kC * c + static_cast<int>(threadIdx.x), G - 1)];
+  }
+
+  // Per-key visibility and log2-weight of chunk c into buffer buf (threads < kC).
+  // A weighted coreset's entry weight was fetched one chunk earlier (r_w), and
+  // the next one is fetched here, so no load is waited for on the spot.
+  __device__ __forceinline__ void meta(int c, int nch, int buf) {
     const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int p = tid + kThreads * j;
-      const bool ok = kC * c + p / KP < wl;
-      *reinterpret_cast<uint4*>(&sm.k[buf][p / KP][(p % KP) * 8]) = ok ? rk[j] : uint4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int p = tid + kThreads * j;
-      const bool ok = kC * c + p / VP < wl;
-      *reinterpret_cast<uint4*>(&sm.v[buf][p / VP][(p % VP) * 8]) = ok ? rv[j] : uint4{0, 0, 0, 0};
-    }
     if (tid < kC) {
       const int r = kC * c + tid;
       const int pos = w0 + r;   // position in the stream
+      float lg = gs.lnw2 - (pos < gs.cnt[0] + gs.cnt[1] ? 0.f : 1.f);
+      if constexpr (!RAW) {
+        if (gs.w != nullptr) {
+          lg = log2f(r_w);
+          if (c + 1 < nch) r_w = entry_weight(c + 1);
+        }
+      }
       const bool gathered = pos < G;
-      const float lg = gs.w != nullptr ? log2f(r_w) : gs.lnw2 - (pos < gs.cnt[0] + gs.cnt[1] ? 0.f : 1.f);
       int posc = gathered ? INT_MIN : (raw.causal ? raw.start + (pos - G) : INT_MIN);
       float lw = gathered ? lg : raw.lnw2;
       posc = r < wl ? posc : INT_MAX;
@@ -196,7 +220,16 @@ struct AttnB {
     }
   }
 
-  __device__ __forceinline__ void consume(int buf, const bool row_ok[NQG]) {
+  // Rows of chunk c beyond the window are zeroed (after its copy has landed).
+  __device__ __forceinline__ void zero_tail(int c, int buf) {
+    const int first = wl - kC * c;   // rows [first, kC) are padding
+    for (int e = threadIdx.x; e < (kC - first) * KP; e += kThreads)
+      reinterpret_cast<uint4*>(&sm.k[buf][first][0])[e] = uint4{0, 0, 0, 0};
+    for (int e = threadIdx.x; e < (kC - first) * VP; e += kThreads)
+      reinterpret_cast<uint4*>(&sm.v[buf][first][0])[e] = uint4{0, 0, 0, 0};
+  }
+
+  __device__ __forceinline__ void consume(int buf, const lds_u16* kbuf, const lds_u16* vbuf, const bool row_ok[NQG]) {
     f32x4_t st[NQG][4];
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg)
@@ -206,7 +239,9 @@ struct AttnB {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&sm.k[buf][kb * 16 + (lane & 15)][kk * 32 + 8 * g]);
+        const int R = kb * 16 + (lane & 15);
+        typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
+        const bf16x8_t kf = *reinterpret_cast<lds_bf16x8*>(kbuf + R * E + 8 * ((4 * kk + g) ^ kswz<E>(R)));
 #pragma unroll
         for (int qg = 0; qg < NQG; ++qg)
           st[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qg][kk], st[qg][kb], 0, 0, 0);
@@ -271,10 +306,13 @@ struct AttnB {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+        // logical elements 16 d + 4 (i16 % 4) .. + 3: piece 2 d + (i16 % 4) / 2, half i16 % 2
+        const int q = 2 * d + ((i16 & 3) >> 1);
+        const int R0 = 32 * hh + 4 * g + (i16 >> 2), R1 = R0 + 16;
         const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)&sm.v[buf][32 * hh + 4 * g + (i16 >> 2)][16 * d + 4 * (i16 & 3)]);
+            (lds_bf16x4*)(vbuf + R0 * D + 8 * (q ^ vswz<D>(R0)) + 4 * (i16 & 1)));
         const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)&sm.v[buf][32 * hh + 16 + 4 * g + (i16 >> 2)][16 * d + 4 * (i16 & 3)]);
+            (lds_bf16x4*)(vbuf + R1 * D + 8 * (q ^ vswz<D>(R1)) + 4 * (i16 & 1)));
         const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int qg = 0; qg < NQG; ++qg)
@@ -292,7 +330,8 @@ struct AttnB {
 #pragma unroll
       for (int i = 0; i < kIdxPT; ++i) {
         const int pos = w0 + min(static_cast<int>(threadIdx.x) + kThreads * i, wl - 1);
-        const int32_t* src = pos < c0 ? gs.p[0] + pos : (pos < c01 ? gs.p[1] + (pos - c0) : gs.p[2] + (pos - c01));
+        const int gp = min(pos, G - 1);   // in bounds of the gathered lists whenever it is read
+        const int32_t* src = gp < c0 ? gs.p[0] + gp : (gp < c01 ? gs.p[1] + (gp - c0) : gs.p[2] + (gp - c01));
         v[i] = pos < G ? *src : raw.start + (pos - G);
       }
 #pragma unroll
@@ -303,9 +342,16 @@ struct AttnB {
       __syncthreads();
     }
     const int nch = (wl + kC - 1) / kC;
-    load(0);
-    store(0, 0);
-    if (nch > 1) load(1);
+    copy(0, (lds_u16*)&sm.k[0][0][0], (lds_u16*)&sm.v[0][0][0]);
+    if constexpr (!RAW) {
+      if (gs.w != nullptr && threadIdx.x < kC) r_w = entry_weight(0);
+    }
+    meta(0, nch, 0);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    if (kC > wl) {
+      __syncthreads();
+      zero_tail(0, 0);
+    }
     __syncthreads();
     for (int c = 0; c < nch; c += 2) {   // unrolled by two: the buffer of each step is a constant
       step<0>(c, nch, row_ok);
@@ -313,14 +359,30 @@ struct AttnB {
     }
   }
 
-  // chunk c sits in buffer B; chunk c + 1 goes from the registers to the other
-  // buffer, chunk c + 2 from memory to the registers
+  // chunk c sits in buffer B; chunk c + 1 is copied into the other buffer meanwhile
   template <int B>
   __device__ __forceinline__ void step(int c, int nch, const bool row_ok[NQG]) {
-    if (c + 1 < nch) store(c + 1, 1 - B);
-    if (c + 2 < nch) load(c + 2);
-    consume(B, row_ok);
+    overlap(c, nch, (const lds_u16*)&sm.k[B][0][0], (const lds_u16*)&sm.v[B][0][0], (lds_u16*)&sm.k[1 - B][0][0],
+            (lds_u16*)&sm.v[1 - B][0][0], row_ok);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);   // this thread's copies have landed
+    if (c + 1 < nch && kC * (c + 2) > wl) {
+      __syncthreads();
+      zero_tail(c + 1, 1 - B);
+    }
     __syncthreads();
+  }
+
+  // The copy into one buffer overlaps the MFMA reads of the other.  The
+  // restrict-qualified views tell the compiler so: without them it would wait
+  // for the copy before the first LDS read of the current buffer.
+  __device__ __forceinline__ void overlap(int c, int nch, const lds_u16* __restrict__ kc,
+                                          const lds_u16* __restrict__ vc, lds_u16* __restrict__ kn,
+                                          lds_u16* __restrict__ vn, const bool row_ok[NQG]) {
+    if (c + 1 < nch) {
+      copy(c + 1, kn, vn);
+      meta(c + 1, nch, (c + 1) & 1);
+    }
+    consume(c & 1, kc, vc, row_ok);
   }
 
   // The whole stream, in windows of at most kIdxCap staged tokens.
