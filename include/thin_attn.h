@@ -118,6 +118,10 @@ size_t thin_attn_workspace_size(const thin_attn_t* h, int64_t B, int64_t T, int6
  * tokens beta n_out .. t (weight 1).  Supported while m / 2 <= n_out for
  * every block (t < 2 n_out^2), else THIN_ENOTSUP.
  *
+ * Sizes: S, T < 2^30, and one batch entry's keys or values must fit 2 GiB
+ * (S * H_kv * max(E, D) * element size < 2^31, H_kv * max(E, D) * element
+ * size < 2^24), else THIN_ENOTSUP.
+ *
  * Arguments: q, k, v, out as described above (out must not alias inputs);
  * seed keys the Philox4x64-10 stream; optional outputs (NULL to skip):
  *   coreset_idx [B * H_kv, capacity] int32 token indices, ascending, padded -1;

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libthin_attn.so")
-SOURCES = ["api.hip", "kvapi.hip", "kh.hip", "attn.hip", "attn_bf16.hip", "kv.hip"]
+SOURCES = ["api.hip", "kvapi.hip", "kh.hip", "attn.hip", "kv.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

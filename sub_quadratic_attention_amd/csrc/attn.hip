@@ -1,26 +1,49 @@
-// Weighted-coreset softmax attention on gfx950 (MFMA for Q K^T and P V only).
+// Weighted-coreset / Express softmax attention on gfx950, fp32 and bf16.
 //
-// out(q) = sum_j w_j exp(s <q, k_j>) v_j / sum_j w_j exp(s <q, k_j>) over the
-// keys a query sees ("Express Language Modeling": attention against a small
-// weighted summary of the keys and values).  ln w_j is folded into the
-// logit, the softmax is taken online (running maximum and sum), and the
-// accumulation is fp32.
+// out(q) = sum_j w_j e^{s <q, k_j>} v_j / sum_j w_j e^{s <q, k_j>} over the keys
+// a query sees ("Express Language Modeling": attention against a small
+// weighted summary of the keys and values).  ln w_j is folded into the logit,
+// the softmax is taken online (running maximum and sum), accumulation is fp32,
+// and both products run on MFMA: v_mfma_f32_16x16x32_bf16 for bf16 inputs,
+// v_mfma_f32_16x16x4f32 for fp32 inputs.
 //
-// A query sees a list of segments.  A segment is either a list of token
-// indices (a coreset, the EXPRESS cache or buffer) with one log-weight or
-// per-point weights, or a raw token range with weight 1 and, for the block
-// being streamed, a causal mask.  Unmasked attention uses one segment per
-// unit; Thinformer Express uses the cache / buffer segments of the state
-// before the query's block plus the raw causal block.
+// The keys a query sees are a gathered part (a coreset, or the cache and
+// buffer index lists of the Express state, each list with its log-weight)
+// followed by a raw token range (weight 1; causal inside the block being
+// streamed).
 //
-// Layout: one workgroup = 4 waves x 16 queries of one (b, h); keys are
-// staged 32 at a time in LDS (K row-major, V transposed for bf16).  The
-// products are computed transposed: S^T = K Q^T puts one query per lane
-// column (lane % 16), so the softmax statistics and the O^T = V^T P^T
-// accumulator of a query live in the same lanes and rescaling needs no lane
-// exchange.
+// Layout:
+//  * one workgroup = 4 waves x 16 NQG queries of one (b, h); two workgroups
+//    fit one CU, so one workgroup's MFMA phase overlaps the other's softmax;
+//  * the keys visible to the workgroup form one stream: its token indices
+//    (gathered lists, then the raw tail) are staged in LDS in windows of up to
+//    kIdxCap keys (a stream of only a raw range needs none), then 64-key chunks
+//    of K and V go through two LDS buffers with one barrier per chunk: chunk
+//    c + 1 is copied from memory straight into LDS (global_load_lds_dwordx4,
+//    16 bytes per lane, no registers) while chunk c is consumed;
+//  * K and V rows sit unpadded in LDS; the 16-byte pieces of row R are stored
+//    permuted (piece q at q ^ f(R)), which the copy does for free by choosing
+//    the global piece each lane fetches, and which puts the operand reads on
+//    distinct banks;
+//  * S^T = K Q^T keeps one query per lane column, so softmax statistics and
+//    the O^T = V^T P^T accumulator of a query share lanes; each K (and V)
+//    fragment read from LDS feeds the NQG query groups of the wave;
+//  * bf16: the V operand of P V is read with the gfx950 transposing LDS read
+//    (ds_read_tr16_b64): within each 16-lane group, lane j receives element
+//    j % 4 of the 8-byte pieces addressed by lanes j/4 + 4k (k = 0..3), so
+//    lanes addressing V[k0 + i/4][d0 + 4 (i % 4)] deliver V[k0..k0+3][d0 + j]
+//    to lane j: four keys of one dimension, as the MFMA operand wants;
+//  * fp32: the order of the reduction inside an MFMA only has to agree between
+//    its operands, so lane group g of k-step t of feature block kq takes
+//    feature 16 kq + 4 g + t (one 16-byte K read per four MFMAs); for P V, a
+//    lane reads four consecutive dimensions of a key row with one 16-byte read
+//    and feeds them to four output blocks whose rows interleave the
+//    dimensions (block 4 j + d4, row r = dimension 64 j + 4 r + d4).
 
+#include <limits.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -29,344 +52,535 @@ namespace thin {
 
 namespace {
 
-constexpr int kQT = 64;   // queries per workgroup
-constexpr int kKC = 32;   // keys per LDS chunk
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kC = 64;          // keys per chunk
+constexpr int kIdxCap = 1536;   // gathered indices staged per window
+constexpr int kIdxPT = kIdxCap / kThreads;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters unconstrained
 
-struct Seg {
-  const int32_t* idx;   // nullptr: raw token range
-  int start;            // first entry of idx, or first token of the range
-  int count;
-  float lnw2;           // log2 of the weight when w == nullptr
-  const float* w;       // per-point weights (indexed like idx), or nullptr
-  int causal;           // raw range streamed causally: key visible iff key <= query
+template <bool BF16, int E, int D>
+constexpr int nqg() { return (BF16 ? (E <= 128 && D <= 128) : D <= 64) ? 2 : 1; }   // 16-query groups per wave
+
+typedef __attribute__((address_space(3))) unsigned char lds_byte;   // LDS views of the buffers
+
+// Piece permutations.  K is read 16 bytes per lane, 16 consecutive rows at one
+// logical piece: 128-byte rows (two per 256 bytes of banks) take
+// q ^ (R / 2 % 8), longer rows q ^ (R % 16).  bf16 V is read 8 bytes per lane
+// by the transposing read, 8 rows x 32 bytes (pieces 2d, 2d + 1) at a time:
+// the permutation keeps the pair together, 2 (R / 2 % 4) for 128-byte rows,
+// 2 (R % 8) for longer ones.  fp32 V is read a whole row per 16 lanes and
+// needs no permutation.
+template <int RB>
+__device__ __forceinline__ int kswz(int R) { return RB == 128 ? (R >> 1) & 7 : R & 15; }
+template <bool BF16, int RB>
+__device__ __forceinline__ int vswz(int R) {
+  if constexpr (!BF16) return 0;
+  else return RB == 128 ? 2 * ((R >> 1) & 3) : 2 * (R & 7);
+}
+
+// Gathered part of a stream: up to three index lists, one after the other.
+// Lists 0 and 1 carry log2-weight lnw2, list 2 half that weight (lnw2 - 1);
+// a single list may instead carry per-entry weights w.
+struct Gather {
+  const int32_t* p[3];
+  int cnt[3];
+  float lnw2;
+  const float* w;
+};
+
+// Raw part: tokens start .. start + count - 1, log2-weight lnw2, causal mask.
+struct Raw {
+  int start, count;
+  float lnw2;
+  int causal;
 };
 
 template <bool BF16, int E, int D>
-struct Smem;
-
-template <int E, int D>
-struct Smem<true, E, D> {
-  uint16_t k[kKC][E + 8];
-  uint16_t vt[D][40];          // V^T, key slots permuted to the P^T operand order
-  float lnw2[kKC];
-  int pos[kKC];
+struct Smem {
+  static constexpr int KB = E * (BF16 ? 2 : 4), VB = D * (BF16 ? 2 : 4);   // row bytes
+  alignas(16) unsigned char k[2][kC * KB];   // 16-byte pieces permuted by kswz(row)
+  alignas(16) unsigned char v[2][kC * VB];   // 16-byte pieces permuted by vswz(row)
+  float lnw2[2][kC];
+  int posc[2][kC];             // key visible to query t iff posc <= t (INT_MIN: always, INT_MAX: never)
+  int idx[kIdxCap];
 };
 
-template <int E, int D>
-struct Smem<false, E, D> {
-  float k[kKC][E + 4];
-  float v[kKC][D + 4];
-  float lnw2[kKC];
-  int pos[kKC];
-};
-
-// key kk of a 32-key chunk -> its slot in the bf16 P^T / V^T operands:
-// lane group g holds keys 4g..4g+3 of each 16-key half as slots 8g..8g+7.
-__device__ __forceinline__ int bf16_slot(int kk) { return 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3); }
-
-template <bool BF16, int E, int D>
+// RAW: the stream is one raw token range (exact attention), tokens computed;
+// otherwise every token of the stream is staged in sm.idx.
+template <bool BF16, int E, int D, bool RAW>
 struct Attn {
-  static constexpr int NQ = BF16 ? E / 32 : E / 4;   // Q fragments per lane
-  static constexpr int ND = D / 16;                  // output blocks of 16 dims
-
-  using QFrag = typename std::conditional<BF16, bf16x8_t, float>::type;
+  static constexpr int ELT = BF16 ? 2 : 4;
+  static constexpr int KB = E * ELT, VB = D * ELT;   // row bytes
+  static constexpr int NQG = nqg<BF16, E, D>();
+  static constexpr int NQF = BF16 ? E / 32 : E / 4;   // Q operand registers per query group
+  static constexpr int ND = D / 16;                   // 16-dimension output blocks
+  static constexpr int KP = KB / 16, VP = VB / 16;    // 16-byte pieces per row
+  static constexpr int KPT = kC * KP / kThreads;      // copies per thread per chunk
+  static constexpr int VPT = kC * VP / kThreads;
+  using QF = typename std::conditional<BF16, bf16x8_t, float>::type;
 
   const AttnLaunch& a;
   Smem<BF16, E, D>& sm;
-  int b, h, hk, unit;
-  int lane, g, qr;   // my query row (token index)
-  bool row_live;
-  QFrag qf[NQ];
-  f32x4_t o[ND];
-  float m_run, l_run;
+  int b, h, hk, unit, lane, g;
+  // K / V rows of this unit: token t starts at kbase + t * kstride bytes;
+  // offsets stay below 2^31 (checked by the host), so they are 32-bit
+  const unsigned char* kbase;
+  const unsigned char* vbase;
+  uint32_t kstride, vstride;
+  int qr[NQG];
+  bool live[NQG];
+  QF qf[NQG][NQF];
+  f32x4_t o[NQG][ND];
+  float m_run[NQG], l_run[NQG];
 
-  __device__ Attn(const AttnLaunch& la, Smem<BF16, E, D>& s, int q0, int bh) : a(la), sm(s) {
+  float r_w;   // weighted coreset: weight of the key this thread describes in the next chunk
+
+  // the stream: G gathered keys, then raw.count raw ones; current window [w0, w0 + wl)
+  Gather gs;
+  Raw raw;
+  int G, w0, wl;
+
+  __device__ __forceinline__ Attn(const AttnLaunch& la, Smem<BF16, E, D>& s, int q0, int bh) : a(la), sm(s) {
     b = bh / a.H;
     h = bh % a.H;
     hk = h / (a.H / a.H_kv);
     unit = b * a.H_kv + hk;
+    kstride = static_cast<uint32_t>(a.H_kv * KB);
+    vstride = static_cast<uint32_t>(a.H_kv * VB);
+    kbase = static_cast<const unsigned char*>(a.k) + (static_cast<int64_t>(b) * a.S * a.H_kv + hk) * KB;
+    vbase = static_cast<const unsigned char*>(a.v) + (static_cast<int64_t>(b) * a.S * a.H_kv + hk) * VB;
     lane = threadIdx.x & 63;
     g = lane >> 4;
-    qr = q0 + 16 * (threadIdx.x >> 6) + (lane & 15);
-    row_live = qr < a.T;
-    const int64_t qrow = ((static_cast<int64_t>(b) * a.T + (row_live ? qr : 0)) * a.H + h) * E;
+    const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int kk = 0; kk < NQ; ++kk) {
+    for (int qg = 0; qg < NQG; ++qg) {
+      qr[qg] = q0 + 16 * NQG * w + 16 * qg + (lane & 15);
+      live[qg] = qr[qg] < a.T;
+      const int64_t qrow = ((static_cast<int64_t>(b) * a.T + (live[qg] ? qr[qg] : 0)) * a.H + h) * E;
       if constexpr (BF16) {
-        const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(static_cast<const uint16_t*>(a.q) + qrow + kk * 32 + 8 * g);
-        qf[kk] = row_live ? *src : bf16x8_t{};
-      } else {
-        qf[kk] = row_live ? static_cast<const float*>(a.q)[qrow + kk * 4 + g] : 0.0f;
-      }
-    }
 #pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m_run = -INFINITY;
-    l_run = 0.f;
-  }
-
-  __device__ __forceinline__ int key_token(const Seg& s, int j) const { return s.idx ? s.idx[s.start + j] : s.start + j; }
-
-  // A chunk of 32 keys travels global -> registers -> LDS, so that the next
-  // chunk's loads are in flight while the current one is consumed.
-  static constexpr int KPT = BF16 ? (kKC * E / 8 + 255) / 256 : (kKC * E / 4 + 255) / 256;   // 16-byte pieces / thread
-  static constexpr int VPT = BF16 ? (kKC * D / 8 + 255) / 256 : (kKC * D / 4 + 255) / 256;
-  struct Chunk {
-    uint4 k[KPT];
-    uint4 v[VPT];
-    int pos;
-    float l2;
-  };
-
-  __device__ __forceinline__ void load(const Seg& s, int c0, int nk, Chunk& ch) const {
-    const int tid = threadIdx.x;
-    const int64_t kv_base = static_cast<int64_t>(b) * a.S;
-    constexpr int KP = BF16 ? E / 8 : E / 4;
-    constexpr int VP = BF16 ? D / 8 : D / 4;
-    constexpr int ELT = BF16 ? 2 : 4;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int p = tid + 256 * j;
-      const int r = p / KP, c = p % KP;
-      ch.k[j] = uint4{0, 0, 0, 0};
-      if (p < kKC * KP && r < nk) {
-        const int64_t row = (kv_base + key_token(s, c0 + r)) * a.H_kv + hk;
-        ch.k[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k) + (row * E + c * (16 / ELT)) * ELT);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int p = tid + 256 * j;
-      const int r = p / VP, c = p % VP;
-      ch.v[j] = uint4{0, 0, 0, 0};
-      if (p < kKC * VP && r < nk) {
-        const int64_t row = (kv_base + key_token(s, c0 + r)) * a.H_kv + hk;
-        ch.v[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) + (row * D + c * (16 / ELT)) * ELT);
-      }
-    }
-    ch.pos = 0x7fffffff;
-    ch.l2 = -INFINITY;
-    if (tid < kKC && tid < nk) {
-      ch.pos = key_token(s, c0 + tid);
-      ch.l2 = s.w ? log2f(s.w[s.start + c0 + tid]) : s.lnw2;
-    }
-  }
-
-  __device__ __forceinline__ void store(const Chunk& ch) {
-    const int tid = threadIdx.x;
-    constexpr int KP = BF16 ? E / 8 : E / 4;
-    constexpr int VP = BF16 ? D / 8 : D / 4;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int p = tid + 256 * j;
-      if (p >= kKC * KP) break;
-      const int r = p / KP, c = p % KP;
-      if constexpr (BF16)
-        *reinterpret_cast<uint4*>(&sm.k[r][c * 8]) = ch.k[j];
-      else
-        *reinterpret_cast<uint4*>(&sm.k[r][c * 4]) = ch.k[j];
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int p = tid + 256 * j;
-      if (p >= kKC * VP) break;
-      const int r = p / VP, c = p % VP;
-      if constexpr (BF16) {
-        const int slot = bf16_slot(r);
-        const uint32_t wv[4] = {ch.v[j].x, ch.v[j].y, ch.v[j].z, ch.v[j].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          sm.vt[c * 8 + 2 * q][slot] = static_cast<uint16_t>(wv[q] & 0xffffu);
-          sm.vt[c * 8 + 2 * q + 1][slot] = static_cast<uint16_t>(wv[q] >> 16);
+        for (int kk = 0; kk < NQF; ++kk) {
+          const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(static_cast<const uint16_t*>(a.q) + qrow + kk * 32 + 8 * g);
+          qf[qg][kk] = live[qg] ? *src : bf16x8_t{};
         }
       } else {
-        *reinterpret_cast<uint4*>(&sm.v[r][c * 4]) = ch.v[j];
+#pragma unroll
+        for (int kq = 0; kq < E / 16; ++kq) {
+          const float4 x = live[qg] ? *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow + 16 * kq + 4 * g)
+                                    : float4{0.f, 0.f, 0.f, 0.f};
+          qf[qg][4 * kq] = x.x, qf[qg][4 * kq + 1] = x.y, qf[qg][4 * kq + 2] = x.z, qf[qg][4 * kq + 3] = x.w;
+        }
       }
-    }
-    if (tid < kKC) {
-      sm.pos[tid] = ch.pos;
-      sm.lnw2[tid] = ch.l2;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) o[qg][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m_run[qg] = -INFINITY;
+      l_run[qg] = 0.f;
     }
   }
 
-  // One chunk of 32 staged keys for this wave's 16 queries.
-  __device__ void consume(const Seg& s, bool row_ok) {
-    f32x4_t st[2];
+  // token of window position r (r < wl)
+  __device__ __forceinline__ int token(int r) const {
+    if constexpr (RAW) return raw.start + w0 + r;
+    else return sm.idx[min(r, kIdxCap - 1)];
+  }
+
+  // Copy chunk c of the window into buffers kdst / vdst, memory -> LDS.  Wave
+  // w fills 16-byte slots [w KPT 64, (w + 1) KPT 64) of K (and likewise of V):
+  // slot s is row s / KP, stored piece s % KP, which holds logical piece
+  // (s % KP) ^ kswz(row).  Rows beyond the window copy the unit's first row;
+  // zero_tail() clears them.
+  __device__ __forceinline__ void copy(int c, lds_byte* kdst, lds_byte* vdst) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    typedef __attribute__((address_space(1))) const void* gptr;
+    typedef __attribute__((address_space(3))) void* lptr;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < KPT; ++i) {
+      const int s = (w * KPT + i) * 64 + lane;
+      const int R = s / KP, P = s % KP;
+      const int r = kC * c + R;
+      const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), kstride) +
+                           static_cast<uint32_t>(16 * (P ^ kswz<KB>(R)));
+      __builtin_amdgcn_global_load_lds((gptr)(kbase + off), (lptr)(kdst + (w * KPT + i) * 1024), 16, 0, 0);
+    }
 #pragma unroll
-      for (int kk = 0; kk < NQ; ++kk) {
-        if constexpr (BF16) {
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&sm.k[c * 16 + (lane & 15)][kk * 32 + 8 * g]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], acc, 0, 0, 0);
-        } else {
-          const float kf = sm.k[c * 16 + (lane & 15)][kk * 4 + g];
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qf[kk], acc, 0, 0, 0);
+    for (int i = 0; i < VPT; ++i) {
+      const int s = (w * VPT + i) * 64 + lane;
+      const int R = s / VP, P = s % VP;
+      const int r = kC * c + R;
+      const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), vstride) +
+                           static_cast<uint32_t>(16 * (P ^ vswz<BF16, VB>(R)));
+      __builtin_amdgcn_global_load_lds((gptr)(vbase + off), (lptr)(vdst + (w * VPT + i) * 1024), 16, 0, 0);
+    }
+  }
+
+  // Weighted coreset: entry weight of the key thread tid describes in chunk c.
+  __device__ __forceinline__ float entry_weight(int c) const {
+    return gs.w[min(w0 + kC * c + static_cast<int>(threadIdx.x), G - 1)];
+  }
+
+  // Per-key visibility and log2-weight of chunk c into buffer buf (threads < kC).
+  // A weighted coreset's entry weight was fetched one chunk earlier (r_w), and
+  // the next one is fetched here, so no load is waited for on the spot.
+  __device__ __forceinline__ void meta(int c, int nch, int buf) {
+    const int tid = threadIdx.x;
+    if (tid < kC) {
+      const int r = kC * c + tid;
+      const int pos = w0 + r;   // position in the stream
+      float lg = gs.lnw2 - (pos < gs.cnt[0] + gs.cnt[1] ? 0.f : 1.f);
+      if constexpr (!RAW) {
+        if (gs.w != nullptr) {
+          lg = log2f(r_w);
+          if (c + 1 < nch) r_w = entry_weight(c + 1);
         }
       }
-      st[c] = acc;
+      const bool gathered = pos < G;
+      int posc = gathered ? INT_MIN : (raw.causal ? raw.start + (pos - G) : INT_MIN);
+      float lw = gathered ? lg : raw.lnw2;
+      posc = r < wl ? posc : INT_MAX;
+      lw = r < wl ? lw : -INFINITY;
+      sm.posc[buf][tid] = posc;
+      sm.lnw2[buf][tid] = lw;
     }
-    // logits (base 2), masks
+  }
+
+  // Rows of chunk c beyond the window are zeroed (after its copy has landed).
+  __device__ __forceinline__ void zero_tail(int c, int buf) {
+    const int first = wl - kC * c;   // rows [first, kC) are padding
+    for (int e = threadIdx.x; e < (kC - first) * KP; e += kThreads)
+      reinterpret_cast<uint4*>(&sm.k[buf][first * KB])[e] = uint4{0, 0, 0, 0};
+    for (int e = threadIdx.x; e < (kC - first) * VP; e += kThreads)
+      reinterpret_cast<uint4*>(&sm.v[buf][first * VB])[e] = uint4{0, 0, 0, 0};
+  }
+
+  // S^T (keys x queries) of the chunk in buffer kbuf: st[qg][kb] holds keys
+  // 16 kb + 4 g + i (i = 0..3) for query lane % 16.
+  __device__ __forceinline__ void scores(const lds_byte* kbuf, f32x4_t st[NQG][4]) const {
+#pragma unroll
+    for (int qg = 0; qg < NQG; ++qg)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) st[qg][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int R0 = lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int R = 16 * kb + R0;
+      if constexpr (BF16) {
+        typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
+#pragma unroll
+        for (int kk = 0; kk < NQF; ++kk) {
+          const bf16x8_t kf = *reinterpret_cast<lds_bf16x8*>(kbuf + R * KB + 16 * ((4 * kk + g) ^ kswz<KB>(R)));
+#pragma unroll
+          for (int qg = 0; qg < NQG; ++qg)
+            st[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qg][kk], st[qg][kb], 0, 0, 0);
+        }
+      } else {
+        typedef __attribute__((address_space(3))) const f32x4_t lds_f4;
+#pragma unroll
+        for (int kq = 0; kq < E / 16; ++kq) {
+          const f32x4_t kf = *reinterpret_cast<lds_f4*>(kbuf + R * KB + 16 * ((4 * kq + g) ^ kswz<KB>(R)));
+          const float kv[4] = {kf[0], kf[1], kf[2], kf[3]};
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int qg = 0; qg < NQG; ++qg)
+              st[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[t], qf[qg][4 * kq + t], st[qg][kb], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void consume(int buf, const lds_byte* kbuf, const lds_byte* vbuf, const bool row_ok[NQG]) {
+    f32x4_t st[NQG][4];
+    scores(kbuf, st);
     const float sc = a.scale * kLog2e;
-    float x[2][4];
-    float mx = -INFINITY;
+    int pc[4][4];
+    float lw[4][4];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int kb = 0; kb < 4; ++kb) {
+      const int4 pv = *reinterpret_cast<const int4*>(&sm.posc[buf][kb * 16 + 4 * g]);
+      const float4 lv = *reinterpret_cast<const float4*>(&sm.lnw2[buf][kb * 16 + 4 * g]);
+      pc[kb][0] = pv.x, pc[kb][1] = pv.y, pc[kb][2] = pv.z, pc[kb][3] = pv.w;
+      lw[kb][0] = lv.x, lw[kb][1] = lv.y, lw[kb][2] = lv.z, lw[kb][3] = lv.w;
+    }
+    // online softmax; p[qg][kb][i] is the weight of key 16 kb + 4 g + i
+    float p[NQG][4][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = c * 16 + 4 * g + i;
-        const bool vis = row_ok && (!s.causal || sm.pos[kk] <= qr);
-        const float l2 = sm.lnw2[kk];
-        const float val = vis ? st[c][i] * sc + l2 : -INFINITY;
-        x[c][i] = val;
-        mx = fmaxf(mx, val);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float p[2][4];
-    float rs = 0.f;
+    for (int qg = 0; qg < NQG; ++qg) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[c][i] = __builtin_amdgcn_exp2f(x[c][i] - m_use);
-        rs += p[c][i];
-      }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+        for (int i = 0; i < 4; ++i) {
+          const bool vis = row_ok[qg] && pc[kb][i] <= qr[qg];
+          const float val = vis ? fmaf(st[qg][kb][i], sc, lw[kb][i]) : -INFINITY;
+          p[qg][kb][i] = val;
+          mx = fmaxf(mx, val);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[qg], mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_use);
+      float rs = 0.f;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] *= alpha;
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[qg][kb][i] = __builtin_amdgcn_exp2f(p[qg][kb][i] - m_use);
+          rs += p[qg][kb][i];
+        }
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      l_run[qg] = l_run[qg] * alpha + rs;
+      m_run[qg] = m_new;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) o[qg][d] *= alpha;
+    }
     if constexpr (BF16) {
-      bf16x8_t pb;
+      bf16x8_t pb[NQG][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = static_cast<__bf16>(p[0][i]);
-        pb[4 + i] = static_cast<__bf16>(p[1][i]);
-      }
+      for (int qg = 0; qg < NQG; ++qg)
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&sm.vt[16 * d + (lane & 15)][8 * g]);
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, o[d], 0, 0, 0);
-      }
-    } else {
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            const float vf = sm.v[c * 16 + 4 * g + i][16 * d + (lane & 15)];
-            o[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf, p[c][i], o[d], 0, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            pb[qg][hh][i] = static_cast<__bf16>(p[qg][2 * hh][i]);
+            pb[qg][hh][4 + i] = static_cast<__bf16>(p[qg][2 * hh + 1][i]);
           }
-    }
-  }
-
-  __device__ void run_segment(const Seg s, bool row_ok) {
-    if (s.count <= 0) return;
-    Chunk ch;
-    load(s, 0, min(kKC, s.count), ch);
-    for (int c0 = 0; c0 < s.count; c0 += kKC) {
-      store(ch);
-      __syncthreads();
-      if (c0 + kKC < s.count) load(s, c0 + kKC, min(kKC, s.count - c0 - kKC), ch);
-      consume(s, row_ok);
-      __syncthreads();
-    }
-  }
-
-  __device__ void store() {
-    if (!row_live) return;
-    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    const int64_t orow = ((static_cast<int64_t>(b) * a.T + qr) * a.H + h) * D;
+      // O^T += V^T P^T: lane group g's operand slots 0-3 / 4-7 are keys
+      // 32hh + 4g + (0..3) and 32hh + 16 + 4g + (0..3) (the S^T layout)
+      const int i16 = lane & 15;
+      typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      const int col = 16 * d + 4 * g;
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          // logical elements 16 d + 4 (i16 % 4) .. + 3: piece 2 d + (i16 % 4) / 2, half i16 % 2
+          const int q = 2 * d + ((i16 & 3) >> 1);
+          const int R0 = 32 * hh + 4 * g + (i16 >> 2), R1 = R0 + 16;
+          const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(vbuf + R0 * VB + 16 * (q ^ vswz<BF16, VB>(R0)) + 8 * (i16 & 1)));
+          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(vbuf + R1 * VB + 16 * (q ^ vswz<BF16, VB>(R1)) + 8 * (i16 & 1)));
+          const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int qg = 0; qg < NQG; ++qg)
+            o[qg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qg][hh], o[qg][d], 0, 0, 0);
+        }
+    } else {
+      // O^T += V^T P^T, four keys per MFMA: key 16 kb + 4 g + i is lane group
+      // g's k-index in step (kb, i); one 16-byte read gives dimensions
+      // 64 j + 4 (lane % 16) .. + 3 of that key for output blocks 4 j .. 4 j + 3
+      typedef __attribute__((address_space(3))) const f32x4_t lds_f4;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * kb + 4 * g + i;
+#pragma unroll
+          for (int j = 0; j < D / 64; ++j) {
+            const f32x4_t vv = *reinterpret_cast<lds_f4*>(vbuf + key * VB + 16 * (16 * j + (lane & 15)));
+            const float vx[4] = {vv[0], vv[1], vv[2], vv[3]};
+#pragma unroll
+            for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+              for (int qg = 0; qg < NQG; ++qg)
+                o[qg][4 * j + d4] = __builtin_amdgcn_mfma_f32_16x16x4f32(vx[d4], p[qg][kb][i], o[qg][4 * j + d4], 0, 0, 0);
+          }
+        }
+    }
+  }
+
+  // One window: its tokens are staged (all loads in flight at once), then
+  // its chunks stream through the two buffers.
+  __device__ __forceinline__ void run_window(const bool row_ok[NQG]) {
+    __syncthreads();   // earlier users of sm.idx and of the buffers are done
+    if constexpr (!RAW) {
+      const int c0 = gs.cnt[0], c01 = gs.cnt[0] + gs.cnt[1];
+      int v[kIdxPT];
+#pragma unroll
+      for (int i = 0; i < kIdxPT; ++i) {
+        const int pos = w0 + min(static_cast<int>(threadIdx.x) + kThreads * i, wl - 1);
+        const int gp = min(pos, G - 1);   // in bounds of the gathered lists whenever it is read
+        const int32_t* src = gp < c0 ? gs.p[0] + gp : (gp < c01 ? gs.p[1] + (gp - c0) : gs.p[2] + (gp - c01));
+        v[i] = pos < G ? *src : raw.start + (pos - G);
+      }
+#pragma unroll
+      for (int i = 0; i < kIdxPT; ++i) {
+        const int e = threadIdx.x + kThreads * i;
+        if (e < wl) sm.idx[e] = v[i];
+      }
+      __syncthreads();
+    }
+    const int nch = (wl + kC - 1) / kC;
+    copy(0, (lds_byte*)&sm.k[0][0], (lds_byte*)&sm.v[0][0]);
+    if constexpr (!RAW) {
+      if (gs.w != nullptr && threadIdx.x < kC) r_w = entry_weight(0);
+    }
+    meta(0, nch, 0);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    if (kC > wl) {
+      __syncthreads();
+      zero_tail(0, 0);
+    }
+    __syncthreads();
+    for (int c = 0; c < nch; c += 2) {   // unrolled by two: the buffer of each step is a constant
+      step<0>(c, nch, row_ok);
+      if (c + 1 < nch) step<1>(c + 1, nch, row_ok);
+    }
+  }
+
+  // chunk c sits in buffer B; chunk c + 1 is copied into the other buffer meanwhile
+  template <int B>
+  __device__ __forceinline__ void step(int c, int nch, const bool row_ok[NQG]) {
+    overlap(c, nch, (const lds_byte*)&sm.k[B][0], (const lds_byte*)&sm.v[B][0], (lds_byte*)&sm.k[1 - B][0],
+            (lds_byte*)&sm.v[1 - B][0], row_ok);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);   // this thread's copies have landed
+    if (c + 1 < nch && kC * (c + 2) > wl) {
+      __syncthreads();
+      zero_tail(c + 1, 1 - B);
+    }
+    __syncthreads();
+  }
+
+  // The copy into one buffer overlaps the MFMA reads of the other.  The
+  // restrict-qualified views tell the compiler so: without them it would wait
+  // for the copy before the first LDS read of the current buffer.
+  __device__ __forceinline__ void overlap(int c, int nch, const lds_byte* __restrict__ kc,
+                                          const lds_byte* __restrict__ vc, lds_byte* __restrict__ kn,
+                                          lds_byte* __restrict__ vn, const bool row_ok[NQG]) {
+    if (c + 1 < nch) {
+      copy(c + 1, kn, vn);
+      meta(c + 1, nch, (c + 1) & 1);
+    }
+    consume(c & 1, kc, vc, row_ok);
+  }
+
+  // The whole stream, in windows of at most kIdxCap staged tokens.
+  __device__ __forceinline__ void run_stream(const Gather& gather, const Raw& r, const bool row_ok[NQG]) {
+    gs = gather;
+    raw = r;
+    G = gs.cnt[0] + gs.cnt[1] + gs.cnt[2];
+    const int L = G + raw.count;
+    const int cap = RAW ? L : kIdxCap;
+    for (w0 = 0; w0 < L; w0 += cap) {
+      wl = min(cap, L - w0);
+      run_window(row_ok);
+    }
+  }
+
+  __device__ __forceinline__ void finish() {
+#pragma unroll
+    for (int qg = 0; qg < NQG; ++qg) {
+      if (!live[qg]) continue;
+      const float inv = l_run[qg] > 0.f ? 1.0f / l_run[qg] : 0.f;
+      const int64_t orow = ((static_cast<int64_t>(b) * a.T + qr[qg]) * a.H + h) * D;
       if constexpr (BF16) {
-        uint16_t* dst = static_cast<uint16_t*>(a.out) + orow + col;
-        const uint32_t lo = float_to_bf16_bits(o[d][0] * inv) | (static_cast<uint32_t>(float_to_bf16_bits(o[d][1] * inv)) << 16);
-        const uint32_t hi = float_to_bf16_bits(o[d][2] * inv) | (static_cast<uint32_t>(float_to_bf16_bits(o[d][3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+        // block d, accumulator element i: dimension 16 d + 4 g + i
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          uint16_t* dst = static_cast<uint16_t*>(a.out) + orow + 16 * d + 4 * g;
+          const uint32_t lo = float_to_bf16_bits(o[qg][d][0] * inv) |
+                              (static_cast<uint32_t>(float_to_bf16_bits(o[qg][d][1] * inv)) << 16);
+          const uint32_t hi = float_to_bf16_bits(o[qg][d][2] * inv) |
+                              (static_cast<uint32_t>(float_to_bf16_bits(o[qg][d][3] * inv)) << 16);
+          *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+        }
       } else {
-        float* dst = static_cast<float*>(a.out) + orow + col;
-        *reinterpret_cast<float4*>(dst) = float4{o[d][0] * inv, o[d][1] * inv, o[d][2] * inv, o[d][3] * inv};
+        // block 4 j + d4, accumulator element i (row 4 g + i): dimension 64 j + 4 (4 g + i) + d4
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float* dst = static_cast<float*>(a.out) + orow + 64 * j + 16 * g + 4 * i;
+            *reinterpret_cast<float4*>(dst) = float4{o[qg][4 * j][i] * inv, o[qg][4 * j + 1][i] * inv,
+                                                     o[qg][4 * j + 2][i] * inv, o[qg][4 * j + 3][i] * inv};
+          }
       }
     }
   }
 };
 
-// Attend to the Express state after beta blocks, then to the raw causal block.
-// Segments: HALVE output (weight m), completed batches of the epoch (m),
-// representatives of the current batch (m / 2), raw tokens (1, causal).
-template <class A>
-__device__ void express_block(A& at, const ExpressView& ev, int beta, int S, int key_end, bool row_ok) {
-  const int unit = at.unit;
-  if (beta < 4) {   // exact phase: every earlier token and the block itself, weight 1
-    at.run_segment(Seg{nullptr, 0, min(key_end, S), 0.f, nullptr, 1}, row_ok);
+// Stream of the queries of block beta (tokens [beta n, (beta + 1) n)) among
+// the workgroup's: the Express state after blocks 0 .. beta-1, then the block
+// itself up to key_end with the causal mask:
+//   beta < 4: everything before is still exact (raw, weight 1);
+//   else, with E = floor(log4 beta), m = 4^E, since = beta - m:
+//     cache   = HALVE output E-1 and batches 3(E-1) .. 3(E-1) + since/m - 1 (weight m),
+//     buffer  = the first (since % m) 2n / m representatives of batch 3(E-1) + since/m
+//               (weight m/2),
+//   each weight as log2 added to the logit.
+__device__ __forceinline__ void express_pass(const ExpressView& ev, int unit, int beta, int S, int key_end,
+                                             Gather& gs, Raw& raw) {
+  gs = Gather{{nullptr, nullptr, nullptr}, {0, 0, 0}, 0.f, nullptr};
+  if (beta < 4) {
+    raw = Raw{0, min(key_end, S), 0.f, 1};
     return;
   }
-  int E = 1;
-  while ((1LL << (2 * (E + 1))) <= beta) ++E;
-  const int m = 1 << (2 * E);
+  int Ep = 1;
+  while ((1LL << (2 * (Ep + 1))) <= beta) ++Ep;
+  const int m = 1 << (2 * Ep);
   const int since = beta - m;
   const int nbc = since / m;
   const int rem = since % m;
-  const float lm = static_cast<float>(2 * E);        // log2 m
-  at.run_segment(Seg{ev.halve_out + (static_cast<int64_t>(unit) * ev.n_halves + (E - 1)) * ev.n, 0, ev.n, lm,
-                     nullptr, 0},
-                 row_ok);
-  if (nbc > 0)
-    at.run_segment(Seg{ev.batch_out + (static_cast<int64_t>(unit) * ev.n_batches_done + 3 * (E - 1)) * ev.n, 0,
-                       nbc * ev.n, lm, nullptr, 0},
-                   row_ok);
-  const int n_rep = static_cast<int>((static_cast<int64_t>(rem) * 2 * ev.n) / m);
-  if (n_rep > 0)
-    at.run_segment(Seg{ev.reps + (static_cast<int64_t>(unit) * ev.n_batches_alloc + 3 * (E - 1) + nbc) * 2 * ev.n, 0,
-                       n_rep, lm - 1.0f, nullptr, 0},
-                   row_ok);
+  gs.lnw2 = static_cast<float>(2 * Ep);
+  gs.p[0] = ev.halve_out + (static_cast<int64_t>(unit) * ev.n_halves + (Ep - 1)) * ev.n;
+  gs.cnt[0] = ev.n;
+  gs.p[1] = ev.batch_out + (static_cast<int64_t>(unit) * ev.n_batches_done + 3 * (Ep - 1)) * ev.n;
+  gs.cnt[1] = nbc * ev.n;
+  gs.p[2] = ev.reps + (static_cast<int64_t>(unit) * ev.n_batches_alloc + 3 * (Ep - 1) + nbc) * 2 * ev.n;
+  gs.cnt[2] = static_cast<int>((static_cast<int64_t>(rem) * 2 * ev.n) / m);
   const int bn = beta * ev.n;
-  at.run_segment(Seg{nullptr, bn, min(key_end, S) - bn, 0.f, nullptr, 1}, row_ok);
+  raw = Raw{bn, min(key_end, S) - bn, 0.f, 1};
 }
 
-template <bool BF16, int E, int D>
-__global__ __launch_bounds__(256) void seg_attention_kernel(AttnLaunch a) {
+// Unmasked: one pass (the coreset, or all S keys).  Causal: one pass per
+// block beta met by the workgroup's queries.
+template <bool BF16, int E, int D, bool RAW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnLaunch a) {
+  constexpr int kQ = 16 * nqg<BF16, E, D>() * kWaves;
+  constexpr int NQG = Attn<BF16, E, D, RAW>::NQG;
   __shared__ Smem<BF16, E, D> sm;
   const int64_t tile = xcd_remap(blockIdx.y * static_cast<int64_t>(gridDim.x) + blockIdx.x,
                                  static_cast<int64_t>(gridDim.x) * gridDim.y);
-  const int q0 = static_cast<int>(tile % gridDim.x) * kQT;
-  const int bh = static_cast<int>(tile / gridDim.x);
-  Attn<BF16, E, D> at(a, sm, q0, bh);
-  if (!a.causal) {
-    const int b = bh / a.H, hk = (bh % a.H) / (a.H / a.H_kv);
-    const int unit = b * a.H_kv + hk;
-    if (a.cs_idx)
-      at.run_segment(Seg{a.cs_idx + unit * a.cs_stride, 0, a.cs_n, a.cs_lnw * kLog2e,
-                         a.cs_w ? a.cs_w + unit * a.cs_stride : nullptr, 0},
-                     true);
-    else
-      at.run_segment(Seg{nullptr, 0, a.S, a.cs_lnw * kLog2e, nullptr, 0}, true);
-  } else {
-    const int n = a.ev.n;
-    const int q_last = min(q0 + kQT - 1, a.T - 1);
-    const int beta_lo = q0 / n, beta_hi = q_last / n;
-    for (int beta = beta_lo; beta <= beta_hi; ++beta) {
-      const int key_end = min(q_last + 1, (beta + 1) * n);
-      express_block(at, a.ev, beta, a.S, key_end, (at.qr / n) == beta);
+  const int q0 = static_cast<int>(tile % gridDim.x) * kQ;
+  Attn<BF16, E, D, RAW> at(a, sm, q0, static_cast<int>(tile / gridDim.x));
+  const int q_last = min(q0 + kQ - 1, a.T - 1);
+  const int n = a.causal ? a.ev.n : 1;
+  const int beta_lo = a.causal ? q0 / n : 0, beta_hi = a.causal ? q_last / n : 0;
+  for (int beta = beta_lo; beta <= beta_hi; ++beta) {
+    Gather gs;
+    Raw raw;
+    bool row_ok[NQG];
+    if (!a.causal) {
+      gs = Gather{{nullptr, nullptr, nullptr}, {0, 0, 0}, a.cs_lnw * kLog2e, nullptr};
+      raw = Raw{0, 0, 0.f, 0};
+      if (a.cs_idx) {
+        gs.p[0] = a.cs_idx + at.unit * a.cs_stride;
+        gs.cnt[0] = a.cs_n;
+        gs.w = a.cs_w ? a.cs_w + at.unit * a.cs_stride : nullptr;
+      } else {
+        raw = Raw{0, a.S, a.cs_lnw * kLog2e, 0};
+      }
+      for (int qg = 0; qg < NQG; ++qg) row_ok[qg] = true;
+    } else {
+      express_pass(a.ev, at.unit, beta, a.S, min(q_last + 1, (beta + 1) * n), gs, raw);
+      for (int qg = 0; qg < NQG; ++qg) row_ok[qg] = (at.qr[qg] / n) == beta;
     }
+    at.run_stream(gs, raw, row_ok);
   }
-  at.store();
+  at.finish();
 }
 
 template <bool BF16, int E, int D>
-hipError_t launch_one(const AttnLaunch& a, hipStream_t s) {
-  dim3 grid((a.T + kQT - 1) / kQT, a.B * a.H);
-  hipLaunchKernelGGL((seg_attention_kernel<BF16, E, D>), grid, dim3(256), 0, s, a);
+hipError_t launch(const AttnLaunch& a, hipStream_t s) {
+  constexpr int kQ = 16 * nqg<BF16, E, D>() * kWaves;
+  dim3 grid((a.T + kQ - 1) / kQ, a.B * a.H);
+  if (!a.causal && a.cs_idx == nullptr)   // exact attention: one raw range, nothing staged
+    hipLaunchKernelGGL((attn_kernel<BF16, E, D, true>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<BF16, E, D, false>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -380,11 +594,15 @@ bool attention_supported(int bf16, int E, int D) {
 hipError_t launch_attention(const AttnLaunch& a, int bf16, int E, int D, hipStream_t s) {
   if (a.T == 0 || a.B * a.H == 0) return hipSuccess;
   if (bf16) {
-    return launch_attention_bf16(a, E, D, s);
+    if (E == 64 && D == 64) return launch<true, 64, 64>(a, s);
+    if (E == 64 && D == 128) return launch<true, 64, 128>(a, s);
+    if (E == 64 && D == 256) return launch<true, 64, 256>(a, s);
+    if (E == 128 && D == 128) return launch<true, 128, 128>(a, s);
+    if (E == 128 && D == 64) return launch<true, 128, 64>(a, s);
   } else {
-    if (E == 64 && D == 64) return launch_one<false, 64, 64>(a, s);
-    if (E == 64 && D == 128) return launch_one<false, 64, 128>(a, s);
-    if (E == 128 && D == 128) return launch_one<false, 128, 128>(a, s);
+    if (E == 64 && D == 64) return launch<false, 64, 64>(a, s);
+    if (E == 64 && D == 128) return launch<false, 64, 128>(a, s);
+    if (E == 128 && D == 128) return launch<false, 128, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }

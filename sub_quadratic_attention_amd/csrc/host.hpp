@@ -137,6 +137,11 @@ inline int check_dims(thin_attn* h, int64_t B, int64_t T, int64_t S, int causal)
   if (B < 0 || T < 0 || S < 0) return fail(h, THIN_EINVAL, "negative size");
   if (B * h->cfg.H_kv > (1LL << 20)) return fail(h, THIN_ENOTSUP, "too many units (B * H_kv)");
   if (S >= (1LL << 30) || T >= (1LL << 30)) return fail(h, THIN_ENOTSUP, "sequence too long");
+  {  // the attention addresses a batch entry's K / V rows with 32-bit byte offsets
+    const int64_t row = static_cast<int64_t>(h->cfg.H_kv) * std::max(h->cfg.E, h->cfg.D) * (h->cfg.dtype == THIN_BF16 ? 2 : 4);
+    if (row >= (1LL << 24) || S * row >= (1LL << 31))
+      return fail(h, THIN_ENOTSUP, "K / V of one batch entry exceed 2 GiB (S * H_kv * max(E, D) * element size)");
+  }
   if (causal) {
     if (T != S) return fail(h, THIN_EINVAL, "causal attention needs T == S (got T=%lld, S=%lld)", (long long)T, (long long)S);
     const int64_t n = cache_size(h, S);

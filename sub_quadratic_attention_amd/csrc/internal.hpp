@@ -140,7 +140,6 @@ hipError_t launch_express_final(const ExpressView& ev, int units, int S, int32_t
 hipError_t launch_fill_coreset(const int32_t* src, int64_t src_stride, int units, int n, float w,
                                int32_t* idx, float* wout, int32_t* len, hipStream_t s);
 hipError_t launch_attention(const AttnLaunch& a, int bf16, int E, int D, hipStream_t s);
-hipError_t launch_attention_bf16(const AttnLaunch& a, int E, int D, hipStream_t s);
 hipError_t launch_philox_words(const uint64_t* ctr, int64_t n, uint64_t seed, uint64_t* out, hipStream_t s);
 
 // Host mirror of the Express schedule (r <= n_out range only).
