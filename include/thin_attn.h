@@ -157,7 +157,8 @@ int thin_attn_coreset_attention(thin_attn_t* h, const void* q, const void* k, co
  * Outputs: kept [B * H_kv, N/2] the kept token of every pair; decisions
  * (optional) [B * H_kv, N/2], 1 = first point kept; gram [B * H_kv, N/2, N/2]
  * float64 receives the pair Gram G_ij = <h_i, h_j>, h_i = kappa(x_2i, .) -
- * kappa(x_2i+1, .) (lower triangle) and is also the kernel's scratch.
+ * kappa(x_2i+1, .) (upper triangle G[i][j], j >= i; the rest is left
+ * unspecified) and is also the kernel's scratch.
  */
 int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, int64_t S,
                       const int32_t* points, int64_t N, uint64_t seed, uint32_t tag, uint64_t bin,

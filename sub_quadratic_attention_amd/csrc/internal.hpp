@@ -30,7 +30,7 @@ struct PointSource {
 
 // Pair Gram of many bins at once.  Bin z holds N points whose token indices
 // are idx[z * idx_stride + 0 .. N); its pairs are (2i, 2i+1).  The launch
-// writes G[z][i][j] = <h_i, h_j> for the lower triangle (row-major P x P,
+// writes G[z][i][j] = <h_i, h_j> for the upper triangle j >= i (row-major P x P,
 // P = N / 2), h_i = kappa(x_2i, .) - kappa(x_2i+1, .).
 struct GramLaunch {
   PointSource src;

@@ -87,11 +87,13 @@ __device__ __forceinline__ double exp_f64(double x) {
   return __builtin_amdgcn_ldexp(p, static_cast<int>(fmax(fmin(n, 2100.0), -2100.0)));
 }
 
-// Tiles.  Bins get the lower-triangular 32 x 32 pair tiles of their own
-// P x P Gram, except bins with P dividing 32 (P < 32), which are packed: a unit's bins
+// Tiles.  Bins get the upper-triangular 32 x 32 pair tiles of their own
+// P x P Gram (G is symmetric; the walk reads G[j][i] for j <= i, so the
+// contribution of pairs j to every later pair i is a contiguous row segment),
+// except bins with P dividing 32 (P < 32), which are packed: a unit's bins
 // are consecutive in its point list, so one diagonal tile of 32 pairs covers
 // 32 / P whole bins and only entries of equal bin are kept.  Blocks lying
-// entirely above the diagonal are skipped (the walk reads j <= i only).
+// entirely below the diagonal are skipped.
 template <bool BF16>
 __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
   const int P = a.N / 2;
@@ -108,10 +110,11 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
     const int tiles = nt * (nt + 1) / 2;
     z = bid / tiles;
     const int t = bid % tiles;
-    tr = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
-    while (tr * (tr + 1) / 2 > t) --tr;
-    while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
-    tc = t - tr * (tr + 1) / 2;
+    // t -> (tc, tr) with tr <= tc: tile row tr, tile column tc of the upper triangle
+    tc = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
+    while (tc * (tc + 1) / 2 > t) --tc;
+    while ((tc + 1) * (tc + 2) / 2 <= t) ++tc;
+    tr = t - tc * (tc + 1) / 2;
     unit = z / a.bins_per_unit;
   }
   const int b = unit / a.src.H_kv;
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
   // does this wave's 16 x 16 pair block hold anything the walk reads?
   const int r0 = 32 * tr + 16 * wr;    // first pair row of the block
   const int c0 = 32 * tc + 16 * wc;    // first pair column
-  bool active = r0 + 15 >= c0;          // not entirely above the diagonal
+  bool active = c0 + 15 >= r0;          // not entirely below the diagonal
   if (packed && active && wr != wc) active = (r0 % P) != 0;   // a bin straddles the two halves
   if (!packed && (r0 >= P || c0 >= P)) active = false;
 
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
     const double gv = (kee - keo) - (koe - koo);
     if (packed) {
       const int bin = row / P;
-      if (bin == col / P && bin < a.bins_per_unit && col <= row)
+      if (bin == col / P && bin < a.bins_per_unit && col >= row)
         a.G[(static_cast<int64_t>(unit) * a.bins_per_unit + bin) * P * P + (row % P) * P + (col % P)] = gv;
     } else if (row < P && col < P) {
       a.G[static_cast<int64_t>(z) * P * P + static_cast<int64_t>(row) * P + col] = gv;
@@ -260,9 +263,9 @@ struct SigmaState {
 
 // Rows q0..q0+63, columns q0..q0+63 of a bin's G into LDS (row stride 65),
 // `PER` consecutive doubles per thread, all loads issued before any store.
-// Entries above the diagonal are copied too: a lane only uses row entries
-// left of its own pair, so they never influence a decision.  Rows and
-// columns beyond P read as 0.
+// Entries below the diagonal are copied too: the chain only reads G[j][i]
+// for j < i (the upper triangle), so they never influence a decision.  Rows
+// and columns beyond P read as 0.
 template <int PER>
 __device__ __forceinline__ void stage_block(const double* G, int P, int q0, double* dst, int t) {
   const int r = (t * PER) >> 6;
@@ -360,9 +363,9 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
     if (w == 0) {
       double alpha = s_alpha[p0 + lane < P ? p0 + lane : 0];
       const double thr = lane < rows ? s_thr[p0 + lane] : 0.0;
-      double g[64];
+      double g[64];   // g[cc] = G[p0 + cc][p0 + lane]: the upper triangle holds it for cc < lane
 #pragma unroll
-      for (int cc = 0; cc < 64; ++cc) g[cc] = blk[lane * 65 + cc];
+      for (int cc = 0; cc < 64; ++cc) g[cc] = blk[cc * 65 + lane];
       uint64_t bits = 0;
 #pragma unroll
       for (int j = 0; j < 64; ++j) {
@@ -385,13 +388,14 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
       stage_block<32>(G, P, p0 + 64, s_G + ((p + 1) & 1) * 64 * 65, tid - 64);
     }
     __syncthreads();
-    // the panel's contribution to every later pair
+    // the panel's contribution to every later pair i: sum_j eta_j G[p0 + j][i],
+    // row segments of the upper triangle, read coalesced across the lanes
     if (p + 1 < np) {
       for (int i = p0 + 64 + tid; i < P; i += 256) {
-        const double* row = G + static_cast<int64_t>(i) * P + p0;
+        const double* col = G + static_cast<int64_t>(p0) * P + i;
         double gv[64];                       // full panel: rows == 64 here; all loads in flight
 #pragma unroll
-        for (int j = 0; j < 64; ++j) gv[j] = row[j];
+        for (int j = 0; j < 64; ++j) gv[j] = col[static_cast<int64_t>(j) * P];
         double acc0 = 0.0, acc1 = 0.0;
 #pragma unroll
         for (int j = 0; j < 64; j += 2) {
@@ -425,7 +429,7 @@ __global__ __launch_bounds__(256) void halving_sweep_small_kernel(SweepLaunch a)
   const double bb = sqrt(b2);
   double g[PMAX];
 #pragma unroll
-  for (int j = 0; j < PMAX; ++j) g[j] = (mine && j < lane) ? G[static_cast<int64_t>(lane) * P + j] : 0.0;
+  for (int j = 0; j < PMAX; ++j) g[j] = (mine && j < lane) ? G[static_cast<int64_t>(j) * P + lane] : 0.0;   // upper triangle
   // thresholds: the recursion runs on uniform values read with readlane
   const double c = sqrt(2.0 * log(2.0 * a.N / a.delta));
   const double k1 = 1.0 + 1.0 / (c * c);
