@@ -157,9 +157,9 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
         const int N = static_cast<int>(p.s0 << (l + 1));
         const int bins = static_cast<int>(S / (p.s0 << (2 * l)));
         const int64_t in_unit = S >> (l - 1);
-        THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(make_gram(src, a, N, in_unit, units, bins, h->scale64, G), st); }));
         thin::SweepLaunch sl = make_sweep(h, G, N, units, bins, a, in_unit, b, seed, thin::kTagCompress,
                                           static_cast<uint64_t>(l) << 20);
+        THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
         sl.out_stride = N / 2;
         sl.dec = decisions;
         sl.dec_per_unit = ndec;
@@ -245,9 +245,8 @@ int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, i
   const hipStream_t st = as_stream(stream);
   thin::PointSource src{k, v, S, c.H_kv, c.E, c.D, c.dtype == THIN_BF16};
   const int n = static_cast<int>(N);
-  const thin::GramLaunch gl = make_gram(src, points, n, n, units, 1, h->scale64, gram);
-  THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gl, st); }));
   thin::SweepLaunch sl = make_sweep(h, gram, n, units, 1, points, n, kept, seed, tag, bin);
+  THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
   sl.dec = decisions;
   sl.dec_per_unit = n / 2;
   THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, st); }));

@@ -156,18 +156,23 @@ inline int check_dims(thin_attn* h, int64_t B, int64_t T, int64_t S, int causal)
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-inline thin::GramLaunch make_gram(const thin::PointSource& src, const int32_t* idx, int N, int64_t unit_stride, int units,
-                           int bins_per_unit, double scale, double* G) {
+// The pair Gram of the bins a walk is about to halve, with that walk's
+// Philox parameters (the Gram launch also forms the walk's thresholds).
+inline thin::GramLaunch gram_for(const thin::SweepLaunch& w, const thin::PointSource& src, double scale) {
   thin::GramLaunch g{};
   g.src = src;
-  g.idx = idx;
-  g.idx_stride = N;
-  g.idx_unit_stride = unit_stride;
-  g.N = N;
-  g.nbins = units * bins_per_unit;
-  g.bins_per_unit = bins_per_unit;
+  g.idx = w.idx_in;
+  g.idx_stride = w.in_stride;
+  g.idx_unit_stride = w.in_unit_stride;
+  g.N = w.N;
+  g.nbins = w.nbins;
+  g.bins_per_unit = w.bins_per_unit;
   g.scale = scale;
-  g.G = G;
+  g.G = const_cast<double*>(w.G);
+  g.seed = w.seed;
+  g.tag = w.tag;
+  g.bin_base = w.bin_base;
+  g.delta = w.delta;
   return g;
 }
 
@@ -260,9 +265,8 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
     const int N = 2 * n;
     const int nb = p.sc.n_batches_done;
     const int64_t ustride = static_cast<int64_t>(p.sc.n_batches_alloc) * N;
-    thin::GramLaunch gl = make_gram(src, reps, N, ustride, units, nb, h->scale64, G);
-    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gl, st); }));
     thin::SweepLaunch sl = make_sweep(h, G, N, units, nb, reps, ustride, bout, seed, thin::kTagBatch, 0);
+    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
     sl.out_stride = n;
     sl.dec = decisions;
     sl.dec_per_unit = ndec;
@@ -272,19 +276,17 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
   // 3. the HALVE chain: halve twice, 4n -> 2n -> n
   for (int e = 0; e < p.sc.n_halves; ++e) {
     THIN_HIP(timed(h, st, "halve_input", [&] { return thin::launch_halve_input(ev, units, e, hin, st); }));
-    const thin::GramLaunch g1 = make_gram(src, hin, 4 * n, 4 * n, units, 1, h->scale64, G);
-    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(g1, st); }));
     thin::SweepLaunch s1 = make_sweep(h, G, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
                                       static_cast<uint64_t>(e));
+    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(s1, src, h->scale64), st); }));
     s1.out_stride = 2 * n;
     s1.dec = decisions;
     s1.dec_per_unit = ndec;
     s1.dec_base = static_cast<int64_t>(6) * n * e;
     THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(s1, st); }));
-    const thin::GramLaunch g2 = make_gram(src, hmid, 2 * n, 2 * n, units, 1, h->scale64, G);
-    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(g2, st); }));
     thin::SweepLaunch s2 = make_sweep(h, G, 2 * n, units, 1, hmid, 2 * n, hout + static_cast<int64_t>(e) * n, seed,
                                       thin::kTagHalveSecond, static_cast<uint64_t>(e));
+    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(s2, src, h->scale64), st); }));
     s2.out_stride = static_cast<int64_t>(p.sc.n_halves) * n;   // unit u -> row u of [units][halves][n]
     s2.dec = decisions;
     s2.dec_per_unit = ndec;

@@ -34,6 +34,12 @@ struct PointSource {
 // P = N / 2), h_i = kappa(x_2i, .) - kappa(x_2i+1, .).
 struct GramLaunch {
   PointSource src;
+  // Thresholds of the walk that follows (bins of P > 64 pairs): pair i's
+  // a_i (1 - 2 u_i) goes to the unused lower triangle, G[i][i-1] for i >= 1
+  // and G[P-1][0] for pair 0, from the Philox stream (pair, bin_base + bin,
+  // unit, tag) under seed and delta.
+  uint64_t seed, tag, bin_base;
+  double delta;
   const int32_t* idx;       // bin (u, j) list at idx + u * idx_unit_stride + j * idx_stride
   int64_t idx_stride;
   int64_t idx_unit_stride;

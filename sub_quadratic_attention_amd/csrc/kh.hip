@@ -87,6 +87,131 @@ __device__ __forceinline__ double exp_f64(double x) {
   return __builtin_amdgcn_ldexp(p, static_cast<int>(fmax(fmin(n, 2100.0), -2100.0)));
 }
 
+// ---------------------------------------------------------------------------
+// Thresholds of the walk.  For pair i: b_i^2 = G_ii,
+// a_i = max(b_i sigma_{i-1} c_N, b_i^2) with c_N = sqrt(2 ln(2N / delta)), and
+// the first point is kept iff u_i < (1 - alpha_i / a_i) / 2, i.e. iff
+// alpha_i < a_i (1 - 2 u_i) (a_i = 0: iff u_i < 1/2).  a_i and sigma_i depend
+// only on the b's, so the thresholds thr_i = a_i (1 - 2 u_i) are formed ahead
+// of the walk.  Bins of more than 64 pairs get them from extra workgroups of
+// the pair-Gram launch (one wave per bin, overlapping the tiles), stored in the
+// lower triangle of the bin's G, which the walk does not otherwise read: pair
+// i >= 1 at G[i][i-1], pair 0 at G[P-1][0].  The one-wave walk of smaller bins
+// forms its own.
+//
+// sigma recursion without a division: with sigma = sqrt(sigma^2),
+//   if b sigma c >= b^2 (a = b sigma c):
+//     sigma^2 += max(0, b^2 (1 + 1/c^2) - 2 sigma b / c)
+//   else (a = b^2):  sigma^2 = max(sigma^2, b^2)
+// which is the published update b^2 max(0, 1 + (b^2 - 2a) sigma^2 / a^2)
+// written out for the two cases of a.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t thr_slot(int i, int P) {
+  return i >= 1 ? static_cast<int64_t>(i) * P + (i - 1) : static_cast<int64_t>(P - 1) * P;
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int i) {
+  const uint64_t bits = __double_as_longlong(x);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(bits), i);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(bits >> 32), i);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Steps 0 .. n-1 of the sigma recursion on the pairs held by the lanes of one
+// wave (lane i: b_i^2 and b_i), from sigma^2 = s2; lane i receives
+// a_i = max(b_i sigma_{i-1} c, b_i^2).  The values depending on b alone are
+// formed lane-parallel first; on the serial path stay one square root, one
+// multiply, one fma, two max, one add and selects (no branches).
+__device__ __forceinline__ double sigma_steps(double& s2, double b2l, double bl, int n, double c, double k1, double k2) {
+  const int lane = threadIdx.x & 63;
+  const double cbl = c * bl, b2k1l = b2l * k1, k2bl = k2 * bl;
+  double al = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const double b2 = readlane_f64(b2l, i);
+    const double cb = readlane_f64(cbl, i);
+    const double b2k1 = readlane_f64(b2k1l, i);
+    const double k2b = readlane_f64(k2bl, i);
+    const double sg = __builtin_amdgcn_sqrt(s2);
+    const double bsc = cb * sg;
+    const double grow = s2 + fmax(0.0, fma(-k2b, sg, b2k1));
+    const double keep = fmax(s2, b2);
+    al = lane == i ? fmax(bsc, b2) : al;
+    s2 = bsc >= b2 ? grow : keep;
+  }
+  return al;
+}
+
+// Threshold of a pair: a (1 - 2 u), or +-inf by u < 1/2 when a = 0.
+__device__ __forceinline__ double threshold(double al, double u) {
+  return al > 0.0 ? al * (1.0 - 2.0 * u) : (u < 0.5 ? INFINITY : -INFINITY);
+}
+
+// b_i^2 of pair i (its two points: fp64 dot products, the same kernel as the
+// Gram, four partial sums per product) and u_i (Philox).
+template <bool BF16>
+__device__ void pair_b2_u(const GramLaunch& a, int z, int i, double& b2, double& u) {
+  const int unit = z / a.bins_per_unit, lb = z % a.bins_per_unit;
+  const int b = unit / a.src.H_kv, h = unit % a.src.H_kv;
+  const int32_t* list = a.idx + static_cast<int64_t>(unit) * a.idx_unit_stride + static_cast<int64_t>(lb) * a.idx_stride;
+  auto dots = [&](const void* base, int F, int64_t re, int64_t ro, double& xx, double& xy, double& yy) {
+    double sxx[4] = {0.0, 0.0, 0.0, 0.0}, sxy[4] = {0.0, 0.0, 0.0, 0.0}, syy[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int f = 0; f < F; f += 8) {
+      Raw8 e8, o8;
+      load8<BF16>(base, re * F + f, e8);
+      load8<BF16>(base, ro * F + f, o8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double x = raw8_at<BF16>(e8, j), y = raw8_at<BF16>(o8, j);
+        sxx[j & 3] = fma(x, x, sxx[j & 3]);
+        sxy[j & 3] = fma(x, y, sxy[j & 3]);
+        syy[j & 3] = fma(y, y, syy[j & 3]);
+      }
+    }
+    xx = (sxx[0] + sxx[1]) + (sxx[2] + sxx[3]);
+    xy = (sxy[0] + sxy[1]) + (sxy[2] + sxy[3]);
+    yy = (syy[0] + syy[1]) + (syy[2] + syy[3]);
+  };
+  const int64_t re = (static_cast<int64_t>(b) * a.src.S + list[2 * i]) * a.src.H_kv + h;
+  const int64_t ro = (static_cast<int64_t>(b) * a.src.S + list[2 * i + 1]) * a.src.H_kv + h;
+  double kee, keo, koo, vee, veo, voo;
+  dots(a.src.k, a.src.E, re, ro, kee, keo, koo);
+  dots(a.src.v, a.src.D, re, ro, vee, veo, voo);
+  const double xee = exp_f64(a.scale * kee) * (vee + 1.0);
+  const double xeo = exp_f64(a.scale * keo) * (veo + 1.0);
+  const double xoo = exp_f64(a.scale * koo) * (voo + 1.0);
+  b2 = fmax((xee - xeo) - (xeo - xoo), 0.0);
+  u = philox_uniform(static_cast<uint64_t>(i), a.bin_base + lb, static_cast<uint64_t>(unit), a.tag, a.seed);
+}
+
+// The sigma recursion of bin z by one wave, 64 pairs at a time, and the
+// thresholds into the lower triangle.  s_b2 / s_u: the bin's b^2 and u already
+// formed (by the whole workgroup), or nullptr to form them here per chunk.
+template <bool BF16>
+__device__ void bin_thresholds(const GramLaunch& a, int z, const double* s_b2, const double* s_u) {
+  const int P = a.N / 2;
+  const int lane = threadIdx.x & 63;
+  double* G = a.G + static_cast<int64_t>(z) * P * P;
+  const double c = sqrt(2.0 * log(2.0 * a.N / a.delta));
+  const double k1 = 1.0 + 1.0 / (c * c);
+  const double k2 = 2.0 / c;
+  double s2 = 0.0;
+  for (int i0 = 0; i0 < P; i0 += 64) {
+    const int i = i0 + lane;
+    const bool mine = i < P;
+    double b2 = 0.0, u = 0.0;
+    if (mine) {
+      if (s_b2) {
+        b2 = s_b2[i];
+        u = s_u[i];
+      } else {
+        pair_b2_u<BF16>(a, z, i, b2, u);
+      }
+    }
+    const double al = sigma_steps(s2, b2, sqrt(b2), min(64, P - i0), c, k1, k2);
+    if (mine) G[thr_slot(i, P)] = threshold(al, u);
+  }
+}
+
 // Tiles.  Bins get the upper-triangular 32 x 32 pair tiles of their own
 // P x P Gram (G is symmetric; the walk reads G[j][i] for j <= i, so the
 // contribution of pairs j to every later pair i is a contiguous row segment),
@@ -94,11 +219,33 @@ __device__ __forceinline__ double exp_f64(double x) {
 // are consecutive in its point list, so one diagonal tile of 32 pairs covers
 // 32 / P whole bins and only entries of equal bin are kept.  Blocks lying
 // entirely below the diagonal are skipped.
+// The first nthr workgroups form the thresholds, the others the tiles.  With
+// few bins (thr_per_wave == 0) a workgroup takes one bin: all its waves form
+// b^2 and u into LDS, then wave 0 runs the recursion; with many, each wave
+// takes one bin on its own, so the thresholds occupy fewer workgroups.
 template <bool BF16>
-__global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
+__global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a, int nthr, int thr_per_wave) {
+  __shared__ double rowF[64][kPad];
+  __shared__ double colF[64][kPad];
+  if (static_cast<int>(blockIdx.x) < nthr) {
+    if (thr_per_wave) {
+      const int z = 4 * blockIdx.x + (threadIdx.x >> 6);
+      if (z < a.nbins) bin_thresholds<BF16>(a, z, nullptr, nullptr);
+      return;   // the whole workgroup: no barrier here
+    }
+    const int z = blockIdx.x;
+    if (z >= a.nbins) return;   // the whole workgroup
+    const int P = a.N / 2;      // b^2 and u of up to 64 * kPad pairs each fit the tile buffers
+    double* s_b2 = &rowF[0][0];
+    double* s_u = &colF[0][0];
+    for (int i = threadIdx.x; i < P; i += 256) pair_b2_u<BF16>(a, z, i, s_b2[i], s_u[i]);
+    __syncthreads();
+    if (threadIdx.x < 64) bin_thresholds<BF16>(a, z, s_b2, s_u);
+    return;
+  }
   const int P = a.N / 2;
   const bool packed = P < 32 && (32 % P) == 0;   // whole bins per tile
-  const int bid = static_cast<int>(xcd_remap(blockIdx.x, gridDim.x));
+  const int bid = static_cast<int>(xcd_remap(blockIdx.x - nthr, gridDim.x - nthr));
   int unit, tr, tc, z;
   if (packed) {
     const int tiles = (a.bins_per_unit * P + 31) / 32;
@@ -119,9 +266,6 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
   }
   const int b = unit / a.src.H_kv;
   const int h = unit % a.src.H_kv;
-
-  __shared__ double rowF[64][kPad];
-  __shared__ double colF[64][kPad];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -218,36 +362,23 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a) {
       const int bin = row / P;
       if (bin == col / P && bin < a.bins_per_unit && col >= row)
         a.G[(static_cast<int64_t>(unit) * a.bins_per_unit + bin) * P * P + (row % P) * P + (col % P)] = gv;
-    } else if (row < P && col < P) {
+    } else if (row < P && col < P && col >= row) {   // below the diagonal: thresholds
       a.G[static_cast<int64_t>(z) * P * P + static_cast<int64_t>(row) * P + col] = gv;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Kernel-halving walk of one bin per workgroup.
+// Kernel-halving walk of one bin per workgroup, on thresholds formed by the
+// pair-Gram launch.
 //
-// For pair i: b_i^2 = G_ii, a_i = max(b_i sigma_{i-1} c_N, b_i^2) with
-// c_N = sqrt(2 ln(2N / delta)), and the first point is kept iff
-// u_i < (1 - alpha_i / a_i) / 2, i.e. iff alpha_i < a_i (1 - 2 u_i)
-// (a_i = 0: iff u_i < 1/2).  a_i and sigma_i depend only on the b's, so the
-// thresholds thr_i = a_i (1 - 2 u_i) can be computed ahead of the walk.
-//
-// The walk runs in panels of 64 pairs.  alpha_i = sum_{j<i} eta_j G_ij is
+// The walk runs in panels of 64 pairs.  alpha_i = sum_{j<i} eta_j G_ji is
 // kept for every pair in LDS.  For panel p:
 //   wave 0   takes the 64 decisions: lane l holds alpha of pair p0+l and its
-//            row of the panel's diagonal block; one ballot per decision;
+//            column of the panel's diagonal block; one ballot per decision;
 //   wave 1-2 stage the next panel's diagonal block (double buffered);
-//   wave 3   runs the sigma recursion for the next panel's thresholds;
-// then all waves add the panel's contribution eta_p G[:, p] to the alpha of
-// every later pair (independent row loads, many in flight).
-//
-// sigma recursion without a division: with sigma = sqrt(sigma^2),
-//   if b sigma c >= b^2 (a = b sigma c):
-//     sigma^2 += max(0, b^2 (1 + 1/c^2) - 2 sigma b / c)
-//   else (a = b^2):  sigma^2 = max(sigma^2, b^2)
-// which is the published update b^2 max(0, 1 + (b^2 - 2a) sigma^2 / a^2)
-// written out for the two cases of a.
+// then all waves add the panel's contribution sum_j eta_j G[j][i] to the
+// alpha of every later pair (coalesced row segments, many in flight).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t dec_offset(const SweepLaunch& a, int lb, int P) {
   if (a.dec_mode == 1) {   // Express batch k = lb: HALVE 0, then (3 batches, HALVE) per epoch
@@ -256,10 +387,6 @@ __device__ __forceinline__ int64_t dec_offset(const SweepLaunch& a, int lb, int 
   }
   return a.dec_base + static_cast<int64_t>(lb) * P;
 }
-
-struct SigmaState {
-  double s2;
-};
 
 // Rows q0..q0+63, columns q0..q0+63 of a bin's G into LDS (row stride 65),
 // `PER` consecutive doubles per thread, all loads issued before any store.
@@ -279,12 +406,6 @@ __device__ __forceinline__ void stage_block(const double* G, int P, int q0, doub
   for (int j = 0; j < PER; ++j) dst[r * 65 + cb + j] = v[j];
 }
 
-__device__ __forceinline__ double readlane_f64(double x, int i) {
-  const uint64_t bits = __double_as_longlong(x);
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(bits), i);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(bits >> 32), i);
-  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
-}
 
 // Thresholds of the pairs [i0, i0 + 64) by one wave: lane l holds b^2, b and
 // u of pair i0 + l in registers; the recursion runs on uniform values read
@@ -292,30 +413,6 @@ __device__ __forceinline__ double readlane_f64(double x, int i) {
 // threshold of pair i0 + i.  The only serial operation besides fma / max is
 // sqrt(sigma^2); the hardware fp64 square root is used (its error is far
 // below the 1e-6 decision margins that matter).
-__device__ __forceinline__ void sigma_chain_wave(SigmaState& st, const double* s_b2, const double* s_b, double* s_thr,
-                                                 int i0, int P, double c, double k1, double k2) {
-  const int lane = threadIdx.x & 63;
-  const int n = min(64, P - i0);
-  const bool mine = lane < n;
-  const double b2l = mine ? s_b2[i0 + lane] : 0.0;
-  const double bl = mine ? s_b[i0 + lane] : 0.0;
-  const double ul = mine ? s_thr[i0 + lane] : 0.0;
-  double s2 = st.s2;
-  double thr = 0.0;
-  for (int i = 0; i < n; ++i) {
-    const double b2 = readlane_f64(b2l, i);
-    const double bb = readlane_f64(bl, i);
-    const double u = readlane_f64(ul, i);
-    const double sg = __builtin_amdgcn_sqrt(s2);
-    const double bsc = bb * sg * c;
-    const double aa = fmax(bsc, b2);
-    const double t = aa > 0.0 ? aa * (1.0 - 2.0 * u) : (u < 0.5 ? INFINITY : -INFINITY);
-    thr = lane == i ? t : thr;
-    s2 = bsc >= b2 ? s2 + fmax(0.0, b2 * k1 - k2 * sg * bb) : fmax(s2, b2);
-  }
-  if (mine) s_thr[i0 + lane] = thr;
-  st.s2 = s2;
-}
 
 __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
   extern __shared__ double smem[];
@@ -324,33 +421,21 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
   const int unit = z / a.bins_per_unit;
   const int lb = z % a.bins_per_unit;
   const double* G = a.G + static_cast<int64_t>(z) * P * P;
-  double* s_thr = smem;               // P   (u, then thresholds)
-  double* s_b2 = s_thr + P;           // P
-  double* s_alpha = s_b2 + P;         // P
+  double* s_thr = smem;               // P   thresholds (formed by the pair-Gram launch)
+  double* s_alpha = s_thr + P;        // P
   double* s_eta = s_alpha + P;        // P   (+1 / -1)
-  double* s_b = s_eta + P;            // P   (b = sqrt(b^2))
-  double* s_G = s_b + P;              // 2 x 64 x 65
+  double* s_G = s_eta + P;            // 2 x 64 x 65
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const double c = sqrt(2.0 * log(2.0 * a.N / a.delta));
-  const double k1 = 1.0 + 1.0 / (c * c);
-  const double k2 = 2.0 / c;
 
   for (int i = tid; i < P; i += 256) {
-    s_thr[i] = philox_uniform(static_cast<uint64_t>(i), a.bin_base + lb, static_cast<uint64_t>(unit), a.tag,
-                              a.seed);
-    s_b2[i] = fmax(G[static_cast<int64_t>(i) * P + i], 0.0);
-    s_b[i] = sqrt(s_b2[i]);
+    s_thr[i] = G[thr_slot(i, P)];
     s_alpha[i] = 0.0;
   }
-  __syncthreads();
-  SigmaState sig{0.0};
   const int np = (P + 63) / 64;
-  // panel 0: thresholds and diagonal block
-  if (w == 3) sigma_chain_wave(sig, s_b2, s_b, s_thr, 0, P, c, k1, k2);
-  stage_block<16>(G, P, 0, s_G, tid);
+  stage_block<16>(G, P, 0, s_G, tid);   // panel 0's diagonal block
   __syncthreads();
 
   const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
@@ -381,9 +466,7 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
         out[i] = in[2 * i + (first ? 0 : 1)];
         if (dec) dec[i] = first ? 1 : 0;
       }
-    } else if (w == 3) {
-      if (p + 1 < np) sigma_chain_wave(sig, s_b2, s_b, s_thr, p0 + 64, P, c, k1, k2);
-    } else if (p + 1 < np) {
+    } else if (w <= 2 && p + 1 < np) {
       // waves 1 and 2 stage the next diagonal block
       stage_block<32>(G, P, p0 + 64, s_G + ((p + 1) & 1) * 64 * 65, tid - 64);
     }
@@ -422,34 +505,17 @@ __global__ __launch_bounds__(256) void halving_sweep_small_kernel(SweepLaunch a)
   const int lb = z % a.bins_per_unit;
   const double* G = a.G + static_cast<int64_t>(z) * P * P;
   const bool mine = lane < P;
+  double g[PMAX];
+#pragma unroll
+  for (int j = 0; j < PMAX; ++j) g[j] = (mine && j < lane) ? G[static_cast<int64_t>(j) * P + lane] : 0.0;   // upper triangle
+  // thresholds of at most 64 pairs, formed here (b^2 from the Gram diagonal)
   const double u = mine ? philox_uniform(static_cast<uint64_t>(lane), a.bin_base + lb, static_cast<uint64_t>(unit),
                                          a.tag, a.seed)
                         : 0.0;
   const double b2 = mine ? fmax(G[static_cast<int64_t>(lane) * P + lane], 0.0) : 0.0;
-  const double bb = sqrt(b2);
-  double g[PMAX];
-#pragma unroll
-  for (int j = 0; j < PMAX; ++j) g[j] = (mine && j < lane) ? G[static_cast<int64_t>(j) * P + lane] : 0.0;   // upper triangle
-  // thresholds: the recursion runs on uniform values read with readlane
   const double c = sqrt(2.0 * log(2.0 * a.N / a.delta));
-  const double k1 = 1.0 + 1.0 / (c * c);
-  const double k2 = 2.0 / c;
-  double thr = 0.0;
   double s2 = 0.0;
-  for (int i = 0; i < P; ++i) {
-    const double b2i = readlane_f64(b2, i);
-    const double bi = readlane_f64(bb, i);
-    const double ui = readlane_f64(u, i);
-    const double sg = __builtin_amdgcn_sqrt(s2);
-    const double bsc = bi * sg * c;
-    const double aa = fmax(bsc, b2i);
-    const double t = aa > 0.0 ? aa * (1.0 - 2.0 * ui) : (ui < 0.5 ? INFINITY : -INFINITY);
-    if (lane == i) thr = t;
-    if (bsc >= b2i)
-      s2 = s2 + fmax(0.0, b2i * k1 - k2 * sg * bi);
-    else
-      s2 = fmax(s2, b2i);
-  }
+  const double thr = threshold(sigma_steps(s2, b2, sqrt(b2), P, c, 1.0 + 1.0 / (c * c), 2.0 / c), u);
   double alpha = 0.0;
   uint64_t bits = 0;
 #pragma unroll
@@ -620,15 +686,20 @@ hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s) {
     blocks = static_cast<int64_t>(nt) * (nt + 1) / 2 * a.nbins;
   }
   if (blocks == 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>(blocks));
+  // threshold workgroups for bins of P > 64 pairs (the walks of the large sweep
+  // kernel): one per bin while there are at most 64 bins, else four bins each;
+  // a multiple of 8 so that the tiles keep their XCD mapping
+  const int per_wave = (a.nbins > 64 || P > 64 * kPad) ? 1 : 0;
+  const int nthr = P > 64 ? (per_wave ? (a.nbins + 31) / 32 * 8 : (a.nbins + 7) / 8 * 8) : 0;
+  dim3 grid(static_cast<unsigned>(blocks + nthr));
   if (a.src.bf16)
-    hipLaunchKernelGGL(pair_gram_kernel<true>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(pair_gram_kernel<true>, grid, dim3(256), 0, s, a, nthr, per_wave);
   else
-    hipLaunchKernelGGL(pair_gram_kernel<false>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(pair_gram_kernel<false>, grid, dim3(256), 0, s, a, nthr, per_wave);
   return hipGetLastError();
 }
 
-size_t sweep_lds_bytes(int N) { return (5 * static_cast<size_t>(N / 2) + 2 * 64 * 65) * sizeof(double); }
+size_t sweep_lds_bytes(int N) { return (3 * static_cast<size_t>(N / 2) + 2 * 64 * 65) * sizeof(double); }
 
 hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s) {
   if (a.N / 2 <= 16) {

@@ -162,9 +162,8 @@ int halve_slots(thin_kv& kv, const int32_t* in, int N, int32_t* out, uint32_t ta
                 int64_t dec_per_unit, int64_t dec_base, double* G, hipStream_t st) {
   thin_attn* h = kv.h;
   const thin::PointSource src = state_source(kv);
-  const thin::GramLaunch gl = make_gram(src, in, N, N, kv.units, 1, h->scale64, G);
-  THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gl, st); }));
   thin::SweepLaunch sl = make_sweep(h, G, N, kv.units, 1, in, N, out, kv.seed, tag, bin);
+  THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
   sl.dec = dec;
   sl.dec_per_unit = dec_per_unit;
   sl.dec_base = dec_base;
