@@ -133,6 +133,7 @@ struct Attn {
   bool live[NQG];
   QF qf[NQG][NQF];
   f32x4_t o[NQG][ND];
+  f32x4_t osum[NQG];   // bf16: row sums of P (all four elements equal)
   float m_run[NQG], l_run[NQG];
 
   float r_w;   // weighted coreset: weight of the key this thread describes in the next chunk
@@ -141,6 +142,11 @@ struct Attn {
   Gather gs;
   Raw raw;
   int G, w0, wl;
+  // key visible to query group qg iff its posc < qlim[qg] (qr + 1, or INT_MIN
+  // when the query is not in the stream's block); rows_ok: every query of the
+  // wave is (then only causal keys need the test)
+  int qlim[NQG];
+  bool rows_ok;
 
   __device__ __forceinline__ Attn(const AttnLaunch& la, Smem<BF16, E, D>& s, int q0, int bh) : a(la), sm(s) {
     b = bh / a.H;
@@ -175,6 +181,7 @@ struct Attn {
       }
 #pragma unroll
       for (int d = 0; d < ND; ++d) o[qg][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      osum[qg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       m_run[qg] = -INFINITY;
       l_run[qg] = 0.f;
     }
@@ -290,9 +297,12 @@ struct Attn {
     }
   }
 
-  __device__ __forceinline__ void consume(int buf, const lds_byte* kbuf, const lds_byte* vbuf, const bool row_ok[NQG]) {
+  __device__ __forceinline__ void consume(int c, int buf, const lds_byte* kbuf, const lds_byte* vbuf) {
     f32x4_t st[NQG][4];
     scores(kbuf, st);
+    // padding keys carry log-weight -inf; only causal keys and queries outside
+    // the stream's block need the visibility test
+    const bool masked = !rows_ok || (raw.causal && w0 + kC * (c + 1) > G);
     const float sc = a.scale * kLog2e;
     int pc[4][4];
     float lw[4][4];
@@ -305,37 +315,54 @@ struct Attn {
     }
     // online softmax; p[qg][kb][i] is the weight of key 16 kb + 4 g + i
     float p[NQG][4][4];
+    if (masked) {   // two copies of the logit loop, so the common one carries no test
+#pragma unroll
+      for (int qg = 0; qg < NQG; ++qg)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            p[qg][kb][i] = pc[kb][i] < qlim[qg] ? fmaf(st[qg][kb][i], sc, lw[kb][i]) : -INFINITY;
+    } else {
+#pragma unroll
+      for (int qg = 0; qg < NQG; ++qg)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[qg][kb][i] = fmaf(st[qg][kb][i], sc, lw[kb][i]);
+    }
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool vis = row_ok[qg] && pc[kb][i] <= qr[qg];
-          const float val = vis ? fmaf(st[qg][kb][i], sc, lw[kb][i]) : -INFINITY;
-          p[qg][kb][i] = val;
-          mx = fmaxf(mx, val);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, p[qg][kb][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run[qg], mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_use);
-      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[qg][kb][i] = __builtin_amdgcn_exp2f(p[qg][kb][i] - m_use);
-          rs += p[qg][kb][i];
-        }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
-      l_run[qg] = l_run[qg] * alpha + rs;
-      m_run[qg] = m_new;
+        for (int i = 0; i < 4; ++i) p[qg][kb][i] = __builtin_amdgcn_exp2f(p[qg][kb][i] - m_use);
+      if constexpr (!BF16) {   // bf16: the row sum comes out of the P V MFMAs (a block of ones)
+        float rs = 0.f;
 #pragma unroll
-      for (int d = 0; d < ND; ++d) o[qg][d] *= alpha;
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rs += p[qg][kb][i];
+        rs += __shfl_xor(rs, 16, 64);
+        rs += __shfl_xor(rs, 32, 64);
+        l_run[qg] = l_run[qg] * alpha + rs;
+      }
+      m_run[qg] = m_new;
+      if (__ballot(alpha != 1.0f)) {   // most chunks leave every maximum where it was
+#pragma unroll
+        for (int d = 0; d < ND; ++d) o[qg][d] *= alpha;
+        if constexpr (BF16) osum[qg] *= alpha;
+      }
     }
     if constexpr (BF16) {
       bf16x8_t pb[NQG][2];
@@ -368,6 +395,14 @@ struct Attn {
           for (int qg = 0; qg < NQG; ++qg)
             o[qg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qg][hh], o[qg][d], 0, 0, 0);
         }
+      // a 16-row block of ones: every row of its output is the query's sum of P
+      const bf16x8_t ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                             (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int qg = 0; qg < NQG; ++qg)
+          osum[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qg][hh], osum[qg], 0, 0, 0);
     } else {
       // O^T += V^T P^T, four keys per MFMA: key 16 kb + 4 g + i is lane group
       // g's k-index in step (kb, i); one 16-byte read gives dimensions
@@ -394,7 +429,7 @@ struct Attn {
 
   // One window: its tokens are staged (all loads in flight at once), then
   // its chunks stream through the two buffers.
-  __device__ __forceinline__ void run_window(const bool row_ok[NQG]) {
+  __device__ __forceinline__ void run_window() {
     __syncthreads();   // earlier users of sm.idx and of the buffers are done
     if constexpr (!RAW) {
       const int c0 = gs.cnt[0], c01 = gs.cnt[0] + gs.cnt[1];
@@ -426,16 +461,16 @@ struct Attn {
     }
     __syncthreads();
     for (int c = 0; c < nch; c += 2) {   // unrolled by two: the buffer of each step is a constant
-      step<0>(c, nch, row_ok);
-      if (c + 1 < nch) step<1>(c + 1, nch, row_ok);
+      step<0>(c, nch);
+      if (c + 1 < nch) step<1>(c + 1, nch);
     }
   }
 
   // chunk c sits in buffer B; chunk c + 1 is copied into the other buffer meanwhile
   template <int B>
-  __device__ __forceinline__ void step(int c, int nch, const bool row_ok[NQG]) {
+  __device__ __forceinline__ void step(int c, int nch) {
     overlap(c, nch, (const lds_byte*)&sm.k[B][0], (const lds_byte*)&sm.v[B][0], (lds_byte*)&sm.k[1 - B][0],
-            (lds_byte*)&sm.v[1 - B][0], row_ok);
+            (lds_byte*)&sm.v[1 - B][0]);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);   // this thread's copies have landed
     if (c + 1 < nch && kC * (c + 2) > wl) {
       __syncthreads();
@@ -449,24 +484,31 @@ struct Attn {
   // for the copy before the first LDS read of the current buffer.
   __device__ __forceinline__ void overlap(int c, int nch, const lds_byte* __restrict__ kc,
                                           const lds_byte* __restrict__ vc, lds_byte* __restrict__ kn,
-                                          lds_byte* __restrict__ vn, const bool row_ok[NQG]) {
+                                          lds_byte* __restrict__ vn) {
     if (c + 1 < nch) {
       copy(c + 1, kn, vn);
       meta(c + 1, nch, (c + 1) & 1);
     }
-    consume(c & 1, kc, vc, row_ok);
+    consume(c, c & 1, kc, vc);
   }
 
   // The whole stream, in windows of at most kIdxCap staged tokens.
   __device__ __forceinline__ void run_stream(const Gather& gather, const Raw& r, const bool row_ok[NQG]) {
     gs = gather;
     raw = r;
+    bool all = true;
+#pragma unroll
+    for (int qg = 0; qg < NQG; ++qg) {
+      qlim[qg] = row_ok[qg] ? qr[qg] + 1 : INT_MIN;
+      all = all && row_ok[qg];
+    }
+    rows_ok = __ballot(!all) == 0;
     G = gs.cnt[0] + gs.cnt[1] + gs.cnt[2];
     const int L = G + raw.count;
     const int cap = RAW ? L : kIdxCap;
     for (w0 = 0; w0 < L; w0 += cap) {
       wl = min(cap, L - w0);
-      run_window(row_ok);
+      run_window();
     }
   }
 
@@ -474,7 +516,8 @@ struct Attn {
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg) {
       if (!live[qg]) continue;
-      const float inv = l_run[qg] > 0.f ? 1.0f / l_run[qg] : 0.f;
+      const float l = BF16 ? osum[qg][0] : l_run[qg];
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
       const int64_t orow = ((static_cast<int64_t>(b) * a.T + qr[qg]) * a.H + h) * D;
       if constexpr (BF16) {
         // block d, accumulator element i: dimension 16 d + 4 g + i
