@@ -25,14 +25,44 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Pair Gram.  One workgroup (4 waves) computes a 32 x 32 tile of pairs
-// (64 x 64 points) with fp64 MFMA 16x16x4.  Wave (wr, wc) owns the 16 x 16
-// pair block (16 wr.., 16 wc..) and keeps four accumulators per pass:
-// even-even, even-odd, odd-even and odd-odd point products, so the pair
-// combination G = k_ee - k_eo - k_oe + k_oo needs no lane exchange.
-// Pass 0 accumulates <k, k'>, pass 1 <v, v'>.
+// (64 x 64 points); wave (wr, wc) owns the 16 x 16 pair block (16 wr..,
+// 16 wc..).  The products run on the fp64 MFMA 4x4x4 with four blocks: block
+// beta of an instruction multiplies A[m][k] (lane 16 k + 4 beta + m) by
+// B[k][n] (lane 16 k + 4 beta + n) into D[m][n] (lane 16 m + 4 beta + n).
+// A carries the same four row points in every block and B sixteen column
+// points, four per block, so one instruction is a 4 x 16 strip of point
+// products over four features.  A wave keeps 8 row quads (the even and the
+// odd points of its 16 row pairs, four pairs each) against 2 column sets
+// (even and odd points of its 16 column pairs): the four point products of a
+// pair pair land in one lane, and G = k_ee - k_eo - k_oe + k_oo needs no lane
+// exchange.  Pass 0 accumulates <k, k'>, pass 1 <v, v'>.
+//
+// On gfx950 this form of the fp64 MFMA sustains about 1.5x the rate of the
+// 16x16x4 form, and vector instructions issued between fp64 MFMAs delay them,
+// so the inner loop holds nothing but LDS reads and MFMAs: points are widened
+// to fp64 once, when a step of 16 features is staged (loaded into registers
+// one step ahead, then written to LDS, double buffered).  The tile's 64 row
+// points take slots 0..63 and its column points 64..127 (a diagonal tile
+// reads its columns from the row slots); within a set, slot s holds the point
+// of parity (s >> 2) & 1 of pair 4 (s >> 3) + (s & 3), so every row quad is
+// four consecutive slots.  A slot's eight 16-byte pieces (two features each)
+// are stored XOR-swizzled by gswz(slot), which puts the sixteen column points
+// a B read touches into distinct LDS banks.
 // ---------------------------------------------------------------------------
-constexpr int kChunk = 32;             // features staged per step
-constexpr int kPad = kChunk + 1;
+constexpr int kStageF = 16;            // features staged per step
+constexpr int kStage = kStageF * 8;    // bytes of one staged point
+constexpr int kSlots = 128;            // row and column points of a tile
+constexpr int kThrCap = 2048;          // pairs whose b^2 and u a threshold workgroup keeps in LDS
+constexpr int kRing = 4;               // staging register sets
+constexpr int kAhead = 3;              // steps a load is issued ahead of its use
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef double f64x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int gswz(int slot) { return ((slot >> 1) & 1) | ((slot >> 2) & 6); }
+
+// tile point (0..63) held by slot s of a set
+__device__ __forceinline__ int slot_point(int s) { return 8 * (s >> 3) + 2 * (s & 3) + ((s >> 2) & 1); }
 
 // 8 consecutive features of one point, kept raw until they are staged.
 struct Raw8 {
@@ -218,31 +248,130 @@ __device__ void bin_thresholds(const GramLaunch& a, int z, const double* s_b2, c
 // except bins with P dividing 32 (P < 32), which are packed: a unit's bins
 // are consecutive in its point list, so one diagonal tile of 32 pairs covers
 // 32 / P whole bins and only entries of equal bin are kept.  Blocks lying
-// entirely below the diagonal are skipped.
-// The first nthr workgroups form the thresholds, the others the tiles.  With
-// few bins (thr_per_wave == 0) a workgroup takes one bin: all its waves form
-// b^2 and u into LDS, then wave 0 runs the recursion; with many, each wave
-// takes one bin on its own, so the thresholds occupy fewer workgroups.
+// entirely below the diagonal are skipped.  Points beyond the bin (or the
+// unit's last bin) are loaded from a valid point; the entries they touch are
+// never stored.
 template <bool BF16>
-__global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a, int nthr, int thr_per_wave) {
-  __shared__ double rowF[64][kPad];
-  __shared__ double colF[64][kPad];
-  if (static_cast<int>(blockIdx.x) < nthr) {
-    if (thr_per_wave) {
-      const int z = 4 * blockIdx.x + (threadIdx.x >> 6);
-      if (z < a.nbins) bin_thresholds<BF16>(a, z, nullptr, nullptr);
-      return;   // the whole workgroup: no barrier here
-    }
-    const int z = blockIdx.x;
-    if (z >= a.nbins) return;   // the whole workgroup
-    const int P = a.N / 2;      // b^2 and u of up to 64 * kPad pairs each fit the tile buffers
-    double* s_b2 = &rowF[0][0];
-    double* s_u = &colF[0][0];
-    for (int i = threadIdx.x; i < P; i += 256) pair_b2_u<BF16>(a, z, i, s_b2[i], s_u[i]);
-    __syncthreads();
-    if (threadIdx.x < 64) bin_thresholds<BF16>(a, z, s_b2, s_u);
-    return;
+struct GramTile {
+  int lane, wr, wc, nK, nst;
+  bool active, loader;
+  int cbase;                       // first slot of the column set (0 on the diagonal)
+  int wofs;                        // this thread's staging slot and half, as an LDS byte offset base
+  const unsigned char* kp;         // staging: this thread's point row in K and V, plus its half
+  const unsigned char* vp;
+  u32x4_t raw[kRing][2];           // staging registers, a ring over steps: 8 features (bf16: [0] only)
+  double acc[2][2][4][2];          // [pass][row parity][row quad][column parity]
+
+  // Staging role: thread t loads features 8 (t & 1) .. + 7 of step st for the
+  // point of slot t >> 1 (threads of slots >= 64 idle on a diagonal tile).
+  // Loads are issued unconditionally (steps past the end repeat the last one,
+  // idle threads read a valid row) so that no branch hides them from the
+  // wait counting: a write waits for its own step only.
+  template <int R>
+  __device__ __forceinline__ void load(int st) {
+    st = st < nst ? st : nst - 1;
+    const bool vpass = st >= nK;
+    const unsigned char* src = (vpass ? vp : kp) + (vpass ? st - nK : st) * (kStageF * (BF16 ? 2 : 4));
+    raw[R][0] = *reinterpret_cast<const u32x4_t*>(src);
+    if constexpr (!BF16) raw[R][1] = *reinterpret_cast<const u32x4_t*>(src + 16);
   }
+
+  template <int R>
+  __device__ __forceinline__ double feature(int j) const {
+    if constexpr (BF16) {
+      const uint32_t word = raw[R][0][j >> 1];
+      return static_cast<double>(__uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16)));
+    } else {
+      return static_cast<double>(__uint_as_float(raw[R][j >> 2][j & 3]));
+    }
+  }
+
+  // The staged features, widened, into buffer dst: pieces 4 (t & 1) + i of
+  // the slot, two features each.
+  template <int R>
+  __device__ __forceinline__ void write(lds_byte* dst) const {
+    typedef __attribute__((address_space(3))) f64x2_t lds_f64x2;
+    if (!loader) return;
+    const int slot = wofs >> 1, half = wofs & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int piece = (4 * half + i) ^ gswz(slot);
+      *reinterpret_cast<lds_f64x2*>(dst + slot * kStage + 16 * piece) = f64x2_t{feature<R>(2 * i), feature<R>(2 * i + 1)};
+    }
+  }
+
+  // All products of one staged step into acc[PASS]: lane group k reads piece
+  // k + 4 jj of its row quads and column points; element e of those pieces
+  // (feature 8 jj + 2 k + e) is one MFMA k-step.
+  template <int PASS>
+  __device__ __forceinline__ void consume(const lds_byte* cur) {
+    typedef __attribute__((address_space(3))) const f64x2_t lds_f64x2;
+    const int k = lane >> 4;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      f64x2_t ra[2][4], rb[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int slot = 32 * wr + 8 * r + 4 * e + (lane & 3);
+          ra[e][r] = *reinterpret_cast<lds_f64x2*>(cur + slot * kStage + 16 * ((k + 4 * jj) ^ gswz(slot)));
+        }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int slot = cbase + 32 * wc + 8 * ((lane >> 2) & 3) + 4 * c + (lane & 3);
+        rb[c] = *reinterpret_cast<lds_f64x2*>(cur + slot * kStage + 16 * ((k + 4 * jj) ^ gswz(slot)));
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            acc[PASS][e][r][0] = __builtin_amdgcn_mfma_f64_4x4x4f64(ra[e][r][x], rb[0][x], acc[PASS][e][r][0], 0, 0, 0);
+            acc[PASS][e][r][1] = __builtin_amdgcn_mfma_f64_4x4x4f64(ra[e][r][x], rb[1][x], acc[PASS][e][r][1], 0, 0, 0);
+          }
+    }
+  }
+
+  // Step st (st % kRing == R) is in buffer R & 1.  Step st + 1, loaded
+  // kAhead - 1 steps ago, is written to the other buffer, the load of step
+  // st + kAhead issued, then the products of step st taken.
+  template <int PASS, int R>
+  __device__ __forceinline__ void step(int st, lds_byte* smem) {
+    if (st + 1 < nst) write<(R + 1) % kRing>(smem + ((R + 1) & 1) * kSlots * kStage);
+    load<(R + kAhead) % kRing>(st + kAhead);
+    if (active) consume<PASS>(smem + (R & 1) * kSlots * kStage);
+    __syncthreads();
+  }
+
+  template <int PASS>
+  __device__ __forceinline__ void steps(int st, lds_byte* smem) {   // st % kRing == 0
+    step<PASS, 0>(st, smem);
+    step<PASS, 1>(st + 1, smem);
+    step<PASS, 2>(st + 2, smem);
+    step<PASS, 3>(st + 3, smem);
+  }
+};
+
+// e^x in fp64 for the Gram entries: x = (256 n' + j) ln2 / 256 + r with
+// |r| <= ln2 / 512, e^x = 2^n' T[j] (1 + r + r^2/2 + r^3/6 + r^4/24); the
+// truncation is below 4e-17 relative, and T[j] = 2^(j/256) comes from exp_f64.
+__device__ __forceinline__ double exp_tab(double x, const double* T) {
+  double n = __builtin_rint(x * 369.3299304675746);    // 256 / ln 2
+  n = fmax(fmin(n, 540000.0), -540000.0);
+  double r = fma(-n, 0x1.62e42fefa39efp-9, x);
+  r = fma(-n, 0x1.abc9e3b39803fp-64, r);
+  double p = fma(r, 0.041666666666666664, 0.16666666666666666);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const int ni = static_cast<int>(n);
+  return __builtin_amdgcn_ldexp(T[ni & 255] * p, ni >> 8);
+}
+
+template <bool BF16>
+__device__ void gram_tile(const GramLaunch& a, int nthr, lds_byte* smem, double* T) {
   const int P = a.N / 2;
   const bool packed = P < 32 && (32 % P) == 0;   // whole bins per tile
   const int bid = static_cast<int>(xcd_remap(blockIdx.x - nthr, gridDim.x - nthr));
@@ -266,98 +395,74 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a, int nthr, 
   }
   const int b = unit / a.src.H_kv;
   const int h = unit % a.src.H_kv;
+  const bool diag = tr == tc;          // rows and columns are the same points
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int wr = w >> 1, wc = w & 1;
+  GramTile<BF16> t;
+  t.lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  t.wr = w >> 1;
+  t.wc = w & 1;
+  t.cbase = diag ? 0 : 64;
+  t.nK = a.src.E / kStageF;
+  t.nst = t.nK + a.src.D / kStageF;
 
-  // loader role: point lp of the row / column sets, features lf .. lf+7
-  const int lp = tid >> 2;
-  const int lf = (tid & 3) * 8;
   const int64_t ubase = static_cast<int64_t>(unit) * a.idx_unit_stride;
-  auto token = [&](int q) -> int {   // q-th point of the tile's range; -1 if none
+  auto token = [&](int q) -> int {   // q-th point of the tile's range; the range's first if none
     if (packed) {
       const int bin = q / a.N;
-      if (bin >= a.bins_per_unit) return -1;
-      return a.idx[ubase + static_cast<int64_t>(bin) * a.idx_stride + q % a.N];
+      const bool in = bin < a.bins_per_unit;
+      return a.idx[ubase + static_cast<int64_t>(in ? bin : 0) * a.idx_stride + (in ? q % a.N : 0)];
     }
-    if (q >= a.N) return -1;
-    return a.idx[ubase + static_cast<int64_t>(z % a.bins_per_unit) * a.idx_stride + q];
+    return a.idx[ubase + static_cast<int64_t>(z % a.bins_per_unit) * a.idx_stride + (q < a.N ? q : 0)];
   };
-  const bool diag = tr == tc;          // rows and columns are the same points
-  const int rtok = token(64 * tr + lp);
-  const int ctok = diag ? rtok : token(64 * tc + lp);
-  const bool rvalid = rtok >= 0;
-  const bool cvalid = ctok >= 0;
-  const int64_t rrow = rvalid ? (static_cast<int64_t>(b) * a.src.S + rtok) * a.src.H_kv + h : 0;
-  const int64_t crow = cvalid ? (static_cast<int64_t>(b) * a.src.S + ctok) * a.src.H_kv + h : 0;
-  double (*colS)[kPad] = diag ? rowF : colF;
+  {
+    const int slot = threadIdx.x >> 1, half = threadIdx.x & 1;
+    t.wofs = threadIdx.x;
+    t.loader = slot < (diag ? 64 : 128);
+    const int tp = slot_point(slot & 63);
+    const int tok = t.loader ? token((slot < 64 ? 64 * tr : 64 * tc) + tp) : 0;
+    const int elt = BF16 ? 2 : 4;
+    const int64_t row = (static_cast<int64_t>(b) * a.src.S + tok) * a.src.H_kv + h;
+    t.kp = static_cast<const unsigned char*>(a.src.k) + (row * a.src.E + 8 * half) * elt;
+    t.vp = static_cast<const unsigned char*>(a.src.v) + (row * a.src.D + 8 * half) * elt;
+  }
 
   // does this wave's 16 x 16 pair block hold anything the walk reads?
-  const int r0 = 32 * tr + 16 * wr;    // first pair row of the block
-  const int c0 = 32 * tc + 16 * wc;    // first pair column
-  bool active = c0 + 15 >= r0;          // not entirely below the diagonal
-  if (packed && active && wr != wc) active = (r0 % P) != 0;   // a bin straddles the two halves
+  const int r0 = 32 * tr + 16 * t.wr;    // first pair row of the block
+  const int c0 = 32 * tc + 16 * t.wc;    // first pair column
+  bool active = c0 + 15 >= r0;            // not entirely below the diagonal
+  if (packed && active && t.wr != t.wc) active = (r0 % P) != 0;   // a bin straddles the two halves
   if (!packed && (r0 >= P || c0 >= P)) active = false;
-
-  f64x4_t acc[2][4];
+  t.active = active;
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[p][q] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t.acc[p][e][r][0] = t.acc[p][e][r][1] = 0.0;
 
-  const int pr = 16 * wr + (lane & 15);   // pair row inside the tile
-  const int pc = 16 * wc + (lane & 15);   // pair column inside the tile
-  const int kq = lane >> 4;
-
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int F = pass ? a.src.D : a.src.E;
-    const void* base = pass ? a.src.v : a.src.k;
-    Raw8 nr{}, nc{};
-    if (rvalid) load8<BF16>(base, rrow * F + lf, nr);
-    if (cvalid && !diag) load8<BF16>(base, crow * F + lf, nc);
-    for (int f0 = 0; f0 < F; f0 += kChunk) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        rowF[lp][lf + j] = rvalid ? raw8_at<BF16>(nr, j) : 0.0;
-        if (!diag) colF[lp][lf + j] = cvalid ? raw8_at<BF16>(nc, j) : 0.0;
-      }
-      __syncthreads();
-      if (f0 + kChunk < F) {     // prefetch the next stage while this one is used
-        if (rvalid) load8<BF16>(base, rrow * F + f0 + kChunk + lf, nr);
-        if (cvalid && !diag) load8<BF16>(base, crow * F + f0 + kChunk + lf, nc);
-      }
-      if (active) {
-#pragma unroll
-        for (int kk = 0; kk < kChunk / 4; ++kk) {
-          const int kf = kk * 4 + kq;
-          const double Ae = rowF[2 * pr][kf];
-          const double Ao = rowF[2 * pr + 1][kf];
-          const double Be = colS[2 * pc][kf];
-          const double Bo = colS[2 * pc + 1][kf];
-          acc[pass][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ae, Be, acc[pass][0], 0, 0, 0);
-          acc[pass][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ae, Bo, acc[pass][1], 0, 0, 0);
-          acc[pass][2] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ao, Be, acc[pass][2], 0, 0, 0);
-          acc[pass][3] = __builtin_amdgcn_mfma_f64_16x16x4f64(Ao, Bo, acc[pass][3], 0, 0, 0);
-        }
-      }
-      __syncthreads();
-    }
-  }
+  // 2^(j/256), j = 0..255, for exp_tab (published by the barrier below)
+  T[threadIdx.x] = exp_f64(threadIdx.x * 0.0027076061740622863);   // ln 2 / 256
+  t.template load<0>(0);
+  t.template load<1>(1);
+  t.template load<2>(2);
+  t.template write<0>(smem);
+  __syncthreads();
+  for (int st = 0; st < t.nK; st += kRing) t.template steps<0>(st, smem);   // E and D are multiples of kRing steps
+  for (int st = t.nK; st < t.nst; st += kRing) t.template steps<1>(st, smem);
   if (!active) return;
 
-  // fp64 16x16x4 accumulator element i of lane l is (row l / 16 + 4 i, column l % 16)
-  const int col = c0 + (lane & 15);
+  // accumulator of lane l: row point (l >> 4) of its quad, column (l & 15) of its set
+  const int col = c0 + (t.lane & 15);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = r0 + kq + 4 * i;
-    const double kee = exp_f64(a.scale * acc[0][0][i]) * (acc[1][0][i] + 1.0);
-    const double keo = exp_f64(a.scale * acc[0][1][i]) * (acc[1][1][i] + 1.0);
-    const double koe = exp_f64(a.scale * acc[0][2][i]) * (acc[1][2][i] + 1.0);
-    const double koo = exp_f64(a.scale * acc[0][3][i]) * (acc[1][3][i] + 1.0);
-    const double gv = (kee - keo) - (koe - koo);
+  for (int r = 0; r < 4; ++r) {
+    const int row = r0 + 4 * r + (t.lane >> 4);
+    double kx[2][2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) kx[e][c] = exp_tab(a.scale * t.acc[0][e][r][c], T) * (t.acc[1][e][r][c] + 1.0);
+    const double gv = (kx[0][0] - kx[0][1]) - (kx[1][0] - kx[1][1]);
     if (packed) {
       const int bin = row / P;
       if (bin == col / P && bin < a.bins_per_unit && col >= row)
@@ -366,6 +471,32 @@ __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a, int nthr, 
       a.G[static_cast<int64_t>(z) * P * P + static_cast<int64_t>(row) * P + col] = gv;
     }
   }
+}
+
+// The first nthr workgroups form the thresholds, the others the tiles.  With
+// few bins (thr_per_wave == 0) a workgroup takes one bin: all its waves form
+// b^2 and u into LDS, then wave 0 runs the recursion; with many, each wave
+// takes one bin on its own, so the thresholds occupy fewer workgroups.
+template <bool BF16>
+__global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a, int nthr, int thr_per_wave) {
+  __shared__ __attribute__((aligned(16))) double smem[2 * kSlots * kStage / sizeof(double) + 256];
+  if (static_cast<int>(blockIdx.x) < nthr) {
+    if (thr_per_wave) {
+      const int z = 4 * blockIdx.x + (threadIdx.x >> 6);
+      if (z < a.nbins) bin_thresholds<BF16>(a, z, nullptr, nullptr);
+      return;   // the whole workgroup: no barrier here
+    }
+    const int z = blockIdx.x;
+    if (z >= a.nbins) return;   // the whole workgroup
+    const int P = a.N / 2;      // b^2 and u of up to kThrCap pairs each fit the tile buffers
+    double* s_b2 = smem;
+    double* s_u = smem + kThrCap;
+    for (int i = threadIdx.x; i < P; i += 256) pair_b2_u<BF16>(a, z, i, s_b2[i], s_u[i]);
+    __syncthreads();
+    if (threadIdx.x < 64) bin_thresholds<BF16>(a, z, s_b2, s_u);
+    return;
+  }
+  gram_tile<BF16>(a, nthr, (lds_byte*)smem, smem + 2 * kSlots * kStage / sizeof(double));
 }
 
 // ---------------------------------------------------------------------------
@@ -689,7 +820,7 @@ hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s) {
   // threshold workgroups for bins of P > 64 pairs (the walks of the large sweep
   // kernel): one per bin while there are at most 64 bins, else four bins each;
   // a multiple of 8 so that the tiles keep their XCD mapping
-  const int per_wave = (a.nbins > 64 || P > 64 * kPad) ? 1 : 0;
+  const int per_wave = (a.nbins > 64 || P > kThrCap) ? 1 : 0;
   const int nthr = P > 64 ? (per_wave ? (a.nbins + 31) / 32 * 8 : (a.nbins + 7) / 8 * 8) : 0;
   dim3 grid(static_cast<unsigned>(blocks + nthr));
   if (a.src.bf16)
