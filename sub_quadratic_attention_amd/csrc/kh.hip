@@ -16,6 +16,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -476,15 +478,16 @@ __device__ void gram_tile(const GramLaunch& a, int nthr, lds_byte* smem, double*
 // The first nthr workgroups form the thresholds, the others the tiles.  With
 // few bins (thr_per_wave == 0) a workgroup takes one bin: all its waves form
 // b^2 and u into LDS, then wave 0 runs the recursion; with many, each wave
-// takes one bin on its own, so the thresholds occupy fewer workgroups.
+// takes bins on its own, 4 nthr apart, so the thresholds hold few workgroup
+// slots while the tiles run.
 template <bool BF16>
 __global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a, int nthr, int thr_per_wave) {
   __shared__ __attribute__((aligned(16))) double smem[2 * kSlots * kStage / sizeof(double) + 256];
   if (static_cast<int>(blockIdx.x) < nthr) {
     if (thr_per_wave) {
-      const int z = 4 * blockIdx.x + (threadIdx.x >> 6);
-      if (z < a.nbins) bin_thresholds<BF16>(a, z, nullptr, nullptr);
-      return;   // the whole workgroup: no barrier here
+      for (int z = 4 * blockIdx.x + (threadIdx.x >> 6); z < a.nbins; z += 4 * nthr)
+        bin_thresholds<BF16>(a, z, nullptr, nullptr);
+      return;   // the whole workgroup: no barrier in this mode
     }
     const int z = blockIdx.x;
     if (z >= a.nbins) return;   // the whole workgroup
@@ -818,10 +821,12 @@ hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s) {
   }
   if (blocks == 0) return hipSuccess;
   // threshold workgroups for bins of P > 64 pairs (the walks of the large sweep
-  // kernel): one per bin while there are at most 64 bins, else four bins each;
-  // a multiple of 8 so that the tiles keep their XCD mapping
+  // kernel): one per bin while there are at most 64 bins, else at most 64 with
+  // a bin per wave at a time; a multiple of 8 so that the tiles keep their XCD
+  // mapping
   const int per_wave = (a.nbins > 64 || P > kThrCap) ? 1 : 0;
-  const int nthr = P > 64 ? (per_wave ? (a.nbins + 31) / 32 * 8 : (a.nbins + 7) / 8 * 8) : 0;
+  int nthr = 0;
+  if (P > 64) nthr = per_wave ? std::min((a.nbins + 31) / 32 * 8, 64) : (a.nbins + 7) / 8 * 8;
   dim3 grid(static_cast<unsigned>(blocks + nthr));
   if (a.src.bf16)
     hipLaunchKernelGGL(pair_gram_kernel<true>, grid, dim3(256), 0, s, a, nthr, per_wave);

@@ -119,87 +119,109 @@ __global__ void kv_summary_kernel(const int32_t* tok, int slots, int n, int nC, 
 // Visible keys = cache slots [0, nC) (log2 weight lw_c), buffer slots
 // [4n, 4n + nBf) (lw_b), raw slots [6n, 6n + nRaw) (weight 1) and the new
 // token itself (read from the caller's k1 / v1).  The key range is split
-// across workgroups; each writes a partial (max, sum, unnormalised output)
-// per query head, merged by kv_combine_kernel.
+// across workgroups of kSplitKeys keys; each writes a partial (max, sum,
+// unnormalised output) per query head, merged by kv_combine_kernel.
+//
+// Every memory read of a workgroup is issued up front: the queries, one key
+// row per thread (threads < kSplitKeys) and the split's value rows, 16 bytes
+// per load, coalesced, into LDS.  The logits are one key per thread for all
+// G heads; P V then runs from LDS with one thread per (head, pair of
+// dimensions).
 // ---------------------------------------------------------------------------
-constexpr int kSplitKeys = 128;   // keys per workgroup (2 per lane... 32 per wave)
+constexpr int kSplitKeys = 128;   // keys per workgroup
+
+// Row of visible key kk: its state row u * slots + slot, or -1 for the new token (kk = total - 1).
+__device__ __forceinline__ int64_t key_state_row(const KvDecodeLaunch& a, int u, int kk, int total) {
+  const int slot = kk < a.nC ? kk : (kk < a.nC + a.nBf ? 4 * a.n + kk - a.nC : 6 * a.n + kk - a.nC - a.nBf);
+  return kk < total - 1 ? static_cast<int64_t>(u) * a.slots + slot : -1;
+}
 
 template <bool BF16, int E, int D, int G>
 __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
+  constexpr int ELT = BF16 ? 2 : 4;
+  constexpr int VP = D * ELT / 16;                      // 16-byte pieces per value row
+  constexpr int VLOADS = kSplitKeys * VP / 256;         // value pieces per thread
+  constexpr int KP = E * ELT / 16;                      // 16-byte pieces per key row
   const int u = blockIdx.y;
   const int split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = u / a.H_kv, hk = u % a.H_kv;
   const int total = a.nC + a.nBf + a.nRaw + 1;
   const int k0 = split * kSplitKeys;
-  const int k1 = min(total, k0 + kSplitKeys);
-  constexpr int ELT = BF16 ? 2 : 4;
+  const int nk = min(total, k0 + kSplitKeys) - k0;
 
+  __shared__ __attribute__((aligned(16))) unsigned char sv[kSplitKeys * D * ELT];
   __shared__ float sq[G][E];
   __shared__ float sp[G][kSplitKeys];
   __shared__ float red[4][G];
-  __shared__ float smax[G];
+  __shared__ float smax[G], ssum[G];
 
+  // value rows of the split (rows past the range are not read)
+  uint4 vr[VLOADS];
+#pragma unroll
+  for (int i = 0; i < VLOADS; ++i) {
+    const int piece = tid + 256 * i, j = piece / VP;
+    const int64_t r = key_state_row(a, u, k0 + j, total);
+    const uint4* src = r >= 0 ? reinterpret_cast<const uint4*>(static_cast<const char*>(a.state_v) + r * (D * ELT))
+                              : reinterpret_cast<const uint4*>(static_cast<const char*>(a.v1) +
+                                                               (static_cast<int64_t>(b) * a.H_kv + hk) * (D * ELT));
+    vr[i] = j < nk ? src[piece % VP] : uint4{0u, 0u, 0u, 0u};
+  }
+  // this thread's key row
+  const int kk = k0 + tid;
+  const bool live = tid < kSplitKeys && tid < nk;
+  uint4 kr[KP];
+  if (live) {
+    const int64_t r = key_state_row(a, u, kk, total);
+    const uint4* krow = r >= 0 ? reinterpret_cast<const uint4*>(static_cast<const char*>(a.state_k) + r * (E * ELT))
+                               : reinterpret_cast<const uint4*>(static_cast<const char*>(a.k1) +
+                                                                (static_cast<int64_t>(b) * a.H_kv + hk) * (E * ELT));
+#pragma unroll
+    for (int i = 0; i < KP; ++i) kr[i] = krow[i];
+  }
   // queries of the group
   for (int x = tid; x < G * E; x += 256) {
     const int gh = x / E, e = x % E;
     const int64_t off = (static_cast<int64_t>(b) * a.H + hk * G + gh) * E + e;
     sq[gh][e] = BF16 ? bf16_bits_to_float(static_cast<const uint16_t*>(a.q)[off]) : static_cast<const float*>(a.q)[off];
   }
+#pragma unroll
+  for (int i = 0; i < VLOADS; ++i) reinterpret_cast<uint4*>(sv)[tid + 256 * i] = vr[i];
   __syncthreads();
 
-  // logits: one key per thread (threads beyond the range idle)
-  const int kk = k0 + tid;
+  // logits: one key per thread
   float logit[G];
-  const bool live = tid < kSplitKeys && kk < k1;
   if (live) {
-    const char* krow;
-    float lw;
-    if (kk < a.nC) {
-      krow = static_cast<const char*>(a.state_k) + (static_cast<int64_t>(u) * a.slots + kk) * E * ELT;
-      lw = a.lw_c;
-    } else if (kk < a.nC + a.nBf) {
-      krow = static_cast<const char*>(a.state_k) + (static_cast<int64_t>(u) * a.slots + 4 * a.n + kk - a.nC) * E * ELT;
-      lw = a.lw_b;
-    } else if (kk < total - 1) {
-      krow = static_cast<const char*>(a.state_k) +
-             (static_cast<int64_t>(u) * a.slots + 6 * a.n + kk - a.nC - a.nBf) * E * ELT;
-      lw = 0.f;
-    } else {
-      krow = static_cast<const char*>(a.k1) + (static_cast<int64_t>(b) * a.H_kv + hk) * E * ELT;
-      lw = 0.f;
-    }
+    const float lw = kk < a.nC ? a.lw_c : (kk < a.nC + a.nBf ? a.lw_b : 0.f);
     float acc[G];
 #pragma unroll
     for (int gh = 0; gh < G; ++gh) acc[gh] = 0.f;
-    for (int e0 = 0; e0 < E; e0 += 16 / ELT) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(krow + e0 * ELT);
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const uint32_t wv[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
       float kv[16 / ELT];
       if constexpr (BF16) {
-        const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          kv[2 * j] = bf16_bits_to_float(static_cast<uint16_t>(wv[j] & 0xffffu));
-          kv[2 * j + 1] = bf16_bits_to_float(static_cast<uint16_t>(wv[j] >> 16));
+          kv[2 * j] = __uint_as_float(wv[j] << 16);
+          kv[2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
         }
       } else {
-        kv[0] = __uint_as_float(raw.x);
-        kv[1] = __uint_as_float(raw.y);
-        kv[2] = __uint_as_float(raw.z);
-        kv[3] = __uint_as_float(raw.w);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kv[j] = __uint_as_float(wv[j]);
       }
 #pragma unroll
       for (int gh = 0; gh < G; ++gh)
 #pragma unroll
-        for (int j = 0; j < 16 / ELT; ++j) acc[gh] += sq[gh][e0 + j] * kv[j];
+        for (int j = 0; j < 16 / ELT; ++j) acc[gh] = fmaf(sq[gh][i * (16 / ELT) + j], kv[j], acc[gh]);
     }
 #pragma unroll
-    for (int gh = 0; gh < G; ++gh) logit[gh] = acc[gh] * a.scale_log2 + lw;
+    for (int gh = 0; gh < G; ++gh) logit[gh] = fmaf(acc[gh], a.scale_log2, lw);
   } else {
 #pragma unroll
     for (int gh = 0; gh < G; ++gh) logit[gh] = -INFINITY;
   }
-  // max over the split
+  // max and sum over the split
 #pragma unroll
   for (int gh = 0; gh < G; ++gh) {
     float m = logit[gh];
@@ -218,32 +240,34 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
     if (lane == 0) red[w][gh] = s;
   }
   __syncthreads();
-  // P V: thread = (head, dim); rows read coalesced
+  if (tid < G) ssum[tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+  // P V from LDS: thread = (head, two dimensions)
   float* part = a.partial + ((static_cast<int64_t>(u) * gridDim.x + split) * G) * (D + 2);
-  for (int x = tid; x < G * D; x += 256) {
-    const int gh = x / D, d = x % D;
-    float acc = 0.f;
-    for (int j = 0; j < k1 - k0; ++j) {
-      const int key = k0 + j;
-      const char* vrow;
-      if (key < a.nC)
-        vrow = static_cast<const char*>(a.state_v) + (static_cast<int64_t>(u) * a.slots + key) * D * ELT;
-      else if (key < a.nC + a.nBf)
-        vrow = static_cast<const char*>(a.state_v) + (static_cast<int64_t>(u) * a.slots + 4 * a.n + key - a.nC) * D * ELT;
-      else if (key < total - 1)
-        vrow = static_cast<const char*>(a.state_v) +
-               (static_cast<int64_t>(u) * a.slots + 6 * a.n + key - a.nC - a.nBf) * D * ELT;
-      else
-        vrow = static_cast<const char*>(a.v1) + (static_cast<int64_t>(b) * a.H_kv + hk) * D * ELT;
-      const float vv = BF16 ? bf16_bits_to_float(reinterpret_cast<const uint16_t*>(vrow)[d])
-                            : reinterpret_cast<const float*>(vrow)[d];
-      acc += sp[gh][j] * vv;
+  for (int x = tid; x < G * D / 2; x += 256) {
+    const int gh = x / (D / 2), d2 = x % (D / 2);
+    float o0 = 0.f, o1 = 0.f;
+    for (int j = 0; j < nk; ++j) {
+      const float p = sp[gh][j];
+      float v0, v1;
+      if constexpr (BF16) {
+        const uint32_t vv = reinterpret_cast<const uint32_t*>(sv + j * D * ELT)[d2];
+        v0 = __uint_as_float(vv << 16);
+        v1 = __uint_as_float(vv & 0xffff0000u);
+      } else {
+        const float2 vv = reinterpret_cast<const float2*>(sv + j * D * ELT)[d2];
+        v0 = vv.x;
+        v1 = vv.y;
+      }
+      o0 = fmaf(p, v0, o0);
+      o1 = fmaf(p, v1, o1);
     }
-    part[gh * (D + 2) + d] = acc;
+    part[gh * (D + 2) + 2 * d2] = o0;
+    part[gh * (D + 2) + 2 * d2 + 1] = o1;
   }
+  __syncthreads();
   if (tid < G) {
     part[tid * (D + 2) + D] = smax[tid];
-    part[tid * (D + 2) + D + 1] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    part[tid * (D + 2) + D + 1] = ssum[tid];
   }
 }
 
