@@ -131,8 +131,12 @@ struct KvDecodeLaunch {
   int nC, nBf, nRaw;    // visible cache, buffer and raw rows (before the new token)
   float lw_c, lw_b;     // log2 weights of cache and buffer rows
   float scale_log2;     // softmax scale * log2(e)
-  float* partial;       // [units][splits][G][D + 2]
+  float* partial;       // [units][splits][G][D + 4] (rows padded to 16 bytes)
   int splits;
+  int32_t* state_tok;   // token index of every state slot
+  int new_slot;         // raw-block slot the new token takes
+  int32_t new_tok;      // its stream position
+  int32_t* cnt;         // [units] splits done (zero before and after each launch)
 };
 
 // Launchers (return hipError_t of the launch).
@@ -157,6 +161,7 @@ ExpressSchedule express_schedule(int64_t S, int n);
 hipError_t launch_kv_rows(const KvRowsLaunch& a, hipStream_t s);
 hipError_t launch_kv_block_reps(int units, int n, int64_t t0, int log2r, uint64_t seed, int32_t* list, hipStream_t s);
 hipError_t launch_kv_iota(int32_t* out, int units, int cnt, int first, hipStream_t s);
+hipError_t launch_kv_fill(int32_t* out, int64_t n, int32_t value, hipStream_t s);
 hipError_t launch_kv_decode(const KvDecodeLaunch& a, int bf16, int E, int D, int G, hipStream_t s);
 bool kv_decode_supported(int bf16, int E, int D, int G);
 hipError_t launch_kv_summary(const int32_t* tok, int units, int slots, int n, int nC, int nBf, int nRaw, float wc,

@@ -83,6 +83,11 @@ __global__ void kv_block_reps_kernel(int units, int n, int64_t t0, int log2r, ui
   list[i] = static_cast<int32_t>(6 * n + ((g << log2r) + off - t0));
 }
 
+__global__ void kv_fill_kernel(int32_t* out, int64_t n, int32_t value) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = value;
+}
+
 __global__ void kv_iota_kernel(int32_t* out, int units, int cnt, int first) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= static_cast<int64_t>(units) * cnt) return;
@@ -120,7 +125,9 @@ __global__ void kv_summary_kernel(const int32_t* tok, int slots, int n, int nC, 
 // [4n, 4n + nBf) (lw_b), raw slots [6n, 6n + nRaw) (weight 1) and the new
 // token itself (read from the caller's k1 / v1).  The key range is split
 // across workgroups of kSplitKeys keys; each writes a partial (max, sum,
-// unnormalised output) per query head, merged by kv_combine_kernel.
+// unnormalised output) per query head, and the last workgroup of a unit to
+// finish (a per-unit counter, zero before and after the launch) merges them.
+// Workgroup 0 of a unit also appends the new token to the raw block.
 //
 // Every memory read of a workgroup is issued up front: the queries, one key
 // row per thread (threads < kSplitKeys) and the split's value rows, 16 bytes
@@ -134,6 +141,93 @@ constexpr int kSplitKeys = 128;   // keys per workgroup
 __device__ __forceinline__ int64_t key_state_row(const KvDecodeLaunch& a, int u, int kk, int total) {
   const int slot = kk < a.nC ? kk : (kk < a.nC + a.nBf ? 4 * a.n + kk - a.nC : 6 * a.n + kk - a.nC - a.nBf);
   return kk < total - 1 ? static_cast<int64_t>(u) * a.slots + slot : -1;
+}
+
+// Partials cross workgroups (and XCDs, whose L2s are not coherent with each
+// other) through device-scope atomic stores and loads, which go to the
+// coherence point, so no cache-wide fence is needed.
+__device__ __forceinline__ void put_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_partial(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the partials of unit u (run by its last workgroup): out = sum_s
+// 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s.  When the unit's partials fit
+// kMergeBytes, they are copied into LDS in one round (LDS-DMA loads with the
+// device-coherent cache policy, 16 bytes a lane, all in flight at once); the
+// per-split weights are then formed by one thread per head and every output
+// sums its splits from LDS.  Otherwise each output reads its splits itself.
+constexpr int kMergeBytes = 64 * 1024;
+constexpr int kMergeSplits = 64;
+constexpr int kDmaSc1 = 16;   // cache policy of a device-scope coherent load (sc1)
+
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void combine_unit(const float* partial, int u, int splits, int H, int H_kv, void* out,
+                                             unsigned char* lds) {
+  constexpr int PS = D + 4;   // floats per partial row
+  __shared__ float s_w[kMergeSplits][G];
+  const int b = u / H_kv, hk = u % H_kv;
+  const float* unit_p = partial + static_cast<int64_t>(u) * splits * G * PS;
+  const int pieces = splits * G * PS / 4;
+  const bool fast = splits <= kMergeSplits && (pieces + 63) / 64 * 1024 <= kMergeBytes;
+  const float* sp = reinterpret_cast<const float*>(lds);
+  if (fast) {
+    typedef __attribute__((address_space(1))) const void* gptr;
+    typedef __attribute__((address_space(3))) void* lptr;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int i = w; i < (pieces + 63) / 64; i += 4) {
+      const int piece = min(64 * i + lane, pieces - 1);   // lanes past the end reload the last piece into padding
+      __builtin_amdgcn_global_load_lds((gptr)(unit_p + 4 * piece), (lptr)(lds + 1024 * i), 16, 0, kDmaSc1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x < G) {
+      const int gh = threadIdx.x;
+      float m = -INFINITY;
+      for (int s = 0; s < splits; ++s) m = fmaxf(m, sp[(s * G + gh) * PS + D]);
+      float den = 0.f;
+      for (int s = 0; s < splits; ++s) {
+        const float ms = sp[(s * G + gh) * PS + D];
+        const float e = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - m);
+        s_w[s][gh] = e;
+        den = fmaf(e, sp[(s * G + gh) * PS + D + 1], den);
+      }
+      const float inv = 1.0f / den;
+      for (int s = 0; s < splits; ++s) s_w[s][gh] *= inv;
+    }
+    __syncthreads();
+  }
+  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
+    const int gh = x / D, d = x % D;
+    float o;
+    if (fast) {
+      o = 0.f;
+      for (int s = 0; s < splits; ++s) o = fmaf(s_w[s][gh], sp[(s * G + gh) * PS + d], o);
+    } else {
+      const float* base = unit_p + static_cast<int64_t>(gh) * PS;
+      float m = -INFINITY;
+#pragma unroll 8
+      for (int s = 0; s < splits; ++s) m = fmaxf(m, get_partial(base + static_cast<int64_t>(s) * G * PS + D));
+      float num = 0.f, den = 0.f;
+#pragma unroll 8
+      for (int s = 0; s < splits; ++s) {
+        const float* p = base + static_cast<int64_t>(s) * G * PS;
+        const float ms = get_partial(p + D);
+        const float sc = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - m);
+        num = fmaf(sc, get_partial(p + d), num);
+        den = fmaf(sc, get_partial(p + D + 1), den);
+      }
+      o = num / den;
+    }
+    const int64_t off = (static_cast<int64_t>(b) * H + hk * G + gh) * D + d;
+    if constexpr (BF16)
+      static_cast<uint16_t*>(out)[off] = float_to_bf16_bits(o);
+    else
+      static_cast<float*>(out)[off] = o;
+  }
 }
 
 template <bool BF16, int E, int D, int G>
@@ -150,8 +244,11 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
   const int k0 = split * kSplitKeys;
   const int nk = min(total, k0 + kSplitKeys) - k0;
 
-  __shared__ __attribute__((aligned(16))) unsigned char sv[kSplitKeys * D * ELT];
-  __shared__ float sq[G][E];
+  constexpr int PS = D + 4;                              // floats per partial row (16-byte multiple)
+  // value rows of the split; later the unit's partials when this workgroup merges
+  constexpr int kBuf = kSplitKeys * D * ELT > kMergeBytes ? kSplitKeys * D * ELT : kMergeBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char sv[kBuf];
+  __shared__ __attribute__((aligned(16))) float sq[G][E];
   __shared__ float sp[G][kSplitKeys];
   __shared__ float red[4][G];
   __shared__ float smax[G], ssum[G];
@@ -213,7 +310,13 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
 #pragma unroll
       for (int gh = 0; gh < G; ++gh)
 #pragma unroll
-        for (int j = 0; j < 16 / ELT; ++j) acc[gh] = fmaf(sq[gh][i * (16 / ELT) + j], kv[j], acc[gh]);
+        for (int j4 = 0; j4 < 16 / ELT; j4 += 4) {   // the group's queries, 16 bytes per LDS read (same for all lanes)
+          const float4 qv = *reinterpret_cast<const float4*>(&sq[gh][i * (16 / ELT) + j4]);
+          acc[gh] = fmaf(qv.x, kv[j4], acc[gh]);
+          acc[gh] = fmaf(qv.y, kv[j4 + 1], acc[gh]);
+          acc[gh] = fmaf(qv.z, kv[j4 + 2], acc[gh]);
+          acc[gh] = fmaf(qv.w, kv[j4 + 3], acc[gh]);
+        }
     }
 #pragma unroll
     for (int gh = 0; gh < G; ++gh) logit[gh] = fmaf(acc[gh], a.scale_log2, lw);
@@ -242,7 +345,7 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
   __syncthreads();
   if (tid < G) ssum[tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
   // P V from LDS: thread = (head, two dimensions)
-  float* part = a.partial + ((static_cast<int64_t>(u) * gridDim.x + split) * G) * (D + 2);
+  float* part = a.partial + ((static_cast<int64_t>(u) * gridDim.x + split) * G) * PS;
   for (int x = tid; x < G * D / 2; x += 256) {
     const int gh = x / (D / 2), d2 = x % (D / 2);
     float o0 = 0.f, o1 = 0.f;
@@ -261,47 +364,45 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
       o0 = fmaf(p, v0, o0);
       o1 = fmaf(p, v1, o1);
     }
-    part[gh * (D + 2) + 2 * d2] = o0;
-    part[gh * (D + 2) + 2 * d2 + 1] = o1;
+    put_partial(part + gh * PS + 2 * d2, o0);
+    put_partial(part + gh * PS + 2 * d2 + 1, o1);
   }
-  __syncthreads();
   if (tid < G) {
-    part[tid * (D + 2) + D] = smax[tid];
-    part[tid * (D + 2) + D + 1] = ssum[tid];
+    put_partial(part + tid * PS + D, smax[tid]);
+    put_partial(part + tid * PS + D + 1, ssum[tid]);
   }
-}
-
-template <bool BF16, int D, int G>
-__global__ void kv_combine_kernel(const float* partial, int splits, int H, int H_kv, void* out) {
-  const int u = blockIdx.x;
-  const int b = u / H_kv, hk = u % H_kv;
-  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
-    const int gh = x / D, d = x % D;
-    float m = -INFINITY;
-    for (int s = 0; s < splits; ++s) m = fmaxf(m, partial[((static_cast<int64_t>(u) * splits + s) * G + gh) * (D + 2) + D]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float* p = partial + ((static_cast<int64_t>(u) * splits + s) * G + gh) * (D + 2);
-      const float sc = p[D] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(p[D] - m);
-      num += sc * p[d];
-      den += sc * p[D + 1];
-    }
-    const float o = num / den;
-    const int64_t off = (static_cast<int64_t>(b) * H + hk * G + gh) * D + d;
-    if constexpr (BF16)
-      static_cast<uint16_t*>(out)[off] = float_to_bf16_bits(o);
-    else
-      static_cast<float*>(out)[off] = o;
+  // workgroup 0: the new token joins the raw block (slot new_slot, which no
+  // workgroup of this launch reads)
+  if (split == 0) {
+    const int64_t dst = static_cast<int64_t>(u) * a.slots + a.new_slot;
+    const int64_t src = static_cast<int64_t>(b) * a.H_kv + hk;
+    if (tid < KP)
+      reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.state_k)) + dst * (E * ELT))[tid] =
+          reinterpret_cast<const uint4*>(static_cast<const char*>(a.k1) + src * (E * ELT))[tid];
+    else if (tid < KP + VP)
+      reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.state_v)) + dst * (D * ELT))[tid - KP] =
+          reinterpret_cast<const uint4*>(static_cast<const char*>(a.v1) + src * (D * ELT))[tid - KP];
+    else if (tid == KP + VP)
+      a.state_tok[dst] = a.new_tok;
   }
+  // the last workgroup of the unit merges the partials: every thread's
+  // partial stores have completed (reached the coherence point) before the
+  // workgroup's count is taken, and the merge reads them from there
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&a.cnt[u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             static_cast<int>(gridDim.x) - 1;
+  __syncthreads();
+  if (!s_last) return;   // the whole workgroup
+  combine_unit<BF16, D, G>(a.partial, u, gridDim.x, a.H, a.H_kv, a.out, sv);
+  if (tid == 0) __hip_atomic_store(&a.cnt[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool BF16, int E, int D, int G>
 hipError_t decode_one(const KvDecodeLaunch& a, int splits, hipStream_t s) {
   hipLaunchKernelGGL((kv_decode_kernel<BF16, E, D, G>), dim3(splits, a.units), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((kv_combine_kernel<BF16, D, G>), dim3(a.units), dim3(256), 0, s, a.partial, splits, a.H, a.H_kv,
-                     a.out);
   return hipGetLastError();
 }
 
@@ -320,6 +421,12 @@ hipError_t launch_kv_rows(const KvRowsLaunch& a, hipStream_t s) {
 hipError_t launch_kv_block_reps(int units, int n, int64_t t0, int log2r, uint64_t seed, int32_t* list, hipStream_t s) {
   const int64_t total = static_cast<int64_t>(units) * (n >> log2r);
   hipLaunchKernelGGL(kv_block_reps_kernel, dim3(grid1d(total, 256)), dim3(256), 0, s, units, n, t0, log2r, seed, list);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_fill(int32_t* out, int64_t n, int32_t value, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_fill_kernel, dim3(grid1d(n, 256)), dim3(256), 0, s, out, n, value);
   return hipGetLastError();
 }
 

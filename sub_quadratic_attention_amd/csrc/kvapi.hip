@@ -24,12 +24,13 @@ struct thin_kv {
   int64_t tokens;   // tokens ingested
   int64_t m;        // inflation factor
   int nC, nBf, nRaw, nb, nh;
+  bool cnt_ready;   // the decode's per-unit split counters are known to be zero
 };
 
 namespace {
 
 struct KvLayout {
-  size_t off_k, off_v, off_tok, bytes;
+  size_t off_k, off_v, off_tok, off_cnt, bytes;
 };
 
 int elt_of(const thin_attn* h) { return h->cfg.dtype == THIN_BF16 ? 2 : 4; }
@@ -41,6 +42,7 @@ KvLayout kv_layout(const thin_attn* h, int64_t units, int64_t n) {
   k.off_k = L.add(static_cast<size_t>(rows) * h->cfg.E * elt_of(h));
   k.off_v = L.add(static_cast<size_t>(rows) * h->cfg.D * elt_of(h));
   k.off_tok = L.add(static_cast<size_t>(rows) * sizeof(int32_t));
+  k.off_cnt = L.add(static_cast<size_t>(units) * sizeof(int32_t));   // decode split counters (zero between calls)
   k.bytes = L.total;
   return k;
 }
@@ -57,7 +59,7 @@ KvWs kv_ws(const thin_attn* h, int64_t units, int64_t n) {
   w.off_lc = L.add(sizeof(int32_t) * units * 4 * n);
   w.off_g = L.add(sizeof(double) * units * 4 * n * n);
   const int G = h->cfg.H / h->cfg.H_kv;
-  w.off_part = L.add(sizeof(float) * units * thin::kv_decode_splits(static_cast<int>(n)) * G * (h->cfg.D + 2));
+  w.off_part = L.add(sizeof(float) * units * thin::kv_decode_splits(static_cast<int>(n)) * G * (h->cfg.D + 4));
   w.bytes = L.total;
   return w;
 }
@@ -320,6 +322,7 @@ int thin_attn_kv_create(thin_attn_t* h, void* state, size_t state_bytes, int64_t
   kv->tokens = 0;
   kv->m = 1;
   kv->nC = kv->nBf = kv->nRaw = kv->nb = kv->nh = 0;
+  kv->cnt_ready = false;
   *out = kv;
   return THIN_OK;
 }
@@ -409,13 +412,21 @@ int thin_attn_kv_decode(thin_kv_t* kv, const void* q, const void* k1, const void
   a.lw_b = kv->m >= 2 ? static_cast<float>(log2(static_cast<double>(kv->m / 2))) : 0.f;
   a.scale_log2 = static_cast<float>(h->scale64 * 1.4426950408889634);
   a.partial = reinterpret_cast<float*>(ws + W.off_part);
+  // the same launch appends the token to the raw block (slot 6n + nRaw)
+  a.state_tok = reinterpret_cast<int32_t*>(kv->state + L.off_tok);
+  a.new_slot = 6 * kv->n + kv->nRaw;
+  a.new_tok = static_cast<int32_t>(kv->tokens);
+  a.cnt = reinterpret_cast<int32_t*>(kv->state + L.off_cnt);
+  if (!kv->cnt_ready) {   // first decode on this state: zero the split counters
+    THIN_HIP(thin::launch_kv_fill(a.cnt, kv->units, 0, st));
+    kv->cnt_ready = true;
+  }
   THIN_HIP(timed(h, st, "kv_decode", [&] {
     return thin::launch_kv_decode(a, c.dtype == THIN_BF16, c.E, c.D, c.H / c.H_kv, st);
   }));
-  // 2. the token joins the raw block; a finished block is ingested
+  // 2. the token has joined the raw block; a finished block is ingested
   const int64_t ndec = decisions_for(*kv, 1);
   int64_t dec_pos = 0;
-  if ((rc = put_tokens(*kv, k1, v1, 1, 0, 1, 6 * kv->n + kv->nRaw, kv->tokens, nullptr, 0, st))) return rc;
   kv->nRaw += 1;
   kv->tokens += 1;
   if (kv->nRaw == kv->n && (rc = ingest_block(*kv, ws, decisions, ndec, dec_pos, st))) return rc;
@@ -468,6 +479,7 @@ int thin_attn_kv_import(thin_kv_t* kv, const void* host, size_t bytes) {
   kv->nh = m.nh;
   kv->tokens = m.tokens;
   kv->m = m.m;
+  kv->cnt_ready = false;
   return THIN_OK;
 }
 
