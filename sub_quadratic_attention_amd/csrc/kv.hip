@@ -124,18 +124,21 @@ __global__ void kv_summary_kernel(const int32_t* tok, int slots, int n, int nC, 
 // Visible keys = cache slots [0, nC) (log2 weight lw_c), buffer slots
 // [4n, 4n + nBf) (lw_b), raw slots [6n, 6n + nRaw) (weight 1) and the new
 // token itself (read from the caller's k1 / v1).  The key range is split
-// across workgroups of kSplitKeys keys; each writes a partial (max, sum,
+// across workgroups of KPW keys (32, 64 or 128, the smallest whose partials
+// the merge can hold in LDS, so short states still spread over many
+// workgroups); each writes a partial (max, sum,
 // unnormalised output) per query head, and the last workgroup of a unit to
 // finish (a per-unit counter, zero before and after the launch) merges them.
 // Workgroup 0 of a unit also appends the new token to the raw block.
 //
-// Every memory read of a workgroup is issued up front: the queries, one key
-// row per thread (threads < kSplitKeys) and the split's value rows, 16 bytes
-// per load, coalesced, into LDS.  The logits are one key per thread for all
-// G heads; P V then runs from LDS with one thread per (head, pair of
-// dimensions).
+// Every memory read of a workgroup is issued up front: the queries, the key
+// rows (256 / KPW threads per key, each holding every (256 / KPW)-th 16-byte
+// piece, so a wave reads whole rows coalesced) and the split's value rows
+// into LDS.  The threads of a key form partial dots for all G heads and sum
+// them with lane shuffles; P V then runs from LDS with one thread per (head,
+// pair of dimensions).
 // ---------------------------------------------------------------------------
-constexpr int kSplitKeys = 128;   // keys per workgroup
+constexpr int kMinSplitKeys = 32;   // smallest keys per workgroup
 
 // Row of visible key kk: its state row u * slots + slot, or -1 for the new token (kk = total - 1).
 __device__ __forceinline__ int64_t key_state_row(const KvDecodeLaunch& a, int u, int kk, int total) {
@@ -184,19 +187,17 @@ __device__ __forceinline__ void combine_unit(const float* partial, int u, int sp
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x < G) {
-      const int gh = threadIdx.x;
-      float m = -INFINITY;
-      for (int s = 0; s < splits; ++s) m = fmaxf(m, sp[(s * G + gh) * PS + D]);
-      float den = 0.f;
-      for (int s = 0; s < splits; ++s) {
-        const float ms = sp[(s * G + gh) * PS + D];
-        const float e = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - m);
-        s_w[s][gh] = e;
-        den = fmaf(e, sp[(s * G + gh) * PS + D + 1], den);
-      }
-      const float inv = 1.0f / den;
-      for (int s = 0; s < splits; ++s) s_w[s][gh] *= inv;
+    // weights of head gh: one wave, a lane per split
+    for (int gh = w; gh < G; gh += 4) {
+      const bool in = lane < splits;
+      const float ms = in ? sp[(lane * G + gh) * PS + D] : -INFINITY;
+      const float ls = in ? sp[(lane * G + gh) * PS + D + 1] : 0.f;
+      float m = ms;
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      const float e = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - m);
+      float den = e * ls;
+      for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+      if (in) s_w[lane][gh] = e / den;
     }
     __syncthreads();
   }
@@ -230,26 +231,30 @@ __device__ __forceinline__ void combine_unit(const float* partial, int u, int sp
   }
 }
 
-template <bool BF16, int E, int D, int G>
+template <bool BF16, int E, int D, int G, int KPW>
 __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
   constexpr int ELT = BF16 ? 2 : 4;
+  constexpr int FP = 16 / ELT;                          // features per 16-byte piece
   constexpr int VP = D * ELT / 16;                      // 16-byte pieces per value row
-  constexpr int VLOADS = kSplitKeys * VP / 256;         // value pieces per thread
+  constexpr int VLOADS = KPW * VP / 256;                // value pieces per thread
   constexpr int KP = E * ELT / 16;                      // 16-byte pieces per key row
+  constexpr int TPK = 256 / KPW;                        // threads per key
+  constexpr int KPT = KP / TPK;                         // key pieces per thread
+  static_assert(KPT * TPK == KP && VLOADS * 256 == KPW * VP, "key or value rows do not tile the workgroup");
   const int u = blockIdx.y;
   const int split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = u / a.H_kv, hk = u % a.H_kv;
   const int total = a.nC + a.nBf + a.nRaw + 1;
-  const int k0 = split * kSplitKeys;
-  const int nk = min(total, k0 + kSplitKeys) - k0;
+  const int k0 = split * KPW;
+  const int nk = min(total, k0 + KPW) - k0;
 
   constexpr int PS = D + 4;                              // floats per partial row (16-byte multiple)
   // value rows of the split; later the unit's partials when this workgroup merges
-  constexpr int kBuf = kSplitKeys * D * ELT > kMergeBytes ? kSplitKeys * D * ELT : kMergeBytes;
+  constexpr int kBuf = KPW * D * ELT > kMergeBytes ? KPW * D * ELT : kMergeBytes;
   __shared__ __attribute__((aligned(16))) unsigned char sv[kBuf];
   __shared__ __attribute__((aligned(16))) float sq[G][E];
-  __shared__ float sp[G][kSplitKeys];
+  __shared__ float sp[G][KPW];
   __shared__ float red[4][G];
   __shared__ float smax[G], ssum[G];
 
@@ -264,17 +269,18 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
                                                                (static_cast<int64_t>(b) * a.H_kv + hk) * (D * ELT));
     vr[i] = j < nk ? src[piece % VP] : uint4{0u, 0u, 0u, 0u};
   }
-  // this thread's key row
-  const int kk = k0 + tid;
-  const bool live = tid < kSplitKeys && tid < nk;
-  uint4 kr[KP];
+  // this thread's share of key kk: pieces slice, slice + TPK, ...
+  const int jk = tid / TPK, slice = tid % TPK;
+  const int kk = k0 + jk;
+  const bool live = jk < nk;
+  uint4 kr[KPT];
   if (live) {
     const int64_t r = key_state_row(a, u, kk, total);
     const uint4* krow = r >= 0 ? reinterpret_cast<const uint4*>(static_cast<const char*>(a.state_k) + r * (E * ELT))
                                : reinterpret_cast<const uint4*>(static_cast<const char*>(a.k1) +
                                                                 (static_cast<int64_t>(b) * a.H_kv + hk) * (E * ELT));
 #pragma unroll
-    for (int i = 0; i < KP; ++i) kr[i] = krow[i];
+    for (int i = 0; i < KPT; ++i) kr[i] = krow[slice + TPK * i];
   }
   // queries of the group
   for (int x = tid; x < G * E; x += 256) {
@@ -286,17 +292,16 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
   for (int i = 0; i < VLOADS; ++i) reinterpret_cast<uint4*>(sv)[tid + 256 * i] = vr[i];
   __syncthreads();
 
-  // logits: one key per thread
-  float logit[G];
+  // logits: the TPK threads of a key sum their partial dots
+  float acc[G];
+#pragma unroll
+  for (int gh = 0; gh < G; ++gh) acc[gh] = 0.f;
   if (live) {
-    const float lw = kk < a.nC ? a.lw_c : (kk < a.nC + a.nBf ? a.lw_b : 0.f);
-    float acc[G];
 #pragma unroll
-    for (int gh = 0; gh < G; ++gh) acc[gh] = 0.f;
-#pragma unroll
-    for (int i = 0; i < KP; ++i) {
+    for (int i = 0; i < KPT; ++i) {
+      const int piece = slice + TPK * i;
       const uint32_t wv[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-      float kv[16 / ELT];
+      float kv[FP];
       if constexpr (BF16) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -310,25 +315,31 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
 #pragma unroll
       for (int gh = 0; gh < G; ++gh)
 #pragma unroll
-        for (int j4 = 0; j4 < 16 / ELT; j4 += 4) {   // the group's queries, 16 bytes per LDS read (same for all lanes)
-          const float4 qv = *reinterpret_cast<const float4*>(&sq[gh][i * (16 / ELT) + j4]);
+        for (int j4 = 0; j4 < FP; j4 += 4) {   // the group's queries, 16 bytes per LDS read
+          const float4 qv = *reinterpret_cast<const float4*>(&sq[gh][piece * FP + j4]);
           acc[gh] = fmaf(qv.x, kv[j4], acc[gh]);
           acc[gh] = fmaf(qv.y, kv[j4 + 1], acc[gh]);
           acc[gh] = fmaf(qv.z, kv[j4 + 2], acc[gh]);
           acc[gh] = fmaf(qv.w, kv[j4 + 3], acc[gh]);
         }
     }
-#pragma unroll
-    for (int gh = 0; gh < G; ++gh) logit[gh] = fmaf(acc[gh], a.scale_log2, lw);
-  } else {
-#pragma unroll
-    for (int gh = 0; gh < G; ++gh) logit[gh] = -INFINITY;
   }
-  // max and sum over the split
+  float logit[G];
+  const float lw = kk < a.nC ? a.lw_c : (kk < a.nC + a.nBf ? a.lw_b : 0.f);
+#pragma unroll
+  for (int gh = 0; gh < G; ++gh) {
+    float d = acc[gh];
+#pragma unroll
+    for (int off = 1; off < TPK; off <<= 1) d += __shfl_xor(d, off, 64);
+    logit[gh] = live ? fmaf(d, a.scale_log2, lw) : -INFINITY;
+  }
+  // max and sum over the split (the threads of a key hold the same logit, so
+  // the wave reductions run over lanes TPK apart: one lane per key)
 #pragma unroll
   for (int gh = 0; gh < G; ++gh) {
     float m = logit[gh];
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+#pragma unroll
+    for (int off = 32; off >= TPK; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     if (lane == 0) red[w][gh] = m;
   }
   __syncthreads();
@@ -337,9 +348,10 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
 #pragma unroll
   for (int gh = 0; gh < G; ++gh) {
     const float p = live ? __builtin_amdgcn_exp2f(logit[gh] - smax[gh]) : 0.f;
-    if (tid < kSplitKeys) sp[gh][tid] = p;
+    if (slice == 0) sp[gh][jk] = p;
     float s = p;
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+#pragma unroll
+    for (int off = 32; off >= TPK; off >>= 1) s += __shfl_xor(s, off, 64);
     if (lane == 0) red[w][gh] = s;
   }
   __syncthreads();
@@ -400,15 +412,37 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
   if (tid == 0) __hip_atomic_store(&a.cnt[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Keys per workgroup: the smallest of 32, 64, 128 whose partials the merge
+// holds in LDS (else 128, merged from global memory).
+template <int D, int G>
+int decode_keys_per_wg(int total) {
+  for (int kpw = kMinSplitKeys; kpw < 128; kpw *= 2) {
+    const int splits = (total + kpw - 1) / kpw;
+    const int pieces = splits * G * (D + 4) / 4;
+    if (splits <= kMergeSplits && (pieces + 63) / 64 * 1024 <= kMergeBytes) return kpw;
+  }
+  return 128;
+}
+
 template <bool BF16, int E, int D, int G>
-hipError_t decode_one(const KvDecodeLaunch& a, int splits, hipStream_t s) {
-  hipLaunchKernelGGL((kv_decode_kernel<BF16, E, D, G>), dim3(splits, a.units), dim3(256), 0, s, a);
+hipError_t decode_one(const KvDecodeLaunch& a, hipStream_t s) {
+  const int total = a.nC + a.nBf + a.nRaw + 1;
+  const int kpw = decode_keys_per_wg<D, G>(total);
+  KvDecodeLaunch b = a;
+  b.splits = (total + kpw - 1) / kpw;
+  const dim3 grid(b.splits, a.units);
+  if (kpw == 32)
+    hipLaunchKernelGGL((kv_decode_kernel<BF16, E, D, G, 32>), grid, dim3(256), 0, s, b);
+  else if (kpw == 64)
+    hipLaunchKernelGGL((kv_decode_kernel<BF16, E, D, G, 64>), grid, dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL((kv_decode_kernel<BF16, E, D, G, 128>), grid, dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int kv_decode_splits(int n) { return (7 * n + kSplitKeys) / kSplitKeys; }
+int kv_decode_splits(int n) { return (7 * n + kMinSplitKeys) / kMinSplitKeys; }   // 7n + 1 keys at most
 
 hipError_t launch_kv_rows(const KvRowsLaunch& a, hipStream_t s) {
   const int per_row = (a.E + a.D) * a.elt / 16 + 1;
@@ -451,11 +485,8 @@ bool kv_decode_supported(int bf16, int E, int D, int G) {
 }
 
 hipError_t launch_kv_decode(const KvDecodeLaunch& a, int bf16, int E, int D, int G, hipStream_t s) {
-  const int splits = (a.nC + a.nBf + a.nRaw + 1 + kSplitKeys - 1) / kSplitKeys;
-  KvDecodeLaunch b = a;
-  b.splits = splits;
 #define THIN_KV_CASE(BF, EE, DD, GG) \
-  if (bf16 == BF && E == EE && D == DD && G == GG) return decode_one<BF, EE, DD, GG>(b, splits, s);
+  if (bf16 == BF && E == EE && D == DD && G == GG) return decode_one<BF, EE, DD, GG>(a, s);
   THIN_KV_CASE(1, 128, 128, 1)
   THIN_KV_CASE(1, 128, 128, 2)
   THIN_KV_CASE(1, 128, 128, 4)

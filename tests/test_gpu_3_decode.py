@@ -89,6 +89,14 @@ def test_decode_fp32_gqa8():
     _check("fp32 G=8", d, 32, 8, 1, 128, 128)
 
 
+def test_decode_long_state_gqa8():
+    """n=256, history of 3840 tokens: 768 cache + 384 buffer rows, so each decode step sees
+    1153..1216 keys, split over workgroups of 128 keys (with 8 heads sharing a KV head the
+    partials of smaller splits would not fit the merge's LDS)."""
+    d = _stream(5, 3840, 64, Hkv=1, H=8)
+    _check("n=256 long state, G=8", d, 256, 8, 1, 128, 128)
+
+
 def test_decode_matches_causal_forward():
     """A decode step sees what a causal forward query at the same token sees."""
     from sub_quadratic_attention_amd.binding import ThinAttention
