@@ -65,6 +65,24 @@ constexpr int nqg() { return (BF16 ? (E <= 128 && D <= 128) : D <= 64) ? 2 : 1; 
 
 typedef __attribute__((address_space(3))) unsigned char lds_byte;   // LDS views of the buffers
 
+// Maximum / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups
+// holding one query's keys) with the gfx950 lane swaps, which stay in the
+// VALU (a shuffle through ds_bpermute waits on an LDS round trip).  Each swap
+// returns both halves, so max / sum of the pair is the value of lane l ^ 32
+// (then l ^ 16) combined with lane l's, identically in both lanes.
+__device__ __forceinline__ float group_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Piece permutations.  K is read 16 bytes per lane, 16 consecutive rows at one
 // logical piece: 128-byte rows (two per 256 bytes of banks) take
 // q ^ (R / 2 % 8), longer rows q ^ (R % 16).  bf16 V is read 8 bytes per lane
@@ -338,8 +356,7 @@ struct Attn {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, p[qg][kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = group_max(mx);
       const float m_new = fmaxf(m_run[qg], mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_use);
@@ -353,8 +370,7 @@ struct Attn {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) rs += p[qg][kb][i];
-        rs += __shfl_xor(rs, 16, 64);
-        rs += __shfl_xor(rs, 32, 64);
+        rs = group_sum(rs);
         l_run[qg] = l_run[qg] * alpha + rs;
       }
       m_run[qg] = m_new;
