@@ -105,8 +105,13 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt):
     if not causal:
         j, s0 = compress_depth(S)
         n_out = S >> j
-        gram_entries = sum((S // (s0 * 4 ** l)) * (s0 * 2 ** (l + 1)) * (s0 * 2 ** (l + 1) + 1) // 2
-                           for l in range(1, j + 1))
+        # levels of bins of at most 16 points run in the fused small-bin kernel
+        # (it reads each point of the level once: HBM-bound), the others on
+        # the pair-Gram tiles
+        small = lambda N: N <= 16 and E % 32 == 0 and D % 32 == 0
+        levels = [(S // (s0 * 4 ** l), s0 * 2 ** (l + 1)) for l in range(1, j + 1)]   # (bins, N) per unit
+        gram_entries = sum(bins * N * (N + 1) // 2 for bins, N in levels if not small(N))
+        small_bytes = units * sum(bins * N * (E + D) * elt + bins * (N // 2) * 5 for bins, N in levels if small(N))
         keys = n_out
         pairs_eff = B * H * T * S
         visible = B * H * T * keys
@@ -116,6 +121,7 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt):
         while n_out * n_out < S:
             n_out *= 2
         gram_entries = express_gram_entries(S, n_out)
+        small_bytes = 0
         pairs_eff = B * H * T * (T + 1) // 2
         visible = B * H * express_visible_total(S, n_out)
         attn_bytes = (B * T * H * E + units * S * (E + D) + B * T * H * D) * elt
@@ -123,7 +129,8 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt):
         n_out=n_out,
         pairs_eff=pairs_eff,
         attention=dict(flops=2.0 * visible * (E + D), bytes=attn_bytes),
-        pair_gram=dict(flops=2.0 * (E + D) * gram_entries * units, bytes=None),
+        pair_gram=dict(flops=2.0 * (E + D) * gram_entries * units, bytes=None) if gram_entries else None,
+        small_halving=dict(flops=None, bytes=small_bytes) if small_bytes else None,
     )
 
 
@@ -324,6 +331,12 @@ def main():
         w = wm.get(label)
         if not w:
             return None
+        if w["flops"] is None:   # bandwidth-bound: algorithmic bytes only
+            per_launch_bytes = w["bytes"] / r["launches_per_step"]
+            gbs = per_launch_bytes / (r["avg_ms"] * 1e-3) / 1e9
+            return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK["hbm_GBs"], "unit": "GB/s",
+                    "frac": round(gbs / PEAK["hbm_GBs"], 4), "traffic": None, "kernel": label,
+                    "work_per_launch_bytes": per_launch_bytes, "avg_launch_ms": r["avg_ms"]}
         per_launch_flops = w["flops"] / r["launches_per_step"]
         peak_key = "f64" if label == "pair_gram" else dt
         achieved = per_launch_flops / (r["avg_ms"] * 1e-3) / 1e12

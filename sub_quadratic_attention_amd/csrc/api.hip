@@ -159,12 +159,17 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
         const int64_t in_unit = S >> (l - 1);
         thin::SweepLaunch sl = make_sweep(h, G, N, units, bins, a, in_unit, b, seed, thin::kTagCompress,
                                           static_cast<uint64_t>(l) << 20);
-        THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
         sl.out_stride = N / 2;
         sl.dec = decisions;
         sl.dec_per_unit = ndec;
         sl.dec_base = dec_base;
-        THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, st); }));
+        if (thin::small_halving_supported(N, c.E, c.D)) {   // small bins: Gram and walk in one kernel
+          THIN_HIP(timed(h, st, "small_halving",
+                         [&] { return thin::launch_small_halving(gram_for(sl, src, h->scale64), sl, st); }));
+        } else {
+          THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
+          THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, st); }));
+        }
         dec_base += static_cast<int64_t>(bins) * (N / 2);
         std::swap(a, b);
       }

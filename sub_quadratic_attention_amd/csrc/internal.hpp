@@ -142,6 +142,10 @@ struct KvDecodeLaunch {
 // Launchers (return hipError_t of the launch).
 hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s);
 hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s);
+// Bins of at most 16 points: the pair Gram, thresholds and walk of a
+// GramLaunch / SweepLaunch pair in one kernel (same outputs as the two).
+bool small_halving_supported(int N, int E, int D);
+hipError_t launch_small_halving(const GramLaunch& g, const SweepLaunch& a, hipStream_t s);
 hipError_t launch_iota(int32_t* out, int64_t units, int64_t n, int64_t stride, hipStream_t s);
 hipError_t launch_express_reps(const ExpressView& ev, int units, uint64_t seed, int32_t* reps, hipStream_t s);
 hipError_t launch_halve_input(const ExpressView& ev, int units, int e, int32_t* halve_in, hipStream_t s);

@@ -806,6 +806,145 @@ __global__ void philox_words_kernel(const uint64_t* ctr, int64_t n, uint64_t see
   out[4 * i + 3] = x[3];
 }
 
+// ---------------------------------------------------------------------------
+// Bins of at most 16 points: Gram, thresholds and walk in one launch.  A wave
+// takes a tile of 16 points of one unit -- 16 / N whole bins -- and forms
+// their point Gram X X^T, keys and values apart, on the fp64 MFMA 16x16x4
+// (A[i][k] at lane i + 16 k, B[k][j] at lane j + 16 k, D[i][j] in lane
+// j + 16 (i % 4), element i / 4): for X X^T the A and B operands are the same
+// register, lane l holding a feature of point l % 16 from quarter l / 16 of
+// the features.  kappa of every point pair goes to LDS (products across bins
+// are formed and never read).  Lane q then takes pair q of the tile: its
+// pair-Gram column (the same expression as the tiles), the sigma recursion
+// of its bin up to itself, its threshold, and the walk, one ballot per step
+// for all the tile's bins together.
+// ---------------------------------------------------------------------------
+constexpr int kSmallN = 16;   // points per tile (and largest bin of the fused path)
+
+template <bool BF16>
+__device__ __forceinline__ void small_features(const unsigned char* p, double x[8]) {
+  if constexpr (BF16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = static_cast<double>(__uint_as_float(v[j] << 16));
+      x[2 * j + 1] = static_cast<double>(__uint_as_float(v[j] & 0xffff0000u));
+    }
+  } else {
+    const uint4 w0 = reinterpret_cast<const uint4*>(p)[0], w1 = reinterpret_cast<const uint4*>(p)[1];
+    const uint32_t v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = static_cast<double>(__uint_as_float(v[j]));
+  }
+}
+
+// <x_i, x_j> over the F features of row `row` of every point: lane l takes
+// features [F/4 (l / 16), F/4 (l / 16 + 1)) of its point, eight per load (F
+// a multiple of 32).  Loads go out four at a time before their MFMAs, and
+// four accumulators keep four MFMAs in flight.
+template <bool BF16>
+__device__ __forceinline__ f64x4_t small_gram(const unsigned char* row, int F) {
+  const int quarter = (threadIdx.x & 63) >> 4;
+  const int elt = BF16 ? 2 : 4;
+  const unsigned char* p = row + static_cast<int64_t>(quarter) * (F / 4) * elt;
+  const int groups = F / 32;   // loads of eight features per lane
+  f64x4_t acc[4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  for (int g0 = 0; g0 < groups; g0 += 4) {
+    double x[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) small_features<BF16>(p + min(g0 + j, groups - 1) * 8 * elt, x[j]);   // (repeats are not used)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (g0 + j >= groups) break;   // uniform
+#pragma unroll
+      for (int f = 0; f < 8; ++f) acc[f & 3] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[j][f], x[j][f], acc[f & 3], 0, 0, 0);
+    }
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void small_halving_kernel(GramLaunch g, SweepLaunch a) {
+  __shared__ double s_kap[4][kSmallN][kSmallN + 1];   // kappa of the tile's point pairs, per wave
+  const int N = g.N, P = N / 2;
+  const int bpt = kSmallN / N;                        // whole bins per tile
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int units = g.nbins / g.bins_per_unit;
+  const int tpu = (g.bins_per_unit + bpt - 1) / bpt;   // tiles per unit
+  const int t = blockIdx.x * 4 + w;
+  if (t >= units * tpu) return;   // whole wave: no barrier in this kernel
+  const int unit = t / tpu, bin0 = (t % tpu) * bpt;
+  const int b = unit / g.src.H_kv, h = unit % g.src.H_kv;
+
+  // point lane % 16 of the tile (points past the tile's bins load its first point)
+  {
+    const int pt = lane & 15, pb = pt / N;
+    const bool ok = pb < bpt && bin0 + pb < g.bins_per_unit;
+    const int tok = g.idx[static_cast<int64_t>(unit) * g.idx_unit_stride +
+                          static_cast<int64_t>(ok ? bin0 + pb : bin0) * g.idx_stride + (ok ? pt % N : 0)];
+    const int elt = BF16 ? 2 : 4;
+    const int64_t row = (static_cast<int64_t>(b) * g.src.S + tok) * g.src.H_kv + h;
+    const f64x4_t kd = small_gram<BF16>(static_cast<const unsigned char*>(g.src.k) + row * g.src.E * elt, g.src.E);
+    const f64x4_t vd = small_gram<BF16>(static_cast<const unsigned char*>(g.src.v) + row * g.src.D * elt, g.src.D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_kap[w][(lane >> 4) + 4 * i][lane & 15] = exp_f64(g.scale * kd[i]) * (vd[i] + 1.0);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // lane q: pair i of bin bq of the tile
+  const int bq = lane / P, i = lane % P;
+  const bool mine = lane < bpt * P && bin0 + bq < g.bins_per_unit;
+  const int lb = bin0 + (mine ? bq : 0);
+  const int o = (mine ? bq : 0) * N;   // the bin's first point in the tile
+  auto gpair = [&](int r, int c) -> double {   // pair-Gram entry (row pair r, column pair c) of the lane's bin
+    const double* k0 = s_kap[w][o + 2 * r];
+    const double* k1 = s_kap[w][o + 2 * r + 1];
+    return (k0[o + 2 * c] - k0[o + 2 * c + 1]) - (k1[o + 2 * c] - k1[o + 2 * c + 1]);
+  };
+  double gcol[kSmallN / 2];
+#pragma unroll
+  for (int j = 0; j < kSmallN / 2; ++j) gcol[j] = (mine && j < i) ? gpair(j, i) : 0.0;
+  // sigma recursion of the bin through pair i (the arithmetic of sigma_steps)
+  const double c = sqrt(2.0 * log(2.0 * N / g.delta));
+  const double k1 = 1.0 + 1.0 / (c * c), k2 = 2.0 / c;
+  double s2 = 0.0, al = 0.0;
+  for (int k = 0; k <= i; ++k) {
+    const double b2 = fmax(gpair(k, k), 0.0), bk = sqrt(b2);
+    const double cb = c * bk, b2k1 = b2 * k1, k2b = k2 * bk;
+    const double sg = __builtin_amdgcn_sqrt(s2);
+    const double bsc = cb * sg;
+    const double grow = s2 + fmax(0.0, fma(-k2b, sg, b2k1));
+    const double keep = fmax(s2, b2);
+    al = fmax(bsc, b2);
+    s2 = bsc >= b2 ? grow : keep;
+  }
+  const double u = mine ? philox_uniform(static_cast<uint64_t>(i), a.bin_base + lb, static_cast<uint64_t>(unit), a.tag,
+                                         a.seed)
+                        : 0.0;
+  const double thr = threshold(al, u);
+  double alpha = 0.0;
+  uint32_t bits = 0;
+  const int first_lane = lane - i;   // pair 0 of the lane's bin
+#pragma unroll
+  for (int j = 0; j < kSmallN / 2; ++j) {
+    if (j >= P) continue;   // uniform
+    const uint64_t m = __ballot(alpha < thr);
+    const bool first = (m >> ((first_lane + j) & 63)) & 1ull;   // (lanes past the bins read any bit)
+    bits |= static_cast<uint32_t>(first) << j;
+    alpha += first ? gcol[j] : -gcol[j];
+  }
+  if (mine) {
+    const bool first = (bits >> i) & 1u;
+    const int z = unit * g.bins_per_unit + lb;
+    const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
+    a.idx_out[static_cast<int64_t>(z) * a.out_stride + i] = in[2 * i + (first ? 0 : 1)];
+    if (a.dec) a.dec[static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) + i] = first ? 1 : 0;
+  }
+}
+
 inline unsigned grid1d(int64_t n, int block) { return static_cast<unsigned>((n + block - 1) / block); }
 
 }  // namespace
@@ -853,6 +992,25 @@ hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(halving_sweep_kernel, dim3(a.nbins), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+bool small_halving_supported(int N, int E, int D) {
+  return N >= 2 && N <= kSmallN && N % 2 == 0 && E % 32 == 0 && D % 32 == 0;
+}
+
+hipError_t launch_small_halving(const GramLaunch& g, const SweepLaunch& a, hipStream_t s) {
+  if (!small_halving_supported(g.N, g.src.E, g.src.D) || g.N != a.N || g.nbins != a.nbins ||
+      g.bins_per_unit != a.bins_per_unit)
+    return hipErrorInvalidValue;
+  if (g.nbins == 0) return hipSuccess;
+  const int bpt = kSmallN / g.N;
+  const int64_t waves = static_cast<int64_t>(g.nbins / g.bins_per_unit) * ((g.bins_per_unit + bpt - 1) / bpt);
+  const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+  if (g.src.bf16)
+    hipLaunchKernelGGL(small_halving_kernel<true>, grid, dim3(256), 0, s, g, a);
+  else
+    hipLaunchKernelGGL(small_halving_kernel<false>, grid, dim3(256), 0, s, g, a);
   return hipGetLastError();
 }
 

@@ -47,6 +47,21 @@ def test_unmasked_ragged_and_gqa():
     run_and_compare("unmasked S=208 GQA", d, False, H, Hkv, 64, 128)
 
 
+@pytest.mark.parametrize("S,dtype", [(48, "bf16"), (16, "f32"), (64 * 4, "bf16")])
+def test_unmasked_small_bins(S, dtype):
+    """Bins of at most 16 points (Gram and walk fused): S=48 gives 12-point bins (one per
+    16-point tile), S=16 a tile holding a single 8-point bin, S=256 tiles of 4, 2 and 1 bins;
+    six units."""
+    rng = np.random.default_rng(S)
+    B, T, H, Hkv = 3, 37, 4, 2
+    cast = inputs.bf16_round if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    d = dict(q=cast(rng.standard_normal((B, T, H, 64)) * 0.5),
+             k=cast(rng.standard_normal((B, S, Hkv, 64)) * 0.5), dtype=dtype)
+    D = 128 if dtype == "bf16" else 64
+    d["v"] = cast(rng.standard_normal((B, S, Hkv, D)))
+    run_and_compare(f"unmasked small bins S={S} {dtype}", d, False, H, Hkv, 64, D)
+
+
 def test_vit_token_mixing_reduced():
     """56x56 ViT tokens (S=3136, n_out=392), two batch entries, sampled outputs."""
     d = inputs.vit_token_mixing(seed=0, B=2)
