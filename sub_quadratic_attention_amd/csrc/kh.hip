@@ -814,7 +814,8 @@ __global__ void philox_words_kernel(const uint64_t* ctr, int64_t n, uint64_t see
 // j + 16 (i % 4), element i / 4): for X X^T the A and B operands are the same
 // register, lane l holding a feature of point l % 16 from quarter l / 16 of
 // the features.  kappa of every point pair goes to LDS (products across bins
-// are formed and never read).  Lane q then takes pair q of the tile: its
+// are formed and never read).  Bins of 4 or 8 points use the 4x4x4 form
+// instead, which forms only products inside a bin.  Lane q then takes pair q of the tile: its
 // pair-Gram column (the same expression as the tiles), the sigma recursion
 // of its bin up to itself, its threshold, and the walk, one ballot per step
 // for all the tile's bins together.
@@ -840,20 +841,20 @@ __device__ __forceinline__ void small_features(const unsigned char* p, double x[
 }
 
 // <x_i, x_j> over the F features of row `row` of every point: lane l takes
-// features [F/4 (l / 16), F/4 (l / 16 + 1)) of its point, eight per load (F
-// a multiple of 32).  Loads go out four at a time before their MFMAs, and
+// the blocks of eight features 4 g + l / 16 of its point, one per load (F a
+// multiple of 32; the four lanes of a point read 64 contiguous bytes).  Loads go out four at a time before their MFMAs, and
 // four accumulators keep four MFMAs in flight.
 template <bool BF16>
 __device__ __forceinline__ f64x4_t small_gram(const unsigned char* row, int F) {
   const int quarter = (threadIdx.x & 63) >> 4;
   const int elt = BF16 ? 2 : 4;
-  const unsigned char* p = row + static_cast<int64_t>(quarter) * (F / 4) * elt;
+  const unsigned char* p = row + quarter * 8 * elt;   // lane quarter q: feature blocks 4 g + q of 8
   const int groups = F / 32;   // loads of eight features per lane
   f64x4_t acc[4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
   for (int g0 = 0; g0 < groups; g0 += 4) {
     double x[4][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) small_features<BF16>(p + min(g0 + j, groups - 1) * 8 * elt, x[j]);   // (repeats are not used)
+    for (int j = 0; j < 4; ++j) small_features<BF16>(p + min(g0 + j, groups - 1) * 32 * elt, x[j]);   // (repeats are not used)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (g0 + j >= groups) break;   // uniform
@@ -862,6 +863,42 @@ __device__ __forceinline__ f64x4_t small_gram(const unsigned char* row, int F) {
     }
   }
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// Bins of 4 or 8 points on the fp64 MFMA 4x4x4 with four blocks (A[m][k] at
+// lane 16 k + 4 b + m, B[k][n] at lane 16 k + 4 b + n, D[m][n] at lane
+// 16 m + 4 b + n): lane l holds point l % 16 = 4 b + (l % 4) of the tile, so
+// block b with A = B = that register is the 4 x 4 Gram of quad b (d0), and
+// with B = the point of quad b ^ 1 (PAIR) the products of quads b and b ^ 1
+// (d1).  Nothing is formed across bins.
+template <bool BF16, bool PAIR>
+__device__ __forceinline__ void small_gram44(const unsigned char* row, const unsigned char* prow, int F, double& d0,
+                                             double& d1) {
+  const int quarter = (threadIdx.x & 63) >> 4;
+  const int elt = BF16 ? 2 : 4;
+  const int off = quarter * 8 * elt;   // feature blocks 4 g + quarter of 8, as in small_gram
+  const int groups = F / 32;
+  double a0[2] = {0.0, 0.0}, a1[2] = {0.0, 0.0};
+  for (int g0 = 0; g0 < groups; g0 += 4) {
+    double x[4][8], y[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gj = min(g0 + j, groups - 1);   // (repeats are not used)
+      small_features<BF16>(row + off + gj * 32 * elt, x[j]);
+      if constexpr (PAIR) small_features<BF16>(prow + off + gj * 32 * elt, y[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (g0 + j >= groups) break;   // uniform
+#pragma unroll
+      for (int f = 0; f < 8; ++f) {
+        a0[f & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(x[j][f], x[j][f], a0[f & 1], 0, 0, 0);
+        if constexpr (PAIR) a1[f & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(x[j][f], y[j][f], a1[f & 1], 0, 0, 0);
+      }
+    }
+  }
+  d0 = a0[0] + a0[1];
+  d1 = a1[0] + a1[1];
 }
 
 template <bool BF16>
@@ -877,16 +914,34 @@ __global__ __launch_bounds__(256) void small_halving_kernel(GramLaunch g, SweepL
   const int unit = t / tpu, bin0 = (t % tpu) * bpt;
   const int b = unit / g.src.H_kv, h = unit % g.src.H_kv;
 
-  // point lane % 16 of the tile (points past the tile's bins load its first point)
-  {
-    const int pt = lane & 15, pb = pt / N;
+  // the row of point pt of the tile (points past the tile's bins read its first point)
+  const int elt = BF16 ? 2 : 4;
+  auto point_row = [&](int pt) -> int64_t {
+    const int pb = pt / N;
     const bool ok = pb < bpt && bin0 + pb < g.bins_per_unit;
     const int tok = g.idx[static_cast<int64_t>(unit) * g.idx_unit_stride +
                           static_cast<int64_t>(ok ? bin0 + pb : bin0) * g.idx_stride + (ok ? pt % N : 0)];
-    const int elt = BF16 ? 2 : 4;
-    const int64_t row = (static_cast<int64_t>(b) * g.src.S + tok) * g.src.H_kv + h;
-    const f64x4_t kd = small_gram<BF16>(static_cast<const unsigned char*>(g.src.k) + row * g.src.E * elt, g.src.E);
-    const f64x4_t vd = small_gram<BF16>(static_cast<const unsigned char*>(g.src.v) + row * g.src.D * elt, g.src.D);
+    return (static_cast<int64_t>(b) * g.src.S + tok) * g.src.H_kv + h;
+  };
+  const unsigned char* K = static_cast<const unsigned char*>(g.src.k);
+  const unsigned char* V = static_cast<const unsigned char*>(g.src.v);
+  const int64_t row = point_row(lane & 15);
+  if (N <= 8) {   // 4x4x4: the quad Grams (and, for 8 points, quad b against quad b ^ 1)
+    const int m = lane >> 4, qb = (lane >> 2) & 3, n = lane & 3;
+    double kd0, kd1, vd0, vd1;
+    if (N == 8) {
+      const int64_t prow = point_row((lane & 15) ^ 4);
+      small_gram44<BF16, true>(K + row * g.src.E * elt, K + prow * g.src.E * elt, g.src.E, kd0, kd1);
+      small_gram44<BF16, true>(V + row * g.src.D * elt, V + prow * g.src.D * elt, g.src.D, vd0, vd1);
+      s_kap[w][4 * qb + m][4 * (qb ^ 1) + n] = exp_f64(g.scale * kd1) * (vd1 + 1.0);
+    } else {
+      small_gram44<BF16, false>(K + row * g.src.E * elt, nullptr, g.src.E, kd0, kd1);
+      small_gram44<BF16, false>(V + row * g.src.D * elt, nullptr, g.src.D, vd0, vd1);
+    }
+    s_kap[w][4 * qb + m][4 * qb + n] = exp_f64(g.scale * kd0) * (vd0 + 1.0);
+  } else {        // 16x16x4: every point pair of the tile
+    const f64x4_t kd = small_gram<BF16>(K + row * g.src.E * elt, g.src.E);
+    const f64x4_t vd = small_gram<BF16>(V + row * g.src.D * elt, g.src.D);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_kap[w][(lane >> 4) + 4 * i][lane & 15] = exp_f64(g.scale * kd[i]) * (vd[i] + 1.0);
   }
