@@ -56,7 +56,7 @@ constexpr int kStage = kStageF * 8;    // bytes of one staged point
 constexpr int kSlots = 128;            // row and column points of a tile
 constexpr int kThrCap = 2048;          // pairs whose b^2 and u a threshold workgroup keeps in LDS
 constexpr int kRing = 4;               // staging register sets
-constexpr int kAhead = 3;              // steps a load is issued ahead of its use
+constexpr int kAhead = 2;              // steps a load is issued ahead of its use (keeps 4 workgroups per CU)
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef double f64x2_t __attribute__((ext_vector_type(2)));
@@ -447,7 +447,6 @@ __device__ void gram_tile(const GramLaunch& a, int nthr, lds_byte* smem, double*
   T[threadIdx.x] = exp_f64(threadIdx.x * 0.0027076061740622863);   // ln 2 / 256
   t.template load<0>(0);
   t.template load<1>(1);
-  t.template load<2>(2);
   t.template write<0>(smem);
   __syncthreads();
   for (int st = 0; st < t.nK; st += kRing) t.template steps<0>(st, smem);   // E and D are multiples of kRing steps
@@ -481,7 +480,7 @@ __device__ void gram_tile(const GramLaunch& a, int nthr, lds_byte* smem, double*
 // takes bins on its own, 4 nthr apart, so the thresholds hold few workgroup
 // slots while the tiles run.
 template <bool BF16>
-__global__ __launch_bounds__(256) void pair_gram_kernel(GramLaunch a, int nthr, int thr_per_wave) {
+__global__ __launch_bounds__(256, 4) void pair_gram_kernel(GramLaunch a, int nthr, int thr_per_wave) {
   __shared__ __attribute__((aligned(16))) double smem[2 * kSlots * kStage / sizeof(double) + 256];
   if (static_cast<int>(blockIdx.x) < nthr) {
     if (thr_per_wave) {
