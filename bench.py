@@ -6,10 +6,10 @@ A step is one thin_attn_forward call (thinning + coreset attention) on one
 batch of seeded synthetic input already resident in HBM.  The default
 workload is the 56x56-token ViT token-mixing layer (B=64, S=3136, fp32).
 Prints ONE JSON line with the throughput in effective queries*keys per
-second (the pairs exact attention would evaluate), the per-kernel launch
-times measured with HIP events on the launch stream over the timed region
-(for the decode workload, whose launches take ~10 us, over a second run of
-the same steps, so that the events do not slow the timed one),
+second (the pairs exact attention would evaluate), timed without
+instrumentation, then the per-kernel launch times measured with HIP events
+on the launch stream over a second run of the same steps (events around
+every launch would slow the timed one, markedly for ~10 us decode launches),
 the roofline of the dominant kernel, the exact-attention comparators on the
 same GPU and the float64 CPU oracle's rate on a bounded sample.
 """
@@ -312,16 +312,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ta.set_timing(True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # the same steps again with events around every launch (per-kernel table, roofline)
+    ta.set_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     recs = ta.timing_records()
     ta.set_timing(False)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     wm = work_model(args.workload, B, T, S, H, Hkv, E, D, causal, elt)
     per_kernel = {}
