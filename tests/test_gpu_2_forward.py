@@ -124,3 +124,32 @@ def test_determinism_and_seed():
     assert torch.equal(a, b) and torch.equal(ea["coreset_idx"], eb["coreset_idx"])
     assert not torch.equal(ea["coreset_idx"], ec["coreset_idx"])
     say("[determinism] ok")
+
+
+# ---- degenerate shapes --------------------------------------------------------
+
+@pytest.mark.parametrize("causal,S,T", [(False, 1, 5), (False, 3, 2), (False, 4, 7), (False, 5, 1),
+                                        (True, 1, 1), (True, 2, 2), (True, 3, 3), (True, 9, 9)])
+def test_tiny_sequences(causal, S, T):
+    """S of 1 to 9 tokens: no thinning (S < 4, or a causal state that never fills), the
+    smallest Compress (S=4: one 4-point bin), a 2-token cache with a partial block."""
+    rng = np.random.default_rng(100 + S)
+    B, H, Hkv = 2, 2, 1
+    d = dict(q=rng.standard_normal((B, T, H, 64)).astype(np.float32),
+             k=rng.standard_normal((B, S, Hkv, 64)).astype(np.float32),
+             v=rng.standard_normal((B, S, Hkv, 64)).astype(np.float32), dtype="f32")
+    run_and_compare(f"tiny causal={causal} S={S} T={T}", d, causal, H, Hkv, 64, 64, n_out=2 if causal else 0)
+
+
+@pytest.mark.parametrize("B,T", [(0, 8), (2, 0)])
+def test_empty_batch_or_queries(B, T):
+    """B = 0 or T = 0: the call succeeds and touches nothing."""
+    from sub_quadratic_attention_amd.binding import ThinAttention
+    ta = ThinAttention(64, 64, 1, 1, torch.float32)
+    S = 16
+    q = torch.zeros((B, T, 1, 64), device="cuda")
+    k = torch.zeros((B, S, 1, 64), device="cuda")
+    v = torch.zeros((B, S, 1, 64), device="cuda")
+    out = ta.forward(q, k, v, causal=False)
+    torch.cuda.synchronize()
+    assert out.shape == (B, T, 1, 64)
