@@ -111,8 +111,12 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt):
         # (it reads each point of the level once: HBM-bound), the others on
         # the pair-Gram tiles
         small = lambda N: N <= 16 and E % 32 == 0 and D % 32 == 0
+        # bins of 20-32 points: one workgroup per bin, Gram and walk fused (fp64 MFMA)
+        medium = lambda N: 16 < N <= 32 and N % 4 == 0 and E % 32 == 0 and D % 32 == 0 and \
+            N * ((E + D) * elt + 16) <= 96 * 1024
         levels = [(S // (s0 * 4 ** l), s0 * 2 ** (l + 1)) for l in range(1, j + 1)]   # (bins, N) per unit
-        gram_entries = sum(bins * N * (N + 1) // 2 for bins, N in levels if not small(N))
+        gram_entries = sum(bins * N * (N + 1) // 2 for bins, N in levels if not small(N) and not medium(N))
+        medium_entries = sum(bins * N * (N + 1) // 2 for bins, N in levels if medium(N))
         small_bytes = units * sum(bins * N * (E + D) * elt + bins * (N // 2) * 5 for bins, N in levels if small(N))
         keys = n_out
         pairs_eff = B * H * T * S
@@ -124,6 +128,7 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt):
             n_out *= 2
         gram_entries = express_gram_entries(S, n_out)
         small_bytes = 0
+        medium_entries = 0
         pairs_eff = B * H * T * (T + 1) // 2
         visible = B * H * express_visible_total(S, n_out)
         attn_bytes = (B * T * H * E + units * S * (E + D) + B * T * H * D) * elt
@@ -133,6 +138,7 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt):
         attention=dict(flops=2.0 * visible * (E + D), bytes=attn_bytes),
         pair_gram=dict(flops=2.0 * (E + D) * gram_entries * units, bytes=None) if gram_entries else None,
         small_halving=dict(flops=None, bytes=small_bytes) if small_bytes else None,
+        medium_halving=dict(flops=2.0 * (E + D) * medium_entries * units, bytes=None) if medium_entries else None,
     )
 
 
@@ -350,7 +356,7 @@ def main():
                     "frac": round(gbs / PEAK["hbm_GBs"], 4), "traffic": None, "kernel": label,
                     "work_per_launch_bytes": per_launch_bytes, "avg_launch_ms": r["avg_ms"]}
         per_launch_flops = w["flops"] / r["launches_per_step"]
-        peak_key = "f64" if label == "pair_gram" else dt
+        peak_key = "f64" if label in ("pair_gram", "medium_halving") else dt
         achieved = per_launch_flops / (r["avg_ms"] * 1e-3) / 1e12
         res = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK[peak_key], "unit": "TFLOP/s",
                "frac": round(achieved / PEAK[peak_key], 4), "traffic": None, "kernel": label,

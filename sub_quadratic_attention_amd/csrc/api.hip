@@ -166,6 +166,9 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
         if (thin::small_halving_supported(N, c.E, c.D)) {   // small bins: Gram and walk in one kernel
           THIN_HIP(timed(h, st, "small_halving",
                          [&] { return thin::launch_small_halving(gram_for(sl, src, h->scale64), sl, st); }));
+        } else if (thin::medium_halving_supported(N, c.E, c.D, bf16)) {   // one workgroup per bin
+          THIN_HIP(timed(h, st, "medium_halving",
+                         [&] { return thin::launch_medium_halving(gram_for(sl, src, h->scale64), sl, st); }));
         } else {
           THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
           THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, st); }));

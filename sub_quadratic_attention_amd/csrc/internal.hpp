@@ -146,6 +146,9 @@ hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s);
 // GramLaunch / SweepLaunch pair in one kernel (same outputs as the two).
 bool small_halving_supported(int N, int E, int D);
 hipError_t launch_small_halving(const GramLaunch& g, const SweepLaunch& a, hipStream_t s);
+// Bins of 20 to 32 points: the same in one workgroup per bin.
+bool medium_halving_supported(int N, int E, int D, int bf16);
+hipError_t launch_medium_halving(const GramLaunch& g, const SweepLaunch& a, hipStream_t s);
 hipError_t launch_iota(int32_t* out, int64_t units, int64_t n, int64_t stride, hipStream_t s);
 hipError_t launch_express_reps(const ExpressView& ev, int units, uint64_t seed, int32_t* reps, hipStream_t s);
 hipError_t launch_halve_input(const ExpressView& ev, int units, int e, int32_t* halve_in, hipStream_t s);

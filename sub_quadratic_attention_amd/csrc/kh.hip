@@ -999,6 +999,151 @@ __global__ __launch_bounds__(256) void small_halving_kernel(GramLaunch g, SweepL
   }
 }
 
+// ---------------------------------------------------------------------------
+// Bins of 20 to 32 points (a multiple of 4): one workgroup per bin.  The
+// bin's rows go to LDS (one spare 16-byte piece per row spreads the operand
+// reads over the banks); its point Gram is formed in 4 x 4 blocks of quads,
+// the upper triangle of the quad grid, four blocks per fp64 MFMA 4x4x4 (block
+// b of lane 16 k + 4 b + j: A = its row quad's point j, B = its column quad's
+// point j), the blocks dealt round-robin to the waves; kappa goes to LDS for
+// (i, j) and (j, i).  Wave 0 then runs the walk exactly as the small sweep.
+// ---------------------------------------------------------------------------
+constexpr int kMediumN = 32;   // (64-point bins ran faster on the tiles)
+
+// Eight features at p (LDS), widened.
+template <bool BF16>
+__device__ __forceinline__ void medium_features(const lds_byte* p, double x[8]) {
+  typedef __attribute__((address_space(3))) const u32x4_t lds_u4;
+  if constexpr (BF16) {
+    const u32x4_t w = *reinterpret_cast<lds_u4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = static_cast<double>(__uint_as_float(w[j] << 16));
+      x[2 * j + 1] = static_cast<double>(__uint_as_float(w[j] & 0xffff0000u));
+    }
+  } else {
+    const u32x4_t w0 = reinterpret_cast<lds_u4*>(p)[0], w1 = reinterpret_cast<lds_u4*>(p)[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = static_cast<double>(__uint_as_float(w0[j]));
+      x[4 + j] = static_cast<double>(__uint_as_float(w1[j]));
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void medium_halving_kernel(GramLaunch g, SweepLaunch a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_rows[];
+  __shared__ double s_kap[kMediumN][kMediumN + 1];
+  const int N = g.N, P = N / 2, Q = N / 4;
+  const int z = blockIdx.x;
+  const int unit = z / g.bins_per_unit, lb = z % g.bins_per_unit;
+  const int b = unit / g.src.H_kv, h = unit % g.src.H_kv;
+  const int elt = BF16 ? 2 : 4;
+  const int KP = g.src.E * elt / 16, VP = g.src.D * elt / 16;   // 16-byte pieces of a K / V row
+  const int RS = (KP + VP + 1) * 16;                            // staged row stride (bytes)
+  lds_byte* rows = (lds_byte*)s_rows;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  // the bin's rows into LDS, up to 16 pieces per thread in flight
+  {
+    const int32_t* list = g.idx + static_cast<int64_t>(unit) * g.idx_unit_stride + static_cast<int64_t>(lb) * g.idx_stride;
+    const uint4* K = static_cast<const uint4*>(g.src.k);
+    const uint4* V = static_cast<const uint4*>(g.src.v);
+    const int pieces = N * (KP + VP);
+    for (int x0 = 0; x0 < pieces; x0 += 16 * 256) {
+      uint4 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int x = min(x0 + 256 * i + tid, pieces - 1);
+        const int pt = x / (KP + VP), c = x % (KP + VP);
+        const int64_t row = (static_cast<int64_t>(b) * g.src.S + list[pt]) * g.src.H_kv + h;
+        v[i] = c < KP ? K[row * KP + c] : V[row * VP + (c - KP)];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int x = x0 + 256 * i + tid;
+        if (x < pieces) {
+          const int pt = x / (KP + VP), c = x % (KP + VP);
+          *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(rows + pt * RS + 16 * c) = u32x4_t{v[i].x, v[i].y, v[i].z, v[i].w};
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // kappa of the upper quad blocks
+  {
+    const int nblk = Q * (Q + 1) / 2, ngroups = (nblk + 3) / 4;
+    const int m = lane >> 4, beta = (lane >> 2) & 3, j = lane & 3;
+    for (int gi = w; gi < ngroups; gi += 4) {
+      const int blk = min(4 * gi + beta, nblk - 1);   // (spare blocks of the last group repeat the last one)
+      int rq = 0, rem = blk;
+      while (rem >= Q - rq) {
+        rem -= Q - rq;
+        ++rq;
+      }
+      const int cq = rq + rem;
+      const lds_byte* pa = rows + (4 * rq + j) * RS + m * 8 * elt;   // feature blocks 4 t + m of eight
+      const lds_byte* pb = rows + (4 * cq + j) * RS + m * 8 * elt;
+      double kd[2] = {0.0, 0.0}, vd[2] = {0.0, 0.0};
+      for (int t = 0; t < g.src.E / 32; ++t) {
+        double xa[8], xb[8];
+        medium_features<BF16>(pa + t * 32 * elt, xa);
+        medium_features<BF16>(pb + t * 32 * elt, xb);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) kd[f & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(xa[f], xb[f], kd[f & 1], 0, 0, 0);
+      }
+      for (int t = 0; t < g.src.D / 32; ++t) {
+        double xa[8], xb[8];
+        medium_features<BF16>(pa + KP * 16 + t * 32 * elt, xa);
+        medium_features<BF16>(pb + KP * 16 + t * 32 * elt, xb);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) vd[f & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(xa[f], xb[f], vd[f & 1], 0, 0, 0);
+      }
+      // D[m][n] of block beta sits in lane 16 m + 4 beta + n: points (4 rq + m, 4 cq + n)
+      const double kap = exp_f64(g.scale * (kd[0] + kd[1])) * ((vd[0] + vd[1]) + 1.0);
+      if (4 * gi + beta < nblk) {
+        s_kap[4 * rq + m][4 * cq + j] = kap;
+        s_kap[4 * cq + j][4 * rq + m] = kap;
+      }
+    }
+  }
+  __syncthreads();
+  if (w != 0) return;   // the walk: one wave
+
+  auto gpair = [&](int r, int c) -> double {   // pair-Gram entry (row pair r, column pair c)
+    return (s_kap[2 * r][2 * c] - s_kap[2 * r][2 * c + 1]) - (s_kap[2 * r + 1][2 * c] - s_kap[2 * r + 1][2 * c + 1]);
+  };
+  const bool mine = lane < P;
+  double gc[kMediumN / 2];
+#pragma unroll
+  for (int j = 0; j < kMediumN / 2; ++j) gc[j] = (mine && j < lane) ? gpair(j, lane) : 0.0;
+  const double u = mine ? philox_uniform(static_cast<uint64_t>(lane), a.bin_base + lb, static_cast<uint64_t>(unit),
+                                         a.tag, a.seed)
+                        : 0.0;
+  const double b2 = mine ? fmax(gpair(lane, lane), 0.0) : 0.0;
+  const double c = sqrt(2.0 * log(2.0 * a.N / a.delta));
+  double s2 = 0.0;
+  const double thr = threshold(sigma_steps(s2, b2, sqrt(b2), P, c, 1.0 + 1.0 / (c * c), 2.0 / c), u);
+  double alpha = 0.0;
+  uint64_t bits = 0;
+#pragma unroll
+  for (int j = 0; j < kMediumN / 2; ++j) {
+    if (j >= P) continue;   // uniform
+    const uint64_t mb = __ballot(alpha < thr);
+    const bool first = (mb >> j) & 1ull;
+    bits |= static_cast<uint64_t>(first) << j;
+    alpha += first ? gc[j] : -gc[j];
+  }
+  if (mine) {
+    const bool first = (bits >> lane) & 1ull;
+    const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
+    a.idx_out[static_cast<int64_t>(z) * a.out_stride + lane] = in[2 * lane + (first ? 0 : 1)];
+    if (a.dec) a.dec[static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) + lane] = first ? 1 : 0;
+  }
+}
+
 inline unsigned grid1d(int64_t n, int block) { return static_cast<unsigned>((n + block - 1) / block); }
 
 }  // namespace
@@ -1065,6 +1210,41 @@ hipError_t launch_small_halving(const GramLaunch& g, const SweepLaunch& a, hipSt
     hipLaunchKernelGGL(small_halving_kernel<true>, grid, dim3(256), 0, s, g, a);
   else
     hipLaunchKernelGGL(small_halving_kernel<false>, grid, dim3(256), 0, s, g, a);
+  return hipGetLastError();
+}
+
+static size_t medium_rows_lds(int N, int E, int D, int bf16) {
+  const int elt = bf16 ? 2 : 4;
+  return static_cast<size_t>(N) * ((E + D) * elt + 16);
+}
+
+bool medium_halving_supported(int N, int E, int D, int bf16) {
+  return N > kSmallN && N <= kMediumN && N % 4 == 0 && E % 32 == 0 && D % 32 == 0 &&
+         medium_rows_lds(N, E, D, bf16) <= 96 * 1024;
+}
+
+hipError_t launch_medium_halving(const GramLaunch& g, const SweepLaunch& a, hipStream_t s) {
+  if (!medium_halving_supported(g.N, g.src.E, g.src.D, g.src.bf16) || g.N != a.N || g.nbins != a.nbins ||
+      g.bins_per_unit != a.bins_per_unit)
+    return hipErrorInvalidValue;
+  if (g.nbins == 0) return hipSuccess;
+  const size_t lds = medium_rows_lds(g.N, g.src.E, g.src.D, g.src.bf16);
+  if (lds > 64 * 1024) {
+    static bool set[64][2];   // once per device and element type (for the largest size)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!set[dev][g.src.bf16 ? 1 : 0]) {
+      const void* fn = g.src.bf16 ? reinterpret_cast<const void*>(medium_halving_kernel<true>)
+                                  : reinterpret_cast<const void*>(medium_halving_kernel<false>);
+      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+      if (e != hipSuccess) return e;
+      set[dev][g.src.bf16 ? 1 : 0] = true;
+    }
+  }
+  if (g.src.bf16)
+    hipLaunchKernelGGL(medium_halving_kernel<true>, dim3(g.nbins), dim3(256), lds, s, g, a);
+  else
+    hipLaunchKernelGGL(medium_halving_kernel<false>, dim3(g.nbins), dim3(256), lds, s, g, a);
   return hipGetLastError();
 }
 

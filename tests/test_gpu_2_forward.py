@@ -62,6 +62,20 @@ def test_unmasked_small_bins(S, dtype):
     run_and_compare(f"unmasked small bins S={S} {dtype}", d, False, H, Hkv, 64, D)
 
 
+@pytest.mark.parametrize("S,dtype", [(80, "f32"), (192, "bf16"), (1024, "bf16")])
+def test_unmasked_medium_bins(S, dtype):
+    """Bins of 20-32 points (one workgroup per bin, Gram and walk fused) beside the other
+    paths: S=80 gives 20- and 40-point bins, S=192 12-, 24- and 48-point bins, S=1024 4- to
+    64-point bins; six units."""
+    rng = np.random.default_rng(7 + S)
+    B, T, H, Hkv = 3, 29, 2, 2
+    cast = inputs.bf16_round if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    D = 128 if dtype == "bf16" else 64
+    d = dict(q=cast(rng.standard_normal((B, T, H, 64)) * 0.5), k=cast(rng.standard_normal((B, S, Hkv, 64)) * 0.5),
+             v=cast(rng.standard_normal((B, S, Hkv, D))), dtype=dtype)
+    run_and_compare(f"unmasked medium bins S={S} {dtype}", d, False, H, Hkv, 64, D)
+
+
 def test_vit_token_mixing_reduced():
     """56x56 ViT tokens (S=3136, n_out=392), two batch entries, sampled outputs."""
     d = inputs.vit_token_mixing(seed=0, B=2)
