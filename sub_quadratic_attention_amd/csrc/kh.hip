@@ -821,28 +821,28 @@ __global__ void philox_words_kernel(const uint64_t* ctr, int64_t n, uint64_t see
 // ---------------------------------------------------------------------------
 constexpr int kSmallN = 16;   // points per tile (and largest bin of the fused path)
 
+
+// Eight features of one point kept raw (bf16: one 16-byte load, fp32: two)
+// until their MFMAs, then widened one at a time.
 template <bool BF16>
-__device__ __forceinline__ void small_features(const unsigned char* p, double x[8]) {
-  if constexpr (BF16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = static_cast<double>(__uint_as_float(v[j] << 16));
-      x[2 * j + 1] = static_cast<double>(__uint_as_float(v[j] & 0xffff0000u));
-    }
-  } else {
-    const uint4 w0 = reinterpret_cast<const uint4*>(p)[0], w1 = reinterpret_cast<const uint4*>(p)[1];
-    const uint32_t v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = static_cast<double>(__uint_as_float(v[j]));
+struct SmallRaw {
+  u32x4_t w[BF16 ? 1 : 2];
+  __device__ __forceinline__ void load(const unsigned char* p) {
+    w[0] = *reinterpret_cast<const u32x4_t*>(p);
+    if constexpr (!BF16) w[1] = *reinterpret_cast<const u32x4_t*>(p + 16);
   }
-}
+  __device__ __forceinline__ double operator[](int f) const {
+    if constexpr (BF16) return static_cast<double>(__uint_as_float((f & 1) ? (w[0][f >> 1] & 0xffff0000u) : (w[0][f >> 1] << 16)));
+    else return static_cast<double>(__uint_as_float(w[f >> 2][f & 3]));
+  }
+};
+constexpr int kSmallBatch = 8;   // loads of eight features in flight per lane
 
 // <x_i, x_j> over the F features of row `row` of every point: lane l takes
 // the blocks of eight features 4 g + l / 16 of its point, one per load (F a
-// multiple of 32; the four lanes of a point read 64 contiguous bytes).  Loads go out four at a time before their MFMAs, and
-// four accumulators keep four MFMAs in flight.
+// multiple of 32; the four lanes of a point read 64 contiguous bytes).
+// Loads go out kSmallBatch at a time before their MFMAs, and four
+// accumulators keep four MFMAs in flight.
 template <bool BF16>
 __device__ __forceinline__ f64x4_t small_gram(const unsigned char* row, int F) {
   const int quarter = (threadIdx.x & 63) >> 4;
@@ -850,15 +850,18 @@ __device__ __forceinline__ f64x4_t small_gram(const unsigned char* row, int F) {
   const unsigned char* p = row + quarter * 8 * elt;   // lane quarter q: feature blocks 4 g + q of 8
   const int groups = F / 32;   // loads of eight features per lane
   f64x4_t acc[4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
-  for (int g0 = 0; g0 < groups; g0 += 4) {
-    double x[4][8];
+  for (int g0 = 0; g0 < groups; g0 += kSmallBatch) {
+    SmallRaw<BF16> x[kSmallBatch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) small_features<BF16>(p + min(g0 + j, groups - 1) * 32 * elt, x[j]);   // (repeats are not used)
+    for (int j = 0; j < kSmallBatch; ++j) x[j].load(p + min(g0 + j, groups - 1) * 32 * elt);   // (repeats are not used)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kSmallBatch; ++j) {
       if (g0 + j >= groups) break;   // uniform
 #pragma unroll
-      for (int f = 0; f < 8; ++f) acc[f & 3] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[j][f], x[j][f], acc[f & 3], 0, 0, 0);
+      for (int f = 0; f < 8; ++f) {
+        const double v = x[j][f];
+        acc[f & 3] = __builtin_amdgcn_mfma_f64_16x16x4f64(v, v, acc[f & 3], 0, 0, 0);
+      }
     }
   }
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
@@ -877,22 +880,24 @@ __device__ __forceinline__ void small_gram44(const unsigned char* row, const uns
   const int elt = BF16 ? 2 : 4;
   const int off = quarter * 8 * elt;   // feature blocks 4 g + quarter of 8, as in small_gram
   const int groups = F / 32;
+  constexpr int BATCH = PAIR ? kSmallBatch / 2 : kSmallBatch;
   double a0[2] = {0.0, 0.0}, a1[2] = {0.0, 0.0};
-  for (int g0 = 0; g0 < groups; g0 += 4) {
-    double x[4][8], y[4][8];
+  for (int g0 = 0; g0 < groups; g0 += BATCH) {
+    SmallRaw<BF16> x[BATCH], y[BATCH];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < BATCH; ++j) {
       const int gj = min(g0 + j, groups - 1);   // (repeats are not used)
-      small_features<BF16>(row + off + gj * 32 * elt, x[j]);
-      if constexpr (PAIR) small_features<BF16>(prow + off + gj * 32 * elt, y[j]);
+      x[j].load(row + off + gj * 32 * elt);
+      if constexpr (PAIR) y[j].load(prow + off + gj * 32 * elt);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < BATCH; ++j) {
       if (g0 + j >= groups) break;   // uniform
 #pragma unroll
       for (int f = 0; f < 8; ++f) {
-        a0[f & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(x[j][f], x[j][f], a0[f & 1], 0, 0, 0);
-        if constexpr (PAIR) a1[f & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(x[j][f], y[j][f], a1[f & 1], 0, 0, 0);
+        const double v = x[j][f];
+        a0[f & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(v, v, a0[f & 1], 0, 0, 0);
+        if constexpr (PAIR) a1[f & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(v, y[j][f], a1[f & 1], 0, 0, 0);
       }
     }
   }
