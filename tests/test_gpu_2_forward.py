@@ -37,6 +37,13 @@ def test_unmasked_disabled_is_exact():
     assert s["decisions"] == 0
 
 
+def test_unmasked_oversampling():
+    """Oversampling g = 1: Compress stops one level earlier (S=256: n_out 32 instead of 16)."""
+    d = inputs.unmasked_small(seed=2)
+    s = run_and_compare("unmasked g=1", d, False, 1, 1, 64, 64, g=1)
+    assert s["decisions"] > 0
+
+
 def test_unmasked_ragged_and_gqa():
     """S = 4^2 * 13 (base blocks of 13), T ragged, 2 query heads per KV head, bf16."""
     rng = np.random.default_rng(3)

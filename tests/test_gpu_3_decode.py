@@ -138,3 +138,33 @@ def test_kv_decode_full_size_window():
     """The 131k-token, 8-KV-head state (n_out 512) and 1024 decode steps; every output checked."""
     d = inputs.kv_decode(seed=0)
     _check("kv_decode S0=131072 x 1024 steps", d, 512, 32, 8, 128, 128)
+
+
+def test_long_generation():
+    """Long generation: 8000 decode steps after a 16-token history with n_out = 128 cross two
+    HALVEs and many batch halvings per KV head; every output and decision is checked."""
+    d = _stream(6, 16, 8000, Hkv=2, H=4, E=64, D=64)
+    _check("long generation n_out=128", d, 128, 4, 2, 64, 64)
+
+
+def test_decode_cache_size_curve():
+    """Cache size against error: 500 decode steps with n_out = 16, 32, 64 (two, one and one
+    HALVE); each stream matches the replayed oracle, and the error against exact causal
+    attention falls as the cache grows."""
+    S0, steps, H, Hkv = 16, 500, 4, 2
+    d = _stream(7, S0, steps, Hkv=Hkv, H=H, E=64, D=64)
+    k = np.concatenate([d["k_hist"], d["k_steps"]], axis=1)
+    v = np.concatenate([d["v_hist"], d["v_steps"]], axis=1)
+    B = k.shape[0]
+    rows = np.array([(b, S0 + i, h) for b in range(B) for i in range(steps) for h in range(H)])
+    q = np.zeros((B, S0 + steps, H, 64))
+    q[:, S0:] = d["q_steps"]
+    exact = fwd.exact(q, k, v, causal=True, queries=rows).reshape(B, steps, H, 64)
+    sizes = (16, 32, 64)
+    errs = []
+    for n in sizes:
+        out = _check(f"decode n_out={n}", d, n, H, Hkv, 64, 64)
+        errs.append(att.rel_frobenius_error(out, exact))
+    say("[decode] cache size vs error (relative Frobenius against exact): " +
+        ", ".join(f"n_out={n}: {e:.4f}" for n, e in zip(sizes, errs)))
+    assert errs[2] < errs[1] < errs[0]
