@@ -142,14 +142,14 @@ def test_kv_decode_full_size_window():
 
 def test_long_generation():
     """Long generation: 8000 decode steps after a 16-token history with n_out = 128 cross two
-    HALVEs and many batch halvings per KV head; every output and decision is checked."""
+    HALVEs and five batch halvings per KV head; every output and decision is checked."""
     d = _stream(6, 16, 8000, Hkv=2, H=4, E=64, D=64)
     _check("long generation n_out=128", d, 128, 4, 2, 64, 64)
 
 
 def test_decode_cache_size_curve():
-    """Cache size against error: 500 decode steps with n_out = 16, 32, 64 (two, one and one
-    HALVE); each stream matches the replayed oracle, and the error against exact causal
+    """Cache size against error: 500 decode steps with n_out = 16, 32, 64 (two, two and one
+    HALVEs); each stream matches the replayed oracle, and the error against exact causal
     attention falls as the cache grows."""
     S0, steps, H, Hkv = 16, 500, 4, 2
     d = _stream(7, S0, steps, Hkv=Hkv, H=H, E=64, D=64)
