@@ -33,6 +33,7 @@ WORKLOADS = {
     "biggan_self_attention": (dict(), False, 1, 1, 64, 256),
     "causal_prefill": (dict(), True, 32, 32, 128, 128),
     "kv_decode": (dict(), True, 32, 8, 128, 128),
+    "selected_keys": (dict(), False, 32, 8, 128, 128),   # thinning after a KV selector (top 4096 of 32768 keys)
 }
 
 
@@ -308,12 +309,22 @@ def main():
     B, T = q.shape[:2]
     S = k.shape[1]
     ta = ThinAttention(E, D, H, Hkv, tdt)
-    ws = ta.workspace(B, T, S, causal)
     out = torch.empty((B, T, H, D), dtype=tdt, device="cuda")
     stream = torch.cuda.current_stream()
+    sel = d.get("key_idx")   # thinning after a selector: the list is the point set (L keys per unit)
+    if sel is not None:
+        key_idx = torch.from_numpy(sel).cuda()
+        L = sel.shape[2]
+        ws = ta.workspace(B, T, L, False)
 
-    def step():
-        ta.forward(q, k, v, causal=causal, seed=0, workspace=ws, out=out, stream=stream)
+        def step():
+            ta.forward_subset(q, k, v, key_idx, seed=0, workspace=ws, out=out, stream=stream)
+    else:
+        L = S
+        ws = ta.workspace(B, T, S, causal)
+
+        def step():
+            ta.forward(q, k, v, causal=causal, seed=0, workspace=ws, out=out, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -332,7 +343,7 @@ def main():
     recs = ta.timing_records()
     ta.set_timing(False)
 
-    wm = work_model(args.workload, B, T, S, H, Hkv, E, D, causal, elt)
+    wm = work_model(args.workload, B, T, L, H, Hkv, E, D, causal, elt)   # (a selector's list: its L keys)
     per_kernel = {}
     for label, ms in recs:
         r = per_kernel.setdefault(label, dict(launches=0, total_ms=0.0))
@@ -376,6 +387,9 @@ def main():
     # exact comparators on the same GPU
     exact = {}
     if not args.no_exact:
+        if sel is not None:   # exact attention over the selected keys
+            gi = key_idx.long().permute(0, 2, 1)[..., None]
+            k, v = (torch.gather(x, 1, gi.expand(-1, -1, -1, x.shape[3])) for x in (k, v))
         qt, kt, vt = (x.permute(0, 2, 1, 3).contiguous() for x in (q, k, v))
         if Hkv != H:
             kt = kt.repeat_interleave(H // Hkv, dim=1)
@@ -391,7 +405,7 @@ def main():
         torch.cuda.synchronize()
         exact["sdpa_ms"] = (time.perf_counter() - a) * 1e3 / n_ex
         del qt, kt, vt
-        if not causal:
+        if not causal and sel is None:
             ex = ThinAttention(E, D, H, Hkv, tdt)
             for _ in range(2):
                 ex.coreset_attention(q, k, v, out=out)
@@ -418,6 +432,16 @@ def main():
                 a = time.perf_counter()
                 ofwd.forward(sub["q"], sub["k"], sub["v"], causal=True, queries=rows)
                 sec = time.perf_counter() - a
+        elif sel is not None:
+            hk = min(Hkv, 2)
+            g = H // Hkv
+            sub = dict(q=d["q"][:, :, :hk * g], k=d["k"][:, :, :hk], v=d["v"][:, :, :hk])
+            pairs = B * hk * g * T * L
+            desc = f"{hk} of {Hkv} KV heads ({hk * g} query heads), every query (thinning + attention)"
+            with threadpool_limits(1):
+                a = time.perf_counter()
+                ofwd.forward_subset(sub["q"], sub["k"], sub["v"], sel[:, :hk])
+                sec = time.perf_counter() - a
         else:
             nb = B if args.workload != "biggan_self_attention" else min(B, 8)
             sub = {x: d[x][:nb] for x in ("q", "k", "v")}
@@ -443,8 +467,8 @@ def main():
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "H": H, "H_kv": Hkv, "T": T, "S": S, "E": E, "D": D,
-                   "causal": causal, "n_out": wm["n_out"], "seed": 0},
+        "config": dict({"workload": args.workload, "B": B, "H": H, "H_kv": Hkv, "T": T, "S": S, "E": E, "D": D,
+                        "causal": causal, "n_out": wm["n_out"], "seed": 0}, **({"L": L} if sel is not None else {})),
         "kernels": {l: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                     for l, r in per_kernel.items()},
         "roofline": roofline,

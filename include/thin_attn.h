@@ -140,6 +140,31 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Unmasked Thinformer attention over a caller-chosen subset of the keys
+ * (thinning after a KV selector: the "Express Language Modeling" explainer
+ * on gist.science, "Experimental Results", accelerated KV cache compression,
+ * where the thinning step is decoupled from how the initial keys were
+ * chosen).  Unit (b, h_kv) thins the L keys key_idx[unit * L + i] (token
+ * indices into k / v, each in [0, S), in the order given; any order and
+ * repeats allowed) exactly as thin_attn_forward thins S keys in token order:
+ * the Compress recursion over list positions, with the coreset size rule,
+ * decision layout and Philox streams of an unmasked forward with S = L.
+ * Every query then attends to that coreset.  key_idx is read on the device;
+ * entries outside [0, S) are not detected (out-of-range reads).
+ *
+ * Sizes: as thin_attn_forward (unmasked) for S, and L >= 1.  The workspace
+ * is thin_attn_workspace_size(h, B, T, L, 0) bytes; the optional outputs
+ * have the shapes of an unmasked forward with S = L (capacity
+ * thin_attn_coreset_capacity(h, L, 0), decision_count(h, L, 0)) and hold
+ * token indices into k / v.
+ */
+int thin_attn_forward_subset(thin_attn_t* h, const void* q, const void* k, const void* v,
+                             const int32_t* key_idx, int64_t B, int64_t T, int64_t S, int64_t L,
+                             uint64_t seed, void* out, int32_t* coreset_idx, float* coreset_w,
+                             int32_t* coreset_len, uint8_t* decisions,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Weighted-coreset attention alone (no thinning): every query of unit
  * (b, h_kv) attends to the n keys idx[unit * n + j] (token indices into k / v,
  * each in [0, S)) with weights w[unit * n + j] > 0 (w may be NULL: weight 1).

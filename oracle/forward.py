@@ -99,6 +99,52 @@ def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
     return {"out": out, "coreset": coreset, "log": logs, "stats": stats, "n_out": size}
 
 
+def forward_subset(q, k, v, key_idx, seed=0, scale=None, g=0, delta=0.5, queries=None, decisions=None,
+                   tie_margin=1e-6):
+    """Unmasked Thinformer over a chosen key list per unit (thinning after a KV
+    selector: the "Express Language Modeling" explainer on gist.science,
+    "Experimental Results", accelerated KV cache compression, where the
+    thinning step no longer depends on how the initial keys were picked).
+
+    key_idx [B, H_kv, L] lists, per unit, token indices into k / v in the order
+    to thin.  The list is the point sequence of an unmasked forward with
+    S = L (the same recursion, size rule, decision layout and random streams);
+    its coreset positions map back to tokens through the list.  Returns the
+    same dict as ``forward``, coreset indices being tokens.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    key_idx = np.asarray(key_idx, dtype=np.int64)
+    B, T, H, E = q.shape
+    _, S, Hkv, _ = k.shape
+    D = v.shape[3]
+    L = key_idx.shape[2]
+    assert key_idx.shape == (B, Hkv, L) and key_idx.min() >= 0 and key_idx.max() < S
+    group = H // Hkv
+    s = 1.0 / math.sqrt(E) if scale is None else float(scale)
+    if queries is None:
+        want = [(b, t, h) for b in range(B) for t in range(T) for h in range(H)]
+    else:
+        want = [tuple(int(x) for x in row) for row in np.asarray(queries).reshape(-1, 3)]
+    stats = khm.HalvingStats()
+    coreset, logs = {}, {}
+    for b in range(B):
+        for hk in range(Hkv):
+            unit = b * Hkv + hk
+            sel = key_idx[b, hk]
+            ov = None if decisions is None else cmp.flat_to_log(decisions[unit], L, g)
+            pos, w, log = cmp.thin_unmasked(k[b, sel, hk, :], v[b, sel, hk, :], s, delta, seed, unit, g,
+                                            override=ov, stats=stats)
+            coreset[unit] = (sel[pos], np.full(len(pos), w))
+            logs[unit] = cmp.log_to_flat(log, L, g)
+    results = np.zeros((len(want), D))
+    for n, (b, t, h) in enumerate(want):
+        tok, w = coreset[b * Hkv + h // group]
+        results[n] = att.weighted_attention(q[b, t, h][None, :], k[b, tok, h // group, :], v[b, tok, h // group, :],
+                                            w, s)[0]
+    out = results.reshape(B, T, H, D) if queries is None else results
+    return {"out": out, "coreset": coreset, "log": logs, "stats": stats, "n_out": cmp.coreset_size(L, g)}
+
+
 def exact(q, k, v, causal=False, scale=None, queries=None):
     """Exact softmax attention with the same conventions (GQA, sampling)."""
     q, k, v = _as64(q), _as64(k), _as64(v)

@@ -45,6 +45,8 @@ _SIGNATURES = {
     "thin_attn_forward": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3
                           + [ctypes.c_int, ctypes.c_uint64] + [ctypes.c_void_p] * 6
                           + [ctypes.c_size_t, ctypes.c_void_p]),
+    "thin_attn_forward_subset": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 4
+                                 + [ctypes.c_uint64] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
     "thin_attn_coreset_attention": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 3
                                     + [ctypes.c_int64] * 3 + [ctypes.c_void_p, ctypes.c_void_p,
                                                               ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
@@ -203,6 +205,42 @@ class ThinAttention:
             extra.update(coreset_idx=idx, coreset_w=w, coreset_len=ln)
         if return_decisions:
             extra["decisions"] = dec[:, :self.decision_count(S, causal)]
+        return (out, extra) if extra else out
+
+    def forward_subset(self, q, k, v, key_idx, seed=0, return_coreset=False, return_decisions=False,
+                       workspace=None, out=None, stream=None):
+        """Unmasked attention against the coreset of a chosen key list per unit:
+        key_idx [B, H_kv, L] int32 token indices into k / v (thin_attn_forward_subset)."""
+        q, k, v = self._inputs(q, k, v)
+        B, T = q.shape[:2]
+        S = k.shape[1]
+        key_idx = key_idx.to(torch.int32).contiguous()
+        if key_idx.dim() != 3 or key_idx.shape[:2] != (B, self.H_kv):
+            raise ValueError(f"key_idx must be [B, H_kv, L] = [{B}, {self.H_kv}, L]; got {tuple(key_idx.shape)}")
+        L = key_idx.shape[2]
+        units = B * self.H_kv
+        dev = q.device
+        if out is None:
+            out = torch.empty((B, T, self.H, self.D), dtype=self.dtype, device=dev)
+        if workspace is None:
+            workspace = self.workspace(B, T, L, False, dev)
+        idx = w = ln = dec = None
+        if return_coreset:
+            cap = self.coreset_capacity(L, False)
+            idx = torch.empty((units, cap), dtype=torch.int32, device=dev)
+            w = torch.empty((units, cap), dtype=torch.float32, device=dev)
+            ln = torch.empty((units,), dtype=torch.int32, device=dev)
+        if return_decisions:
+            dec = torch.empty((units, max(self.decision_count(L, False), 1)), dtype=torch.uint8, device=dev)
+        rc = self.lib.thin_attn_forward_subset(self.h, _ptr(q), _ptr(k), _ptr(v), _ptr(key_idx), B, T, S, L,
+                                               ctypes.c_uint64(seed), _ptr(out), _ptr(idx), _ptr(w), _ptr(ln),
+                                               _ptr(dec), _ptr(workspace), workspace.numel(), _stream(stream))
+        self._check(rc)
+        extra = {}
+        if return_coreset:
+            extra.update(coreset_idx=idx, coreset_w=w, coreset_len=ln)
+        if return_decisions:
+            extra["decisions"] = dec[:, :self.decision_count(L, False)]
         return (out, extra) if extra else out
 
     def coreset_attention(self, q, k, v, idx=None, w=None, out=None, stream=None):

@@ -107,6 +107,68 @@ int thin_attn_timing_read(thin_attn_t* h, int64_t i, char* label, size_t label_l
   return THIN_OK;
 }
 
+// Unmasked path: the Compress recursion over a key list per unit (keys ==
+// nullptr: tokens 0 .. L-1 in order, L == S), then coreset attention.
+static int unmasked_path(thin_attn_t* h, const thin::PointSource& src, thin::AttnLaunch& al, const int32_t* keys,
+                         int64_t L, int units, uint64_t seed, uint8_t* decisions, int64_t ndec, char* ws,
+                         hipStream_t st, int32_t* coreset_idx, float* coreset_w, int32_t* coreset_len) {
+  const thin_attn_config& c = h->cfg;
+  const int bf16 = c.dtype == THIN_BF16;
+  const int64_t B = al.B;
+  const UnmaskedPlan p = plan_unmasked(h, B, L);
+  const int32_t* coreset = keys;   // no thinning: the list itself (nullptr: all keys in order)
+  if (p.j > 0) {
+    int32_t* a = reinterpret_cast<int32_t*>(ws + p.off_a);
+    int32_t* b = reinterpret_cast<int32_t*>(ws + p.off_b);
+    double* G = reinterpret_cast<double*>(ws + p.off_g);
+    const int32_t* in = keys;
+    if (!keys) {
+      THIN_HIP(timed(h, st, "iota", [&] { return thin::launch_iota(a, units, L, L, st); }));
+      in = a;
+    }
+    int32_t* outl = b;
+    int64_t dec_base = 0;
+    for (int l = 1; l <= p.j; ++l) {
+      // level l: bins of N = s0 2^(l+1) points; every level's lists are dense [unit][L >> (l-1)]
+      const int N = static_cast<int>(p.s0 << (l + 1));
+      const int bins = static_cast<int>(L / (p.s0 << (2 * l)));
+      const int64_t in_unit = L >> (l - 1);
+      thin::SweepLaunch sl = make_sweep(h, G, N, units, bins, in, in_unit, outl, seed, thin::kTagCompress,
+                                        static_cast<uint64_t>(l) << 20);
+      sl.out_stride = N / 2;
+      sl.dec = decisions;
+      sl.dec_per_unit = ndec;
+      sl.dec_base = dec_base;
+      if (thin::small_halving_supported(N, c.E, c.D)) {   // small bins: Gram and walk in one kernel
+        THIN_HIP(timed(h, st, "small_halving",
+                       [&] { return thin::launch_small_halving(gram_for(sl, src, h->scale64), sl, st); }));
+      } else if (thin::medium_halving_supported(N, c.E, c.D, bf16)) {   // one workgroup per bin
+        THIN_HIP(timed(h, st, "medium_halving",
+                       [&] { return thin::launch_medium_halving(gram_for(sl, src, h->scale64), sl, st); }));
+      } else {
+        THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
+        THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, st); }));
+      }
+      dec_base += static_cast<int64_t>(bins) * (N / 2);
+      in = outl;
+      outl = outl == b ? a : b;
+    }
+    coreset = in;   // the last level's output: dense [unit][n_out]
+  }
+  const int64_t n_cs = p.j > 0 ? p.n_out : L;
+  const float w = static_cast<float>(static_cast<int64_t>(1) << p.j);
+  al.causal = 0;
+  al.cs_idx = coreset;
+  al.cs_w = nullptr;
+  al.cs_n = static_cast<int>(n_cs);
+  al.cs_stride = coreset ? n_cs : 0;
+  al.cs_lnw = coreset ? logf(w) : 0.f;
+  THIN_HIP(timed(h, st, "attention", [&] { return thin::launch_attention(al, bf16, c.E, c.D, st); }));
+  THIN_HIP(thin::launch_fill_coreset(coreset, al.cs_stride, units, static_cast<int>(n_cs), w, coreset_idx, coreset_w,
+                                     coreset_len, st));
+  return THIN_OK;
+}
+
 int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* v, int64_t B, int64_t T, int64_t S,
                       int causal, uint64_t seed, void* out, int32_t* coreset_idx, float* coreset_w,
                       int32_t* coreset_len, uint8_t* decisions, void* workspace, size_t workspace_bytes,
@@ -143,53 +205,9 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
   al.H_kv = c.H_kv;
   al.scale = h->scale;
 
-  if (!causal) {
-    const UnmaskedPlan p = plan_unmasked(h, B, S);
-    const int32_t* coreset = nullptr;
-    if (p.j > 0) {
-      int32_t* a = reinterpret_cast<int32_t*>(ws + p.off_a);
-      int32_t* b = reinterpret_cast<int32_t*>(ws + p.off_b);
-      double* G = reinterpret_cast<double*>(ws + p.off_g);
-      THIN_HIP(timed(h, st, "iota", [&] { return thin::launch_iota(a, units, S, S, st); }));
-      int64_t dec_base = 0;
-      for (int l = 1; l <= p.j; ++l) {
-        // level l: bins of N = s0 2^(l+1) points; every level's lists are dense [unit][S >> (l-1)]
-        const int N = static_cast<int>(p.s0 << (l + 1));
-        const int bins = static_cast<int>(S / (p.s0 << (2 * l)));
-        const int64_t in_unit = S >> (l - 1);
-        thin::SweepLaunch sl = make_sweep(h, G, N, units, bins, a, in_unit, b, seed, thin::kTagCompress,
-                                          static_cast<uint64_t>(l) << 20);
-        sl.out_stride = N / 2;
-        sl.dec = decisions;
-        sl.dec_per_unit = ndec;
-        sl.dec_base = dec_base;
-        if (thin::small_halving_supported(N, c.E, c.D)) {   // small bins: Gram and walk in one kernel
-          THIN_HIP(timed(h, st, "small_halving",
-                         [&] { return thin::launch_small_halving(gram_for(sl, src, h->scale64), sl, st); }));
-        } else if (thin::medium_halving_supported(N, c.E, c.D, bf16)) {   // one workgroup per bin
-          THIN_HIP(timed(h, st, "medium_halving",
-                         [&] { return thin::launch_medium_halving(gram_for(sl, src, h->scale64), sl, st); }));
-        } else {
-          THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
-          THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, st); }));
-        }
-        dec_base += static_cast<int64_t>(bins) * (N / 2);
-        std::swap(a, b);
-      }
-      coreset = a;   // the last level's output: dense [unit][n_out]
-    }
-    const float w = static_cast<float>(static_cast<int64_t>(1) << p.j);
-    al.causal = 0;
-    al.cs_idx = coreset;
-    al.cs_w = nullptr;
-    al.cs_n = static_cast<int>(coreset ? p.n_out : S);
-    al.cs_stride = coreset ? p.n_out : 0;
-    al.cs_lnw = coreset ? logf(w) : 0.f;
-    THIN_HIP(timed(h, st, "attention", [&] { return thin::launch_attention(al, bf16, c.E, c.D, st); }));
-    THIN_HIP(thin::launch_fill_coreset(coreset, al.cs_stride, units, static_cast<int>(p.n_out), w, coreset_idx,
-                                       coreset_w, coreset_len, st));
-    return THIN_OK;
-  }
+  if (!causal)
+    return unmasked_path(h, src, al, nullptr, S, units, seed, decisions, ndec, ws, st, coreset_idx, coreset_w,
+                         coreset_len);
 
   // ---- causal: Thinformer Express ----
   const int64_t nn = cache_size(h, S);
@@ -204,6 +222,41 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
   THIN_HIP(thin::launch_express_final(ev, units, static_cast<int>(S), coreset_idx, coreset_w, coreset_len, 6LL * n,
                                       st));
   return THIN_OK;
+}
+
+int thin_attn_forward_subset(thin_attn_t* h, const void* q, const void* k, const void* v, const int32_t* key_idx,
+                             int64_t B, int64_t T, int64_t S, int64_t L, uint64_t seed, void* out,
+                             int32_t* coreset_idx, float* coreset_w, int32_t* coreset_len, uint8_t* decisions,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h) return THIN_EINVAL;
+  h->err.clear();
+  int rc = check_dims(h, B, T, S, 0);
+  if (rc) return rc;
+  if (L < 1 || L >= (1LL << 30)) return fail(h, THIN_EINVAL, "key list length L must be in [1, 2^30) (got %lld)", (long long)L);
+  if (B * T == 0) return THIN_OK;
+  if (S == 0) return fail(h, THIN_EINVAL, "S must be positive");
+  if (!q || !k || !v || !out || !key_idx) return fail(h, THIN_EINVAL, "null q, k, v, out or key_idx");
+  const size_t need = thin_attn_workspace_size(h, B, T, L, 0);
+  if (need > 256 && (!workspace || workspace_bytes < need))
+    return fail(h, THIN_ENOMEM, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(h, THIN_EINVAL, "workspace must be 256-byte aligned");
+  const thin_attn_config& c = h->cfg;
+  const int units = static_cast<int>(B * c.H_kv);
+  thin::PointSource src{k, v, S, c.H_kv, c.E, c.D, c.dtype == THIN_BF16};
+  thin::AttnLaunch al{};
+  al.q = q;
+  al.k = k;
+  al.v = v;
+  al.out = out;
+  al.B = static_cast<int>(B);
+  al.T = static_cast<int>(T);
+  al.S = static_cast<int>(S);
+  al.H = c.H;
+  al.H_kv = c.H_kv;
+  al.scale = h->scale;
+  return unmasked_path(h, src, al, key_idx, L, units, seed, decisions, thin_attn_decision_count(h, L, 0),
+                       static_cast<char*>(workspace), as_stream(stream), coreset_idx, coreset_w, coreset_len);
 }
 
 int thin_attn_coreset_attention(thin_attn_t* h, const void* q, const void* k, const void* v, int64_t B, int64_t T,

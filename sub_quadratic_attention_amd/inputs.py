@@ -143,12 +143,38 @@ def kv_decode(seed=0, B=1, Hkv=8, H=32, S0=131072, steps=1024, E=128, D=128,
                 v_steps=v[:, S0:], q_steps=q, dtype=dtype, causal=True)
 
 
+def top_k_keys(k, q, L):
+    """Stand-in KV selector (the role SnapKV-style selection plays before thinning): per unit
+    (b, h_kv), the L keys with the largest |<k, mean query of the unit's heads>|, in token order."""
+    B, S, Hkv, E = k.shape
+    group = q.shape[2] // Hkv
+    qm = np.asarray(q, dtype=np.float64).reshape(B, q.shape[1], Hkv, group, E).mean(axis=(1, 3))
+    score = np.abs(np.einsum("bshe,bhe->bhs", np.asarray(k, dtype=np.float64), qm))
+    return np.sort(np.argsort(-score, axis=2, kind="stable")[:, :, :L], axis=2).astype(np.int32)
+
+
+def selected_keys(seed=0, B=1, H=32, Hkv=8, S=32768, T=1024, L=4096, E=128, D=128, dtype="bf16"):
+    """Thinning after a KV selector: an LLM layer's 32k keys (4 outlier channels per head, as
+    in the causal prefill), T queries, and per KV head the top-L keys of the stand-in selector."""
+    rq, rk, rv, rx = _streams(seed, 4)
+    q = rq.standard_normal((B, T, H, E))
+    k = rk.standard_normal((B, S, Hkv, E))
+    for h in range(Hkv):
+        ch = rx.choice(E, 4, replace=False)
+        q[:, :, h * (H // Hkv):(h + 1) * (H // Hkv), ch] *= 8.0
+        k[:, :, h, ch] *= 8.0
+    q, k = _cast(q, dtype), _cast(k, dtype)
+    return dict(q=q, k=k, v=_cast(rv.standard_normal((B, S, Hkv, D)), dtype), key_idx=top_k_keys(k, q, L),
+                dtype=dtype, causal=False)
+
+
 WORKLOADS = {
     "unmasked_small": unmasked_small,
     "vit_token_mixing": vit_token_mixing,
     "biggan_self_attention": biggan_self_attention,
     "causal_prefill": causal_prefill,
     "kv_decode": kv_decode,
+    "selected_keys": selected_keys,
 }
 
 

@@ -5,7 +5,8 @@ import pytest
 import torch
 
 from sub_quadratic_attention_amd import inputs
-from tests.parity import run_and_compare, sample_queries, say
+from oracle import attention as att
+from tests.parity import TOL, run_and_compare, sample_queries, say, to_gpu, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -174,3 +175,42 @@ def test_empty_batch_or_queries(B, T):
     out = ta.forward(q, k, v, causal=False)
     torch.cuda.synchronize()
     assert out.shape == (B, T, 1, 64)
+
+
+# ---- thinning after a KV selector -------------------------------------------
+
+@pytest.mark.parametrize("S,L,dtype", [(4096, 1024, "bf16"), (3000, 768, "f32"), (500, 192, "bf16"),
+                                       (300, 50, "f32")])
+def test_thinning_after_selector(S, L, dtype):
+    """thin_attn_forward_subset on a top-L selection: decisions, coreset (tokens through the
+    list) and outputs against the replayed oracle; L = 50 is too short to thin (the list itself
+    is the coreset), L = 192 and 768 run 12- to 96-point bins, L = 1024 4- to 64-point bins."""
+    from oracle import forward as fwd
+    from sub_quadratic_attention_amd.binding import ThinAttention
+    rng = np.random.default_rng(S + L)
+    B, T, H, Hkv = 2, 33, 4, 2
+    D = 128 if dtype == "bf16" else 64
+    cast = inputs.bf16_round if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    q = cast(rng.standard_normal((B, T, H, 64)) * 0.5)
+    k = cast(rng.standard_normal((B, S, Hkv, 64)) * 0.5)
+    v = cast(rng.standard_normal((B, S, Hkv, D)))
+    sel = inputs.top_k_keys(k, q, L)
+    ta = ThinAttention(64, D, H, Hkv, torch_dtype(dtype))
+    out, ex = ta.forward_subset(to_gpu(q, dtype), to_gpu(k, dtype), to_gpu(v, dtype), torch.from_numpy(sel).cuda(),
+                                return_coreset=True, return_decisions=True)
+    torch.cuda.synchronize()
+    units = B * Hkv
+    dec = ex["decisions"].cpu().numpy()
+    ref = fwd.forward_subset(q, k, v, sel, decisions={u: dec[u] for u in range(units)})
+    st = ref["stats"]
+    say(f"[subset] S={S} L={L} {dtype}: decisions={st.decisions} near_ties={st.near_ties} fails={st.fails}")
+    assert st.fails == 0 and st.near_ties <= 0.005 * max(st.decisions, 1)
+    idx, w, ln = (x.cpu().numpy() for x in (ex["coreset_idx"], ex["coreset_w"], ex["coreset_len"]))
+    for u in range(units):
+        tok, wt = ref["coreset"][u]
+        assert ln[u] == len(tok)
+        assert np.array_equal(idx[u, :ln[u]], tok)
+        assert np.array_equal(w[u, :ln[u]], wt.astype(np.float32))
+    err = att.max_abs_error(out.float().cpu().numpy().astype(np.float64), ref["out"])
+    say(f"[subset] S={S} L={L}: max|gpu - oracle| = {err:.3g}")
+    assert err <= TOL[dtype]

@@ -129,3 +129,34 @@ def test_error_shrinks_with_coreset_size():
         o = fwd.forward(d["q"][:, :64], d["k"], d["v"], g=g)["out"]
         errs.append(att.rel_frobenius_error(o, ref))
     assert errs[0] > errs[1] > errs[2], errs
+
+
+def test_forward_subset_reduces_to_forward():
+    """Thinning a key list is the unmasked forward on the listed keys: with the identity list it
+    is forward itself, and with a top-k list it equals forward on the gathered keys, its coreset
+    mapped back through the list."""
+    from oracle import forward as fwd
+    rng = np.random.default_rng(11)
+    B, T, S, H, Hkv, E, D = 2, 5, 96, 2, 1, 8, 6
+    q = rng.standard_normal((B, T, H, E))
+    k = rng.standard_normal((B, S, Hkv, E))
+    v = rng.standard_normal((B, S, Hkv, D))
+    ident = np.broadcast_to(np.arange(S), (B, Hkv, S))
+    a, b = fwd.forward(q, k, v), fwd.forward_subset(q, k, v, ident)
+    assert np.array_equal(a["out"], b["out"])
+    for u in a["coreset"]:
+        assert np.array_equal(a["coreset"][u][0], b["coreset"][u][0])
+        assert np.array_equal(a["log"][u], b["log"][u])
+    # a top-48 list by |<k, mean q>|, in token order
+    L = 48
+    score = np.abs(np.einsum("bshe,be->bhs", k, q.mean(axis=(1, 2))))
+    sel = np.sort(np.argsort(-score, axis=2)[:, :, :L], axis=2)
+    c = fwd.forward_subset(q, k, v, sel)
+    kg = np.stack([k[bb, sel[bb, 0], :, :] for bb in range(B)])
+    vg = np.stack([v[bb, sel[bb, 0], :, :] for bb in range(B)])
+    d = fwd.forward(q, kg, vg)
+    assert np.array_equal(c["out"], d["out"])
+    for u in c["coreset"]:
+        bb = u // Hkv
+        assert np.array_equal(c["coreset"][u][0], sel[bb, 0][d["coreset"][u][0]])
+        assert c["coreset"][u][1].sum() == L
