@@ -42,6 +42,19 @@ extern "C" {
 
 enum thin_dtype { THIN_F32 = 0, THIN_BF16 = 1 };
 
+/* Configuration flags (thin_attn_config.flags).
+ * THIN_GREEDY_SIGNS: every kernel-halving walk takes its signs greedily
+ *   instead of at random: pair i keeps its first point exactly when the
+ *   running signed sum alpha_i = sum_{j<i} eta_j <h_j, h_i> is negative, and
+ *   its second point otherwise (alpha_i = 0 included, so the first pair of
+ *   every bin keeps its second point).  The sigma recursion and the draws u_i
+ *   play no part.  This is the deterministic accuracy/cost variant of the
+ *   self-balancing walk the Thinformer pages build on ("Kernel halving",
+ *   Compress); the pages' sub-Gaussian guarantee is stated for the randomised
+ *   walk only.  Representative draws of the Express batches stay random.
+ *   Off by default. */
+enum thin_flags { THIN_GREEDY_SIGNS = 1u };
+
 enum thin_status {
   THIN_OK = 0,
   THIN_EINVAL = -1,   /* bad argument: null pointer, shape, dtype, layout */
@@ -63,7 +76,7 @@ typedef struct thin_attn_config {
                       thinning (exact causal attention)                                */
   double delta;    /* kernel-halving failure parameter; <= 0 means 0.5                */
   float scale;     /* softmax scale s; 0 means 1/sqrt(E)                              */
-  uint32_t flags;  /* reserved, must be 0                                             */
+  uint32_t flags;  /* 0 or THIN_GREEDY_SIGNS; other bits are rejected                 */
 } thin_attn_config;
 
 typedef struct thin_attn thin_attn_t;

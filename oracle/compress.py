@@ -55,7 +55,7 @@ def decisions_per_unit(S, g=0):
 
 
 def thin_unmasked(K, V, scale, delta, seed, unit, g=0, override=None,
-                  stats=None):
+                  stats=None, greedy=False):
     """Coreset of one unit: (idx ascending int64 [n_out], weight, log).
 
     K [S, E], V [S, D] float64.  ``log`` maps (level, bin) to the kept-first
@@ -76,7 +76,7 @@ def thin_unmasked(K, V, scale, delta, seed, unit, g=0, override=None,
         ov = None if override is None else override[(level, start // (4 ** level * s0))]
         keep_first, _ = khm.kernel_halving(K[pts], V[pts], scale, delta, seed,
                                            unit, bin_id, philox.TAG_COMPRESS,
-                                           override=ov, stats=stats)
+                                           override=ov, stats=stats, greedy=greedy)
         log[(level, start // (4 ** level * s0))] = keep_first
         return pts[khm.kept_positions(keep_first)]
 

@@ -54,12 +54,13 @@ class ExpressCache:
     """The EXPRESS weighted cache of one unit (one batch entry and KV head)."""
 
     def __init__(self, n_out, K, V, scale, delta, seed, unit,
-                 override=None, stats=None):
+                 override=None, stats=None, greedy=False):
         assert n_out >= 2 and (n_out & (n_out - 1)) == 0
         self.n_out = n_out
         self.K, self.V = K, V
         self.scale, self.delta, self.seed, self.unit = scale, delta, seed, unit
         self.override = override
+        self.greedy = greedy
         self.stats = stats
         self.m = 1
         self.cache = np.zeros(0, dtype=np.int64)
@@ -75,7 +76,7 @@ class ExpressCache:
         keep_first, _ = khm.kernel_halving(self.K[pts], self.V[pts], self.scale,
                                            self.delta, self.seed, self.unit,
                                            bin_id, tag, override=ov,
-                                           stats=self.stats)
+                                           stats=self.stats, greedy=self.greedy)
         self.log.append(((tag, bin_id), keep_first))
         return pts[khm.kept_positions(keep_first)]
 
@@ -173,7 +174,7 @@ def flat_to_log(flat, S, n_out):
 
 
 def run_unit(K, V, n_out, scale, delta, seed, unit, query_positions=None,
-             override=None, stats=None):
+             override=None, stats=None, greedy=False):
     """Thinformer Express over one unit's S tokens.
 
     Returns (visible, final, log):
@@ -183,7 +184,7 @@ def run_unit(K, V, n_out, scale, delta, seed, unit, query_positions=None,
     """
     S = K.shape[0]
     cache = ExpressCache(n_out, K, V, scale, delta, seed, unit,
-                         override=override, stats=stats)
+                         override=override, stats=stats, greedy=greedy)
     wanted = None if query_positions is None else set(int(t) for t in query_positions)
     visible = {}
     n_blocks = math.ceil(S / n_out)

@@ -31,9 +31,10 @@ def _as64(x):
 
 
 def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
-            delta=0.5, queries=None, decisions=None, tie_margin=1e-6):
+            delta=0.5, queries=None, decisions=None, tie_margin=1e-6, greedy=False):
     """Run the path.  ``queries``: None for the full output, or an int array of
-    (b, t, h) rows for sampled outputs.
+    (b, t, h) rows for sampled outputs.  ``greedy``: every kernel halving
+    takes greedy signs (u_i = 1/2, see oracle.kernel_halving).
 
     Returns a dict with
       out      [B, T, H, D] (or [n_queries, D]) float64
@@ -77,7 +78,7 @@ def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
                 if decisions is not None:
                     ov = cmp.flat_to_log(decisions[unit], S, g)
                 idx, w, log = cmp.thin_unmasked(K, V, s, delta, seed, unit, g,
-                                                override=ov, stats=stats)
+                                                override=ov, stats=stats, greedy=greedy)
                 coreset[unit] = (idx, np.full(len(idx), w))
                 logs[unit] = cmp.log_to_flat(log, S, g)
                 for n, bb, t, h in rows:
@@ -89,7 +90,7 @@ def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
                     ov = exp.flat_to_log(decisions[unit], S, size)
                 visible, final, log = exp.run_unit(
                     K, V, size, s, delta, seed, unit,
-                    query_positions=[t for _, _, t, _ in rows], override=ov, stats=stats)
+                    query_positions=[t for _, _, t, _ in rows], override=ov, stats=stats, greedy=greedy)
                 coreset[unit] = final
                 logs[unit] = exp.log_to_flat(log)
                 for n, bb, t, h in rows:
@@ -100,7 +101,7 @@ def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
 
 
 def forward_subset(q, k, v, key_idx, seed=0, scale=None, g=0, delta=0.5, queries=None, decisions=None,
-                   tie_margin=1e-6):
+                   tie_margin=1e-6, greedy=False):
     """Unmasked Thinformer over a chosen key list per unit (thinning after a KV
     selector: the "Express Language Modeling" explainer on gist.science,
     "Experimental Results", accelerated KV cache compression, where the
@@ -133,7 +134,7 @@ def forward_subset(q, k, v, key_idx, seed=0, scale=None, g=0, delta=0.5, queries
             sel = key_idx[b, hk]
             ov = None if decisions is None else cmp.flat_to_log(decisions[unit], L, g)
             pos, w, log = cmp.thin_unmasked(k[b, sel, hk, :], v[b, sel, hk, :], s, delta, seed, unit, g,
-                                            override=ov, stats=stats)
+                                            override=ov, stats=stats, greedy=greedy)
             coreset[unit] = (sel[pos], np.full(len(pos), w))
             logs[unit] = cmp.log_to_flat(log, L, g)
     results = np.zeros((len(want), D))
@@ -171,7 +172,7 @@ def exact(q, k, v, causal=False, scale=None, queries=None):
 
 
 def decode(k_hist, v_hist, q_steps, k_steps, v_steps, n_out=None, seed=0,
-           scale=None, delta=0.5, decisions=None, tie_margin=1e-6):
+           scale=None, delta=0.5, decisions=None, tie_margin=1e-6, greedy=False):
     """Token-by-token Express decode of one batch entry per unit.
 
     k_hist [B, S0, H_kv, E] is ingested first; then step i appends
@@ -200,7 +201,7 @@ def decode(k_hist, v_hist, q_steps, k_steps, v_steps, n_out=None, seed=0,
             ov = None
             if decisions is not None:
                 ov = exp.flat_to_log(decisions[unit], (total // size) * size, size)
-            cache = exp.ExpressCache(size, K, V, s, delta, seed, unit, override=ov, stats=stats)
+            cache = exp.ExpressCache(size, K, V, s, delta, seed, unit, override=ov, stats=stats, greedy=greedy)
             for t in range(total):
                 if t >= S0:
                     idx, w = cache.visible(t)

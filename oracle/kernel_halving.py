@@ -36,6 +36,16 @@ eta_i = +1 keeps x_{2i}, -1 keeps x_{2i+1}; the kept points carry twice the
 input weight.  The decision margin is |u_i - p~_i| (relative to a_i by
 construction).
 
+Greedy signs (``greedy=True``), the deterministic variant: eta_i = +1 exactly
+when alpha_i < 0, else -1 (alpha_i = 0, so pair 0 of every bin, keeps
+x_{2i+1}); a_i, sigma and u play no part.  It is written on alpha's sign, not
+as the walk with u_i = 1/2: in 1 - alpha / a the sign of alpha is rounded away
+once |alpha| < 2^-53 a, which keys with heavy outlier channels (kernel values
+spread over tens of orders of magnitude) reach.  Its margin is
+|alpha_i| / sum_{j<i} |G_ij|, alpha against the rounding scale of its own sum
+(0 when that sum is 0).  The sub-Gaussian guarantee of the walk holds for the
+randomised signs only.
+
 Parity pins (tests/test_oracle_kh.py): brute-force recomputation of every
 b_i, alpha_i, a_i, sigma_i and p_i from explicit kernel sums on tiny bins;
 the MMD identity ||mean(kept) - mean(all)||^2 = eta^T G eta / (4 P^2) against
@@ -78,7 +88,7 @@ class HalvingStats:
 
 
 def kernel_halving(Kpts, Vpts, scale, delta, seed, unit, bin_id, tag,
-                   override=None, stats=None, tie_margin=1e-6, G=None):
+                   override=None, stats=None, tie_margin=1e-6, G=None, greedy=False):
     """One kernel halving pass over an ordered list of N = 2P points.
 
     Kpts [N, E], Vpts [N, D] are the points' keys and values (float64).
@@ -107,9 +117,14 @@ def kernel_halving(Kpts, Vpts, scale, delta, seed, unit, bin_id, tag,
         a = max(b * math.sqrt(sigma2) * c_N, b2)
         p_tilde = 0.5 * (1.0 - alpha / a) if a > 0.0 else 0.5
         p = min(max(p_tilde, 0.0), 1.0)
-        u = philox.uniform(i, bin_id, unit, tag, seed)
-        first = u < p
-        margin = abs(u - p_tilde)
+        if greedy:
+            first = alpha < 0.0
+            scale_i = float(np.abs(G[i, :i]).sum())
+            margin = abs(alpha) / scale_i if scale_i > 0.0 else 0.0
+        else:
+            u = philox.uniform(i, bin_id, unit, tag, seed)
+            first = u < p
+            margin = abs(u - p_tilde)
         margins[i] = margin
         if stats is not None:
             stats.decisions += 1

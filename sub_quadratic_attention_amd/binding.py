@@ -14,6 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libthin_attn.so")
 
 THIN_F32, THIN_BF16 = 0, 1
+THIN_GREEDY_SIGNS = 1
 _STATUS = {0: "THIN_OK", -1: "THIN_EINVAL", -2: "THIN_ENOTSUP", -3: "THIN_ENOMEM", -4: "THIN_EHIP"}
 
 
@@ -120,12 +121,14 @@ class ThinAttention:
     indices and weights) and its kernel-halving decisions.
     """
 
-    def __init__(self, E, D, H, H_kv=None, dtype=torch.float32, g=0, n_out=0, delta=0.5, scale=0.0):
+    def __init__(self, E, D, H, H_kv=None, dtype=torch.float32, g=0, n_out=0, delta=0.5, scale=0.0,
+                 greedy=False):
         self.lib = load_library()
         self.E, self.D, self.H = E, D, H
         self.H_kv = H if H_kv is None else H_kv
         self.dtype = dtype
-        cfg = _Config(_dtype_code(dtype), E, D, H, self.H_kv, g, n_out, delta, scale, 0)
+        cfg = _Config(_dtype_code(dtype), E, D, H, self.H_kv, g, n_out, delta, scale,
+                      THIN_GREEDY_SIGNS if greedy else 0)
         h = ctypes.c_void_p()
         rc = self.lib.thin_attn_create(ctypes.byref(cfg), ctypes.byref(h))
         if rc != 0:

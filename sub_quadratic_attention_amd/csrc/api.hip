@@ -16,7 +16,7 @@ int thin_attn_create(const thin_attn_config* cfg, thin_attn_t** out) {
   if (c.g < 0) return fail(nullptr, THIN_EINVAL, "g must be >= 0");
   if (c.n_out < 0 || (c.n_out > 0 && (!pow2(c.n_out) || c.n_out < 2)))
     return fail(nullptr, THIN_EINVAL, "n_out must be 0 or a power of two >= 2");
-  if (c.flags != 0) return fail(nullptr, THIN_EINVAL, "flags must be 0");
+  if (c.flags & ~static_cast<uint32_t>(THIN_GREEDY_SIGNS)) return fail(nullptr, THIN_EINVAL, "unknown flags 0x%x", c.flags);
   if (!(c.scale >= 0.0f) || !std::isfinite(c.scale)) return fail(nullptr, THIN_EINVAL, "scale must be finite and >= 0");
   if (!thin::attention_supported(c.dtype == THIN_BF16, c.E, c.D))
     return fail(nullptr, THIN_ENOTSUP, "head dims E=%d D=%d not built for this dtype", c.E, c.D);

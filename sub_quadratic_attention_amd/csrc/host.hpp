@@ -173,6 +173,7 @@ inline thin::GramLaunch gram_for(const thin::SweepLaunch& w, const thin::PointSo
   g.tag = w.tag;
   g.bin_base = w.bin_base;
   g.delta = w.delta;
+  g.greedy = w.greedy;
   return g;
 }
 
@@ -195,6 +196,7 @@ inline thin::SweepLaunch make_sweep(const thin_attn* h, const double* G, int N, 
   s.tag = tag;
   s.bin_base = bin_base;
   s.delta = h->delta;
+  s.greedy = (h->cfg.flags & THIN_GREEDY_SIGNS) != 0;
   return s;
 }
 

@@ -40,6 +40,7 @@ struct GramLaunch {
   // unit, tag) under seed and delta.
   uint64_t seed, tag, bin_base;
   double delta;
+  int greedy;               // 1: u_i = 1/2 for every pair (greedy signs)
   const int32_t* idx;       // bin (u, j) list at idx + u * idx_unit_stride + j * idx_stride
   int64_t idx_stride;
   int64_t idx_unit_stride;
@@ -69,6 +70,7 @@ struct SweepLaunch {
   uint32_t tag;
   uint64_t bin_base;        // Philox bin id = bin_base + bin-in-unit
   double delta;
+  int greedy;               // 1: u_i = 1/2 for every pair (greedy signs)
 };
 
 // Express schedule view used by the causal attention kernel and helpers.

@@ -178,6 +178,12 @@ __device__ __forceinline__ double threshold(double al, double u) {
   return al > 0.0 ? al * (1.0 - 2.0 * u) : (u < 0.5 ? INFINITY : -INFINITY);
 }
 
+// The threshold a walk step compares alpha with: greedy signs keep the first
+// point exactly when alpha < 0, whatever a and u are.
+__device__ __forceinline__ double step_threshold(int greedy, double al, double u) {
+  return greedy ? 0.0 : threshold(al, u);
+}
+
 // b_i^2 of pair i (its two points: fp64 dot products, the same kernel as the
 // Gram, four partial sums per product) and u_i (Philox).
 template <bool BF16>
@@ -240,7 +246,7 @@ __device__ void bin_thresholds(const GramLaunch& a, int z, const double* s_b2, c
       }
     }
     const double al = sigma_steps(s2, b2, sqrt(b2), min(64, P - i0), c, k1, k2);
-    if (mine) G[thr_slot(i, P)] = threshold(al, u);
+    if (mine) G[thr_slot(i, P)] = step_threshold(a.greedy, al, u);
   }
 }
 
@@ -648,7 +654,8 @@ __global__ __launch_bounds__(256) void halving_sweep_small_kernel(SweepLaunch a)
   const double b2 = mine ? fmax(G[static_cast<int64_t>(lane) * P + lane], 0.0) : 0.0;
   const double c = sqrt(2.0 * log(2.0 * a.N / a.delta));
   double s2 = 0.0;
-  const double thr = threshold(sigma_steps(s2, b2, sqrt(b2), P, c, 1.0 + 1.0 / (c * c), 2.0 / c), u);
+  const double thr =
+      step_threshold(a.greedy, sigma_steps(s2, b2, sqrt(b2), P, c, 1.0 + 1.0 / (c * c), 2.0 / c), u);
   double alpha = 0.0;
   uint64_t bits = 0;
 #pragma unroll
@@ -983,7 +990,7 @@ __global__ __launch_bounds__(256) void small_halving_kernel(GramLaunch g, SweepL
   const double u = mine ? philox_uniform(static_cast<uint64_t>(i), a.bin_base + lb, static_cast<uint64_t>(unit), a.tag,
                                          a.seed)
                         : 0.0;
-  const double thr = threshold(al, u);
+  const double thr = step_threshold(a.greedy, al, u);
   double alpha = 0.0;
   uint32_t bits = 0;
   const int first_lane = lane - i;   // pair 0 of the lane's bin
@@ -1130,7 +1137,8 @@ __global__ __launch_bounds__(256) void medium_halving_kernel(GramLaunch g, Sweep
   const double b2 = mine ? fmax(gpair(lane, lane), 0.0) : 0.0;
   const double c = sqrt(2.0 * log(2.0 * a.N / a.delta));
   double s2 = 0.0;
-  const double thr = threshold(sigma_steps(s2, b2, sqrt(b2), P, c, 1.0 + 1.0 / (c * c), 2.0 / c), u);
+  const double thr =
+      step_threshold(a.greedy, sigma_steps(s2, b2, sqrt(b2), P, c, 1.0 + 1.0 / (c * c), 2.0 / c), u);
   double alpha = 0.0;
   uint64_t bits = 0;
 #pragma unroll

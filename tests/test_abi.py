@@ -52,12 +52,18 @@ def _create(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), -1), (dict(H=3, H_kv=2), -1), (dict(n_out=3), -1), (dict(g=-1), -1),
-    (dict(flags=1), -1), (dict(E=96), -2), (dict(dtype=0, E=64, D=256), -2), (dict(E=0), -1),
+    (dict(flags=2), -1), (dict(flags=0x80000001), -1), (dict(E=96), -2), (dict(dtype=0, E=64, D=256), -2), (dict(E=0), -1),
 ])
 def test_create_rejects(kw, code):
     rc, h = _create(**kw)
     assert rc == code
     assert _lib().thin_attn_last_error(None)
+
+
+def test_create_accepts_greedy_signs():
+    rc, h = _create(flags=binding.THIN_GREEDY_SIGNS)
+    assert rc == 0
+    _lib().thin_attn_destroy(h)
 
 
 @pytest.mark.parametrize("S", [256, 3136, 4096, 16, 12, 7])

@@ -97,6 +97,17 @@ def test_biggan_reduced():
     run_and_compare("biggan B=2", d, False, 1, 1, 64, 256, queries=qs)
 
 
+def test_greedy_signs_unmasked():
+    """Greedy signs (u = 1/2 in every walk) over BigGAN-shaped bins, N = 4 .. 128
+    (small, medium and Gram + sweep kernels).  The decisions do not depend on the seed."""
+    d = inputs.biggan_self_attention(seed=5, B=1)
+    qs = sample_queries(1, 4096, 1, 300, always=[(0, 4095, 0)])
+    s0 = run_and_compare("biggan greedy seed 0", d, False, 1, 1, 64, 256, queries=qs, greedy=True)
+    s1 = run_and_compare("biggan greedy seed 9", d, False, 1, 1, 64, 256, queries=qs, greedy=True, seed=9,
+                         check_error=False)
+    assert np.array_equal(s0["dec"], s1["dec"]) and np.array_equal(s0["idx"], s1["idx"])
+
+
 # ---- causal (Thinformer Express) -------------------------------------------
 
 def test_causal_three_halves_ragged():
@@ -109,6 +120,13 @@ def test_causal_small_cache_tiles_span_blocks():
     """n_out=16 < query tile: tiles see several blocks' states."""
     d = inputs.causal_prefill(seed=1, H=1, S=500, E=64, D=64)
     run_and_compare("causal S=500 n=16", d, True, 1, 1, 64, 64, n_out=16)
+
+
+def test_greedy_signs_causal():
+    """Greedy signs in Express: batch halvings and HALVEs (bins of 4n = 256 points take the
+    Gram + sweep kernels with thresholds in the Gram's lower triangle)."""
+    d = inputs.causal_prefill(seed=6, H=2, S=4096 + 64 * 3 + 37)
+    run_and_compare("causal greedy S=4325 n=64", d, True, 2, 2, 128, 128, n_out=64, greedy=True)
 
 
 def test_causal_gqa_fp32():

@@ -21,13 +21,13 @@ def _gpu():
     binding.load_library()
 
 
-def _run_stream(d, n, H, Hkv, E, D, seed=0, chunks=None):
+def _run_stream(d, n, H, Hkv, E, D, seed=0, chunks=None, greedy=False):
     """Ingest the history (in `chunks` appends, or one bulk append), then decode step by step.
 
     Returns (outputs [B, steps, H, D] float64, decisions per unit (flat, chronological), state)."""
     from sub_quadratic_attention_amd.binding import KVState, ThinAttention
     dt = d["dtype"]
-    ta = ThinAttention(E, D, H, Hkv, torch_dtype(dt))
+    ta = ThinAttention(E, D, H, Hkv, torch_dtype(dt), greedy=greedy)
     B = d["k_hist"].shape[0]
     st = KVState(ta, B, n, seed=seed)
     kh, vh = to_gpu(d["k_hist"], dt), to_gpu(d["v_hist"], dt)
@@ -48,12 +48,12 @@ def _run_stream(d, n, H, Hkv, E, D, seed=0, chunks=None):
     return out, dec, st
 
 
-def _check(name, d, n, H, Hkv, E, D, seed=0, chunks=None):
+def _check(name, d, n, H, Hkv, E, D, seed=0, chunks=None, greedy=False):
     say(f"[decode] {name}")
-    out, dec, st = _run_stream(d, n, H, Hkv, E, D, seed, chunks)
+    out, dec, st = _run_stream(d, n, H, Hkv, E, D, seed, chunks, greedy)
     units = dec.shape[0]
     ref, stats, logs = fwd.decode(d["k_hist"], d["v_hist"], d["q_steps"], d["k_steps"], d["v_steps"],
-                                  n_out=n, seed=seed, decisions={u: dec[u] for u in range(units)})
+                                  n_out=n, seed=seed, decisions={u: dec[u] for u in range(units)}, greedy=greedy)
     say(f"[decode] {name}: decisions={stats.decisions} near_ties={stats.near_ties} fails={stats.fails}")
     assert stats.decisions == dec.shape[1] * units
     assert stats.fails == 0 and stats.near_ties <= 0.005 * max(stats.decisions, 1)
@@ -76,6 +76,12 @@ def test_decode_crosses_batch_and_halve():
     """n=32: bulk history of 1900 tokens, 200 decode steps across a batch halving and a HALVE (token 2048)."""
     d = _stream(0, 1900, 200, Hkv=2, H=8)
     _check("bulk 1900 + 200 steps", d, 32, 8, 2, 128, 128)
+
+
+def test_decode_greedy_signs():
+    """Greedy-sign halvings in the streaming state: the same stream as above, u = 1/2 in every walk."""
+    d = _stream(0, 1900, 200, Hkv=2, H=8)
+    _check("greedy bulk 1900 + 200 steps", d, 32, 8, 2, 128, 128, greedy=True)
 
 
 def test_decode_block_path_from_empty():

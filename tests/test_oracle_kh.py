@@ -178,3 +178,60 @@ def test_replay_counts_flips():
         assert st.near_ties == 1 and st.fails == 0
     else:
         assert st.fails == 1 and st.near_ties == 0
+
+
+@pytest.mark.parametrize("N,seed", [(2, 0), (4, 1), (8, 2), (16, 3), (16, 4)])
+def test_greedy_signs_by_brute_force(N, seed):
+    """Greedy signs: pair i keeps its first point exactly when the walk's value
+    alpha_i (recomputed from pointwise kernel sums) is negative, whatever the seed."""
+    rng = np.random.default_rng(100 + seed)
+    K, V = _points(rng, N)
+    s = 0.9
+    kap = lambda i, j: _kap_scalar(K[i], V[i], K[j], V[j], s)
+    keeps = [khm.kernel_halving(K, V, s, 0.5, sd, 3, 17, philox.TAG_COMPRESS, greedy=True)[0] for sd in (0, 7)]
+    assert np.array_equal(keeps[0], keeps[1])
+    keep = keeps[0]
+    eta = []
+    for i in range(N // 2):
+        x, xp = 2 * i, 2 * i + 1
+        alpha = 0.0
+        for j in range(i):
+            alpha += eta[j] * (kap(2 * j, x) - kap(2 * j + 1, x) - kap(2 * j, xp) + kap(2 * j + 1, xp))
+        assert keep[i] == (alpha < 0)
+        eta.append(1.0 if alpha < 0 else -1.0)
+
+
+@pytest.mark.parametrize("N,seed", [(8, 0), (32, 1), (64, 2)])
+def test_greedy_walk_norm_bound(N, seed):
+    """Each greedy step adds b_i^2 + 2 eta_i alpha_i <= b_i^2 to ||psi||^2, so every
+    prefix of the walk has ||psi_i||^2 <= sum_{j<=i} b_j^2 (checked on the pair
+    Gram); the randomised walk has no such per-prefix bound."""
+    rng = np.random.default_rng(200 + seed)
+    K, V = _points(rng, N, E=6, D=4)
+    s = 0.8
+    keep, _ = khm.kernel_halving(K, V, s, 0.5, seed, 0, 0, 0, greedy=True)
+    G = khm.pair_gram(K, V, s)
+    eta = np.where(keep, 1.0, -1.0)
+    for i in range(1, N // 2 + 1):
+        e = eta[:i]
+        assert e @ G[:i, :i] @ e <= np.trace(G[:i, :i]) * (1 + 1e-12) + 1e-300
+
+
+def test_greedy_degenerate_pair_keeps_second():
+    """b = 0 gives p = 1/2 and u = 1/2: the strict test u < p keeps the second point."""
+    K = np.zeros((2, 3)); V = np.ones((2, 2))
+    keep, margins = khm.kernel_halving(K, V, 1.0, 0.5, 4, 5, 9, 1, greedy=True)
+    assert not keep[0] and margins[0] == 0.0
+
+
+def test_greedy_sign_survives_wide_dynamic_range():
+    """A pair whose alpha is far below a (|alpha| / a ~ 1e-40) still takes alpha's sign:
+    pair 0 (alpha = 0) keeps its second point, so pair 1 has alpha = -G_01 and keeps its
+    first point when G_01 > 0, its second when G_01 < 0."""
+    dummy = np.zeros((6, 1))
+    for g01 in (1.0, -1.0):
+        G = np.array([[1e40, g01, 0.0], [g01, 1e20, 0.0], [0.0, 0.0, 1.0]])
+        keep, margins = khm.kernel_halving(dummy, dummy, 1.0, 0.5, 0, 0, 0, 0, G=G, greedy=True)
+        assert not keep[0]
+        assert keep[1] == (g01 > 0)
+        assert margins[1] == 1.0 and margins[2] == 0.0
