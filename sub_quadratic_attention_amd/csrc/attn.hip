@@ -115,19 +115,23 @@ struct Raw {
   int causal;
 };
 
-template <bool BF16, int E, int D>
+// NB chunk buffers: two let the copy of the next chunk overlap the current
+// one; a stream of at most one chunk (a coreset of <= kC keys) needs one,
+// which leaves LDS for more workgroups per CU.
+template <bool BF16, int E, int D, int NB>
 struct Smem {
   static constexpr int KB = E * (BF16 ? 2 : 4), VB = D * (BF16 ? 2 : 4);   // row bytes
-  alignas(16) unsigned char k[2][kC * KB];   // 16-byte pieces permuted by kswz(row)
-  alignas(16) unsigned char v[2][kC * VB];   // 16-byte pieces permuted by vswz(row)
-  float lnw2[2][kC];
-  int posc[2][kC];             // key visible to query t iff posc <= t (INT_MIN: always, INT_MAX: never)
+  alignas(16) unsigned char k[NB][kC * KB];   // 16-byte pieces permuted by kswz(row)
+  alignas(16) unsigned char v[NB][kC * VB];   // 16-byte pieces permuted by vswz(row)
+  float lnw2[NB][kC];
+  int posc[NB][kC];             // key visible to query t iff posc <= t (INT_MIN: always, INT_MAX: never)
   int idx[kIdxCap];
 };
 
 // RAW: the stream is one raw token range (exact attention), tokens computed;
-// otherwise every token of the stream is staged in sm.idx.
-template <bool BF16, int E, int D, bool RAW>
+// otherwise every token of the stream is staged in sm.idx.  NB = 1: every
+// window is a single chunk (the launcher picks it only then).
+template <bool BF16, int E, int D, bool RAW, int NB>
 struct Attn {
   static constexpr int ELT = BF16 ? 2 : 4;
   static constexpr int KB = E * ELT, VB = D * ELT;   // row bytes
@@ -140,7 +144,7 @@ struct Attn {
   using QF = typename std::conditional<BF16, bf16x8_t, float>::type;
 
   const AttnLaunch& a;
-  Smem<BF16, E, D>& sm;
+  Smem<BF16, E, D, NB>& sm;
   int b, h, hk, unit, lane, g;
   // K / V rows of this unit: token t starts at kbase + t * kstride bytes;
   // offsets stay below 2^31 (checked by the host), so they are 32-bit
@@ -166,7 +170,7 @@ struct Attn {
   int qlim[NQG];
   bool rows_ok;
 
-  __device__ __forceinline__ Attn(const AttnLaunch& la, Smem<BF16, E, D>& s, int q0, int bh) : a(la), sm(s) {
+  __device__ __forceinline__ Attn(const AttnLaunch& la, Smem<BF16, E, D, NB>& s, int q0, int bh) : a(la), sm(s) {
     b = bh / a.H;
     h = bh % a.H;
     hk = h / (a.H / a.H_kv);
@@ -478,19 +482,22 @@ struct Attn {
     __syncthreads();
     for (int c = 0; c < nch; c += 2) {   // unrolled by two: the buffer of each step is a constant
       step<0>(c, nch);
-      if (c + 1 < nch) step<1>(c + 1, nch);
+      if constexpr (NB == 2) {
+        if (c + 1 < nch) step<1>(c + 1, nch);
+      }
     }
   }
 
   // chunk c sits in buffer B; chunk c + 1 is copied into the other buffer meanwhile
   template <int B>
   __device__ __forceinline__ void step(int c, int nch) {
-    overlap(c, nch, (const lds_byte*)&sm.k[B][0], (const lds_byte*)&sm.v[B][0], (lds_byte*)&sm.k[1 - B][0],
-            (lds_byte*)&sm.v[1 - B][0]);
+    constexpr int NX = NB == 2 ? 1 - B : B;   // (NB = 1: there is no next chunk)
+    overlap(c, nch, (const lds_byte*)&sm.k[B][0], (const lds_byte*)&sm.v[B][0], (lds_byte*)&sm.k[NX][0],
+            (lds_byte*)&sm.v[NX][0]);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);   // this thread's copies have landed
     if (c + 1 < nch && kC * (c + 2) > wl) {
       __syncthreads();
-      zero_tail(c + 1, 1 - B);
+      zero_tail(c + 1, NX);
     }
     __syncthreads();
   }
@@ -596,15 +603,15 @@ __device__ __forceinline__ void express_pass(const ExpressView& ev, int unit, in
 
 // Unmasked: one pass (the coreset, or all S keys).  Causal: one pass per
 // block beta met by the workgroup's queries.
-template <bool BF16, int E, int D, bool RAW>
+template <bool BF16, int E, int D, bool RAW, int NB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnLaunch a) {
   constexpr int kQ = 16 * nqg<BF16, E, D>() * kWaves;
-  constexpr int NQG = Attn<BF16, E, D, RAW>::NQG;
-  __shared__ Smem<BF16, E, D> sm;
+  constexpr int NQG = Attn<BF16, E, D, RAW, NB>::NQG;
+  __shared__ Smem<BF16, E, D, NB> sm;
   const int64_t tile = xcd_remap(blockIdx.y * static_cast<int64_t>(gridDim.x) + blockIdx.x,
                                  static_cast<int64_t>(gridDim.x) * gridDim.y);
   const int q0 = static_cast<int>(tile % gridDim.x) * kQ;
-  Attn<BF16, E, D, RAW> at(a, sm, q0, static_cast<int>(tile / gridDim.x));
+  Attn<BF16, E, D, RAW, NB> at(a, sm, q0, static_cast<int>(tile / gridDim.x));
   const int q_last = min(q0 + kQ - 1, a.T - 1);
   const int n = a.causal ? a.ev.n : 1;
   const int beta_lo = a.causal ? q0 / n : 0, beta_hi = a.causal ? q_last / n : 0;
@@ -637,9 +644,11 @@ hipError_t launch(const AttnLaunch& a, hipStream_t s) {
   constexpr int kQ = 16 * nqg<BF16, E, D>() * kWaves;
   dim3 grid((a.T + kQ - 1) / kQ, a.B * a.H);
   if (!a.causal && a.cs_idx == nullptr)   // exact attention: one raw range, nothing staged
-    hipLaunchKernelGGL((attn_kernel<BF16, E, D, true>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<BF16, E, D, true, 2>), grid, dim3(kThreads), 0, s, a);
+  else if (!a.causal && a.cs_n <= kC)     // a coreset of one chunk: one buffer
+    hipLaunchKernelGGL((attn_kernel<BF16, E, D, false, 1>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_kernel<BF16, E, D, false>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<BF16, E, D, false, 2>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
