@@ -603,8 +603,14 @@ __device__ __forceinline__ void express_pass(const ExpressView& ev, int unit, in
 
 // Unmasked: one pass (the coreset, or all S keys).  Causal: one pass per
 // block beta met by the workgroup's queries.
+// Waves per SIMD the register budget is set for: three where a one-buffer
+// build fits 168 registers without spilling (bf16, E = 64, D = 64 or 256).
+template <bool BF16, int E, int D, int NB>
+constexpr int attn_waves() { return (NB == 1 && BF16 && E == 64 && (D == 64 || D == 256)) ? 3 : 2; }
+
 template <bool BF16, int E, int D, bool RAW, int NB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnLaunch a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_waves<BF16, E, D, NB>()))) void attn_kernel(
+    AttnLaunch a) {
   constexpr int kQ = 16 * nqg<BF16, E, D>() * kWaves;
   constexpr int NQG = Attn<BF16, E, D, RAW, NB>::NQG;
   __shared__ Smem<BF16, E, D, NB> sm;
