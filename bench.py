@@ -34,7 +34,10 @@ WORKLOADS = {
     "causal_prefill": (dict(), True, 32, 32, 128, 128),
     "kv_decode": (dict(), True, 32, 8, 128, 128),
     "selected_keys": (dict(), False, 32, 8, 128, 128),   # thinning after a KV selector (top 4096 of 32768 keys)
+    # the ViT layer under the sqrt(S) size rule: base subsampling, then the Compress (56 coreset points)
+    "vit_token_mixing_subsampled": (dict(), False, 1, 1, 64, 64),
 }
+FLAGS = {"vit_token_mixing_subsampled": dict(subsample_base=True)}   # ThinAttention options per workload
 
 
 def _traffic(label, workload):
@@ -64,6 +67,14 @@ def compress_depth(S, g=0):
     while S % (4 ** (j + 1)) == 0 and S // (4 ** (j + 1)) >= 4 ** g:
         j += 1
     return j, S // (4 ** j)
+
+
+def base_stride(S, g=0):
+    """Stratum length of base subsampling: largest divisor r of s0 with r^2 <= s0 (1 if no level)."""
+    j, s0 = compress_depth(S, g)
+    if j == 0:
+        return 1
+    return max(r for r in range(1, s0 + 1) if s0 % r == 0 and r * r <= s0 and s0 // r >= 4 ** g)
 
 
 def express_visible_total(S, n):
@@ -102,10 +113,12 @@ def express_gram_entries(S, n):
     return halves * (tri(4 * n) + tri(2 * n)) + done * tri(2 * n)
 
 
-def work_model(name, B, T, S, H, Hkv, E, D, causal, elt):
+def work_model(name, B, T, S, H, Hkv, E, D, causal, elt, subsample_base=False):
     """Per-forward algorithmic flops / bytes of each kernel label."""
     units = B * Hkv
     if not causal:
+        S_full = S
+        S = S // base_stride(S) if subsample_base else S   # the list the Compress runs on
         j, s0 = compress_depth(S)
         n_out = S >> j
         # levels of bins of at most 16 points run in the fused small-bin kernel
@@ -120,7 +133,7 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt):
         medium_entries = sum(bins * N * (N + 1) // 2 for bins, N in levels if medium(N))
         small_bytes = units * sum(bins * N * (E + D) * elt + bins * (N // 2) * 5 for bins, N in levels if small(N))
         keys = n_out
-        pairs_eff = B * H * T * S
+        pairs_eff = B * H * T * S_full
         visible = B * H * T * keys
         attn_bytes = (B * T * H * (E + D) + units * n_out * (E + D)) * elt
     else:
@@ -308,7 +321,8 @@ def main():
     q, k, v = (torch.from_numpy(d[x]).to(tdt).cuda() for x in ("q", "k", "v"))
     B, T = q.shape[:2]
     S = k.shape[1]
-    ta = ThinAttention(E, D, H, Hkv, tdt)
+    opts = FLAGS.get(args.workload, {})
+    ta = ThinAttention(E, D, H, Hkv, tdt, **opts)
     out = torch.empty((B, T, H, D), dtype=tdt, device="cuda")
     stream = torch.cuda.current_stream()
     sel = d.get("key_idx")   # thinning after a selector: the list is the point set (L keys per unit)
@@ -343,7 +357,7 @@ def main():
     recs = ta.timing_records()
     ta.set_timing(False)
 
-    wm = work_model(args.workload, B, T, L, H, Hkv, E, D, causal, elt)   # (a selector's list: its L keys)
+    wm = work_model(args.workload, B, T, L, H, Hkv, E, D, causal, elt, **opts)   # (a selector's list: its L keys)
     per_kernel = {}
     for label, ms in recs:
         r = per_kernel.setdefault(label, dict(launches=0, total_ms=0.0))
@@ -449,7 +463,7 @@ def main():
             desc = f"{nb} of {B} batch entries, every query (thinning + attention)"
             with threadpool_limits(1):
                 a = time.perf_counter()
-                ofwd.forward(sub["q"], sub["k"], sub["v"], causal=False)
+                ofwd.forward(sub["q"], sub["k"], sub["v"], causal=False, **opts)
                 sec = time.perf_counter() - a
         cpu = {"value": pairs / sec, "unit": "queries·keys/s", "cores": 1, "kind": "oracle",
                "sample": desc, "seconds": round(sec, 3)}
@@ -468,7 +482,8 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": dict({"workload": args.workload, "B": B, "H": H, "H_kv": Hkv, "T": T, "S": S, "E": E, "D": D,
-                        "causal": causal, "n_out": wm["n_out"], "seed": 0}, **({"L": L} if sel is not None else {})),
+                        "causal": causal, "n_out": wm["n_out"], "seed": 0}, **({"L": L} if sel is not None else {}),
+                       **opts),
         "kernels": {l: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                     for l, r in per_kernel.items()},
         "roofline": roofline,

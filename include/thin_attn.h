@@ -53,7 +53,19 @@ enum thin_dtype { THIN_F32 = 0, THIN_BF16 = 1 };
  *   Compress); the pages' sub-Gaussian guarantee is stated for the randomised
  *   walk only.  Representative draws of the Express batches stay random.
  *   Off by default. */
-enum thin_flags { THIN_GREEDY_SIGNS = 1u };
+/* THIN_SUBSAMPLE_BASE: unmasked thinning (thin_attn_forward with causal = 0
+ *   and thin_attn_forward_subset) first keeps one random point of every
+ *   stratum of r consecutive points of the list, r the largest divisor of the
+ *   Compress base block s0 (L = 4^j s0, j >= 1) with r * r <= s0 and
+ *   s0 / r >= 4^g; the Compress then runs on those L / r points and every
+ *   coreset point carries weight r 2^j'.  For s0 = r^2 the coreset has
+ *   sqrt(L) points (56 for the 56 x 56 ViT grid instead of 392), the size the
+ *   Thinformer pages quote for their unmasked experiments.  Stratum t keeps
+ *   point t r + min(floor(u r), r - 1), u the Philox4x64-10 uniform of counter
+ *   (t, 0, unit, 5) under the call's seed.  r = 1 (no Compress level, or s0
+ *   without such a divisor) changes nothing.  thin_attn_coreset_size,
+ *   thin_attn_decision_count and thin_attn_workspace_size follow the flag. */
+enum thin_flags { THIN_GREEDY_SIGNS = 1u, THIN_SUBSAMPLE_BASE = 2u };
 
 enum thin_status {
   THIN_OK = 0,
@@ -76,7 +88,7 @@ typedef struct thin_attn_config {
                       thinning (exact causal attention)                                */
   double delta;    /* kernel-halving failure parameter; <= 0 means 0.5                */
   float scale;     /* softmax scale s; 0 means 1/sqrt(E)                              */
-  uint32_t flags;  /* 0 or THIN_GREEDY_SIGNS; other bits are rejected                 */
+  uint32_t flags;  /* THIN_GREEDY_SIGNS | THIN_SUBSAMPLE_BASE; other bits rejected      */
 } thin_attn_config;
 
 typedef struct thin_attn thin_attn_t;

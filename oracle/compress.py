@@ -22,6 +22,20 @@ Bin id of the halving of the block starting at token t on level l:
 Pins: the size rule (n_out 16 / 392 / 64 for S = 256 / 3136 / 4096), weights
 summing to S, indices ascending and unique with one point of every pair,
 and exact attention when thinning is disabled (4^g >= S gives j = 0).
+
+Base subsampling (``subsample_base=True``), the alternative size rule: the
+pages quote coresets of about sqrt(S) points, which the recursion above gives
+for S a power of four but not for S = 3136 = 4^3 * 49 (392 = 7 sqrt(S)).
+Reading taken: before the Compress, every base block is stratified: each run
+of r consecutive points keeps one uniformly drawn point, r the largest
+divisor of s0 with r^2 <= s0 and s0 / r >= 4^g (r = 1 leaves the list
+alone; so does j = 0).  Stratum t keeps point t r + min(floor(u r), r - 1),
+u = uniform(t, 0, unit, TAG_BASE_SAMPLE, seed).  The Compress then runs on
+the L = S / r kept points by the rule above (depth and decision log those of
+L), and each coreset point carries weight r 2^j, so the weights still sum to
+S; with s0 = r^2 the coreset has sqrt(S) points (56 for S = 3136).  Pins:
+sizes (56 / 14 / 12 for S = 3136 / 196 / 144), weights summing to S, one
+point per stratum inside it, uniform offsets, r = 1 equal to the plain rule.
 """
 
 import numpy as np
@@ -38,13 +52,39 @@ def compress_depth(S, g=0):
     return j, S // (4 ** j)
 
 
-def coreset_size(S, g=0):
-    j, _ = compress_depth(S, g)
-    return S >> j
+def base_stride(S, g=0, subsample_base=False):
+    """Stratum length r of base subsampling (1 when it is off or changes nothing)."""
+    if not subsample_base:
+        return 1
+    j, s0 = compress_depth(S, g)
+    if j == 0:
+        return 1
+    return max(r for r in range(1, s0 + 1) if s0 % r == 0 and r * r <= s0 and s0 // r >= 4 ** g)
 
 
-def decisions_per_unit(S, g=0):
+def thinned_length(S, g=0, subsample_base=False):
+    """Length of the list the Compress runs on (S, or S / r after base subsampling)."""
+    return S // base_stride(S, g, subsample_base)
+
+
+def base_sample(S, r, seed, unit):
+    """Positions kept by base subsampling: one per stratum of r, ascending."""
+    out = np.empty(S // r, dtype=np.int64)
+    for t in range(S // r):
+        u = philox.uniform(t, 0, unit, philox.TAG_BASE_SAMPLE, seed)
+        out[t] = t * r + min(int(np.floor(u * r)), r - 1)
+    return out
+
+
+def coreset_size(S, g=0, subsample_base=False):
+    L = thinned_length(S, g, subsample_base)
+    j, _ = compress_depth(L, g)
+    return L >> j
+
+
+def decisions_per_unit(S, g=0, subsample_base=False):
     """Number of halving decisions of one unit (sum over levels)."""
+    S = thinned_length(S, g, subsample_base)
     j, s0 = compress_depth(S, g)
     total = 0
     for level in range(1, j + 1):
@@ -55,7 +95,7 @@ def decisions_per_unit(S, g=0):
 
 
 def thin_unmasked(K, V, scale, delta, seed, unit, g=0, override=None,
-                  stats=None, greedy=False):
+                  stats=None, greedy=False, subsample_base=False):
     """Coreset of one unit: (idx ascending int64 [n_out], weight, log).
 
     K [S, E], V [S, D] float64.  ``log`` maps (level, bin) to the kept-first
@@ -63,6 +103,12 @@ def thin_unmasked(K, V, scale, delta, seed, unit, g=0, override=None,
     another implementation's decisions (replay).
     """
     S = K.shape[0]
+    r = base_stride(S, g, subsample_base)
+    if r > 1:
+        pos = base_sample(S, r, seed, unit)
+        idx, w, log = thin_unmasked(K[pos], V[pos], scale, delta, seed, unit, g, override=override,
+                                    stats=stats, greedy=greedy)
+        return pos[idx], w * r, log
     j, s0 = compress_depth(S, g)
     log = {}
 

@@ -31,10 +31,12 @@ def _as64(x):
 
 
 def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
-            delta=0.5, queries=None, decisions=None, tie_margin=1e-6, greedy=False):
+            delta=0.5, queries=None, decisions=None, tie_margin=1e-6, greedy=False,
+            subsample_base=False):
     """Run the path.  ``queries``: None for the full output, or an int array of
     (b, t, h) rows for sampled outputs.  ``greedy``: every kernel halving
-    takes greedy signs (u_i = 1/2, see oracle.kernel_halving).
+    takes greedy signs (see oracle.kernel_halving); ``subsample_base``: the
+    unmasked Compress runs after base subsampling (see oracle.compress).
 
     Returns a dict with
       out      [B, T, H, D] (or [n_queries, D]) float64
@@ -55,7 +57,8 @@ def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
         assert S == T, "causal attention needs key length T"
         size = exp.default_cache_size(S) if n_out is None else int(n_out)
     else:
-        size = cmp.coreset_size(S, g)
+        size = cmp.coreset_size(S, g, subsample_base)
+    Lt = cmp.thinned_length(S, g, subsample_base)   # the unmasked decision log's list length
 
     if queries is None:
         want = [(b, t, h) for b in range(B) for t in range(T) for h in range(H)]
@@ -76,11 +79,12 @@ def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
             if not causal:
                 ov = None
                 if decisions is not None:
-                    ov = cmp.flat_to_log(decisions[unit], S, g)
+                    ov = cmp.flat_to_log(decisions[unit], Lt, g)
                 idx, w, log = cmp.thin_unmasked(K, V, s, delta, seed, unit, g,
-                                                override=ov, stats=stats, greedy=greedy)
+                                                override=ov, stats=stats, greedy=greedy,
+                                                subsample_base=subsample_base)
                 coreset[unit] = (idx, np.full(len(idx), w))
-                logs[unit] = cmp.log_to_flat(log, S, g)
+                logs[unit] = cmp.log_to_flat(log, Lt, g)
                 for n, bb, t, h in rows:
                     results[n] = att.weighted_attention(q[bb, t, h][None, :], K[idx], V[idx],
                                                         coreset[unit][1], s)[0]
@@ -101,7 +105,7 @@ def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
 
 
 def forward_subset(q, k, v, key_idx, seed=0, scale=None, g=0, delta=0.5, queries=None, decisions=None,
-                   tie_margin=1e-6, greedy=False):
+                   tie_margin=1e-6, greedy=False, subsample_base=False):
     """Unmasked Thinformer over a chosen key list per unit (thinning after a KV
     selector: the "Express Language Modeling" explainer on gist.science,
     "Experimental Results", accelerated KV cache compression, where the
@@ -126,24 +130,27 @@ def forward_subset(q, k, v, key_idx, seed=0, scale=None, g=0, delta=0.5, queries
         want = [(b, t, h) for b in range(B) for t in range(T) for h in range(H)]
     else:
         want = [tuple(int(x) for x in row) for row in np.asarray(queries).reshape(-1, 3)]
+    Lt = cmp.thinned_length(L, g, subsample_base)
     stats = khm.HalvingStats()
     coreset, logs = {}, {}
     for b in range(B):
         for hk in range(Hkv):
             unit = b * Hkv + hk
             sel = key_idx[b, hk]
-            ov = None if decisions is None else cmp.flat_to_log(decisions[unit], L, g)
+            ov = None if decisions is None else cmp.flat_to_log(decisions[unit], Lt, g)
             pos, w, log = cmp.thin_unmasked(k[b, sel, hk, :], v[b, sel, hk, :], s, delta, seed, unit, g,
-                                            override=ov, stats=stats, greedy=greedy)
+                                            override=ov, stats=stats, greedy=greedy,
+                                            subsample_base=subsample_base)
             coreset[unit] = (sel[pos], np.full(len(pos), w))
-            logs[unit] = cmp.log_to_flat(log, L, g)
+            logs[unit] = cmp.log_to_flat(log, Lt, g)
     results = np.zeros((len(want), D))
     for n, (b, t, h) in enumerate(want):
         tok, w = coreset[b * Hkv + h // group]
         results[n] = att.weighted_attention(q[b, t, h][None, :], k[b, tok, h // group, :], v[b, tok, h // group, :],
                                             w, s)[0]
     out = results.reshape(B, T, H, D) if queries is None else results
-    return {"out": out, "coreset": coreset, "log": logs, "stats": stats, "n_out": cmp.coreset_size(L, g)}
+    return {"out": out, "coreset": coreset, "log": logs, "stats": stats,
+            "n_out": cmp.coreset_size(L, g, subsample_base)}
 
 
 def exact(q, k, v, causal=False, scale=None, queries=None):

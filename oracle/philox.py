@@ -39,6 +39,7 @@ TAG_BATCH = 1
 TAG_HALVE_FIRST = 2
 TAG_HALVE_SECOND = 3
 TAG_SUBSAMPLE = 4
+TAG_BASE_SAMPLE = 5
 
 
 def philox4x64_10(counter, key):

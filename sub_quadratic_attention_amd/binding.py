@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libthin_attn.so")
 
 THIN_F32, THIN_BF16 = 0, 1
 THIN_GREEDY_SIGNS = 1
+THIN_SUBSAMPLE_BASE = 2
 _STATUS = {0: "THIN_OK", -1: "THIN_EINVAL", -2: "THIN_ENOTSUP", -3: "THIN_ENOMEM", -4: "THIN_EHIP"}
 
 
@@ -122,13 +123,13 @@ class ThinAttention:
     """
 
     def __init__(self, E, D, H, H_kv=None, dtype=torch.float32, g=0, n_out=0, delta=0.5, scale=0.0,
-                 greedy=False):
+                 greedy=False, subsample_base=False):
         self.lib = load_library()
         self.E, self.D, self.H = E, D, H
         self.H_kv = H if H_kv is None else H_kv
         self.dtype = dtype
         cfg = _Config(_dtype_code(dtype), E, D, H, self.H_kv, g, n_out, delta, scale,
-                      THIN_GREEDY_SIGNS if greedy else 0)
+                      (THIN_GREEDY_SIGNS if greedy else 0) | (THIN_SUBSAMPLE_BASE if subsample_base else 0))
         h = ctypes.c_void_p()
         rc = self.lib.thin_attn_create(ctypes.byref(cfg), ctypes.byref(h))
         if rc != 0:

@@ -16,7 +16,8 @@ int thin_attn_create(const thin_attn_config* cfg, thin_attn_t** out) {
   if (c.g < 0) return fail(nullptr, THIN_EINVAL, "g must be >= 0");
   if (c.n_out < 0 || (c.n_out > 0 && (!pow2(c.n_out) || c.n_out < 2)))
     return fail(nullptr, THIN_EINVAL, "n_out must be 0 or a power of two >= 2");
-  if (c.flags & ~static_cast<uint32_t>(THIN_GREEDY_SIGNS)) return fail(nullptr, THIN_EINVAL, "unknown flags 0x%x", c.flags);
+  if (c.flags & ~static_cast<uint32_t>(THIN_GREEDY_SIGNS | THIN_SUBSAMPLE_BASE))
+    return fail(nullptr, THIN_EINVAL, "unknown flags 0x%x", c.flags);
   if (!(c.scale >= 0.0f) || !std::isfinite(c.scale)) return fail(nullptr, THIN_EINVAL, "scale must be finite and >= 0");
   if (!thin::attention_supported(c.dtype == THIN_BF16, c.E, c.D))
     return fail(nullptr, THIN_ENOTSUP, "head dims E=%d D=%d not built for this dtype", c.E, c.D);
@@ -42,10 +43,11 @@ const char* thin_attn_last_error(const thin_attn_t* h) { return h ? h->err.c_str
 int64_t thin_attn_coreset_size(const thin_attn_t* h, int64_t S, int causal) {
   if (!h || S < 0) return THIN_EINVAL;
   if (causal) return cache_size(h, S);
+  const int64_t Lp = S / base_stride(h, S);
   int j;
   int64_t s0;
-  compress_depth(S, h->cfg.g, j, s0);
-  return S >> j;
+  compress_depth(Lp, h->cfg.g, j, s0);
+  return Lp >> j;
 }
 
 int64_t thin_attn_coreset_capacity(const thin_attn_t* h, int64_t S, int causal) {
@@ -61,11 +63,12 @@ int64_t thin_attn_decision_count(const thin_attn_t* h, int64_t S, int causal) {
     if (!causal_schedule_ok(S, n)) return THIN_ENOTSUP;
     return thin::express_schedule(S, static_cast<int>(n)).decisions;
   }
+  const int64_t Lp = S / base_stride(h, S);
   int j;
   int64_t s0;
-  compress_depth(S, h->cfg.g, j, s0);
+  compress_depth(Lp, h->cfg.g, j, s0);
   int64_t total = 0;
-  for (int l = 1; l <= j; ++l) total += (S / (s0 << (2 * l))) * (s0 << l);
+  for (int l = 1; l <= j; ++l) total += (Lp / (s0 << (2 * l))) * (s0 << l);
   return total;
 }
 
@@ -116,6 +119,12 @@ static int unmasked_path(thin_attn_t* h, const thin::PointSource& src, thin::Att
   const int bf16 = c.dtype == THIN_BF16;
   const int64_t B = al.B;
   const UnmaskedPlan p = plan_unmasked(h, B, L);
+  if (p.r > 1) {   // base subsampling: one point per stratum of r; the Compress runs on L / r points
+    int32_t* list = reinterpret_cast<int32_t*>(ws + p.off_list);
+    THIN_HIP(timed(h, st, "base_sample", [&] { return thin::launch_base_sample(keys, L, units, p.r, seed, list, st); }));
+    keys = list;
+    L = p.L;
+  }
   const int32_t* coreset = keys;   // no thinning: the list itself (nullptr: all keys in order)
   if (p.j > 0) {
     int32_t* a = reinterpret_cast<int32_t*>(ws + p.off_a);
@@ -156,7 +165,7 @@ static int unmasked_path(thin_attn_t* h, const thin::PointSource& src, thin::Att
     coreset = in;   // the last level's output: dense [unit][n_out]
   }
   const int64_t n_cs = p.j > 0 ? p.n_out : L;
-  const float w = static_cast<float>(static_cast<int64_t>(1) << p.j);
+  const float w = static_cast<float>(p.r * (static_cast<int64_t>(1) << p.j));
   al.causal = 0;
   al.cs_idx = coreset;
   al.cs_w = nullptr;

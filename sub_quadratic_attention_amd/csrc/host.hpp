@@ -79,19 +79,41 @@ struct Layout {
   }
 };
 
+// Stratum length r of base subsampling (THIN_SUBSAMPLE_BASE) for a list of S
+// points: the largest divisor r of the Compress base block s0 with r^2 <= s0
+// and s0 / r >= 4^g; 1 without the flag or without a Compress level.
+inline int64_t base_stride(const thin_attn* h, int64_t S) {
+  if (!(h->cfg.flags & THIN_SUBSAMPLE_BASE)) return 1;
+  int j;
+  int64_t s0;
+  compress_depth(S, h->cfg.g, j, s0);
+  if (j == 0) return 1;
+  int64_t four_g = 1;
+  for (int i = 0; i < h->cfg.g && four_g <= s0; ++i) four_g *= 4;
+  int64_t best = 1;
+  for (int64_t r = 2; r * r <= s0; ++r)
+    if (s0 % r == 0 && s0 / r >= four_g) best = r;
+  return best;
+}
+
 struct UnmaskedPlan {
+  int64_t r, L;   // base stratum length and the thinned list's length S / r
   int j;
   int64_t s0, n_out;
-  size_t off_a, off_b, off_g;
+  size_t off_list, off_a, off_b, off_g;
   size_t bytes;
 };
 
-inline UnmaskedPlan plan_unmasked(const thin_attn* h, int64_t B, int64_t S) {
+inline UnmaskedPlan plan_unmasked(const thin_attn* h, int64_t B, int64_t S0) {
   UnmaskedPlan p{};
+  p.r = base_stride(h, S0);
+  p.L = S0 / p.r;
+  const int64_t S = p.L;
   compress_depth(S, h->cfg.g, p.j, p.s0);
   p.n_out = S >> p.j;
   const int64_t units = B * h->cfg.H_kv;
   Layout L;
+  if (p.r > 1) p.off_list = L.add(sizeof(int32_t) * units * S);
   if (p.j > 0) {
     p.off_a = L.add(sizeof(int32_t) * units * S);
     p.off_b = L.add(sizeof(int32_t) * units * S);

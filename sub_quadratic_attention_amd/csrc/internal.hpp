@@ -13,6 +13,7 @@ enum : uint32_t {
   kTagHalveFirst = 2,
   kTagHalveSecond = 3,
   kTagSubsample = 4,
+  kTagBaseSample = 5,
 };
 
 
@@ -152,6 +153,11 @@ hipError_t launch_small_halving(const GramLaunch& g, const SweepLaunch& a, hipSt
 bool medium_halving_supported(int N, int E, int D, int bf16);
 hipError_t launch_medium_halving(const GramLaunch& g, const SweepLaunch& a, hipStream_t s);
 hipError_t launch_iota(int32_t* out, int64_t units, int64_t n, int64_t stride, hipStream_t s);
+// Base subsampling: out[u][t] = list[u][t r + min(floor(u_t r), r - 1)], t < L / r,
+// u_t the Philox uniform of (t, 0, u, kTagBaseSample); list == nullptr means
+// position = token.  list is [units][L], out [units][L / r].
+hipError_t launch_base_sample(const int32_t* list, int64_t L, int units, int64_t r, uint64_t seed, int32_t* out,
+                              hipStream_t s);
 hipError_t launch_express_reps(const ExpressView& ev, int units, uint64_t seed, int32_t* reps, hipStream_t s);
 hipError_t launch_halve_input(const ExpressView& ev, int units, int e, int32_t* halve_in, hipStream_t s);
 hipError_t launch_express_final(const ExpressView& ev, int units, int S, int32_t* idx, float* w,

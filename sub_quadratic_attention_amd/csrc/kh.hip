@@ -687,6 +687,20 @@ __global__ void iota_kernel(int32_t* out, int64_t units, int64_t n, int64_t stri
 // (m = 4^e, r = m / 2) covers tokens [4^e n (1 + k % 3), 4^e n (2 + k % 3))
 // in 2n aligned groups of r tokens; each group contributes the token at
 // offset floor(u r), u from counter (group, log2 r, unit, subsample tag).
+// One random point per stratum of r consecutive list entries (base subsampling
+// ahead of the Compress; the strata are the Compress base blocks' sub-blocks).
+__global__ void base_sample_kernel(const int32_t* list, int64_t L, int units, int64_t r, uint64_t seed, int32_t* out) {
+  const int64_t Lp = L / r;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= Lp * units) return;
+  const int unit = static_cast<int>(i / Lp);
+  const int64_t t = i % Lp;
+  const double u = philox_uniform(static_cast<uint64_t>(t), 0, static_cast<uint64_t>(unit), kTagBaseSample, seed);
+  const int64_t off = min(static_cast<int64_t>(floor(u * static_cast<double>(r))), r - 1);
+  const int64_t pos = t * r + off;
+  out[i] = list ? list[static_cast<int64_t>(unit) * L + pos] : static_cast<int32_t>(pos);
+}
+
 __global__ void express_reps_kernel(ExpressView ev, int units, uint64_t seed, int32_t* reps) {
   const int64_t per_unit = static_cast<int64_t>(ev.n_batches_alloc) * 2 * ev.n;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -1264,6 +1278,14 @@ hipError_t launch_medium_halving(const GramLaunch& g, const SweepLaunch& a, hipS
 hipError_t launch_iota(int32_t* out, int64_t units, int64_t n, int64_t stride, hipStream_t s) {
   if (units * n == 0) return hipSuccess;
   hipLaunchKernelGGL(iota_kernel, dim3(grid1d(units * n, 256)), dim3(256), 0, s, out, units, n, stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_base_sample(const int32_t* list, int64_t L, int units, int64_t r, uint64_t seed, int32_t* out,
+                              hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(units) * (L / r);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(base_sample_kernel, dim3(grid1d(total, 256)), dim3(256), 0, s, list, L, units, r, seed, out);
   return hipGetLastError();
 }
 

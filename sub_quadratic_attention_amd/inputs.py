@@ -175,6 +175,7 @@ WORKLOADS = {
     "causal_prefill": causal_prefill,
     "kv_decode": kv_decode,
     "selected_keys": selected_keys,
+    "vit_token_mixing_subsampled": vit_token_mixing,
 }
 
 

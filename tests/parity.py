@@ -44,13 +44,14 @@ def sample_queries(B, T, H, n, seed=0, always=()):
 
 
 def run_and_compare(name, d, causal, H, Hkv, E, D, n_out=0, g=0, seed=0, queries=None, scale=0.0,
-                    check_error=True, greedy=False):
+                    check_error=True, greedy=False, subsample_base=False):
     """Run forward on the GPU and check it against the replayed oracle.  Returns a summary dict."""
     from sub_quadratic_attention_amd.binding import ThinAttention
 
     say(f"[parity] {name}: causal={causal} shapes q{d['q'].shape} k{d['k'].shape} v{d['v'].shape}")
     dt = d["dtype"]
-    ta = ThinAttention(E, D, H, Hkv, torch_dtype(dt), g=g, n_out=n_out, scale=scale, greedy=greedy)
+    ta = ThinAttention(E, D, H, Hkv, torch_dtype(dt), g=g, n_out=n_out, scale=scale, greedy=greedy,
+                       subsample_base=subsample_base)
     q, k, v = (to_gpu(d[x], dt) for x in ("q", "k", "v"))
     out, ex = ta.forward(q, k, v, causal=causal, seed=seed, return_coreset=True, return_decisions=True)
     torch.cuda.synchronize()
@@ -60,7 +61,7 @@ def run_and_compare(name, d, causal, H, Hkv, E, D, n_out=0, g=0, seed=0, queries
     decisions = {u: dec[u] for u in range(units)}
     ref = fwd.forward(d["q"], d["k"], d["v"], causal=causal, seed=seed, g=g,
                       n_out=(n_out or None), queries=queries, decisions=decisions,
-                      scale=(scale or None), greedy=greedy)
+                      scale=(scale or None), greedy=greedy, subsample_base=subsample_base)
     st = ref["stats"]
     say(f"[parity] {name}: decisions={st.decisions} near_ties={st.near_ties} fails={st.fails} "
         f"min_margin={st.min_margin:.3g}")

@@ -52,12 +52,24 @@ def _create(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), -1), (dict(H=3, H_kv=2), -1), (dict(n_out=3), -1), (dict(g=-1), -1),
-    (dict(flags=2), -1), (dict(flags=0x80000001), -1), (dict(E=96), -2), (dict(dtype=0, E=64, D=256), -2), (dict(E=0), -1),
+    (dict(flags=4), -1), (dict(flags=0x80000001), -1), (dict(E=96), -2), (dict(dtype=0, E=64, D=256), -2), (dict(E=0), -1),
 ])
 def test_create_rejects(kw, code):
     rc, h = _create(**kw)
     assert rc == code
     assert _lib().thin_attn_last_error(None)
+
+
+@pytest.mark.parametrize("S,g", [(3136, 0), (196, 0), (144, 0), (4096, 0), (3136, 1), (7, 0), (192, 0)])
+def test_subsample_base_sizes_match_oracle(S, g):
+    lib = _lib()
+    rc, h = _create(flags=binding.THIN_SUBSAMPLE_BASE, g=g)
+    assert rc == 0
+    try:
+        assert lib.thin_attn_coreset_size(h, S, 0) == cmp.coreset_size(S, g, True)
+        assert lib.thin_attn_decision_count(h, S, 0) == cmp.decisions_per_unit(S, g, True)
+    finally:
+        lib.thin_attn_destroy(h)
 
 
 def test_create_accepts_greedy_signs():

@@ -97,6 +97,25 @@ def test_biggan_reduced():
     run_and_compare("biggan B=2", d, False, 1, 1, 64, 256, queries=qs)
 
 
+def test_base_subsampling_full():
+    """Base subsampling, S = 196 = 4 * 49: one point per stratum of 7, then one Compress level
+    (14 points of weight 14), every output, fp32 with GQA."""
+    rng = np.random.default_rng(21)
+    B, S, H, Hkv = 2, 196, 4, 2
+    d = dict(q=(rng.standard_normal((B, S, H, 64)) * 0.5).astype(np.float32),
+             k=(rng.standard_normal((B, S, Hkv, 64)) * 0.5).astype(np.float32),
+             v=rng.standard_normal((B, S, Hkv, 64)).astype(np.float32), dtype="f32")
+    run_and_compare("base subsampling S=196", d, False, H, Hkv, 64, 64, subsample_base=True)
+
+
+def test_base_subsampling_vit():
+    """ViT tokens (S = 3136) with base subsampling: 56 = sqrt(S) coreset points instead of 392."""
+    d = inputs.vit_token_mixing(seed=3, B=2)
+    qs = sample_queries(2, 3136, 1, 300, always=[(1, 3135, 0)])
+    s = run_and_compare("vit base subsampling", d, False, 1, 1, 64, 64, queries=qs, subsample_base=True)
+    assert s["idx"].shape[1] == 56
+
+
 def test_greedy_signs_unmasked():
     """Greedy signs (u = 1/2 in every walk) over BigGAN-shaped bins, N = 4 .. 128
     (small, medium and Gram + sweep kernels).  The decisions do not depend on the seed."""
@@ -197,12 +216,14 @@ def test_empty_batch_or_queries(B, T):
 
 # ---- thinning after a KV selector -------------------------------------------
 
-@pytest.mark.parametrize("S,L,dtype", [(4096, 1024, "bf16"), (3000, 768, "f32"), (500, 192, "bf16"),
-                                       (300, 50, "f32")])
-def test_thinning_after_selector(S, L, dtype):
+@pytest.mark.parametrize("S,L,dtype,sub", [(4096, 1024, "bf16", False), (3000, 768, "f32", False),
+                                           (500, 192, "bf16", False), (300, 50, "f32", False),
+                                           (3000, 784, "f32", True)])
+def test_thinning_after_selector(S, L, dtype, sub):
     """thin_attn_forward_subset on a top-L selection: decisions, coreset (tokens through the
     list) and outputs against the replayed oracle; L = 50 is too short to thin (the list itself
-    is the coreset), L = 192 and 768 run 12- to 96-point bins, L = 1024 4- to 64-point bins."""
+    is the coreset), L = 192 and 768 run 12- to 96-point bins, L = 1024 4- to 64-point bins;
+    L = 784 = 4^2 * 49 with base subsampling thins one point per 7 of the list to 112, then 28."""
     from oracle import forward as fwd
     from sub_quadratic_attention_amd.binding import ThinAttention
     rng = np.random.default_rng(S + L)
@@ -213,13 +234,13 @@ def test_thinning_after_selector(S, L, dtype):
     k = cast(rng.standard_normal((B, S, Hkv, 64)) * 0.5)
     v = cast(rng.standard_normal((B, S, Hkv, D)))
     sel = inputs.top_k_keys(k, q, L)
-    ta = ThinAttention(64, D, H, Hkv, torch_dtype(dtype))
+    ta = ThinAttention(64, D, H, Hkv, torch_dtype(dtype), subsample_base=sub)
     out, ex = ta.forward_subset(to_gpu(q, dtype), to_gpu(k, dtype), to_gpu(v, dtype), torch.from_numpy(sel).cuda(),
                                 return_coreset=True, return_decisions=True)
     torch.cuda.synchronize()
     units = B * Hkv
     dec = ex["decisions"].cpu().numpy()
-    ref = fwd.forward_subset(q, k, v, sel, decisions={u: dec[u] for u in range(units)})
+    ref = fwd.forward_subset(q, k, v, sel, decisions={u: dec[u] for u in range(units)}, subsample_base=sub)
     st = ref["stats"]
     say(f"[subset] S={S} L={L} {dtype}: decisions={st.decisions} near_ties={st.near_ties} fails={st.fails}")
     assert st.fails == 0 and st.near_ties <= 0.005 * max(st.decisions, 1)

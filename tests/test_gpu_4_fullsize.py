@@ -47,3 +47,12 @@ def test_unmasked_small_full_config():
     d = inputs.unmasked_small(seed=0)
     s = run_and_compare("unmasked small", d, False, 1, 1, 64, 64)
     assert s["decisions"] == 240
+
+
+def test_vit_token_mixing_subsampled_full():
+    """The ViT layer under the sqrt(S) size rule: base subsampling (one point per 7), then the
+    Compress of 448 points per unit, 56 coreset points of weight 56."""
+    d = inputs.vit_token_mixing(seed=0)
+    qs = sample_queries(64, 3136, 1, 600, seed=4, always=[(0, 0, 0), (63, 3135, 0)])
+    s = run_and_compare("vit subsampled B=64 S=3136", d, False, 1, 1, 64, 64, queries=qs, subsample_base=True)
+    assert s["decisions"] == 64 * 392 and s["idx"].shape[1] == 56

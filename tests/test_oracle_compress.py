@@ -160,3 +160,51 @@ def test_forward_subset_reduces_to_forward():
         bb = u // Hkv
         assert np.array_equal(c["coreset"][u][0], sel[bb, 0][d["coreset"][u][0]])
         assert c["coreset"][u][1].sum() == L
+
+
+# ---- base subsampling (the sqrt(S) size rule) --------------------------------
+
+@pytest.mark.parametrize("S,g,r,n_out", [(3136, 0, 7, 56), (196, 0, 7, 14), (144, 0, 3, 12), (4096, 0, 1, 64),
+                                         (256, 0, 1, 16), (192, 0, 1, 24), (3136, 1, 7, 56), (7, 0, 1, 7)])
+def test_base_subsampling_sizes(S, g, r, n_out):
+    """r is the largest divisor of s0 with r^2 <= s0; s0 = r^2 gives sqrt(S) points."""
+    assert cmp.base_stride(S, g, True) == r
+    assert cmp.coreset_size(S, g, True) == n_out
+    assert cmp.base_stride(S, g, False) == 1 and cmp.coreset_size(S, g, False) == cmp.coreset_size(S, g)
+    if r * r * (S // (r * r)) == S and math.isqrt(S) ** 2 == S and r > 1:
+        assert n_out == math.isqrt(S)
+
+
+@pytest.mark.parametrize("S,seed", [(196, 0), (3136, 1), (144, 2)])
+def test_base_subsampling_structure_and_weights(S, seed):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((S, 8)) * 0.5
+    V = rng.standard_normal((S, 4))
+    r = cmp.base_stride(S, 0, True)
+    pos = cmp.base_sample(S, r, seed, 3)
+    assert len(pos) == S // r
+    assert np.all(pos // r == np.arange(S // r))            # one point inside every stratum
+    idx, w, log = cmp.thin_unmasked(K, V, 0.3, 0.5, seed, 3, subsample_base=True)
+    assert len(idx) == cmp.coreset_size(S, 0, True)
+    assert w == r * 2 ** cmp.compress_depth(S // r)[0]
+    assert len(idx) * w == S                               # weights sum to S
+    assert np.all(np.isin(idx, pos)) and np.all(np.diff(idx) > 0)
+    assert sum(len(x) for x in log.values()) == cmp.decisions_per_unit(S, 0, True)
+
+
+def test_base_subsampling_offsets_uniform():
+    """Offsets inside strata of 7 over 7000 strata: chi-square with 6 degrees of freedom."""
+    pos = cmp.base_sample(7 * 7000, 7, 11, 0)
+    counts = np.bincount(pos % 7, minlength=7)
+    chi2 = ((counts - 1000.0) ** 2 / 1000.0).sum()
+    assert chi2 < 22.5   # p ~ 0.001
+
+
+def test_base_subsampling_off_when_r_is_one():
+    """S = 4096 (s0 = 1): the flag changes nothing, coreset and log included."""
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((4096, 8)) * 0.5
+    V = rng.standard_normal((4096, 4))
+    a = cmp.thin_unmasked(K, V, 0.3, 0.5, 2, 0, subsample_base=True)
+    b = cmp.thin_unmasked(K, V, 0.3, 0.5, 2, 0)
+    assert np.array_equal(a[0], b[0]) and a[1] == b[1]
