@@ -154,6 +154,7 @@ struct Attn {
   int qr[NQG];
   bool live[NQG];
   QF qf[NQG][NQF];
+  QF qn[NQG][NQF];   // NB = 1: the next tile's operands, fetched ahead
   f32x4_t o[NQG][ND];
   f32x4_t osum[NQG];   // bf16: row sums of P (all four elements equal)
   float m_run[NQG], l_run[NQG];
@@ -181,32 +182,73 @@ struct Attn {
     vbase = static_cast<const unsigned char*>(a.v) + (static_cast<int64_t>(b) * a.S * a.H_kv + hk) * VB;
     lane = threadIdx.x & 63;
     g = lane >> 4;
-    const int w = threadIdx.x >> 6;
+    load_q(q0);
+  }
+
+  // Row of query group qg in the tile starting at q0 (rows >= T are not live).
+  __device__ __forceinline__ int q_row(int q0, int qg) const {
+    return q0 + 16 * NQG * (threadIdx.x >> 6) + 16 * qg + (lane & 15);
+  }
+
+  // The query operands of the tile starting at q0 into dst (zeros past T).
+  __device__ __forceinline__ void fetch_q(int q0, QF (&dst)[NQG][NQF]) const {
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg) {
-      qr[qg] = q0 + 16 * NQG * w + 16 * qg + (lane & 15);
-      live[qg] = qr[qg] < a.T;
-      const int64_t qrow = ((static_cast<int64_t>(b) * a.T + (live[qg] ? qr[qg] : 0)) * a.H + h) * E;
+      const int r = q_row(q0, qg);
+      const bool ok = r < a.T;
+      const int64_t qrow = ((static_cast<int64_t>(b) * a.T + (ok ? r : 0)) * a.H + h) * E;
       if constexpr (BF16) {
 #pragma unroll
         for (int kk = 0; kk < NQF; ++kk) {
           const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(static_cast<const uint16_t*>(a.q) + qrow + kk * 32 + 8 * g);
-          qf[qg][kk] = live[qg] ? *src : bf16x8_t{};
+          dst[qg][kk] = ok ? *src : bf16x8_t{};
         }
       } else {
 #pragma unroll
         for (int kq = 0; kq < E / 16; ++kq) {
-          const float4 x = live[qg] ? *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow + 16 * kq + 4 * g)
-                                    : float4{0.f, 0.f, 0.f, 0.f};
-          qf[qg][4 * kq] = x.x, qf[qg][4 * kq + 1] = x.y, qf[qg][4 * kq + 2] = x.z, qf[qg][4 * kq + 3] = x.w;
+          const float4 x = ok ? *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow + 16 * kq + 4 * g)
+                              : float4{0.f, 0.f, 0.f, 0.f};
+          dst[qg][4 * kq] = x.x, dst[qg][4 * kq + 1] = x.y, dst[qg][4 * kq + 2] = x.z, dst[qg][4 * kq + 3] = x.w;
         }
       }
+    }
+  }
+
+  // Rows of the tile starting at q0; accumulators cleared.
+  __device__ __forceinline__ void start_tile(int q0) {
+#pragma unroll
+    for (int qg = 0; qg < NQG; ++qg) {
+      qr[qg] = q_row(q0, qg);
+      live[qg] = qr[qg] < a.T;
 #pragma unroll
       for (int d = 0; d < ND; ++d) o[qg][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       osum[qg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       m_run[qg] = -INFINITY;
       l_run[qg] = 0.f;
     }
+  }
+
+  // The query tile starting at q0 into registers; accumulators cleared.
+  __device__ __forceinline__ void load_q(int q0) {
+    fetch_q(q0, qf);
+    start_tile(q0);
+  }
+
+  // One-chunk streams (NB = 1): another query tile of the same unit against the
+  // chunk that run_stream left in buffer 0 (nothing writes the buffers after
+  // it is staged, so no barrier is needed).  Unmasked only: every row is in the
+  // stream.  Its operands were fetched into qn one tile earlier; the tile at
+  // q0_next (>= T: none) is fetched now, to land while this one computes.
+  __device__ __forceinline__ void rerun_single(int q0, int q0_next) {
+#pragma unroll
+    for (int qg = 0; qg < NQG; ++qg)
+#pragma unroll
+      for (int kk = 0; kk < NQF; ++kk) qf[qg][kk] = qn[qg][kk];
+    start_tile(q0);
+    fetch_q(q0_next, qn);
+#pragma unroll
+    for (int qg = 0; qg < NQG; ++qg) qlim[qg] = qr[qg] + 1;
+    consume(0, 0, (const lds_byte*)&sm.k[0][0], (const lds_byte*)&sm.v[0][0]);
   }
 
   // token of window position r (r < wl)
@@ -605,6 +647,10 @@ __device__ __forceinline__ void express_pass(const ExpressView& ev, int unit, in
 // block beta met by the workgroup's queries.
 // Waves per SIMD the register budget is set for: three where a one-buffer
 // build fits 168 registers without spilling (bf16, E = 64, D = 64 or 256).
+// Query tiles per workgroup: a one-chunk coreset is staged once and serves
+// kTilesOne consecutive tiles of its unit.
+constexpr int kTilesOne = 4;
+
 template <bool BF16, int E, int D, int NB>
 constexpr int attn_waves() { return (NB == 1 && BF16 && E == 64 && (D == 64 || D == 256)) ? 3 : 2; }
 
@@ -616,8 +662,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_w
   __shared__ Smem<BF16, E, D, NB> sm;
   const int64_t tile = xcd_remap(blockIdx.y * static_cast<int64_t>(gridDim.x) + blockIdx.x,
                                  static_cast<int64_t>(gridDim.x) * gridDim.y);
-  const int q0 = static_cast<int>(tile % gridDim.x) * kQ;
+  const int q0 = static_cast<int>(tile % gridDim.x) * kQ * (NB == 1 ? kTilesOne : 1);
   Attn<BF16, E, D, RAW, NB> at(a, sm, q0, static_cast<int>(tile / gridDim.x));
+  if constexpr (NB == 1) at.fetch_q(q0 + kQ, at.qn);
   const int q_last = min(q0 + kQ - 1, a.T - 1);
   const int n = a.causal ? a.ev.n : 1;
   const int beta_lo = a.causal ? q0 / n : 0, beta_hi = a.causal ? q_last / n : 0;
@@ -643,6 +690,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_w
     at.run_stream(gs, raw, row_ok);
   }
   at.finish();
+  if constexpr (NB == 1) {   // unmasked, one chunk: the next tiles reuse the staged keys
+    for (int t = 1; t < kTilesOne && q0 + t * kQ < a.T; ++t) {
+      at.rerun_single(q0 + t * kQ, t + 1 < kTilesOne ? q0 + (t + 1) * kQ : a.T);
+      at.finish();
+    }
+  }
 }
 
 template <bool BF16, int E, int D>
@@ -651,8 +704,9 @@ hipError_t launch(const AttnLaunch& a, hipStream_t s) {
   dim3 grid((a.T + kQ - 1) / kQ, a.B * a.H);
   if (!a.causal && a.cs_idx == nullptr)   // exact attention: one raw range, nothing staged
     hipLaunchKernelGGL((attn_kernel<BF16, E, D, true, 2>), grid, dim3(kThreads), 0, s, a);
-  else if (!a.causal && a.cs_n <= kC)     // a coreset of one chunk: one buffer
-    hipLaunchKernelGGL((attn_kernel<BF16, E, D, false, 1>), grid, dim3(kThreads), 0, s, a);
+  else if (!a.causal && a.cs_n <= kC)     // a coreset of one chunk: one buffer, kTilesOne tiles per workgroup
+    hipLaunchKernelGGL((attn_kernel<BF16, E, D, false, 1>), dim3((a.T + kQ * kTilesOne - 1) / (kQ * kTilesOne), a.B * a.H),
+                       dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((attn_kernel<BF16, E, D, false, 2>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
