@@ -116,6 +116,18 @@ def test_base_subsampling_vit():
     assert s["idx"].shape[1] == 56
 
 
+def test_greedy_signs_with_base_subsampling():
+    """Both flags: S = 784 = 4^2 * 49, strata of 7 (112 points), greedy walks, every output, bf16."""
+    rng = np.random.default_rng(23)
+    B, S, H, Hkv = 2, 784, 2, 1
+    d = dict(q=inputs.bf16_round(rng.standard_normal((B, S, H, 64)) * 0.5),
+             k=inputs.bf16_round(rng.standard_normal((B, S, Hkv, 64)) * 0.5),
+             v=inputs.bf16_round(rng.standard_normal((B, S, Hkv, 128))), dtype="bf16")
+    s = run_and_compare("greedy + base subsampling S=784", d, False, H, Hkv, 64, 128, greedy=True,
+                        subsample_base=True)
+    assert s["idx"].shape[1] == 28
+
+
 def test_greedy_signs_unmasked():
     """Greedy signs (u = 1/2 in every walk) over BigGAN-shaped bins, N = 4 .. 128
     (small, medium and Gram + sweep kernels).  The decisions do not depend on the seed."""
