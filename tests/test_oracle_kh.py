@@ -235,3 +235,129 @@ def test_greedy_sign_survives_wide_dynamic_range():
         assert not keep[0]
         assert keep[1] == (g01 > 0)
         assert margins[1] == 1.0 and margins[2] == 0.0
+
+
+# ---------------------------------------------------------------------------
+# The threshold schedule a_i / sigma_i, pinned from the walk's observable
+# outputs.  For a non-forced decision the oracle's margin |u_i - p~_i| and its
+# decision give p~_i back (p~_i = u_i + margin when the first point is kept,
+# u_i - margin otherwise), and a_i = alpha_i / (1 - 2 p~_i) with alpha_i
+# summed here from the pair Gram and the kept signs.  The expected a_i are
+# worked out by hand from the published recursion for a few simple Grams.
+# ---------------------------------------------------------------------------
+def _observed_thresholds(kh, G, seed, delta=0.5):
+    P = G.shape[0]
+    dummy = np.zeros((2 * P, 1))
+    keep, margins = kh(dummy, dummy, 1.0, delta, seed, 0, 0, 0, G=G)
+    eta = np.where(keep, 1.0, -1.0)
+    a = [None]
+    for i in range(1, P):
+        u = philox.uniform(i, 0, 0, 0, seed)
+        pt = u + margins[i] if keep[i] else u - margins[i]
+        alpha = sum(eta[j] * G[i, j] for j in range(i))
+        assert 0.0 < pt < 1.0, "the Grams below keep |alpha| far below a"
+        a.append(alpha / (1.0 - 2.0 * pt))
+    return a
+
+
+def _gram(b):
+    """Diagonal b_i^2; below it G_ij = 0.01 (1 + i / 10) 2^j (symmetric), so no signed sum
+    of a row's entries vanishes and |alpha| stays far below every a_i."""
+    P = len(b)
+    G = np.zeros((P, P))
+    for i in range(P):
+        G[i, i] = b[i] ** 2
+        for j in range(i):
+            G[i, j] = G[j, i] = 0.01 * (1 + i / 10) * 2 ** j
+    return G
+
+
+def _expected_unit_b(c):
+    """b = (1, 1, 1, 1).  sigma_1^2 = b_0^2 = 1 (pair 0 has a_0 = b_0^2 and sigma_0 = 0);
+    a_1 = max(b_1 sigma_1 c, b_1^2) = c; sigma_2^2 = 1 + (1 + (1 - 2c)/c^2) = 1 + (1 - 1/c)^2;
+    a_2 = c sigma_2 (> 1); sigma_3^2 = sigma_2^2 + (1 + sigma_2^2/a_2^2 - 2 sigma_2^2/a_2)
+    = sigma_2^2 + 1 + 1/c^2 - 2 sigma_2/c (positive for these c); a_3 = c sigma_3."""
+    s2 = 1.0 + (1.0 - 1.0 / c) ** 2
+    s3 = s2 + 1.0 + 1.0 / c ** 2 - 2.0 * math.sqrt(s2) / c
+    return [None, c, c * math.sqrt(s2), c * math.sqrt(s3)]
+
+
+def _expected_mixed_b(c):
+    """b = (0.1, 1, 2, 1) with c < 10: a_1 = max(0.1 c, 1) = 1 (the b^2 branch);
+    sigma_2^2 = 0.01 + (1 + (1 - 2) 0.01 / 1) = 1 exactly; a_2 = max(2 c, 4) = 2 c (c > 2);
+    sigma_3^2 = 1 + 4 (1 + (4 - 4c) / (4 c^2)) = 5 + 4/c^2 - 4/c; a_3 = max(c sigma_3, 1)."""
+    s3 = 5.0 + 4.0 / c ** 2 - 4.0 / c
+    return [None, 1.0, 2.0 * c, max(c * math.sqrt(s3), 1.0)]
+
+
+def _check_threshold_schedule(kh):
+    N = 8
+    c = math.sqrt(2.0 * math.log(2.0 * N / 0.5))   # c_N with delta_i = delta / N
+    assert 2.0 < c < 10.0
+    for b, expect in (((1.0, 1.0, 1.0, 1.0), _expected_unit_b(c)), ((0.1, 1.0, 2.0, 1.0), _expected_mixed_b(c))):
+        for seed in range(6):
+            got = _observed_thresholds(kh, _gram(b), seed)
+            for i in range(1, 4):
+                assert got[i] == pytest.approx(expect[i], rel=1e-9), (b, seed, i, got[i], expect[i])
+
+
+def _clip_count(kh, nbins=100, N=128):
+    """Decisions whose p~ falls outside [0, 1] (|alpha_i| > a_i) over many random bins."""
+    rng = np.random.default_rng(123)
+    clips = 0
+    for z in range(nbins):
+        K = rng.standard_normal((N, 2)) * 0.5
+        V = rng.standard_normal((N, 2))
+        keep, margins = kh(K, V, 1.0, 0.5, z, 0, z, 0)
+        for i in range(N // 2):
+            u = philox.uniform(i, z, 0, 0, z)
+            pt = u + margins[i] if keep[i] else u - margins[i]
+            clips += not (0.0 <= pt <= 1.0)
+    return clips, nbins * (N // 2)
+
+
+def test_threshold_schedule_closed_forms():
+    """a_1, a_2, a_3 of two hand-worked Grams (both branches of a = max(b sigma c, b^2))."""
+    _check_threshold_schedule(khm.kernel_halving)
+
+
+def test_clip_rate_within_delta():
+    """The self-balancing walk forces a decision (|alpha_i| > a_i) with probability at most
+    delta_i = delta / N at each step (kernel-thinning papers, self-balancing Hilbert walk);
+    over 6400 decisions of N = 128 that bounds the expected count by 25."""
+    clips, decisions = _clip_count(khm.kernel_halving)
+    assert clips <= decisions * 0.5 / 128, (clips, decisions)
+
+
+def _mutant(old, new):
+    import inspect
+    src = inspect.getsource(khm.kernel_halving)
+    assert src.count(old) == 1, old
+    ns = dict(khm.__dict__)
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    return ns["kernel_halving"]
+
+
+SIGMA_UPDATE = "sigma2 = sigma2 + b2 * max(0.0, 1.0 + (b2 - 2.0 * a) * sigma2 / (a * a))"
+
+
+@pytest.mark.parametrize("old,new", [
+    (SIGMA_UPDATE, "sigma2 = 0.0"),                                                  # sigma never updated
+    (SIGMA_UPDATE, SIGMA_UPDATE.replace("1.0 + (b2", "1.0 - (b2")),                 # update sign flipped
+    (SIGMA_UPDATE, SIGMA_UPDATE.replace("b2 * max", "0.5 * b2 * max")),              # update halved
+    ("a = max(b * math.sqrt(sigma2) * c_N, b2)", "a = b * math.sqrt(sigma2) * c_N"),  # b^2 branch dropped
+    ("a = max(b * math.sqrt(sigma2) * c_N, b2)", "a = max(b * sigma2 * c_N, b2)"),    # sigma^2 for sigma
+    ("2.0 * N / delta", "2.0 / delta"),                                              # delta not spread over N
+])
+def test_schedule_pins_catch_planted_mistakes(old, new):
+    """A mistake planted in a copy of the oracle's walk fails the closed forms or the clip bound."""
+    kh = _mutant(old, new)
+    caught = False
+    try:
+        _check_threshold_schedule(kh)
+    except (AssertionError, ZeroDivisionError, ValueError):
+        caught = True
+    if not caught:
+        clips, decisions = _clip_count(kh, nbins=40)
+        caught = clips > decisions * 0.5 / 128
+    assert caught
