@@ -4,14 +4,18 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one thin_attn_forward call (thinning + coreset attention) on one
 batch of seeded synthetic input already resident in HBM.  The default
-workload is the 56x56-token ViT token-mixing layer (B=64, S=3136, fp32).
+workload is the largest single-GPU one, the causal Thinformer Express
+prefill of a decoder layer (B=1, H=32, T=S=32768, E=D=128, bf16).
 Prints ONE JSON line with the throughput in effective queries*keys per
 second (the pairs exact attention would evaluate), timed without
 instrumentation, then the per-kernel launch times measured with HIP events
 on the launch stream over a second run of the same steps (events around
 every launch would slow the timed one, markedly for ~10 us decode launches),
 the roofline of the dominant kernel, the exact-attention comparators on the
-same GPU and the float64 CPU oracle's rate on a bounded sample.
+same GPU (torch SDPA, and this library's own kernels with thinning
+disabled) and the float64 CPU oracle's rate on the host cores: whole units
+(batch entry, KV head) in parallel, one single-threaded process per core,
+started before the GPU is touched.
 """
 
 import argparse
@@ -51,7 +55,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="vit_token_mixing", choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default="causal_prefill", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-exact", action="store_true")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -157,6 +161,80 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt, subsample_base=False):
 
 
 # ---------------------------------------------------------------------------
+# The float64 CPU oracle on the host cores
+# ---------------------------------------------------------------------------
+_CPU = {}   # inputs of the oracle workers (inherited through fork)
+
+
+def host_cores():
+    """Cores this process may run on, at most 16 (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _oracle_unit(u):
+    """One unit of the oracle, single-threaded: returns (effective pairs, seconds)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import forward as ofwd
+    c = _CPU
+    d, name, H, Hkv = c["d"], c["name"], c["H"], c["Hkv"]
+    g = H // Hkv
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        if name == "kv_decode":
+            hk = u
+            ofwd.decode(d["k_hist"][:, :, hk:hk + 1], d["v_hist"][:, :, hk:hk + 1], d["q_steps"][:, :, hk * g:(hk + 1) * g],
+                        d["k_steps"][:, :, hk:hk + 1], d["v_steps"][:, :, hk:hk + 1], n_out=c["n_out"])
+            S0, steps = d["k_hist"].shape[1], d["q_steps"].shape[1]
+            pairs = sum(g * (S0 + i + 1) for i in range(steps))
+        else:
+            b, hk = divmod(u, Hkv)
+            sub = {x: d[x][b:b + 1, :, hk * g:(hk + 1) * g] if x == "q" else d[x][b:b + 1, :, hk:hk + 1]
+                   for x in ("q", "k", "v")}
+            T, S = sub["q"].shape[1], sub["k"].shape[1]
+            if "key_idx" in d:
+                sel = d["key_idx"][b:b + 1, hk:hk + 1]
+                ofwd.forward_subset(sub["q"], sub["k"], sub["v"], sel, **c["opts"])
+                pairs = g * T * sel.shape[2]
+            elif c["causal"]:
+                ofwd.forward(sub["q"], sub["k"], sub["v"], causal=True)
+                pairs = g * T * (T + 1) // 2
+            else:
+                ofwd.forward(sub["q"], sub["k"], sub["v"], causal=False, **c["opts"])
+                pairs = g * T * S
+        return pairs, time.perf_counter() - t0
+
+
+def cpu_baseline(name, d, H, Hkv, causal, opts, n_out=None):
+    """The oracle as it stands, timed on the host cores: every unit of the workload (all
+    queries of a batch entry and KV head, thinning included) mapped over a pool of
+    single-threaded processes, one per core.  Runs before the GPU is initialised (fork)."""
+    import multiprocessing as mp
+    B = d["k_hist"].shape[0] if name == "kv_decode" else d["k"].shape[0]
+    units = B * Hkv
+    cores = host_cores()
+    sample = units
+    _CPU.update(d=d, name=name, H=H, Hkv=Hkv, causal=causal, opts=opts, n_out=n_out)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(min(cores, sample)) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_unit, range(sample), chunksize=1)
+        wall = time.perf_counter() - t0
+    pairs = sum(p for p, _ in res)
+    unit = "KV head" if Hkv > 1 or name == "kv_decode" else "batch entry"
+    what = "ingest + every decode step" if name == "kv_decode" else "thinning + every query"
+    return {"value": pairs / wall, "unit": "queries·keys/s", "cores": min(cores, sample), "kind": "oracle",
+            "sample": f"all {units} units ({unit}) in full ({what}), one single-threaded process per core",
+            "extrapolated": False, "seconds": round(wall, 3),
+            "unit_seconds_mean": round(sum(t for _, t in res) / len(res), 3),
+            "host_cpus": {"affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+                          "cpu_count": os.cpu_count()}}
+
+
+# ---------------------------------------------------------------------------
 def decode_main(args):
     """KV-cache thinning + decode: one step = ingest the 131k-token history into a
     fresh Express state (thinned once), then 1024 one-token decode steps."""
@@ -166,13 +244,16 @@ def decode_main(args):
 
     _, _, H, Hkv, E, D = WORKLOADS["kv_decode"]
     d = inputs.kv_decode(seed=0)
-    kh, vh = (torch.from_numpy(d[x]).to(torch.bfloat16).cuda() for x in ("k_hist", "v_hist"))
-    qs, ks, vs = (torch.from_numpy(d[x]).to(torch.bfloat16).cuda() for x in ("q_steps", "k_steps", "v_steps"))
-    B, S0 = kh.shape[:2]
-    steps_dec = qs.shape[1]
+    S0 = d["k_hist"].shape[1]
     n_out = 2
     while n_out * n_out < S0:
         n_out *= 2
+    # the oracle on the host cores first: its worker processes fork before the GPU is touched
+    cpu = None if args.no_cpu_baseline else cpu_baseline("kv_decode", d, H, Hkv, True, {}, n_out=n_out)
+    kh, vh = (torch.from_numpy(d[x]).to(torch.bfloat16).cuda() for x in ("k_hist", "v_hist"))
+    qs, ks, vs = (torch.from_numpy(d[x]).to(torch.bfloat16).cuda() for x in ("q_steps", "k_steps", "v_steps"))
+    B = kh.shape[0]
+    steps_dec = qs.shape[1]
     ta = ThinAttention(E, D, H, Hkv, torch.bfloat16)
     st = KVState(ta, B, n_out)
     st._workspace(S0)
@@ -261,20 +342,22 @@ def decode_main(args):
         exact["sdpa_decode_step_us"] = (time.perf_counter() - a) * 1e6 / 50
         exact["decode_speedup_vs_sdpa"] = exact["sdpa_decode_step_us"] / decode_us
         del kt, vt
-    cpu = None
-    if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_limits
-        from oracle import forward as ofwd
-        sub = dict(k_hist=d["k_hist"][:, :, :1], v_hist=d["v_hist"][:, :, :1], q_steps=d["q_steps"][:, :256, :H // Hkv],
-                   k_steps=d["k_steps"][:, :256, :1], v_steps=d["v_steps"][:, :256, :1])
-        with threadpool_limits(1):
-            a = time.perf_counter()
-            ofwd.decode(sub["k_hist"], sub["v_hist"], sub["q_steps"], sub["k_steps"], sub["v_steps"], n_out=n_out)
-            sec = time.perf_counter() - a
-        cpair = sum((H // Hkv) * (S0 + i + 1) for i in range(256))
-        cpu = {"value": cpair / sec, "unit": "queries·keys/s", "cores": 1, "kind": "oracle",
-               "sample": f"1 of {Hkv} KV heads with its {H // Hkv} query heads: ingest + 256 of {steps_dec} steps",
-               "seconds": round(sec, 3)}
+        # this library's attention kernel with thinning disabled: the last step's 32 query
+        # heads (one token each) against all S0 + steps keys (unmasked over the whole cache is
+        # exactly the causal decode of the last token)
+        kf, vf = torch.cat([kh, ks], dim=1).contiguous(), torch.cat([vh, vs], dim=1).contiguous()
+        q1 = qs[:, -1:].contiguous()
+        o1 = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device="cuda")
+        ex = ThinAttention(E, D, H, Hkv, torch.bfloat16)
+        for _ in range(3):
+            ex.coreset_attention(q1, kf, vf, out=o1, stream=stream)
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        for _ in range(50):
+            ex.coreset_attention(q1, kf, vf, out=o1, stream=stream)
+        torch.cuda.synchronize()
+        exact["own_exact_kernel_decode_step_us"] = (time.perf_counter() - a) * 1e6 / 50
+        del kf, vf
     line = {
         "metric": METRIC, "value": pairs / (ms_per_step * 1e-3), "unit": "queries·keys/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
@@ -299,10 +382,10 @@ def main():
     from sub_quadratic_attention_amd import inputs
     from sub_quadratic_attention_amd.binding import ThinAttention
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
     if args.calibrate_copy:
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
         n = args.calibrate_copy << 20
         a = torch.ones(n, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -315,13 +398,18 @@ def main():
         return decode_main(args)
     gen_kw, causal, H, Hkv, E, D = WORKLOADS[args.workload]
     d = inputs.workload(args.workload, seed=0, **gen_kw)
+    opts = FLAGS.get(args.workload, {})
+    # the oracle on the host cores first: its worker processes fork before the GPU is touched
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, d, H, Hkv, causal, opts)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
     dt = d["dtype"]
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     elt = 4 if dt == "f32" else 2
     q, k, v = (torch.from_numpy(d[x]).to(tdt).cuda() for x in ("q", "k", "v"))
     B, T = q.shape[:2]
     S = k.shape[1]
-    opts = FLAGS.get(args.workload, {})
     ta = ThinAttention(E, D, H, Hkv, tdt, **opts)
     out = torch.empty((B, T, H, D), dtype=tdt, device="cuda")
     stream = torch.cuda.current_stream()
@@ -401,6 +489,7 @@ def main():
     # exact comparators on the same GPU
     exact = {}
     if not args.no_exact:
+        k_all, v_all = k, v
         if sel is not None:   # exact attention over the selected keys
             gi = key_idx.long().permute(0, 2, 1)[..., None]
             k, v = (torch.gather(x, 1, gi.expand(-1, -1, -1, x.shape[3])) for x in (k, v))
@@ -419,54 +508,33 @@ def main():
         torch.cuda.synchronize()
         exact["sdpa_ms"] = (time.perf_counter() - a) * 1e3 / n_ex
         del qt, kt, vt
-        if not causal and sel is None:
-            ex = ThinAttention(E, D, H, Hkv, tdt)
-            for _ in range(2):
-                ex.coreset_attention(q, k, v, out=out)
-            torch.cuda.synchronize()
-            a = time.perf_counter()
-            for _ in range(n_ex):
-                ex.coreset_attention(q, k, v, out=out)
-            torch.cuda.synchronize()
-            exact["own_exact_kernel_ms"] = (time.perf_counter() - a) * 1e3 / n_ex
-        exact["speedup_vs_sdpa"] = exact["sdpa_ms"] / ms_per_step
-
-    # float64 CPU oracle on a bounded sample of the same workload
-    cpu = None
-    if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_limits
-        from oracle import forward as ofwd
+        # this library's own kernels with thinning disabled: the unmasked coreset attention
+        # over every key (over the selected keys for a selector's list), and the causal forward
+        # with a cache of at least S tokens, which is exact causal attention
         if causal:
-            heads = min(H, 2)
-            rows = np.array([[0, t, h] for h in range(heads) for t in range(0, T, 64)])
-            sub = {x: d[x][:, :, :heads] for x in ("q", "k", "v")}
-            pairs = sum(t + 1 for _, t, _ in rows)
-            desc = f"{heads} of {H} heads (thinning in full), {len(rows)} sampled queries"
-            with threadpool_limits(1):
-                a = time.perf_counter()
-                ofwd.forward(sub["q"], sub["k"], sub["v"], causal=True, queries=rows)
-                sec = time.perf_counter() - a
-        elif sel is not None:
-            hk = min(Hkv, 2)
-            g = H // Hkv
-            sub = dict(q=d["q"][:, :, :hk * g], k=d["k"][:, :, :hk], v=d["v"][:, :, :hk])
-            pairs = B * hk * g * T * L
-            desc = f"{hk} of {Hkv} KV heads ({hk * g} query heads), every query (thinning + attention)"
-            with threadpool_limits(1):
-                a = time.perf_counter()
-                ofwd.forward_subset(sub["q"], sub["k"], sub["v"], sel[:, :hk])
-                sec = time.perf_counter() - a
+            n_ex_out = 2
+            while n_ex_out < S:
+                n_ex_out *= 2
+            ex = ThinAttention(E, D, H, Hkv, tdt, n_out=n_ex_out)
+            ws_ex = ex.workspace(B, T, S, True)
+            own = lambda: ex.forward(q, k, v, causal=True, seed=0, workspace=ws_ex, out=out, stream=stream)
         else:
-            nb = B if args.workload != "biggan_self_attention" else min(B, 8)
-            sub = {x: d[x][:nb] for x in ("q", "k", "v")}
-            pairs = nb * H * T * S
-            desc = f"{nb} of {B} batch entries, every query (thinning + attention)"
-            with threadpool_limits(1):
-                a = time.perf_counter()
-                ofwd.forward(sub["q"], sub["k"], sub["v"], causal=False, **opts)
-                sec = time.perf_counter() - a
-        cpu = {"value": pairs / sec, "unit": "queries·keys/s", "cores": 1, "kind": "oracle",
-               "sample": desc, "seconds": round(sec, 3)}
+            ex = ThinAttention(E, D, H, Hkv, tdt)
+            if sel is not None:
+                own = lambda: ex.coreset_attention(q, k_all, v_all, idx=key_idx.reshape(B * Hkv, -1), out=out,
+                                                   stream=stream)
+            else:
+                own = lambda: ex.coreset_attention(q, k, v, out=out, stream=stream)
+        for _ in range(2):
+            own()
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        for _ in range(n_ex):
+            own()
+        torch.cuda.synchronize()
+        exact["own_exact_kernel_ms"] = (time.perf_counter() - a) * 1e3 / n_ex
+        exact["speedup_vs_sdpa"] = exact["sdpa_ms"] / ms_per_step
+        exact["speedup_vs_own_exact"] = exact["own_exact_kernel_ms"] / ms_per_step
 
     line = {
         "metric": METRIC,

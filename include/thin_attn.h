@@ -26,7 +26,12 @@
  *    synchronisation.
  *  - Return value 0 (THIN_OK) on success, a negative THIN_E* code otherwise.
  *    Argument errors are detected before anything is enqueued; the message
- *    is kept in the handle (thin_attn_last_error).
+ *    is kept in the handle (thin_attn_last_error).  Token indices a caller
+ *    passes in device memory (key_idx, idx, points) can only be checked on
+ *    the device: an entry outside [0, S) is clamped into range, so that no
+ *    read leaves the unit's rows, and flagged; the flag is reported (and
+ *    cleared) as THIN_EINVAL by the next call on the handle that finds it set,
+ *    or by thin_attn_status, which waits for the stream first.
  *  - Same inputs, seed and configuration give bit-identical results.
  *  - One handle must not be used from two host threads at once.
  */
@@ -106,6 +111,12 @@ int thin_attn_destroy(thin_attn_t* h);
  * the last failed thin_attn_create.  Valid until the next call on h. */
 const char* thin_attn_last_error(const thin_attn_t* h);
 
+/* Wait for `stream`, then report index errors the device found in calls
+ * enqueued on the handle so far: THIN_EINVAL (and the flag cleared) if a
+ * caller's token index lay outside [0, S), THIN_EHIP if the wait failed,
+ * THIN_OK otherwise. */
+int thin_attn_status(thin_attn_t* h, void* stream);
+
 /* Coreset size of one unit.  Unmasked: n_out = S / 2^j with
  * j = max{ j : 4^j | S and S / 4^j >= 4^g } (each point of weight 2^j).
  * Causal: the cache size n_out (the configured value or the default rule).
@@ -124,7 +135,13 @@ int64_t thin_attn_decision_count(const thin_attn_t* h, int64_t S, int causal);
 size_t thin_attn_workspace_size(const thin_attn_t* h, int64_t B, int64_t T, int64_t S, int causal);
 
 /*
- * Thinned attention forward.
+ * Thinned attention forward: the Thinformer / Thinformer Express attention
+ * layer of the "Thinformer" README ("Getting Started": a drop-in attention
+ * call on (query, key, value) with a causal switch, returning the output and
+ * the coreset as its second result), with the thinning of "Express Language
+ * Modeling" ("Thinformer Express": kernel halving under kappa_att as the base
+ * halving; "The EXPRESS Meta-Procedure": the causal exact / thin / HALVE
+ * cache).
  *
  * causal = 0 (Thinformer): each unit's S pairs are thinned by a recursive
  * four-way Compress: base blocks of s0 = S / 4^j consecutive tokens; every
@@ -140,8 +157,16 @@ size_t thin_attn_workspace_size(const thin_attn_t* h, int64_t B, int64_t T, int6
  * the cache (thin phase).  When the cache holds 4 n_out points it is halved
  * twice back to n_out and m becomes 4 m (HALVE).  A query at token t in block
  * beta attends to the cache and buffer left by blocks 0 .. beta-1 plus the raw
- * tokens beta n_out .. t (weight 1).  Supported while m / 2 <= n_out for
- * every block (t < 2 n_out^2), else THIN_ENOTSUP.
+ * tokens beta n_out .. t (weight 1).  Supported while the subsampling
+ * groups of every full block fit in one block (m / 2 <= n_out, m the
+ * inflation in force for that block): with n_out = 2^k that is
+ * S <= n_out (4^(e+1) + 1) - 1 for e = floor((k + 1) / 2), e.g. 1039 tokens
+ * for n_out = 16, 131199 for 128, 262399 for 256, about 2.1 M for 512;
+ * beyond, THIN_ENOTSUP.  n_out >= 2048 with S >= 4 n_out is also
+ * THIN_ENOTSUP (the walk of a full cache exceeds one workgroup's LDS).
+ *
+ * causal = 0 needs the last Compress bin, s0 2^(j+1) points, within the
+ * walk's LDS (at most 8106 points), else THIN_ENOTSUP before any launch.
  *
  * Sizes: S, T < 2^30, and one batch entry's keys or values must fit 2 GiB
  * (S * H_kv * max(E, D) * element size < 2^31, H_kv * max(E, D) * element
@@ -174,8 +199,9 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
  * repeats allowed) exactly as thin_attn_forward thins S keys in token order:
  * the Compress recursion over list positions, with the coreset size rule,
  * decision layout and Philox streams of an unmasked forward with S = L.
- * Every query then attends to that coreset.  key_idx is read on the device;
- * entries outside [0, S) are not detected (out-of-range reads).
+ * Every query then attends to that coreset.  key_idx is read on the device
+ * into a copy in the workspace: entries outside [0, S) are clamped into range
+ * and reported (see the conventions above), never read out of bounds.
  *
  * Sizes: as thin_attn_forward (unmasked) for S, and L >= 1.  The workspace
  * is thin_attn_workspace_size(h, B, T, L, 0) bytes; the optional outputs
@@ -193,7 +219,8 @@ int thin_attn_forward_subset(thin_attn_t* h, const void* q, const void* k, const
  * Weighted-coreset attention alone (no thinning): every query of unit
  * (b, h_kv) attends to the n keys idx[unit * n + j] (token indices into k / v,
  * each in [0, S)) with weights w[unit * n + j] > 0 (w may be NULL: weight 1).
- * idx may be NULL with n == S: exact attention over all keys.
+ * idx may be NULL with n == S: exact attention over all keys.  idx entries
+ * outside [0, S) are clamped into range and reported (conventions above).
  */
 int thin_attn_coreset_attention(thin_attn_t* h, const void* q, const void* k, const void* v,
                                 int64_t B, int64_t T, int64_t S, const int32_t* idx,
@@ -208,7 +235,8 @@ int thin_attn_coreset_attention(thin_attn_t* h, const void* q, const void* k, co
  * (optional) [B * H_kv, N/2], 1 = first point kept; gram [B * H_kv, N/2, N/2]
  * float64 receives the pair Gram G_ij = <h_i, h_j>, h_i = kappa(x_2i, .) -
  * kappa(x_2i+1, .) (upper triangle G[i][j], j >= i; the rest is left
- * unspecified) and is also the kernel's scratch.
+ * unspecified) and is also the kernel's scratch.  points outside [0, S) are
+ * clamped into range and reported (conventions above).
  */
 int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, int64_t S,
                       const int32_t* points, int64_t N, uint64_t seed, uint32_t tag, uint64_t bin,
@@ -235,7 +263,8 @@ int thin_attn_philox(const uint64_t* counters, int64_t n, uint64_t seed, uint64_
  * bytes, 256-byte aligned) and the per-call workspace; the returned host
  * handle holds the counters and must be destroyed with thin_attn_kv_destroy
  * before the thin_attn handle it was created from.  Supported while every
- * subsampling group lies in one block (stream length < 2 n_out^2).
+ * subsampling group lies in one block (the stream lengths of the causal
+ * forward above) and for n_out <= 1024.
  */
 typedef struct thin_kv thin_kv_t;
 
@@ -278,7 +307,9 @@ int thin_attn_kv_coreset(thin_kv_t* kv, int32_t* idx, float* w, int32_t* len, vo
 /* Checkpoint of the host counters (the device state is the caller's buffer:
  * copy it alongside).  export with host == NULL returns the bytes needed;
  * import restores the counters into a state created with the same B, heads,
- * n_out and seed. */
+ * n_out and seed.  Every counter is fixed by the token count, so import
+ * rejects (THIN_EINVAL) a record whose counters differ from the schedule of
+ * its token count. */
 int64_t thin_attn_kv_export(const thin_kv_t* kv, void* host, size_t bytes);
 int thin_attn_kv_import(thin_kv_t* kv, const void* host, size_t bytes);
 

@@ -29,6 +29,26 @@ def weighted_attention(q, Kc, Vc, w, scale):
     return (p @ Vc) / p.sum(axis=1, keepdims=True)
 
 
+def express_block_attention(q, K, V, state_idx, state_w, lo, scale):
+    """Outputs of the queries at tokens lo, lo + 1, ... of one Express block (q [T, E],
+    T <= the block's length): each attends to the state its block sees (tokens
+    state_idx with weights state_w) and to the raw tokens lo .. its own token
+    with weight 1.  This is the weighted form above with the causal mask of the
+    raw part written out: token lo + j is visible to the query at lo + i iff
+    j <= i.  K, V hold every token's key and value."""
+    T = q.shape[0]
+    raw = np.arange(lo, lo + T)
+    keys = np.concatenate([np.asarray(state_idx, dtype=np.int64), raw])
+    w = np.concatenate([np.asarray(state_w, dtype=np.float64), np.ones(T)])
+    logits = scale * (q @ K[keys].T)                                   # [T, |state| + T]
+    hidden = np.zeros(logits.shape, dtype=bool)
+    hidden[:, len(state_idx):] = np.arange(T)[None, :] > np.arange(T)[:, None]
+    logits = np.where(hidden, -np.inf, logits)
+    shift = logits.max(axis=1, keepdims=True)
+    p = w[None, :] * np.exp(logits - shift)
+    return (p @ V[keys]) / p.sum(axis=1, keepdims=True)
+
+
 def exact_attention(q, k, v, scale, causal=False, q_positions=None):
     """Plain softmax attention of q [T, E] against k [S, E], v [S, D].
 

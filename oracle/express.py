@@ -199,3 +199,27 @@ def run_unit(K, V, n_out, scale, delta, seed, unit, query_positions=None,
     tail = np.arange(cache.blocks * n_out, S, dtype=np.int64)
     final = (np.concatenate([idx, tail]), np.concatenate([w, np.ones(len(tail))]))
     return visible, final, cache.log
+
+
+def run_unit_blocks(K, V, n_out, scale, delta, seed, unit, override=None, stats=None, greedy=False):
+    """Thinformer Express over one unit's S tokens, reporting per block instead of per query.
+
+    Returns (blocks, final, log): blocks is a list of (lo, hi, idx, w), the
+    state (cache and buffer) that the queries at tokens lo .. hi-1 of one
+    block see besides the raw tokens of their block; final and log as in
+    run_unit.
+    """
+    S = K.shape[0]
+    cache = ExpressCache(n_out, K, V, scale, delta, seed, unit,
+                         override=override, stats=stats, greedy=greedy)
+    blocks = []
+    for beta in range(math.ceil(S / n_out)):
+        lo, hi = beta * n_out, min((beta + 1) * n_out, S)
+        idx, w = cache.summary()
+        blocks.append((lo, hi, idx, w))
+        if hi - lo == n_out:
+            cache.ingest_block(lo)
+    idx, w = cache.summary()
+    tail = np.arange(cache.blocks * n_out, S, dtype=np.int64)
+    final = (np.concatenate([idx, tail]), np.concatenate([w, np.ones(len(tail))]))
+    return blocks, final, cache.log

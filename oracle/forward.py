@@ -32,11 +32,15 @@ def _as64(x):
 
 def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
             delta=0.5, queries=None, decisions=None, tie_margin=1e-6, greedy=False,
-            subsample_base=False):
+            subsample_base=False, block_outputs=False):
     """Run the path.  ``queries``: None for the full output, or an int array of
     (b, t, h) rows for sampled outputs.  ``greedy``: every kernel halving
     takes greedy signs (see oracle.kernel_halving); ``subsample_base``: the
     unmasked Compress runs after base subsampling (see oracle.compress).
+    ``block_outputs`` (full output only): every query of a unit (unmasked) or
+    of an Express block (causal) shares one coreset / state, so their outputs
+    are formed together, as one weighted attention of all those queries,
+    instead of one query at a time; the result agrees to rounding.
 
     Returns a dict with
       out      [B, T, H, D] (or [n_queries, D]) float64
@@ -71,11 +75,24 @@ def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
     stats = khm.HalvingStats()
     coreset, logs = {}, {}
     results = np.zeros((len(want), D))
+    blocked = block_outputs and queries is None
+    full = np.zeros((B, T, H, D)) if blocked else None
     for b in range(B):
         for hk in range(Hkv):
             unit = b * Hkv + hk
             K, V = k[b, :, hk, :], v[b, :, hk, :]
-            rows = by_unit.get(unit, [])
+            rows = [] if blocked else by_unit.get(unit, [])
+            heads = range(hk * group, (hk + 1) * group)
+            if blocked and causal:
+                ov = None if decisions is None else exp.flat_to_log(decisions[unit], S, size)
+                blocks, final, log = exp.run_unit_blocks(K, V, size, s, delta, seed, unit, override=ov,
+                                                         stats=stats, greedy=greedy)
+                coreset[unit] = final
+                logs[unit] = exp.log_to_flat(log)
+                for lo, hi, idx, w in blocks:
+                    for h in heads:
+                        full[b, lo:hi, h] = att.express_block_attention(q[b, lo:hi, h], K, V, idx, w, lo, s)
+                continue
             if not causal:
                 ov = None
                 if decisions is not None:
@@ -85,6 +102,9 @@ def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
                                                 subsample_base=subsample_base)
                 coreset[unit] = (idx, np.full(len(idx), w))
                 logs[unit] = cmp.log_to_flat(log, Lt, g)
+                if blocked:
+                    for h in heads:
+                        full[b, :, h] = att.weighted_attention(q[b, :, h], K[idx], V[idx], coreset[unit][1], s)
                 for n, bb, t, h in rows:
                     results[n] = att.weighted_attention(q[bb, t, h][None, :], K[idx], V[idx],
                                                         coreset[unit][1], s)[0]
@@ -100,7 +120,7 @@ def forward(q, k, v, causal=False, seed=0, scale=None, g=0, n_out=None,
                 for n, bb, t, h in rows:
                     idx, w = visible[t]
                     results[n] = att.weighted_attention(q[bb, t, h][None, :], K[idx], V[idx], w, s)[0]
-    out = results.reshape(B, T, H, D) if queries is None else results
+    out = full if blocked else (results.reshape(B, T, H, D) if queries is None else results)
     return {"out": out, "coreset": coreset, "log": logs, "stats": stats, "n_out": size}
 
 

@@ -39,6 +39,7 @@ _SIGNATURES = {
     "thin_attn_create": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(ctypes.c_void_p)]),
     "thin_attn_destroy": (ctypes.c_int, [ctypes.c_void_p]),
     "thin_attn_last_error": (ctypes.c_char_p, [ctypes.c_void_p]),
+    "thin_attn_status": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
     "thin_attn_coreset_size": (ctypes.c_int64, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]),
     "thin_attn_coreset_capacity": (ctypes.c_int64, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]),
     "thin_attn_decision_count": (ctypes.c_int64, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]),
@@ -145,6 +146,19 @@ class ThinAttention:
         if rc != 0:
             raise ThinAttnError(rc, self.lib.thin_attn_last_error(self.h).decode())
 
+    def status(self, stream=None):
+        """Wait for the stream; raise if a call on this handle read a token index outside [0, S)."""
+        self._check(self.lib.thin_attn_status(self.h, _stream(stream)))
+
+    def _out(self, out, B, T, dev):
+        """The output tensor: a new one, or the caller's, checked against [B, T, H, D] and the dtype."""
+        if out is None:
+            return torch.empty((B, T, self.H, self.D), dtype=self.dtype, device=dev)
+        if tuple(out.shape) != (B, T, self.H, self.D) or out.dtype != self.dtype or not out.is_contiguous() \
+                or out.device != dev:
+            raise ValueError(f"out must be a contiguous {self.dtype} tensor of shape {(B, T, self.H, self.D)} on {dev}")
+        return out
+
     # sizes --------------------------------------------------------------
     def coreset_size(self, S, causal=False):
         return int(self.lib.thin_attn_coreset_size(self.h, S, int(causal)))
@@ -188,8 +202,7 @@ class ThinAttention:
         S = k.shape[1]
         units = B * self.H_kv
         dev = q.device
-        if out is None:
-            out = torch.empty((B, T, self.H, self.D), dtype=self.dtype, device=dev)
+        out = self._out(out, B, T, dev)
         if workspace is None:
             workspace = self.workspace(B, T, S, causal, dev)
         idx = w = ln = dec = None
@@ -218,14 +231,15 @@ class ThinAttention:
         q, k, v = self._inputs(q, k, v)
         B, T = q.shape[:2]
         S = k.shape[1]
+        if key_idx.device != q.device:
+            raise ValueError(f"key_idx must be on {q.device}")
         key_idx = key_idx.to(torch.int32).contiguous()
         if key_idx.dim() != 3 or key_idx.shape[:2] != (B, self.H_kv):
             raise ValueError(f"key_idx must be [B, H_kv, L] = [{B}, {self.H_kv}, L]; got {tuple(key_idx.shape)}")
         L = key_idx.shape[2]
         units = B * self.H_kv
         dev = q.device
-        if out is None:
-            out = torch.empty((B, T, self.H, self.D), dtype=self.dtype, device=dev)
+        out = self._out(out, B, T, dev)
         if workspace is None:
             workspace = self.workspace(B, T, L, False, dev)
         idx = w = ln = dec = None
@@ -252,13 +266,17 @@ class ThinAttention:
         q, k, v = self._inputs(q, k, v)
         B, T = q.shape[:2]
         S = k.shape[1]
-        n = S if idx is None else idx.shape[1]
+        units = B * self.H_kv
+        n = S if idx is None else idx.shape[-1]
         if idx is not None:
+            if idx.device != q.device or idx.numel() != units * n:
+                raise ValueError(f"idx must hold [B * H_kv, n] = [{units}, n] indices on {q.device}")
             idx = idx.to(torch.int32).contiguous()
         if w is not None:
+            if idx is None or w.device != q.device or w.numel() != units * n:
+                raise ValueError(f"w needs idx and must hold [B * H_kv, n] = [{units}, {n}] weights on {q.device}")
             w = w.to(torch.float32).contiguous()
-        if out is None:
-            out = torch.empty((B, T, self.H, self.D), dtype=self.dtype, device=q.device)
+        out = self._out(out, B, T, q.device)
         rc = self.lib.thin_attn_coreset_attention(self.h, _ptr(q), _ptr(k), _ptr(v), B, T, S, _ptr(idx), _ptr(w),
                                                   n, _ptr(out), _stream(stream))
         self._check(rc)

@@ -23,6 +23,21 @@ int thin_attn_create(const thin_attn_config* cfg, thin_attn_t** out) {
     return fail(nullptr, THIN_ENOTSUP, "head dims E=%d D=%d not built for this dtype", c.E, c.D);
   thin_attn* h = new thin_attn();
   h->cfg = c;
+  // the device-visible index-error flag (pinned host memory); without a device
+  // there is none, and nothing can be launched anyway
+  void* flag = nullptr;
+  if (hipHostMalloc(&flag, sizeof(int), hipHostMallocMapped | hipHostMallocPortable | hipHostMallocCoherent) ==
+      hipSuccess) {
+    void* dflag = nullptr;
+    if (hipHostGetDevicePointer(&dflag, flag, 0) == hipSuccess) {
+      h->err_host = static_cast<int*>(flag);
+      h->err_dev = static_cast<int*>(dflag);
+      *h->err_host = 0;
+    } else {
+      (void)hipHostFree(flag);
+    }
+  }
+  (void)hipGetLastError();   // a failed probe above leaves no error behind
   h->delta = c.delta > 0.0 ? c.delta : 0.5;
   h->scale64 = c.scale > 0.0f ? static_cast<double>(c.scale) : 1.0 / sqrt(static_cast<double>(c.E));
   h->scale = static_cast<float>(h->scale64);
@@ -34,11 +49,19 @@ int thin_attn_destroy(thin_attn_t* h) {
   if (!h) return THIN_OK;
   release_timing(h);
   for (auto e : h->pool) (void)hipEventDestroy(e);
+  if (h->err_host) (void)hipHostFree(h->err_host);
   delete h;
   return THIN_OK;
 }
 
 const char* thin_attn_last_error(const thin_attn_t* h) { return h ? h->err.c_str() : g_create_error.c_str(); }
+
+int thin_attn_status(thin_attn_t* h, void* stream) {
+  if (!h) return THIN_EINVAL;
+  h->err.clear();
+  THIN_HIP(hipStreamSynchronize(as_stream(stream)));
+  return take_index_error(h);
+}
 
 int64_t thin_attn_coreset_size(const thin_attn_t* h, int64_t S, int causal) {
   if (!h || S < 0) return THIN_EINVAL;
@@ -187,6 +210,8 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
   if (causal != 0 && causal != 1) return fail(h, THIN_EINVAL, "causal must be 0 or 1");
   int rc = check_dims(h, B, T, S, causal);
   if (rc) return rc;
+  if (!causal && (rc = check_unmasked_plan(h, S))) return rc;
+  if ((rc = take_index_error(h))) return rc;
   if (B * T == 0) return THIN_OK;
   if (!q || !k || !v || !out) return fail(h, THIN_EINVAL, "null q, k, v or out");
   const size_t need = thin_attn_workspace_size(h, B, T, S, causal);
@@ -242,6 +267,8 @@ int thin_attn_forward_subset(thin_attn_t* h, const void* q, const void* k, const
   int rc = check_dims(h, B, T, S, 0);
   if (rc) return rc;
   if (L < 1 || L >= (1LL << 30)) return fail(h, THIN_EINVAL, "key list length L must be in [1, 2^30) (got %lld)", (long long)L);
+  if ((rc = check_unmasked_plan(h, L))) return rc;
+  if ((rc = take_index_error(h))) return rc;
   if (B * T == 0) return THIN_OK;
   if (S == 0) return fail(h, THIN_EINVAL, "S must be positive");
   if (!q || !k || !v || !out || !key_idx) return fail(h, THIN_EINVAL, "null q, k, v, out or key_idx");
@@ -264,8 +291,16 @@ int thin_attn_forward_subset(thin_attn_t* h, const void* q, const void* k, const
   al.H = c.H;
   al.H_kv = c.H_kv;
   al.scale = h->scale;
-  return unmasked_path(h, src, al, key_idx, L, units, seed, decisions, thin_attn_decision_count(h, L, 0),
-                       static_cast<char*>(workspace), as_stream(stream), coreset_idx, coreset_w, coreset_len);
+  // the caller's list is read from a copy clamped into [0, S) (entries outside are reported)
+  char* ws = static_cast<char*>(workspace);
+  int32_t* keys = reinterpret_cast<int32_t*>(ws + plan_unmasked(h, B, L).off_keys);
+  const hipStream_t st = as_stream(stream);
+  THIN_HIP(timed(h, st, "sanitize_indices", [&] {
+    return thin::launch_sanitize_indices(key_idx, static_cast<int64_t>(units) * L, static_cast<int32_t>(S), keys,
+                                         h->err_dev, st);
+  }));
+  return unmasked_path(h, src, al, keys, L, units, seed, decisions, thin_attn_decision_count(h, L, 0), ws, st,
+                       coreset_idx, coreset_w, coreset_len);
 }
 
 int thin_attn_coreset_attention(thin_attn_t* h, const void* q, const void* k, const void* v, int64_t B, int64_t T,
@@ -278,6 +313,7 @@ int thin_attn_coreset_attention(thin_attn_t* h, const void* q, const void* k, co
   if (!q || !k || !v || !out) return fail(h, THIN_EINVAL, "null q, k, v or out");
   if (n <= 0 || n > S) return fail(h, THIN_EINVAL, "coreset size must be in [1, S]");
   if (!idx && n != S) return fail(h, THIN_EINVAL, "idx may be NULL only with n == S");
+  if ((rc = take_index_error(h))) return rc;
   const thin_attn_config& c = h->cfg;
   thin::AttnLaunch al{};
   al.q = q;
@@ -296,6 +332,7 @@ int thin_attn_coreset_attention(thin_attn_t* h, const void* q, const void* k, co
   al.cs_n = static_cast<int>(n);
   al.cs_stride = idx ? n : 0;
   al.cs_lnw = 0.f;
+  al.err = h->err_dev;
   THIN_HIP(thin::launch_attention(al, c.dtype == THIN_BF16, c.E, c.D, as_stream(stream)));
   return THIN_OK;
 }
@@ -308,6 +345,8 @@ int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, i
   if (B < 0 || S <= 0) return fail(h, THIN_EINVAL, "bad B or S");
   if (N < 2 || N > 2048 || (N & 1)) return fail(h, THIN_EINVAL, "N must be even and in [2, 2048]");
   if (tag > 4) return fail(h, THIN_EINVAL, "unknown tag %u", tag);
+  int rc = take_index_error(h);
+  if (rc) return rc;
   if (B == 0) return THIN_OK;
   if (!k || !v || !points || !kept || !gram) return fail(h, THIN_EINVAL, "null k, v, points, kept or gram");
   const thin_attn_config& c = h->cfg;
@@ -316,7 +355,9 @@ int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, i
   thin::PointSource src{k, v, S, c.H_kv, c.E, c.D, c.dtype == THIN_BF16};
   const int n = static_cast<int>(N);
   thin::SweepLaunch sl = make_sweep(h, gram, n, units, 1, points, n, kept, seed, tag, bin);
-  THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
+  thin::GramLaunch gl = gram_for(sl, src, h->scale64);
+  gl.err = h->err_dev;   // the caller's points are clamped into [0, S) and reported
+  THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gl, st); }));
   sl.dec = decisions;
   sl.dec_per_unit = n / 2;
   THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, st); }));

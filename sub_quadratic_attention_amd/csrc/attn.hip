@@ -503,11 +503,17 @@ struct Attn {
         const int32_t* src = gp < c0 ? gs.p[0] + gp : (gp < c01 ? gs.p[1] + (gp - c0) : gs.p[2] + (gp - c01));
         v[i] = pos < G ? *src : raw.start + (pos - G);
       }
+      // a gathered index outside the unit's rows is clamped (and reported): no
+      // read may leave [0, S)
+      bool bad = false;
 #pragma unroll
       for (int i = 0; i < kIdxPT; ++i) {
         const int e = threadIdx.x + kThreads * i;
+        bad = bad || (e < wl && static_cast<unsigned>(v[i]) >= static_cast<unsigned>(a.S));
+        v[i] = min(max(v[i], 0), a.S - 1);
         if (e < wl) sm.idx[e] = v[i];
       }
+      if (bad && a.err) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       __syncthreads();
     }
     const int nch = (wl + kC - 1) / kC;

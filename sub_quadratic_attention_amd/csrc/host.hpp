@@ -27,6 +27,12 @@ struct thin_attn {
   };
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;   // events not in use
+  // Index errors found on the device: one int of pinned host memory mapped
+  // into the device's address space (err_dev); kernels that read a caller's
+  // token indices store 1 there when one lies outside [0, S).  Null when no
+  // device was present at creation (nothing can be launched then).
+  int* err_host = nullptr;
+  int* err_dev = nullptr;
 };
 
 namespace thinhost {
@@ -100,9 +106,16 @@ struct UnmaskedPlan {
   int64_t r, L;   // base stratum length and the thinned list's length S / r
   int j;
   int64_t s0, n_out;
-  size_t off_list, off_a, off_b, off_g;
+  size_t off_keys, off_list, off_a, off_b, off_g;
   size_t bytes;
 };
+
+// LDS one workgroup may hold on gfx950.
+constexpr size_t kLdsLimit = 160 * 1024;
+
+// Can the walk of a bin of N points run?  Bins of more than 128 points keep
+// their thresholds, running sums and signs in LDS.
+inline bool walk_fits(int64_t N) { return N <= 128 || thin::sweep_lds_bytes(static_cast<int>(N)) <= kLdsLimit; }
 
 inline UnmaskedPlan plan_unmasked(const thin_attn* h, int64_t B, int64_t S0) {
   UnmaskedPlan p{};
@@ -113,6 +126,7 @@ inline UnmaskedPlan plan_unmasked(const thin_attn* h, int64_t B, int64_t S0) {
   p.n_out = S >> p.j;
   const int64_t units = B * h->cfg.H_kv;
   Layout L;
+  p.off_keys = L.add(sizeof(int32_t) * units * S0);   // a caller's key list, clamped into range
   if (p.r > 1) p.off_list = L.add(sizeof(int32_t) * units * S);
   if (p.j > 0) {
     p.off_a = L.add(sizeof(int32_t) * units * S);
@@ -170,13 +184,38 @@ inline int check_dims(thin_attn* h, int64_t B, int64_t T, int64_t S, int causal)
     if (!pow2(n) || n < 2) return fail(h, THIN_EINVAL, "n_out must be a power of two >= 2");
     if (!causal_schedule_ok(S, n))
       return fail(h, THIN_ENOTSUP, "subsampling groups would exceed a block (S >= 2 n_out^2)");
+    if (S / n >= 4 && !walk_fits(4 * n))
+      return fail(h, THIN_ENOTSUP, "n_out = %lld: the halving of a full cache (%lld points) exceeds the walk's LDS",
+                  (long long)n, (long long)(4 * n));
   } else if (S == 0 && T > 0) {
     return fail(h, THIN_EINVAL, "S must be positive when T > 0");
   }
   return THIN_OK;
 }
 
+// The unmasked Compress of a list of S points: its largest bin must fit the walk.
+inline int check_unmasked_plan(thin_attn* h, int64_t S) {
+  const UnmaskedPlan p = plan_unmasked(h, 1, S);
+  if (p.j > 0 && !walk_fits(p.s0 << (p.j + 1)))
+    return fail(h, THIN_ENOTSUP, "S = %lld: the last Compress bin of %lld points exceeds the walk's LDS "
+                                 "(base block %lld; choose a length with more factors of 4, or g)",
+                (long long)S, (long long)(p.s0 << (p.j + 1)), (long long)p.s0);
+  return THIN_OK;
+}
+
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// A caller's index list read by an earlier call held entries outside [0, S):
+// report it once (THIN_EINVAL) and clear the flag.  The flag is written by the
+// device, so an error becomes visible here once that call's kernels finished.
+inline int take_index_error(thin_attn* h) {
+  if (!h->err_host) return THIN_OK;
+  volatile int* f = h->err_host;
+  if (*f == 0) return THIN_OK;
+  *f = 0;
+  return fail(h, THIN_EINVAL, "an earlier call on this handle read token indices outside [0, S) "
+                              "(they were clamped into range; its outputs are not meaningful)");
+}
 
 // The pair Gram of the bins a walk is about to halve, with that walk's
 // Philox parameters (the Gram launch also forms the walk's thresholds).

@@ -41,7 +41,7 @@ struct GramLaunch {
   // unit, tag) under seed and delta.
   uint64_t seed, tag, bin_base;
   double delta;
-  int greedy;               // 1: u_i = 1/2 for every pair (greedy signs)
+  int greedy;               // 1: greedy signs (threshold 0: keep the first point iff alpha_i < 0)
   const int32_t* idx;       // bin (u, j) list at idx + u * idx_unit_stride + j * idx_stride
   int64_t idx_stride;
   int64_t idx_unit_stride;
@@ -50,6 +50,8 @@ struct GramLaunch {
   int bins_per_unit;
   double scale;
   double* G;
+  // Point indices outside [0, S) are clamped (and reported through err, when set).
+  int* err;
 };
 
 // Kernel-halving decisions of many bins at once (one workgroup per bin).
@@ -71,7 +73,7 @@ struct SweepLaunch {
   uint32_t tag;
   uint64_t bin_base;        // Philox bin id = bin_base + bin-in-unit
   double delta;
-  int greedy;               // 1: u_i = 1/2 for every pair (greedy signs)
+  int greedy;               // 1: greedy signs (threshold 0: keep the first point iff alpha_i < 0)
 };
 
 // Express schedule view used by the causal attention kernel and helpers.
@@ -101,6 +103,9 @@ struct AttnLaunch {
   int64_t cs_stride;
   float cs_lnw;
   ExpressView ev;
+  // Gathered token indices outside [0, S) are clamped into range (no read
+  // leaves the unit's rows) and, when err is set, reported by storing 1 there.
+  int* err;
 };
 
 // Row moves into / inside the streaming Express state (see kv.hip).
@@ -165,6 +170,11 @@ hipError_t launch_express_final(const ExpressView& ev, int units, int S, int32_t
 hipError_t launch_fill_coreset(const int32_t* src, int64_t src_stride, int units, int n, float w,
                                int32_t* idx, float* wout, int32_t* len, hipStream_t s);
 hipError_t launch_attention(const AttnLaunch& a, int bf16, int E, int D, hipStream_t s);
+// Copy of a caller's index list with every entry clamped into [0, S);
+// stores 1 to *err (when err is set) if any entry was outside.
+hipError_t launch_sanitize_indices(const int32_t* in, int64_t n, int32_t S, int32_t* out, int* err, hipStream_t s);
+// LDS bytes of the walk of one bin of N points (bins of more than 128 points).
+size_t sweep_lds_bytes(int N);
 hipError_t launch_philox_words(const uint64_t* ctr, int64_t n, uint64_t seed, uint64_t* out, hipStream_t s);
 
 // Host mirror of the Express schedule (r <= n_out range only).

@@ -209,8 +209,14 @@ __device__ void pair_b2_u(const GramLaunch& a, int z, int i, double& b2, double&
     xy = (sxy[0] + sxy[1]) + (sxy[2] + sxy[3]);
     yy = (syy[0] + syy[1]) + (syy[2] + syy[3]);
   };
-  const int64_t re = (static_cast<int64_t>(b) * a.src.S + list[2 * i]) * a.src.H_kv + h;
-  const int64_t ro = (static_cast<int64_t>(b) * a.src.S + list[2 * i + 1]) * a.src.H_kv + h;
+  const int32_t te = list[2 * i], to = list[2 * i + 1];
+  if ((static_cast<uint32_t>(te) >= static_cast<uint32_t>(a.src.S) ||
+       static_cast<uint32_t>(to) >= static_cast<uint32_t>(a.src.S)) && a.err)
+    __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  const int64_t S1 = a.src.S - 1;
+  const int64_t ce = te < 0 ? 0 : (te > S1 ? S1 : te), co = to < 0 ? 0 : (to > S1 ? S1 : to);
+  const int64_t re = (static_cast<int64_t>(b) * a.src.S + ce) * a.src.H_kv + h;
+  const int64_t ro = (static_cast<int64_t>(b) * a.src.S + co) * a.src.H_kv + h;
   double kee, keo, koo, vee, veo, voo;
   dots(a.src.k, a.src.E, re, ro, kee, keo, koo);
   dots(a.src.v, a.src.D, re, ro, vee, veo, voo);
@@ -428,7 +434,11 @@ __device__ void gram_tile(const GramLaunch& a, int nthr, lds_byte* smem, double*
     t.wofs = threadIdx.x;
     t.loader = slot < (diag ? 64 : 128);
     const int tp = slot_point(slot & 63);
-    const int tok = t.loader ? token((slot < 64 ? 64 * tr : 64 * tc) + tp) : 0;
+    int tok = t.loader ? token((slot < 64 ? 64 * tr : 64 * tc) + tp) : 0;
+    if (static_cast<uint32_t>(tok) >= static_cast<uint32_t>(a.src.S)) {   // clamped, and reported
+      if (a.err) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      tok = tok < 0 ? 0 : static_cast<int>(a.src.S - 1);
+    }
     const int elt = BF16 ? 2 : 4;
     const int64_t row = (static_cast<int64_t>(b) * a.src.S + tok) * a.src.H_kv + h;
     t.kp = static_cast<const unsigned char*>(a.src.k) + (row * a.src.E + 8 * half) * elt;
@@ -813,6 +823,15 @@ __global__ void fill_coreset_kernel(const int32_t* src, int64_t src_stride, int 
   if (idx) idx[i] = src ? src[u * src_stride + j] : static_cast<int32_t>(j);
   if (w) w[i] = wv;
   if (len && j == 0) len[u] = n;
+}
+
+__global__ void sanitize_indices_kernel(const int32_t* in, int64_t n, int32_t S, int32_t* out, int* err) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t x = in[i];
+  const bool bad = static_cast<uint32_t>(x) >= static_cast<uint32_t>(S);
+  out[i] = bad ? (x < 0 ? 0 : S - 1) : x;
+  if (bad && err) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 __global__ void philox_words_kernel(const uint64_t* ctr, int64_t n, uint64_t seed, uint64_t* out) {
@@ -1315,6 +1334,12 @@ hipError_t launch_fill_coreset(const int32_t* src, int64_t src_stride, int units
   const int64_t total = static_cast<int64_t>(units) * n;
   hipLaunchKernelGGL(fill_coreset_kernel, dim3(grid1d(total, 256)), dim3(256), 0, s, src, src_stride, units, n, w,
                      idx, wout, len);
+  return hipGetLastError();
+}
+
+hipError_t launch_sanitize_indices(const int32_t* in, int64_t n, int32_t S, int32_t* out, int* err, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(sanitize_indices_kernel, dim3(grid1d(n, 256)), dim3(256), 0, s, in, n, S, out, err);
   return hipGetLastError();
 }
 

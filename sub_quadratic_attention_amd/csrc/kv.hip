@@ -397,15 +397,18 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
     else if (tid == KP + VP)
       a.state_tok[dst] = a.new_tok;
   }
-  // the last workgroup of the unit merges the partials: every thread's
-  // partial stores have completed (reached the coherence point) before the
-  // workgroup's count is taken, and the merge reads them from there
+  // the last workgroup of the unit merges the partials.  The workgroup's
+  // partial stores happen before its count (barrier, then a release at device
+  // scope by the counting thread); the workgroup that takes the last count
+  // acquires at device scope before any of its threads reads a partial.
   __shared__ int s_last;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(&a.cnt[u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             static_cast<int>(gridDim.x) - 1;
+  if (tid == 0) {
+    const int prior = __hip_atomic_fetch_add(&a.cnt[u], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prior == static_cast<int>(gridDim.x) - 1;
+    if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
   __syncthreads();
   if (!s_last) return;   // the whole workgroup
   combine_unit<BF16, D, G>(a.partial, u, gridDim.x, a.H, a.H_kv, a.out, sv);

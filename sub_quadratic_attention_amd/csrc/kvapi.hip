@@ -282,6 +282,36 @@ int bulk_ingest(thin_kv& kv, const void* k, const void* v, int64_t n_new, uint8_
   return THIN_OK;
 }
 
+// The counters every state holds after `tokens` tokens (the schedule is fixed
+// by the token count): nblk full blocks; while fewer than 4 the cache holds
+// them all (m = 1); after that, with m = 4^E the largest power of four <= nblk,
+// the cache holds HALVE E's output and the batches completed since, and the
+// buffer one representative per completed group of the batch in progress.
+struct Counters {
+  int64_t m;
+  int nC, nBf, nRaw, nb, nh;
+};
+
+Counters counters_after(int64_t n, int64_t tokens) {
+  Counters c{1, 0, 0, 0, 0, 0};
+  const int64_t nblk = tokens / n;
+  c.nRaw = static_cast<int>(tokens - nblk * n);
+  if (nblk < 4) {
+    c.nC = static_cast<int>(nblk * n);
+    return c;
+  }
+  int E = 1;
+  while ((1LL << (2 * (E + 1))) <= nblk) ++E;
+  const int64_t m = 1LL << (2 * E);
+  const int64_t since = nblk - m, nbc = since / m, rem = since % m;
+  c.m = m;
+  c.nC = static_cast<int>(n * (1 + nbc));
+  c.nBf = static_cast<int>((rem * 2 * n) / m);
+  c.nh = E;
+  c.nb = static_cast<int>(3 * (E - 1) + nbc);
+  return c;
+}
+
 int check_kv(thin_kv* kv) {
   if (!kv || !kv->h) return THIN_EINVAL;
   kv->h->err.clear();
@@ -304,7 +334,9 @@ int thin_attn_kv_create(thin_attn_t* h, void* state, size_t state_bytes, int64_t
   if (B <= 0) return fail(h, THIN_EINVAL, "B must be positive");
   if (n_out == 0) n_out = h->cfg.n_out;
   if (n_out < 2 || !pow2(n_out)) return fail(h, THIN_EINVAL, "n_out must be a power of two >= 2");
-  if (n_out > 4096) return fail(h, THIN_ENOTSUP, "n_out above 4096");
+  if (!walk_fits(4 * n_out))
+    return fail(h, THIN_ENOTSUP, "n_out = %lld: the halving of a full cache (%lld points) exceeds the walk's LDS",
+                (long long)n_out, (long long)(4 * n_out));
   const int G = h->cfg.H / h->cfg.H_kv;
   if (!thin::kv_decode_supported(h->cfg.dtype == THIN_BF16, h->cfg.E, h->cfg.D, G))
     return fail(h, THIN_ENOTSUP, "decode not built for E=%d D=%d and %d query heads per KV head", h->cfg.E, h->cfg.D, G);
@@ -472,6 +504,21 @@ int thin_attn_kv_import(thin_kv_t* kv, const void* host, size_t bytes) {
   if (m.magic != 0x544b5631u || m.version != 1) return fail(kv->h, THIN_EINVAL, "not a state export");
   if (m.B != kv->B || m.units != kv->units || m.n != kv->n || m.seed != kv->seed)
     return fail(kv->h, THIN_EINVAL, "export of a different state (B, heads, n_out or seed)");
+  // every counter is fixed by the token count: a record that disagrees is
+  // corrupt, and restoring it would let later calls address slots outside the
+  // state's rows
+  if (m.tokens < 0 || m.tokens >= (1LL << 30)) return fail(kv->h, THIN_EINVAL, "token count out of range");
+  {
+    thin_kv probe = *kv;
+    probe.tokens = 0;
+    probe.m = 1;
+    probe.nC = probe.nBf = probe.nRaw = probe.nb = probe.nh = 0;
+    if (!kv_range_ok(probe, m.tokens)) return fail(kv->h, THIN_ENOTSUP, "token count beyond the supported schedule");
+  }
+  const Counters want = counters_after(kv->n, m.tokens);
+  if (m.m != want.m || m.nC != want.nC || m.nBf != want.nBf || m.nRaw != want.nRaw || m.nb != want.nb ||
+      m.nh != want.nh)
+    return fail(kv->h, THIN_EINVAL, "state counters do not match the schedule of %lld tokens", (long long)m.tokens);
   kv->nC = m.nC;
   kv->nBf = m.nBf;
   kv->nRaw = m.nRaw;

@@ -176,3 +176,86 @@ def test_timing_records_start_empty():
         assert lib.thin_attn_set_timing(h, 0) == 0
     finally:
         lib.thin_attn_destroy(h)
+
+
+def test_compress_bin_beyond_walk_lds_is_rejected():
+    """S = 16396 = 4 * 4099: one Compress level whose bin holds all 16396 points; its walk
+    would need 263 KB of LDS.  Rejected before any launch (fake device pointers)."""
+    lib = _lib()
+    rc, h = _create()
+    fake = ctypes.c_void_p(0x1000)
+    try:
+        rc = lib.thin_attn_forward(h, fake, fake, fake, 1, 16396, 16396, 0, 0, fake, None, None, None, None,
+                                   ctypes.c_void_p(0x100000), 1 << 40, None)
+        assert rc == -2 and b"LDS" in lib.thin_attn_last_error(h)
+        key_idx = ctypes.c_void_p(0x2000)
+        rc = lib.thin_attn_forward_subset(h, fake, fake, fake, key_idx, 1, 16, 20000, 16396, 0, fake, None, None,
+                                          None, None, ctypes.c_void_p(0x100000), 1 << 40, None)
+        assert rc == -2
+    finally:
+        lib.thin_attn_destroy(h)
+
+
+def test_cache_halving_beyond_walk_lds_is_rejected():
+    """n_out = 2048: a HALVE of 8192 points does not fit the walk's LDS."""
+    lib = _lib()
+    rc, h = _create(dtype=1, E=128, D=128, n_out=2048)
+    fake = ctypes.c_void_p(0x1000)
+    try:
+        rc = lib.thin_attn_forward(h, fake, fake, fake, 1, 8192, 8192, 1, 0, fake, None, None, None, None,
+                                   ctypes.c_void_p(0x100000), 1 << 40, None)
+        assert rc == -2 and b"LDS" in lib.thin_attn_last_error(h)
+        # below four blocks nothing is halved: accepted as far as the argument checks go
+        assert lib.thin_attn_workspace_size(h, 1, 6000, 6000, 1) >= 256
+        kv = ctypes.c_void_p()
+        rc = lib.thin_attn_kv_create(h, ctypes.c_void_p(0x100000), 1 << 40, 1, 2048, 0, ctypes.byref(kv))
+        assert rc == -2
+    finally:
+        lib.thin_attn_destroy(h)
+
+
+def _kv_on_fake_state(lib, h, n=16):
+    """A streaming state over a fake (never touched) device buffer: export / import are host-only."""
+    kv = ctypes.c_void_p()
+    need = lib.thin_attn_kv_state_size(h, 1, n)
+    assert need > 0
+    rc = lib.thin_attn_kv_create(h, ctypes.c_void_p(0x100000), need, 1, n, 7, ctypes.byref(kv))
+    assert rc == 0
+    return kv
+
+
+def test_kv_import_rejects_tampered_counters():
+    """Export of a fresh state, then records whose counters disagree with their token count
+    (raw block past the block, oversized cache, buffer with no epoch) are refused."""
+    import struct
+    lib = _lib()
+    rc, h = _create(dtype=1, E=128, D=128, H=4, H_kv=2)
+    try:
+        kv = _kv_on_fake_state(lib, h)
+        size = lib.thin_attn_kv_export(kv, None, 0)
+        buf = ctypes.create_string_buffer(size)
+        assert lib.thin_attn_kv_export(kv, buf, size) == size
+        fmt = "<IIiiiiiiiiqqQ"   # magic, version, B, units, n, nC, nBf, nRaw, nb, nh, tokens, m, seed
+        assert struct.calcsize(fmt) <= size
+        rec = list(struct.unpack_from(fmt, buf.raw))
+        assert lib.thin_attn_kv_import(kv, buf, size) == 0          # the untouched record
+
+        def imported(**kw):
+            r = list(rec)
+            names = ["magic", "version", "B", "units", "n", "nC", "nBf", "nRaw", "nb", "nh", "tokens", "m", "seed"]
+            for k2, v2 in kw.items():
+                r[names.index(k2)] = v2
+            b2 = ctypes.create_string_buffer(size)
+            struct.pack_into(fmt, b2, 0, *r)
+            return lib.thin_attn_kv_import(kv, b2, size)
+
+        n = rec[4]
+        assert imported(tokens=5 * n + 3, nC=n, nBf=n // 2, nRaw=3, nb=0, nh=1, m=4) == 0   # a consistent record
+        assert imported(nRaw=n + 5, tokens=n + 5) == -1           # raw block longer than a block
+        assert imported(tokens=3 * n, nC=4 * n) == -1             # cache of 4n after 3 blocks
+        assert imported(tokens=2 * n, nC=2 * n, nBf=5) == -1      # buffer before any thin phase
+        assert imported(tokens=-1) == -1
+        assert imported(n=32) == -1                               # another state's record
+        lib.thin_attn_kv_destroy(kv)
+    finally:
+        lib.thin_attn_destroy(h)

@@ -129,7 +129,7 @@ def test_greedy_signs_with_base_subsampling():
 
 
 def test_greedy_signs_unmasked():
-    """Greedy signs (u = 1/2 in every walk) over BigGAN-shaped bins, N = 4 .. 128
+    """Greedy signs (keep the first point iff alpha_i < 0, in every walk) over BigGAN-shaped bins, N = 4 .. 128
     (small, medium and Gram + sweep kernels).  The decisions do not depend on the seed."""
     d = inputs.biggan_self_attention(seed=5, B=1)
     qs = sample_queries(1, 4096, 1, 300, always=[(0, 4095, 0)])

@@ -79,7 +79,7 @@ def test_decode_crosses_batch_and_halve():
 
 
 def test_decode_greedy_signs():
-    """Greedy-sign halvings in the streaming state: the same stream as above, u = 1/2 in every walk."""
+    """Greedy-sign halvings in the streaming state: the same stream as above, keep-first iff alpha_i < 0 in every walk."""
     d = _stream(0, 1900, 200, Hkv=2, H=8)
     _check("greedy bulk 1900 + 200 steps", d, 32, 8, 2, 128, 128, greedy=True)
 

@@ -1,7 +1,10 @@
 """Parity at the benchmark sizes, in the launch configuration bench.py times.
 
-Every unit's decisions and coreset are checked; outputs on sampled queries
-(the oracle computes them one by one), always including the first and last
+Every unit's decisions and coreset are checked, and every output row: the
+oracle forms a unit's (unmasked) or an Express block's (causal) outputs
+together from the replayed coreset.  The approximation error against exact
+attention is taken on sampled queries (exact fp64 attention of every row of
+the causal prefill would be 8.8 TFLOP), always including the first and last
 token of the first and last unit.
 """
 
@@ -25,21 +28,22 @@ def _gpu():
 def test_vit_token_mixing_full():
     d = inputs.vit_token_mixing(seed=0)
     qs = sample_queries(64, 3136, 1, 600, seed=1, always=[(0, 0, 0), (63, 3135, 0)])
-    s = run_and_compare("vit B=64 S=3136", d, False, 1, 1, 64, 64, queries=qs)
+    s = run_and_compare("vit B=64 S=3136", d, False, 1, 1, 64, 64, block_outputs=True, error_queries=qs)
     assert s["decisions"] == 175616
 
 
 def test_biggan_self_attention_full():
     d = inputs.biggan_self_attention(seed=0)
     qs = sample_queries(32, 4096, 1, 600, seed=2, always=[(0, 0, 0), (31, 4095, 0)])
-    s = run_and_compare("biggan B=32 S=4096", d, False, 1, 1, 64, 256, queries=qs)
+    s = run_and_compare("biggan B=32 S=4096", d, False, 1, 1, 64, 256, block_outputs=True, error_queries=qs)
     assert s["decisions"] == 129024
 
 
 def test_causal_prefill_full():
     d = inputs.causal_prefill(seed=0)
     qs = sample_queries(1, 32768, 32, 800, seed=3, always=[(0, 0, 0), (0, 32767, 31), (0, 1023, 5), (0, 1024, 5)])
-    s = run_and_compare("causal prefill H=32 S=32768", d, True, 32, 32, 128, 128, queries=qs)
+    s = run_and_compare("causal prefill H=32 S=32768", d, True, 32, 32, 128, 128, block_outputs=True,
+                        error_queries=qs)
     assert s["decisions"] == 131072
 
 
@@ -54,5 +58,6 @@ def test_vit_token_mixing_subsampled_full():
     Compress of 448 points per unit, 56 coreset points of weight 56."""
     d = inputs.vit_token_mixing(seed=0)
     qs = sample_queries(64, 3136, 1, 600, seed=4, always=[(0, 0, 0), (63, 3135, 0)])
-    s = run_and_compare("vit subsampled B=64 S=3136", d, False, 1, 1, 64, 64, queries=qs, subsample_base=True)
+    s = run_and_compare("vit subsampled B=64 S=3136", d, False, 1, 1, 64, 64, subsample_base=True,
+                        block_outputs=True, error_queries=qs)
     assert s["decisions"] == 64 * 392 and s["idx"].shape[1] == 56

@@ -208,3 +208,13 @@ def test_base_subsampling_off_when_r_is_one():
     a = cmp.thin_unmasked(K, V, 0.3, 0.5, 2, 0, subsample_base=True)
     b = cmp.thin_unmasked(K, V, 0.3, 0.5, 2, 0)
     assert np.array_equal(a[0], b[0]) and a[1] == b[1]
+
+
+def test_block_outputs_match_per_query_unmasked():
+    """Unmasked outputs formed a unit at a time agree with the query-at-a-time path."""
+    rng = np.random.default_rng(19)
+    B, T, S, H, Hkv = 2, 33, 256, 4, 2
+    q = rng.standard_normal((B, T, H, 8)); k = rng.standard_normal((B, S, Hkv, 8)); v = rng.standard_normal((B, S, Hkv, 4))
+    a = fwd.forward(q, k, v, seed=4)
+    b = fwd.forward(q, k, v, seed=4, block_outputs=True)
+    assert np.max(np.abs(a["out"] - b["out"])) <= 1e-13

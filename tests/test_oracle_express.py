@@ -162,3 +162,25 @@ def test_causal_error_shrinks_with_cache_size():
     errs = [att.rel_frobenius_error(fwd.forward(q, k, v, causal=True, n_out=n, queries=rows)["out"], ref)
             for n in (32, 64, 128)]
     assert errs[0] > errs[1] > errs[2], errs
+
+
+@pytest.mark.parametrize("S,n,H,Hkv", [(4096 + 77, 64, 2, 1), (500, 16, 4, 2), (67, 4, 1, 1), (300, 512, 2, 2)])
+def test_block_outputs_match_per_query(S, n, H, Hkv):
+    """Causal outputs formed a block at a time (one masked weighted attention per Express
+    block) agree with the query-at-a-time visible sets, HALVEs included."""
+    rng = np.random.default_rng(S + n)
+    q = rng.standard_normal((1, S, H, 8)); k = rng.standard_normal((1, S, Hkv, 8)); v = rng.standard_normal((1, S, Hkv, 4))
+    a = fwd.forward(q, k, v, causal=True, n_out=n, seed=2)
+    b = fwd.forward(q, k, v, causal=True, n_out=n, seed=2, block_outputs=True)
+    assert np.max(np.abs(a["out"] - b["out"])) <= 1e-12
+    for u in a["coreset"]:
+        assert np.array_equal(a["coreset"][u][0], b["coreset"][u][0])
+        assert np.array_equal(a["log"][u], b["log"][u])
+
+
+def test_block_outputs_exact_when_disabled():
+    rng = np.random.default_rng(3)
+    S = 200
+    q = rng.standard_normal((1, S, 2, 8)); k = rng.standard_normal((1, S, 2, 8)); v = rng.standard_normal((1, S, 2, 4))
+    out = fwd.forward(q, k, v, causal=True, n_out=256, block_outputs=True)["out"]
+    assert np.max(np.abs(out - fwd.exact(q, k, v, causal=True))) <= 1e-12

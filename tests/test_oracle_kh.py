@@ -218,7 +218,7 @@ def test_greedy_walk_norm_bound(N, seed):
 
 
 def test_greedy_degenerate_pair_keeps_second():
-    """b = 0 gives p = 1/2 and u = 1/2: the strict test u < p keeps the second point."""
+    """b = 0 gives alpha_0 = 0 for the first pair: keep-first needs alpha < 0, so the second point is kept."""
     K = np.zeros((2, 3)); V = np.ones((2, 2))
     keep, margins = khm.kernel_halving(K, V, 1.0, 0.5, 4, 5, 9, 1, greedy=True)
     assert not keep[0] and margins[0] == 0.0
