@@ -28,7 +28,7 @@ import time
 import numpy as np
 
 METRIC = "thinned-attention queries·keys/sec & ms/call vs exact attn; HBM GB/s, MFMA %"
-PEAK = {"hbm_GBs": 8000.0, "f32": 157.3, "bf16": 2500.0, "f64": 78.6}   # MI355X: HBM GB/s, dense TFLOP/s
+PEAK = {"hbm_GBs": 8000.0, "f32": 157.3, "bf16": 2500.0, "fp8": 5000.0, "f64": 78.6}   # MI355X: HBM GB/s, dense TFLOP/s
 
 WORKLOADS = {
     # name: (generator kwargs, causal, H, H_kv, E, D)
@@ -40,7 +40,12 @@ WORKLOADS = {
     "selected_keys": (dict(), False, 32, 8, 128, 128),   # thinning after a KV selector (top 4096 of 32768 keys)
     # the ViT layer under the sqrt(S) size rule: base subsampling, then the Compress (56 coreset points)
     "vit_token_mixing_subsampled": (dict(), False, 1, 1, 64, 64),
+    # the causal prefill and the decode state with FP8 (E4M3) inputs
+    "causal_prefill_fp8": (dict(), True, 32, 32, 128, 128),
+    "kv_decode_fp8": (dict(), True, 32, 8, 128, 128),
 }
+TORCH_DTYPE = {"f32": "float32", "bf16": "bfloat16", "fp8": "float8_e4m3fn"}
+ELT = {"f32": 4, "bf16": 2, "fp8": 1}
 FLAGS = {"vit_token_mixing_subsampled": dict(subsample_base=True)}   # ThinAttention options per workload
 
 
@@ -117,7 +122,7 @@ def express_gram_entries(S, n):
     return halves * (tri(4 * n) + tri(2 * n)) + done * tri(2 * n)
 
 
-def work_model(name, B, T, S, H, Hkv, E, D, causal, elt, subsample_base=False):
+def work_model(name, B, T, S, H, Hkv, E, D, causal, elt, subsample_base=False, out_elt=None):
     """Per-forward algorithmic flops / bytes of each kernel label."""
     units = B * Hkv
     if not causal:
@@ -139,7 +144,7 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt, subsample_base=False):
         keys = n_out
         pairs_eff = B * H * T * S_full
         visible = B * H * T * keys
-        attn_bytes = (B * T * H * (E + D) + units * n_out * (E + D)) * elt
+        attn_bytes = (B * T * H * E + units * n_out * (E + D)) * elt + B * T * H * D * (out_elt or elt)
     else:
         n_out = 2
         while n_out * n_out < S:
@@ -149,11 +154,12 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt, subsample_base=False):
         medium_entries = 0
         pairs_eff = B * H * T * (T + 1) // 2
         visible = B * H * express_visible_total(S, n_out)
-        attn_bytes = (B * T * H * E + units * S * (E + D) + B * T * H * D) * elt
+        attn_bytes = (B * T * H * E + units * S * (E + D)) * elt + B * T * H * D * (out_elt or elt)
     return dict(
         n_out=n_out,
         pairs_eff=pairs_eff,
-        attention=dict(flops=2.0 * visible * (E + D), bytes=attn_bytes),
+        attention=dict(flops=2.0 * visible * (E + D), bytes=attn_bytes, qk_flops=2.0 * visible * E,
+                       pv_flops=2.0 * visible * D),
         pair_gram=dict(flops=2.0 * (E + D) * gram_entries * units, bytes=None) if gram_entries else None,
         small_halving=dict(flops=None, bytes=small_bytes) if small_bytes else None,
         medium_halving=dict(flops=2.0 * (E + D) * medium_entries * units, bytes=None) if medium_entries else None,
@@ -242,22 +248,25 @@ def decode_main(args):
     from sub_quadratic_attention_amd import inputs
     from sub_quadratic_attention_amd.binding import KVState, ThinAttention
 
-    _, _, H, Hkv, E, D = WORKLOADS["kv_decode"]
-    d = inputs.kv_decode(seed=0)
+    _, _, H, Hkv, E, D = WORKLOADS[args.workload]
+    d = inputs.workload(args.workload, seed=0)
+    dt = d["dtype"]
+    tdt = getattr(torch, TORCH_DTYPE[dt])
+    odt = torch.bfloat16 if dt == "fp8" else tdt
     S0 = d["k_hist"].shape[1]
     n_out = 2
     while n_out * n_out < S0:
         n_out *= 2
     # the oracle on the host cores first: its worker processes fork before the GPU is touched
     cpu = None if args.no_cpu_baseline else cpu_baseline("kv_decode", d, H, Hkv, True, {}, n_out=n_out)
-    kh, vh = (torch.from_numpy(d[x]).to(torch.bfloat16).cuda() for x in ("k_hist", "v_hist"))
-    qs, ks, vs = (torch.from_numpy(d[x]).to(torch.bfloat16).cuda() for x in ("q_steps", "k_steps", "v_steps"))
+    kh, vh = (torch.from_numpy(d[x]).to(tdt).cuda() for x in ("k_hist", "v_hist"))
+    qs, ks, vs = (torch.from_numpy(d[x]).to(tdt).cuda() for x in ("q_steps", "k_steps", "v_steps"))
     B = kh.shape[0]
     steps_dec = qs.shape[1]
-    ta = ThinAttention(E, D, H, Hkv, torch.bfloat16)
+    ta = ThinAttention(E, D, H, Hkv, tdt)
     st = KVState(ta, B, n_out)
     st._workspace(S0)
-    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, H, D), dtype=odt, device="cuda")
     stream = torch.cuda.current_stream()
 
     def one_pass(timing=False):
@@ -316,22 +325,24 @@ def decode_main(args):
     torch.cuda.synchronize()
     _, _, ln = tmp.coreset()
     vis_rows = int(ln.sum().item())
-    dec_bytes = vis_rows * (E + D) * 2 + B * H * (E + D) * 2
+    dec_bytes = vis_rows * (E + D) * ELT[dt] + B * H * E * ELT[dt] + B * H * D * (2 if dt == "fp8" else ELT[dt])
     kd = per_kernel.get("kv_decode", {})
     roof = None
     if kd:
         gbs = dec_bytes / (kd["avg_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK["hbm_GBs"], "unit": "GB/s",
-                "frac": round(gbs / PEAK["hbm_GBs"], 4), "traffic": _traffic("kv_decode", "kv_decode"),
+                "frac": round(gbs / PEAK["hbm_GBs"], 4), "traffic": _traffic("kv_decode", args.workload),
                 "kernel": "kv_decode",
                 "work_per_launch_bytes": dec_bytes, "avg_launch_ms": kd["avg_ms"]}
     exact = {}
     if not args.no_exact:
         # exact decode over the full cache (GQA by repeating KV heads), one step
-        kt = torch.cat([kh, ks], dim=1).permute(0, 2, 1, 3).repeat_interleave(H // Hkv, dim=1).contiguous()
-        vt = torch.cat([vh, vs], dim=1).permute(0, 2, 1, 3).repeat_interleave(H // Hkv, dim=1).contiguous()
+        # (SDPA has no fp8 kernel: its comparator runs on the same values in bf16)
+        sdt = odt
+        kt = torch.cat([kh, ks], dim=1).to(sdt).permute(0, 2, 1, 3).repeat_interleave(H // Hkv, dim=1).contiguous()
+        vt = torch.cat([vh, vs], dim=1).to(sdt).permute(0, 2, 1, 3).repeat_interleave(H // Hkv, dim=1).contiguous()
         f = torch.nn.functional.scaled_dot_product_attention
-        qq = qs[:, -1].reshape(B, H, 1, E)
+        qq = qs[:, -1].to(sdt).reshape(B, H, 1, E)
         for _ in range(3):
             f(qq, kt, vt)
         torch.cuda.synchronize()
@@ -347,8 +358,8 @@ def decode_main(args):
         # exactly the causal decode of the last token)
         kf, vf = torch.cat([kh, ks], dim=1).contiguous(), torch.cat([vh, vs], dim=1).contiguous()
         q1 = qs[:, -1:].contiguous()
-        o1 = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device="cuda")
-        ex = ThinAttention(E, D, H, Hkv, torch.bfloat16)
+        o1 = torch.empty((B, 1, H, D), dtype=odt, device="cuda")
+        ex = ThinAttention(E, D, H, Hkv, tdt)
         for _ in range(3):
             ex.coreset_attention(q1, kf, vf, out=o1, stream=stream)
         torch.cuda.synchronize()
@@ -361,8 +372,8 @@ def decode_main(args):
     line = {
         "metric": METRIC, "value": pairs / (ms_per_step * 1e-3), "unit": "queries·keys/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "kv_decode", "B": B, "H": H, "H_kv": Hkv, "S0": S0, "decode_steps": steps_dec,
+        "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "H_kv": Hkv, "S0": S0, "decode_steps": steps_dec,
                    "E": E, "D": D, "n_out": n_out, "seed": 0},
         "decode_us_per_token": decode_us,
         "kernels": {l: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
@@ -394,7 +405,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
         return
-    if args.workload == "kv_decode":
+    if args.workload.startswith("kv_decode"):
         return decode_main(args)
     gen_kw, causal, H, Hkv, E, D = WORKLOADS[args.workload]
     d = inputs.workload(args.workload, seed=0, **gen_kw)
@@ -405,13 +416,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dt = d["dtype"]
-    tdt = torch.float32 if dt == "f32" else torch.bfloat16
-    elt = 4 if dt == "f32" else 2
+    tdt = getattr(torch, TORCH_DTYPE[dt])
+    odt = torch.bfloat16 if dt == "fp8" else tdt   # fp8 inputs give bf16 outputs
+    elt = ELT[dt]
     q, k, v = (torch.from_numpy(d[x]).to(tdt).cuda() for x in ("q", "k", "v"))
     B, T = q.shape[:2]
     S = k.shape[1]
     ta = ThinAttention(E, D, H, Hkv, tdt, **opts)
-    out = torch.empty((B, T, H, D), dtype=tdt, device="cuda")
+    out = torch.empty((B, T, H, D), dtype=odt, device="cuda")
     stream = torch.cuda.current_stream()
     sel = d.get("key_idx")   # thinning after a selector: the list is the point set (L keys per unit)
     if sel is not None:
@@ -445,7 +457,8 @@ def main():
     recs = ta.timing_records()
     ta.set_timing(False)
 
-    wm = work_model(args.workload, B, T, L, H, Hkv, E, D, causal, elt, **opts)   # (a selector's list: its L keys)
+    wm = work_model(args.workload, B, T, L, H, Hkv, E, D, causal, elt, out_elt=2 if dt == "fp8" else elt,
+                    **opts)   # (a selector's list: its L keys)
     per_kernel = {}
     for label, ms in recs:
         r = per_kernel.setdefault(label, dict(launches=0, total_ms=0.0))
@@ -470,9 +483,14 @@ def main():
                     "work_per_launch_bytes": per_launch_bytes, "avg_launch_ms": r["avg_ms"]}
         per_launch_flops = w["flops"] / r["launches_per_step"]
         peak_key = "f64" if label in ("pair_gram", "medium_halving") else dt
+        peak = PEAK[peak_key]
+        if label == "attention" and dt == "fp8":
+            # Q K^T on the fp8 MFMA, P V on the bf16 MFMA: the peak of that mix of work
+            peak = w["flops"] / (w["qk_flops"] / PEAK["fp8"] + w["pv_flops"] / PEAK["bf16"])
+            peak_key = "fp8 (Q K^T) + bf16 (P V)"
         achieved = per_launch_flops / (r["avg_ms"] * 1e-3) / 1e12
-        res = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK[peak_key], "unit": "TFLOP/s",
-               "frac": round(achieved / PEAK[peak_key], 4), "traffic": None, "kernel": label,
+        res = {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1), "unit": "TFLOP/s",
+               "frac": round(achieved / peak, 4), "traffic": None, "kernel": label,
                "work_per_launch_flops": per_launch_flops, "avg_launch_ms": r["avg_ms"],
                "dtype": peak_key}
         if w.get("bytes"):
@@ -493,7 +511,8 @@ def main():
         if sel is not None:   # exact attention over the selected keys
             gi = key_idx.long().permute(0, 2, 1)[..., None]
             k, v = (torch.gather(x, 1, gi.expand(-1, -1, -1, x.shape[3])) for x in (k, v))
-        qt, kt, vt = (x.permute(0, 2, 1, 3).contiguous() for x in (q, k, v))
+        # (SDPA has no fp8 kernel: for fp8 inputs its comparator runs on the same values in bf16)
+        qt, kt, vt = (x.to(odt).permute(0, 2, 1, 3).contiguous() for x in (q, k, v))
         if Hkv != H:
             kt = kt.repeat_interleave(H // Hkv, dim=1)
             vt = vt.repeat_interleave(H // Hkv, dim=1)

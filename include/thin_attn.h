@@ -45,7 +45,12 @@
 extern "C" {
 #endif
 
-enum thin_dtype { THIN_F32 = 0, THIN_BF16 = 1 };
+/* Element types of query, key and value.  THIN_FP8_E4M3: OCP FP8 E4M3
+ * (E4M3FN: sign, 4 exponent bits of bias 7, 3 mantissa bits, no infinities,
+ * S.1111.111 NaN) as raw bytes; the output is then bfloat16, and per-tensor
+ * scale factors are the caller's to fold into `scale` (query and key) and
+ * into the output (value). */
+enum thin_dtype { THIN_F32 = 0, THIN_BF16 = 1, THIN_FP8_E4M3 = 2 };
 
 /* Configuration flags (thin_attn_config.flags).
  * THIN_GREEDY_SIGNS: every kernel-halving walk takes its signs greedily
@@ -157,13 +162,11 @@ size_t thin_attn_workspace_size(const thin_attn_t* h, int64_t B, int64_t T, int6
  * the cache (thin phase).  When the cache holds 4 n_out points it is halved
  * twice back to n_out and m becomes 4 m (HALVE).  A query at token t in block
  * beta attends to the cache and buffer left by blocks 0 .. beta-1 plus the raw
- * tokens beta n_out .. t (weight 1).  Supported while the subsampling
- * groups of every full block fit in one block (m / 2 <= n_out, m the
- * inflation in force for that block): with n_out = 2^k that is
- * S <= n_out (4^(e+1) + 1) - 1 for e = floor((k + 1) / 2), e.g. 1039 tokens
- * for n_out = 16, 131199 for 128, 262399 for 256, about 2.1 M for 512;
- * beyond, THIN_ENOTSUP.  n_out >= 2048 with S >= 4 n_out is also
- * THIN_ENOTSUP (the walk of a full cache exceeds one workgroup's LDS).
+ * tokens beta n_out .. t (weight 1).  Once m / 2 > n_out (past about
+ * 2 n_out^2 tokens) a group spans several blocks: its representative joins
+ * the buffer when the block completing the group is ingested, and until then
+ * the group's earlier tokens carry no weight.  n_out >= 2048 with S >= 4 n_out
+ * is THIN_ENOTSUP (the walk of a full cache exceeds one workgroup's LDS).
  *
  * causal = 0 needs the last Compress bin, s0 2^(j+1) points, within the
  * walk's LDS (at most 8106 points), else THIN_ENOTSUP before any launch.
@@ -262,9 +265,10 @@ int thin_attn_philox(const uint64_t* counters, int64_t n, uint64_t seed, uint64_
  * The caller allocates the device state buffer (thin_attn_kv_state_size
  * bytes, 256-byte aligned) and the per-call workspace; the returned host
  * handle holds the counters and must be destroyed with thin_attn_kv_destroy
- * before the thin_attn handle it was created from.  Supported while every
- * subsampling group lies in one block (the stream lengths of the causal
- * forward above) and for n_out <= 1024.
+ * before the thin_attn handle it was created from.  Streams of any length
+ * below 2^30 tokens; n_out <= 1024.  A subsampling group longer than a block
+ * keeps its representative's row in the state from the block that contains
+ * it until the block that completes the group.
  */
 typedef struct thin_kv thin_kv_t;
 

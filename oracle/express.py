@@ -23,16 +23,22 @@ kappa_att).  Where the pages leave a step open the reading is:
   bin = HALVE ordinal) back to n_out points, and m becomes 4 m.
 * A query at token t in block beta = t // n_out sees the cache and buffer as
   they stood after blocks 0 .. beta-1, plus the raw tokens beta*n_out .. t
-  with weight 1.  The weights of what it sees sum to t + 1.
-* Only schedules with m / 2 <= n_out are supported (true for every
-  t < 2 n_out^2, hence for all t < S under the default n_out).
+  with weight 1.
+* Groups longer than a block (r = m / 2 > n_out, reached once t passes about
+  2 n_out^2): a group contributes its representative when the block that
+  completes the group is ingested (the representative itself may lie in an
+  earlier block of the group).  The tokens of a group still in progress are
+  then in no weight until it completes, so the weights a query sees sum to
+  t + 1 - ((beta n_out) mod r) (exactly t + 1 whenever r divides n_out); the
+  cache keeps its size bound regardless of the length, as EXPRESS states.
 * A trailing partial block is never thinned.
 * Lists are kept in token order; the decision log is ordered by the halvings'
   chronological order.
 
 Pins: the HALVE positions (after 4, 16, 64, ... blocks) and the values of m;
 exact causal attention for t < 4 n_out and for n_out >= S; visible set
-below 6 n_out; weights summing to t + 1; streaming == prefill.
+below 6 n_out; weights summing to t + 1 (less the tokens of a group in
+progress); streaming == prefill.
 """
 
 import math
@@ -88,9 +94,8 @@ class ExpressCache:
             self.cache = np.concatenate([self.cache, np.arange(start, start + n)])
         else:
             r = self.m // 2
-            if r > n:
-                raise NotImplementedError("subsampling groups longer than a block")
             log2r = r.bit_length() - 1
+            # the groups this block completes (r > n: at most one, possibly begun blocks ago)
             for g in range(start // r, (start + n) // r):
                 off = philox.uniform_offset(g, log2r, self.unit,
                                             philox.TAG_SUBSAMPLE, self.seed, r)
@@ -139,9 +144,8 @@ def schedule(S, n_out):
             cache += n_out
         else:
             r = m // 2
-            if r > n_out:
-                raise NotImplementedError("subsampling groups longer than a block")
-            for _ in range(n_out // r):
+            start = blk * n_out
+            for _ in range((start + n_out) // r - start // r):   # groups completed by this block
                 buf += 1
                 if buf == 2 * n_out:
                     events.append((philox.TAG_BATCH, nb, n_out))

@@ -13,7 +13,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libthin_attn.so")
 
-THIN_F32, THIN_BF16 = 0, 1
+THIN_F32, THIN_BF16, THIN_FP8_E4M3 = 0, 1, 2
 THIN_GREEDY_SIGNS = 1
 THIN_SUBSAMPLE_BASE = 2
 _STATUS = {0: "THIN_OK", -1: "THIN_EINVAL", -2: "THIN_ENOTSUP", -3: "THIN_ENOMEM", -4: "THIN_EHIP"}
@@ -112,7 +112,14 @@ def _dtype_code(dtype):
         return THIN_F32
     if dtype == torch.bfloat16:
         return THIN_BF16
+    if dtype == torch.float8_e4m3fn:
+        return THIN_FP8_E4M3
     raise ValueError(f"unsupported dtype {dtype}")
+
+
+def output_dtype(dtype):
+    """Element type of the outputs for inputs of `dtype` (bfloat16 for FP8 inputs)."""
+    return torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype
 
 
 class ThinAttention:
@@ -129,6 +136,7 @@ class ThinAttention:
         self.E, self.D, self.H = E, D, H
         self.H_kv = H if H_kv is None else H_kv
         self.dtype = dtype
+        self.out_dtype = output_dtype(dtype)
         cfg = _Config(_dtype_code(dtype), E, D, H, self.H_kv, g, n_out, delta, scale,
                       (THIN_GREEDY_SIGNS if greedy else 0) | (THIN_SUBSAMPLE_BASE if subsample_base else 0))
         h = ctypes.c_void_p()
@@ -153,10 +161,10 @@ class ThinAttention:
     def _out(self, out, B, T, dev):
         """The output tensor: a new one, or the caller's, checked against [B, T, H, D] and the dtype."""
         if out is None:
-            return torch.empty((B, T, self.H, self.D), dtype=self.dtype, device=dev)
-        if tuple(out.shape) != (B, T, self.H, self.D) or out.dtype != self.dtype or not out.is_contiguous() \
+            return torch.empty((B, T, self.H, self.D), dtype=self.out_dtype, device=dev)
+        if tuple(out.shape) != (B, T, self.H, self.D) or out.dtype != self.out_dtype or not out.is_contiguous() \
                 or out.device != dev:
-            raise ValueError(f"out must be a contiguous {self.dtype} tensor of shape {(B, T, self.H, self.D)} on {dev}")
+            raise ValueError(f"out must be a contiguous {self.out_dtype} tensor of shape {(B, T, self.H, self.D)} on {dev}")
         return out
 
     # sizes --------------------------------------------------------------
@@ -388,7 +396,7 @@ class KVState:
     def decode(self, q, k1, v1, out=None, return_decisions=False, stream=None):
         q, k1, v1 = q.contiguous(), k1.contiguous(), v1.contiguous()
         if out is None:
-            out = torch.empty((self.B, self.attn.H, self.attn.D), dtype=self.attn.dtype, device=q.device)
+            out = torch.empty((self.B, self.attn.H, self.attn.D), dtype=self.attn.out_dtype, device=q.device)
         dec = self._decisions(1, return_decisions)
         cnt = self.decision_count(1) if return_decisions else 0
         ws = self._workspace(1)

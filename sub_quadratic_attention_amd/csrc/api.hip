@@ -5,12 +5,14 @@
 
 using namespace thinhost;
 
+
 extern "C" {
 
 int thin_attn_create(const thin_attn_config* cfg, thin_attn_t** out) {
   if (!cfg || !out) return fail(nullptr, THIN_EINVAL, "null argument");
   const thin_attn_config& c = *cfg;
-  if (c.dtype != THIN_F32 && c.dtype != THIN_BF16) return fail(nullptr, THIN_EINVAL, "unknown dtype %d", c.dtype);
+  if (c.dtype != THIN_F32 && c.dtype != THIN_BF16 && c.dtype != THIN_FP8_E4M3)
+    return fail(nullptr, THIN_EINVAL, "unknown dtype %d", c.dtype);
   if (c.E <= 0 || c.D <= 0 || c.H <= 0 || c.H_kv <= 0) return fail(nullptr, THIN_EINVAL, "dims must be positive");
   if (c.H % c.H_kv != 0) return fail(nullptr, THIN_EINVAL, "H %% H_kv != 0");
   if (c.g < 0) return fail(nullptr, THIN_EINVAL, "g must be >= 0");
@@ -19,7 +21,7 @@ int thin_attn_create(const thin_attn_config* cfg, thin_attn_t** out) {
   if (c.flags & ~static_cast<uint32_t>(THIN_GREEDY_SIGNS | THIN_SUBSAMPLE_BASE))
     return fail(nullptr, THIN_EINVAL, "unknown flags 0x%x", c.flags);
   if (!(c.scale >= 0.0f) || !std::isfinite(c.scale)) return fail(nullptr, THIN_EINVAL, "scale must be finite and >= 0");
-  if (!thin::attention_supported(c.dtype == THIN_BF16, c.E, c.D))
+  if (!thin::attention_supported(c.dtype, c.E, c.D))
     return fail(nullptr, THIN_ENOTSUP, "head dims E=%d D=%d not built for this dtype", c.E, c.D);
   thin_attn* h = new thin_attn();
   h->cfg = c;
@@ -83,7 +85,6 @@ int64_t thin_attn_decision_count(const thin_attn_t* h, int64_t S, int causal) {
   if (!h || S < 0) return THIN_EINVAL;
   if (causal) {
     const int64_t n = cache_size(h, S);
-    if (!causal_schedule_ok(S, n)) return THIN_ENOTSUP;
     return thin::express_schedule(S, static_cast<int>(n)).decisions;
   }
   const int64_t Lp = S / base_stride(h, S);
@@ -100,7 +101,6 @@ size_t thin_attn_workspace_size(const thin_attn_t* h, int64_t B, int64_t T, int6
   (void)T;
   if (causal) {
     const int64_t n = cache_size(h, S);
-    if (!causal_schedule_ok(S, n)) return 0;
     return std::max<size_t>(plan_causal(h, B, S, n).bytes, 256);
   }
   return std::max<size_t>(plan_unmasked(h, B, S).bytes, 256);
@@ -139,7 +139,7 @@ static int unmasked_path(thin_attn_t* h, const thin::PointSource& src, thin::Att
                          int64_t L, int units, uint64_t seed, uint8_t* decisions, int64_t ndec, char* ws,
                          hipStream_t st, int32_t* coreset_idx, float* coreset_w, int32_t* coreset_len) {
   const thin_attn_config& c = h->cfg;
-  const int bf16 = c.dtype == THIN_BF16;
+  const int dt = c.dtype;
   const int64_t B = al.B;
   const UnmaskedPlan p = plan_unmasked(h, B, L);
   if (p.r > 1) {   // base subsampling: one point per stratum of r; the Compress runs on L / r points
@@ -174,7 +174,7 @@ static int unmasked_path(thin_attn_t* h, const thin::PointSource& src, thin::Att
       if (thin::small_halving_supported(N, c.E, c.D)) {   // small bins: Gram and walk in one kernel
         THIN_HIP(timed(h, st, "small_halving",
                        [&] { return thin::launch_small_halving(gram_for(sl, src, h->scale64), sl, st); }));
-      } else if (thin::medium_halving_supported(N, c.E, c.D, bf16)) {   // one workgroup per bin
+      } else if (thin::medium_halving_supported(N, c.E, c.D, dt)) {   // one workgroup per bin
         THIN_HIP(timed(h, st, "medium_halving",
                        [&] { return thin::launch_medium_halving(gram_for(sl, src, h->scale64), sl, st); }));
       } else {
@@ -195,7 +195,7 @@ static int unmasked_path(thin_attn_t* h, const thin::PointSource& src, thin::Att
   al.cs_n = static_cast<int>(n_cs);
   al.cs_stride = coreset ? n_cs : 0;
   al.cs_lnw = coreset ? logf(w) : 0.f;
-  THIN_HIP(timed(h, st, "attention", [&] { return thin::launch_attention(al, bf16, c.E, c.D, st); }));
+  THIN_HIP(timed(h, st, "attention", [&] { return thin::launch_attention(al, dt, c.E, c.D, st); }));
   THIN_HIP(thin::launch_fill_coreset(coreset, al.cs_stride, units, static_cast<int>(n_cs), w, coreset_idx, coreset_w,
                                      coreset_len, st));
   return THIN_OK;
@@ -223,8 +223,8 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
   const thin_attn_config& c = h->cfg;
   const int units = static_cast<int>(B * c.H_kv);
   char* ws = static_cast<char*>(workspace);
-  const int bf16 = c.dtype == THIN_BF16;
-  thin::PointSource src{k, v, S, c.H_kv, c.E, c.D, bf16};
+  const int dt = c.dtype;
+  thin::PointSource src{k, v, S, c.H_kv, c.E, c.D, dt};
   const int64_t ndec = thin_attn_decision_count(h, S, causal);
 
   thin::AttnLaunch al{};
@@ -252,11 +252,12 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
   if (rc) return rc;
   al.causal = 1;
   al.ev = ev;
-  THIN_HIP(timed(h, st, "attention", [&] { return thin::launch_attention(al, bf16, c.E, c.D, st); }));
+  THIN_HIP(timed(h, st, "attention", [&] { return thin::launch_attention(al, dt, c.E, c.D, st); }));
   THIN_HIP(thin::launch_express_final(ev, units, static_cast<int>(S), coreset_idx, coreset_w, coreset_len, 6LL * n,
                                       st));
   return THIN_OK;
 }
+
 
 int thin_attn_forward_subset(thin_attn_t* h, const void* q, const void* k, const void* v, const int32_t* key_idx,
                              int64_t B, int64_t T, int64_t S, int64_t L, uint64_t seed, void* out,
@@ -279,7 +280,7 @@ int thin_attn_forward_subset(thin_attn_t* h, const void* q, const void* k, const
     return fail(h, THIN_EINVAL, "workspace must be 256-byte aligned");
   const thin_attn_config& c = h->cfg;
   const int units = static_cast<int>(B * c.H_kv);
-  thin::PointSource src{k, v, S, c.H_kv, c.E, c.D, c.dtype == THIN_BF16};
+  thin::PointSource src{k, v, S, c.H_kv, c.E, c.D, c.dtype};
   thin::AttnLaunch al{};
   al.q = q;
   al.k = k;
@@ -333,7 +334,7 @@ int thin_attn_coreset_attention(thin_attn_t* h, const void* q, const void* k, co
   al.cs_stride = idx ? n : 0;
   al.cs_lnw = 0.f;
   al.err = h->err_dev;
-  THIN_HIP(thin::launch_attention(al, c.dtype == THIN_BF16, c.E, c.D, as_stream(stream)));
+  THIN_HIP(thin::launch_attention(al, c.dtype, c.E, c.D, as_stream(stream)));
   return THIN_OK;
 }
 
@@ -352,7 +353,7 @@ int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, i
   const thin_attn_config& c = h->cfg;
   const int units = static_cast<int>(B * c.H_kv);
   const hipStream_t st = as_stream(stream);
-  thin::PointSource src{k, v, S, c.H_kv, c.E, c.D, c.dtype == THIN_BF16};
+  thin::PointSource src{k, v, S, c.H_kv, c.E, c.D, c.dtype};
   const int n = static_cast<int>(N);
   thin::SweepLaunch sl = make_sweep(h, gram, n, units, 1, points, n, kept, seed, tag, bin);
   thin::GramLaunch gl = gram_for(sl, src, h->scale64);

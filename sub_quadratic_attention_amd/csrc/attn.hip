@@ -1,11 +1,15 @@
-// Weighted-coreset / Express softmax attention on gfx950, fp32 and bf16.
+// Weighted-coreset / Express softmax attention on gfx950, fp32, bf16 and fp8.
 //
 // out(q) = sum_j w_j e^{s <q, k_j>} v_j / sum_j w_j e^{s <q, k_j>} over the keys
 // a query sees ("Express Language Modeling": attention against a small
 // weighted summary of the keys and values).  ln w_j is folded into the logit,
 // the softmax is taken online (running maximum and sum), accumulation is fp32,
 // and both products run on MFMA: v_mfma_f32_16x16x32_bf16 for bf16 inputs,
-// v_mfma_f32_16x16x4f32 for fp32 inputs.
+// v_mfma_f32_16x16x4f32 for fp32 inputs.  FP8 (E4M3) inputs take Q K^T on the
+// gfx950 FP8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, unit scales, one
+// instruction per 128 features) and P V on the bf16 MFMA: V rows are widened
+// to bf16 (exactly) as they are staged, and P is rounded to bf16 as for bf16
+// inputs, so the arithmetic after Q K^T is the bf16 path's.
 //
 // The keys a query sees are a gathered part (a coreset, or the cache and
 // buffer index lists of the Express state, each list with its log-weight)
@@ -60,8 +64,11 @@ constexpr int kIdxPT = kIdxCap / kThreads;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters unconstrained
 
-template <bool BF16, int E, int D>
-constexpr int nqg() { return (BF16 ? (E <= 128 && D <= 128) : D <= 64) ? 2 : 1; }   // 16-query groups per wave
+template <int ET, int E, int D>
+constexpr int nqg() { return (ET != kF32 ? (E <= 128 && D <= 128) : D <= 64) ? 2 : 1; }   // 16-query groups per wave
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) unsigned char lds_byte;   // LDS views of the buffers
 
@@ -93,7 +100,7 @@ __device__ __forceinline__ float group_sum(float x) {
 template <int RB>
 __device__ __forceinline__ int kswz(int R) { return RB == 128 ? (R >> 1) & 7 : R & 15; }
 template <bool BF16, int RB>
-__device__ __forceinline__ int vswz(int R) {
+__device__ __forceinline__ int vswz(int R) {   // BF16: V staged as bf16 rows (bf16 and fp8 inputs)
   if constexpr (!BF16) return 0;
   else return RB == 128 ? 2 * ((R >> 1) & 3) : 2 * (R & 7);
 }
@@ -118,9 +125,10 @@ struct Raw {
 // NB chunk buffers: two let the copy of the next chunk overlap the current
 // one; a stream of at most one chunk (a coreset of <= kC keys) needs one,
 // which leaves LDS for more workgroups per CU.
-template <bool BF16, int E, int D, int NB>
+template <int ET, int E, int D, int NB>
 struct Smem {
-  static constexpr int KB = E * (BF16 ? 2 : 4), VB = D * (BF16 ? 2 : 4);   // row bytes
+  // row bytes: K as given, V as staged (bf16 for fp8 inputs)
+  static constexpr int KB = E * elt_size<ET>(), VB = D * (ET == kF32 ? 4 : 2);
   alignas(16) unsigned char k[NB][kC * KB];   // 16-byte pieces permuted by kswz(row)
   alignas(16) unsigned char v[NB][kC * VB];   // 16-byte pieces permuted by vswz(row)
   float lnw2[NB][kC];
@@ -131,20 +139,26 @@ struct Smem {
 // RAW: the stream is one raw token range (exact attention), tokens computed;
 // otherwise every token of the stream is staged in sm.idx.  NB = 1: every
 // window is a single chunk (the launcher picks it only then).
-template <bool BF16, int E, int D, bool RAW, int NB>
+template <int ET, int E, int D, bool RAW, int NB>
 struct Attn {
-  static constexpr int ELT = BF16 ? 2 : 4;
-  static constexpr int KB = E * ELT, VB = D * ELT;   // row bytes
-  static constexpr int NQG = nqg<BF16, E, D>();
-  static constexpr int NQF = BF16 ? E / 32 : E / 4;   // Q operand registers per query group
+  static constexpr bool BF16 = ET != kF32;            // bf16 P V (bf16 and fp8 inputs)
+  static constexpr bool FP8 = ET == kFP8;
+  static constexpr int ELT = elt_size<ET>();
+  static constexpr int KB = E * ELT;                  // K row bytes (memory and LDS)
+  static constexpr int VB = D * (BF16 ? 2 : 4);       // V row bytes in LDS
+  static constexpr int VGB = D * ELT;                 // V row bytes in memory
+  static constexpr int NQG = nqg<ET, E, D>();
+  static constexpr int NQF = FP8 ? E / 128 : (BF16 ? E / 32 : E / 4);   // Q operand registers per query group
   static constexpr int ND = D / 16;                   // 16-dimension output blocks
-  static constexpr int KP = KB / 16, VP = VB / 16;    // 16-byte pieces per row
+  static constexpr int KP = KB / 16, VP = VB / 16;    // 16-byte pieces per row (LDS)
+  static constexpr int VGP = VGB / 16;                // 16-byte pieces per V row in memory
   static constexpr int KPT = kC * KP / kThreads;      // copies per thread per chunk
   static constexpr int VPT = kC * VP / kThreads;
-  using QF = typename std::conditional<BF16, bf16x8_t, float>::type;
+  static constexpr int VGPT = kC * VGP / kThreads;    // fp8: V pieces loaded per thread per chunk
+  using QF = typename std::conditional<FP8, i32x8_t, typename std::conditional<BF16, bf16x8_t, float>::type>::type;
 
   const AttnLaunch& a;
-  Smem<BF16, E, D, NB>& sm;
+  Smem<ET, E, D, NB>& sm;
   int b, h, hk, unit, lane, g;
   // K / V rows of this unit: token t starts at kbase + t * kstride bytes;
   // offsets stay below 2^31 (checked by the host), so they are 32-bit
@@ -160,6 +174,7 @@ struct Attn {
   float m_run[NQG], l_run[NQG];
 
   float r_w;   // weighted coreset: weight of the key this thread describes in the next chunk
+  uint4 vreg[VGPT > 0 ? VGPT : 1];   // fp8: V pieces of the next chunk, in flight
 
   // the stream: G gathered keys, then raw.count raw ones; current window [w0, w0 + wl)
   Gather gs;
@@ -171,15 +186,15 @@ struct Attn {
   int qlim[NQG];
   bool rows_ok;
 
-  __device__ __forceinline__ Attn(const AttnLaunch& la, Smem<BF16, E, D, NB>& s, int q0, int bh) : a(la), sm(s) {
+  __device__ __forceinline__ Attn(const AttnLaunch& la, Smem<ET, E, D, NB>& s, int q0, int bh) : a(la), sm(s) {
     b = bh / a.H;
     h = bh % a.H;
     hk = h / (a.H / a.H_kv);
     unit = b * a.H_kv + hk;
     kstride = static_cast<uint32_t>(a.H_kv * KB);
-    vstride = static_cast<uint32_t>(a.H_kv * VB);
+    vstride = static_cast<uint32_t>(a.H_kv * VGB);
     kbase = static_cast<const unsigned char*>(a.k) + (static_cast<int64_t>(b) * a.S * a.H_kv + hk) * KB;
-    vbase = static_cast<const unsigned char*>(a.v) + (static_cast<int64_t>(b) * a.S * a.H_kv + hk) * VB;
+    vbase = static_cast<const unsigned char*>(a.v) + (static_cast<int64_t>(b) * a.S * a.H_kv + hk) * VGB;
     lane = threadIdx.x & 63;
     g = lane >> 4;
     load_q(q0);
@@ -197,7 +212,17 @@ struct Attn {
       const int r = q_row(q0, qg);
       const bool ok = r < a.T;
       const int64_t qrow = ((static_cast<int64_t>(b) * a.T + (ok ? r : 0)) * a.H + h) * E;
-      if constexpr (BF16) {
+      if constexpr (FP8) {
+        // lane group g: features 32 g .. 32 g + 31 of each 128 (the K operand uses the same slices)
+#pragma unroll
+        for (int kk = 0; kk < NQF; ++kk) {
+          const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) + qrow + kk * 128 + 32 * g);
+          const uint4 lo = ok ? src[0] : uint4{0u, 0u, 0u, 0u}, hi = ok ? src[1] : uint4{0u, 0u, 0u, 0u};
+          dst[qg][kk] = i32x8_t{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
+                                static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
+                                static_cast<int>(hi.z), static_cast<int>(hi.w)};
+        }
+      } else if constexpr (BF16) {
 #pragma unroll
         for (int kk = 0; kk < NQF; ++kk) {
           const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(static_cast<const uint16_t*>(a.q) + qrow + kk * 32 + 8 * g);
@@ -275,14 +300,52 @@ struct Attn {
                            static_cast<uint32_t>(16 * (P ^ kswz<KB>(R)));
       __builtin_amdgcn_global_load_lds((gptr)(kbase + off), (lptr)(kdst + (w * KPT + i) * 1024), 16, 0, 0);
     }
+    if constexpr (FP8) {   // V through registers: widened to bf16 by store_v once they land
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int s = (w * VPT + i) * 64 + lane;
-      const int R = s / VP, P = s % VP;
-      const int r = kC * c + R;
-      const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), vstride) +
-                           static_cast<uint32_t>(16 * (P ^ vswz<BF16, VB>(R)));
-      __builtin_amdgcn_global_load_lds((gptr)(vbase + off), (lptr)(vdst + (w * VPT + i) * 1024), 16, 0, 0);
+      for (int i = 0; i < VGPT; ++i) {
+        const int s = (w * VGPT + i) * 64 + lane;
+        const int R = s / VGP, P = s % VGP;
+        const int r = kC * c + R;
+        const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), vstride) + static_cast<uint32_t>(16 * P);
+        vreg[i] = *reinterpret_cast<const uint4*>(vbase + off);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int s = (w * VPT + i) * 64 + lane;
+        const int R = s / VP, P = s % VP;
+        const int r = kC * c + R;
+        const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), vstride) +
+                             static_cast<uint32_t>(16 * (P ^ vswz<BF16, VB>(R)));
+        __builtin_amdgcn_global_load_lds((gptr)(vbase + off), (lptr)(vdst + (w * VPT + i) * 1024), 16, 0, 0);
+      }
+    }
+  }
+
+  // fp8: the V pieces copy() loaded (16 values each, landed) as bf16 into buffer vdst:
+  // piece P of row R holds dimensions 16 P .. 16 P + 15, the staged row's pieces 2 P
+  // and 2 P + 1, stored at (2 P) ^ vswz(R) (even, so the two stay adjacent)
+  __device__ __forceinline__ void store_v(lds_byte* vdst) {
+    if constexpr (FP8) {
+      const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      typedef __attribute__((address_space(3))) u32x4v_t lds_u4;
+#pragma unroll
+      for (int i = 0; i < VGPT; ++i) {
+        const int s = (w * VGPT + i) * 64 + lane;
+        const int R = s / VGP, P = s % VGP;
+        const uint32_t wv[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+        uint32_t o[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wv[j]), false);
+          const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wv[j]), true);
+          o[2 * j] = (__float_as_uint(f01[1]) & 0xffff0000u) | (__float_as_uint(f01[0]) >> 16);
+          o[2 * j + 1] = (__float_as_uint(f23[1]) & 0xffff0000u) | (__float_as_uint(f23[0]) >> 16);
+        }
+        lds_byte* row = vdst + R * VB + 16 * ((2 * P) ^ vswz<true, VB>(R));
+        *reinterpret_cast<lds_u4*>(row) = u32x4v_t{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<lds_u4*>(row + 16) = u32x4v_t{o[4], o[5], o[6], o[7]};
+      }
     }
   }
 
@@ -336,7 +399,22 @@ struct Attn {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int R = 16 * kb + R0;
-      if constexpr (BF16) {
+      if constexpr (FP8) {
+        // lane group g: features 32 g .. 32 g + 31 of each 128, logical pieces 2 g and 2 g + 1
+        typedef __attribute__((address_space(3))) const u32x4v_t lds_u4;
+#pragma unroll
+        for (int kk = 0; kk < NQF; ++kk) {
+          const u32x4v_t lo = *reinterpret_cast<lds_u4*>(kbuf + R * KB + 16 * ((8 * kk + 2 * g) ^ kswz<KB>(R)));
+          const u32x4v_t hi = *reinterpret_cast<lds_u4*>(kbuf + R * KB + 16 * ((8 * kk + 2 * g + 1) ^ kswz<KB>(R)));
+          const i32x8_t kf = {static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                              static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                              static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+#pragma unroll
+          for (int qg = 0; qg < NQG; ++qg)   // E4M3 operands (format 0), unit block scales (E8M0 127)
+            st[qg][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[qg][kk], st[qg][kb], 0, 0, 0, 127,
+                                                                          0, 127);
+        }
+      } else if constexpr (BF16) {
         typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 #pragma unroll
         for (int kk = 0; kk < NQF; ++kk) {
@@ -523,6 +601,7 @@ struct Attn {
     }
     meta(0, nch, 0);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    store_v((lds_byte*)&sm.v[0][0]);
     if (kC > wl) {
       __syncthreads();
       zero_tail(0, 0);
@@ -543,6 +622,7 @@ struct Attn {
     overlap(c, nch, (const lds_byte*)&sm.k[B][0], (const lds_byte*)&sm.v[B][0], (lds_byte*)&sm.k[NX][0],
             (lds_byte*)&sm.v[NX][0]);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);   // this thread's copies have landed
+    if (c + 1 < nch) store_v((lds_byte*)&sm.v[NX][0]);
     if (c + 1 < nch && kC * (c + 2) > wl) {
       __syncthreads();
       zero_tail(c + 1, NX);
@@ -657,19 +737,19 @@ __device__ __forceinline__ void express_pass(const ExpressView& ev, int unit, in
 // kTilesOne consecutive tiles of its unit.
 constexpr int kTilesOne = 4;
 
-template <bool BF16, int E, int D, int NB>
-constexpr int attn_waves() { return (NB == 1 && BF16 && E == 64 && (D == 64 || D == 256)) ? 3 : 2; }
+template <int ET, int E, int D, int NB>
+constexpr int attn_waves() { return (NB == 1 && ET == kBF16 && E == 64 && (D == 64 || D == 256)) ? 3 : 2; }
 
-template <bool BF16, int E, int D, bool RAW, int NB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_waves<BF16, E, D, NB>()))) void attn_kernel(
+template <int ET, int E, int D, bool RAW, int NB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_waves<ET, E, D, NB>()))) void attn_kernel(
     AttnLaunch a) {
-  constexpr int kQ = 16 * nqg<BF16, E, D>() * kWaves;
-  constexpr int NQG = Attn<BF16, E, D, RAW, NB>::NQG;
-  __shared__ Smem<BF16, E, D, NB> sm;
+  constexpr int kQ = 16 * nqg<ET, E, D>() * kWaves;
+  constexpr int NQG = Attn<ET, E, D, RAW, NB>::NQG;
+  __shared__ Smem<ET, E, D, NB> sm;
   const int64_t tile = xcd_remap(blockIdx.y * static_cast<int64_t>(gridDim.x) + blockIdx.x,
                                  static_cast<int64_t>(gridDim.x) * gridDim.y);
   const int q0 = static_cast<int>(tile % gridDim.x) * kQ * (NB == 1 ? kTilesOne : 1);
-  Attn<BF16, E, D, RAW, NB> at(a, sm, q0, static_cast<int>(tile / gridDim.x));
+  Attn<ET, E, D, RAW, NB> at(a, sm, q0, static_cast<int>(tile / gridDim.x));
   if constexpr (NB == 1) at.fetch_q(q0 + kQ, at.qn);
   const int q_last = min(q0 + kQ - 1, a.T - 1);
   const int n = a.causal ? a.ev.n : 1;
@@ -704,39 +784,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_w
   }
 }
 
-template <bool BF16, int E, int D>
+template <int ET, int E, int D>
 hipError_t launch(const AttnLaunch& a, hipStream_t s) {
-  constexpr int kQ = 16 * nqg<BF16, E, D>() * kWaves;
+  constexpr int kQ = 16 * nqg<ET, E, D>() * kWaves;
   dim3 grid((a.T + kQ - 1) / kQ, a.B * a.H);
   if (!a.causal && a.cs_idx == nullptr)   // exact attention: one raw range, nothing staged
-    hipLaunchKernelGGL((attn_kernel<BF16, E, D, true, 2>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<ET, E, D, true, 2>), grid, dim3(kThreads), 0, s, a);
   else if (!a.causal && a.cs_n <= kC)     // a coreset of one chunk: one buffer, kTilesOne tiles per workgroup
-    hipLaunchKernelGGL((attn_kernel<BF16, E, D, false, 1>), dim3((a.T + kQ * kTilesOne - 1) / (kQ * kTilesOne), a.B * a.H),
+    hipLaunchKernelGGL((attn_kernel<ET, E, D, false, 1>), dim3((a.T + kQ * kTilesOne - 1) / (kQ * kTilesOne), a.B * a.H),
                        dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_kernel<BF16, E, D, false, 2>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<ET, E, D, false, 2>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool attention_supported(int bf16, int E, int D) {
-  if (bf16) return (E == 64 && (D == 64 || D == 128 || D == 256)) || (E == 128 && (D == 128 || D == 64));
+bool attention_supported(int dtype, int E, int D) {
+  if (dtype == kFP8) return E == 128 && D == 128;
+  if (dtype == kBF16) return (E == 64 && (D == 64 || D == 128 || D == 256)) || (E == 128 && (D == 128 || D == 64));
   return (E == 64 && (D == 64 || D == 128)) || (E == 128 && D == 128);
 }
 
-hipError_t launch_attention(const AttnLaunch& a, int bf16, int E, int D, hipStream_t s) {
+hipError_t launch_attention(const AttnLaunch& a, int dtype, int E, int D, hipStream_t s) {
   if (a.T == 0 || a.B * a.H == 0) return hipSuccess;
-  if (bf16) {
-    if (E == 64 && D == 64) return launch<true, 64, 64>(a, s);
-    if (E == 64 && D == 128) return launch<true, 64, 128>(a, s);
-    if (E == 64 && D == 256) return launch<true, 64, 256>(a, s);
-    if (E == 128 && D == 128) return launch<true, 128, 128>(a, s);
-    if (E == 128 && D == 64) return launch<true, 128, 64>(a, s);
+  if (dtype == kFP8) {
+    if (E == 128 && D == 128) return launch<kFP8, 128, 128>(a, s);
+  } else if (dtype == kBF16) {
+    if (E == 64 && D == 64) return launch<kBF16, 64, 64>(a, s);
+    if (E == 64 && D == 128) return launch<kBF16, 64, 128>(a, s);
+    if (E == 64 && D == 256) return launch<kBF16, 64, 256>(a, s);
+    if (E == 128 && D == 128) return launch<kBF16, 128, 128>(a, s);
+    if (E == 128 && D == 64) return launch<kBF16, 128, 64>(a, s);
   } else {
-    if (E == 64 && D == 64) return launch<false, 64, 64>(a, s);
-    if (E == 64 && D == 128) return launch<false, 64, 128>(a, s);
-    if (E == 128 && D == 128) return launch<false, 128, 128>(a, s);
+    if (E == 64 && D == 64) return launch<kF32, 64, 64>(a, s);
+    if (E == 64 && D == 128) return launch<kF32, 64, 128>(a, s);
+    if (E == 128 && D == 128) return launch<kF32, 128, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -12,10 +12,23 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(double)))) double f64x4_t;
 
 // ---------------------------------------------------------------------------
-// Input element access.  Inputs are float32 or bfloat16 (raw 16-bit patterns).
+// Input element access.  Inputs are float32, bfloat16 (raw 16-bit patterns) or
+// OCP FP8 E4M3 (E4M3FN: 1 sign, 4 exponent bits of bias 7, 3 mantissa bits,
+// no infinities; raw bytes).
 // ---------------------------------------------------------------------------
-struct F32Tag {};
-struct BF16Tag {};
+enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };   // element types, as the C ABI numbers them
+
+template <int ET>
+constexpr int elt_size() { return ET == kF32 ? 4 : (ET == kBF16 ? 2 : 1); }
+
+// The low byte of `word` as an E4M3 value, widened exactly (gfx950 converts
+// the OCP format).
+__device__ __forceinline__ float fp8_low_to_float(uint32_t word) {
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), 0);
+}
+
+// Byte b (0..3) of `word` as an E4M3 value.
+__device__ __forceinline__ float fp8_byte_to_float(uint32_t word, int b) { return fp8_low_to_float(word >> (8 * b)); }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -54,6 +54,9 @@ inline int fail(thin_attn* h, int code, const char* fmt, ...) {
 
 inline bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// Bytes of one element of q, k, v.
+inline int elt_bytes(int dtype) { return dtype == THIN_F32 ? 4 : (dtype == THIN_BF16 ? 2 : 1); }
+
 inline int64_t default_cache_size(int64_t S) {
   int64_t p = 2;
   while (p * p < S) p *= 2;
@@ -161,20 +164,12 @@ inline CausalPlan plan_causal(const thin_attn* h, int64_t B, int64_t S, int64_t 
   return p;
 }
 
-// Largest subsampling group reached must fit in a block (m / 2 <= n).
-inline bool causal_schedule_ok(int64_t S, int64_t n) {
-  const int64_t nblk = S / n;
-  for (int e = 1; (static_cast<int64_t>(1) << (2 * e)) < nblk; ++e)
-    if ((static_cast<int64_t>(1) << (2 * e - 1)) > n) return false;
-  return true;
-}
-
 inline int check_dims(thin_attn* h, int64_t B, int64_t T, int64_t S, int causal) {
   if (B < 0 || T < 0 || S < 0) return fail(h, THIN_EINVAL, "negative size");
   if (B * h->cfg.H_kv > (1LL << 20)) return fail(h, THIN_ENOTSUP, "too many units (B * H_kv)");
   if (S >= (1LL << 30) || T >= (1LL << 30)) return fail(h, THIN_ENOTSUP, "sequence too long");
   {  // the attention addresses a batch entry's K / V rows with 32-bit byte offsets
-    const int64_t row = static_cast<int64_t>(h->cfg.H_kv) * std::max(h->cfg.E, h->cfg.D) * (h->cfg.dtype == THIN_BF16 ? 2 : 4);
+    const int64_t row = static_cast<int64_t>(h->cfg.H_kv) * std::max(h->cfg.E, h->cfg.D) * elt_bytes(h->cfg.dtype);
     if (row >= (1LL << 24) || S * row >= (1LL << 31))
       return fail(h, THIN_ENOTSUP, "K / V of one batch entry exceed 2 GiB (S * H_kv * max(E, D) * element size)");
   }
@@ -182,8 +177,6 @@ inline int check_dims(thin_attn* h, int64_t B, int64_t T, int64_t S, int causal)
     if (T != S) return fail(h, THIN_EINVAL, "causal attention needs T == S (got T=%lld, S=%lld)", (long long)T, (long long)S);
     const int64_t n = cache_size(h, S);
     if (!pow2(n) || n < 2) return fail(h, THIN_EINVAL, "n_out must be a power of two >= 2");
-    if (!causal_schedule_ok(S, n))
-      return fail(h, THIN_ENOTSUP, "subsampling groups would exceed a block (S >= 2 n_out^2)");
     if (S / n >= 4 && !walk_fits(4 * n))
       return fail(h, THIN_ENOTSUP, "n_out = %lld: the halving of a full cache (%lld points) exceeds the walk's LDS",
                   (long long)n, (long long)(4 * n));

@@ -18,7 +18,8 @@ enum : uint32_t {
 
 
 // Where the points of one unit (batch entry b, KV head h) live:
-// key [B, S, H_kv, E] and value [B, S, H_kv, D], row-major, fp32 or bf16.
+// key [B, S, H_kv, E] and value [B, S, H_kv, D], row-major, of element type
+// dtype (kF32, kBF16 or kFP8).
 struct PointSource {
   const void* k;
   const void* v;
@@ -26,7 +27,7 @@ struct PointSource {
   int H_kv;
   int E;
   int D;
-  int bf16;
+  int dtype;
 };
 
 // Pair Gram of many bins at once.  Bin z holds N points whose token indices
@@ -155,7 +156,7 @@ hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s);
 bool small_halving_supported(int N, int E, int D);
 hipError_t launch_small_halving(const GramLaunch& g, const SweepLaunch& a, hipStream_t s);
 // Bins of 20 to 32 points: the same in one workgroup per bin.
-bool medium_halving_supported(int N, int E, int D, int bf16);
+bool medium_halving_supported(int N, int E, int D, int dtype);
 hipError_t launch_medium_halving(const GramLaunch& g, const SweepLaunch& a, hipStream_t s);
 hipError_t launch_iota(int32_t* out, int64_t units, int64_t n, int64_t stride, hipStream_t s);
 // Base subsampling: out[u][t] = list[u][t r + min(floor(u_t r), r - 1)], t < L / r,
@@ -169,7 +170,7 @@ hipError_t launch_express_final(const ExpressView& ev, int units, int S, int32_t
                                 int32_t* len, int64_t cap, hipStream_t s);
 hipError_t launch_fill_coreset(const int32_t* src, int64_t src_stride, int units, int n, float w,
                                int32_t* idx, float* wout, int32_t* len, hipStream_t s);
-hipError_t launch_attention(const AttnLaunch& a, int bf16, int E, int D, hipStream_t s);
+hipError_t launch_attention(const AttnLaunch& a, int dtype, int E, int D, hipStream_t s);
 // Copy of a caller's index list with every entry clamped into [0, S);
 // stores 1 to *err (when err is set) if any entry was outside.
 hipError_t launch_sanitize_indices(const int32_t* in, int64_t n, int32_t S, int32_t* out, int* err, hipStream_t s);
@@ -186,12 +187,16 @@ ExpressSchedule express_schedule(int64_t S, int n);
 hipError_t launch_kv_rows(const KvRowsLaunch& a, hipStream_t s);
 hipError_t launch_kv_block_reps(int units, int n, int64_t t0, int log2r, uint64_t seed, int32_t* list, hipStream_t s);
 hipError_t launch_kv_iota(int32_t* out, int units, int cnt, int first, hipStream_t s);
+// Representative of subsampling group g (2^log2r tokens) per unit: list[u] = base + (token - lo)
+// if the token lies in [lo, hi), else fallback.
+hipError_t launch_kv_group_rep(int units, int64_t g, int log2r, uint64_t seed, int64_t lo, int64_t hi, int64_t base,
+                               int32_t fallback, int32_t* list, hipStream_t s);
 hipError_t launch_kv_fill(int32_t* out, int64_t n, int32_t value, hipStream_t s);
-hipError_t launch_kv_decode(const KvDecodeLaunch& a, int bf16, int E, int D, int G, hipStream_t s);
-bool kv_decode_supported(int bf16, int E, int D, int G);
+hipError_t launch_kv_decode(const KvDecodeLaunch& a, int dtype, int E, int D, int G, hipStream_t s);
+bool kv_decode_supported(int dtype, int E, int D, int G);
 hipError_t launch_kv_summary(const int32_t* tok, int units, int slots, int n, int nC, int nBf, int nRaw, float wc,
                              float wb, int32_t* idx, float* w, int32_t* len, int cap, hipStream_t s);
 int kv_decode_splits(int n);
-bool attention_supported(int bf16, int E, int D);
+bool attention_supported(int dtype, int E, int D);
 
 }  // namespace thin

@@ -9,8 +9,8 @@
 // kernel-thinning papers (Dwivedi and Mackey, "Kernel Thinning"; Shetty,
 // Dwivedi and Mackey, "Distribution Compression in Near-linear Time").
 //
-// Precision: every dot product is accumulated in fp64 (products of fp32 or
-// bf16 inputs are exact in fp64) and exp is evaluated in fp64, so that the
+// Precision: every dot product is accumulated in fp64 (products of fp32,
+// bf16 or fp8 inputs are exact in fp64) and exp is evaluated in fp64, so that the
 // randomised sign decisions agree with a float64 reference except at true
 // near-ties.
 
@@ -68,12 +68,16 @@ __device__ __forceinline__ int slot_point(int s) { return 8 * (s >> 3) + 2 * (s 
 
 // 8 consecutive features of one point, kept raw until they are staged.
 struct Raw8 {
-  uint4 w[2];   // fp32: two float4; bf16: w[0] only
+  uint4 w[2];   // fp32: two float4; bf16: w[0] only; fp8: w[0].x, w[0].y
 };
 
-template <bool BF16>
+template <int ET>
 __device__ __forceinline__ void load8(const void* base, int64_t off, Raw8& r) {
-  if constexpr (BF16) {
+  if constexpr (ET == kFP8) {
+    const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + off);
+    r.w[0].x = x.x;
+    r.w[0].y = x.y;
+  } else if constexpr (ET == kBF16) {
     r.w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
   } else {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + off);
@@ -82,9 +86,11 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, Raw8& r) {
   }
 }
 
-template <bool BF16>
+template <int ET>
 __device__ __forceinline__ double raw8_at(const Raw8& r, int j) {
-  if constexpr (BF16) {
+  if constexpr (ET == kFP8) {
+    return fp8_byte_to_float(j < 4 ? r.w[0].x : r.w[0].y, j & 3);
+  } else if constexpr (ET == kBF16) {
     const uint32_t word = (j < 2 ? r.w[0].x : j < 4 ? r.w[0].y : j < 6 ? r.w[0].z : r.w[0].w);
     return bf16_bits_to_float(static_cast<uint16_t>((j & 1) ? (word >> 16) : (word & 0xffffu)));
   } else {
@@ -186,7 +192,7 @@ __device__ __forceinline__ double step_threshold(int greedy, double al, double u
 
 // b_i^2 of pair i (its two points: fp64 dot products, the same kernel as the
 // Gram, four partial sums per product) and u_i (Philox).
-template <bool BF16>
+template <int ET>
 __device__ void pair_b2_u(const GramLaunch& a, int z, int i, double& b2, double& u) {
   const int unit = z / a.bins_per_unit, lb = z % a.bins_per_unit;
   const int b = unit / a.src.H_kv, h = unit % a.src.H_kv;
@@ -195,11 +201,11 @@ __device__ void pair_b2_u(const GramLaunch& a, int z, int i, double& b2, double&
     double sxx[4] = {0.0, 0.0, 0.0, 0.0}, sxy[4] = {0.0, 0.0, 0.0, 0.0}, syy[4] = {0.0, 0.0, 0.0, 0.0};
     for (int f = 0; f < F; f += 8) {
       Raw8 e8, o8;
-      load8<BF16>(base, re * F + f, e8);
-      load8<BF16>(base, ro * F + f, o8);
+      load8<ET>(base, re * F + f, e8);
+      load8<ET>(base, ro * F + f, o8);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const double x = raw8_at<BF16>(e8, j), y = raw8_at<BF16>(o8, j);
+        const double x = raw8_at<ET>(e8, j), y = raw8_at<ET>(o8, j);
         sxx[j & 3] = fma(x, x, sxx[j & 3]);
         sxy[j & 3] = fma(x, y, sxy[j & 3]);
         syy[j & 3] = fma(y, y, syy[j & 3]);
@@ -230,7 +236,7 @@ __device__ void pair_b2_u(const GramLaunch& a, int z, int i, double& b2, double&
 // The sigma recursion of bin z by one wave, 64 pairs at a time, and the
 // thresholds into the lower triangle.  s_b2 / s_u: the bin's b^2 and u already
 // formed (by the whole workgroup), or nullptr to form them here per chunk.
-template <bool BF16>
+template <int ET>
 __device__ void bin_thresholds(const GramLaunch& a, int z, const double* s_b2, const double* s_u) {
   const int P = a.N / 2;
   const int lane = threadIdx.x & 63;
@@ -248,7 +254,7 @@ __device__ void bin_thresholds(const GramLaunch& a, int z, const double* s_b2, c
         b2 = s_b2[i];
         u = s_u[i];
       } else {
-        pair_b2_u<BF16>(a, z, i, b2, u);
+        pair_b2_u<ET>(a, z, i, b2, u);
       }
     }
     const double al = sigma_steps(s2, b2, sqrt(b2), min(64, P - i0), c, k1, k2);
@@ -265,7 +271,7 @@ __device__ void bin_thresholds(const GramLaunch& a, int z, const double* s_b2, c
 // entirely below the diagonal are skipped.  Points beyond the bin (or the
 // unit's last bin) are loaded from a valid point; the entries they touch are
 // never stored.
-template <bool BF16>
+template <int ET>
 struct GramTile {
   int lane, wr, wc, nK, nst;
   bool active, loader;
@@ -273,7 +279,7 @@ struct GramTile {
   int wofs;                        // this thread's staging slot and half, as an LDS byte offset base
   const unsigned char* kp;         // staging: this thread's point row in K and V, plus its half
   const unsigned char* vp;
-  u32x4_t raw[kRing][2];           // staging registers, a ring over steps: 8 features (bf16: [0] only)
+  u32x4_t raw[kRing][2];           // staging registers, a ring over steps: 8 features (bf16: [0]; fp8: [0].xy)
   double acc[2][2][4][2];          // [pass][row parity][row quad][column parity]
 
   // Staging role: thread t loads features 8 (t & 1) .. + 7 of step st for the
@@ -285,14 +291,22 @@ struct GramTile {
   __device__ __forceinline__ void load(int st) {
     st = st < nst ? st : nst - 1;
     const bool vpass = st >= nK;
-    const unsigned char* src = (vpass ? vp : kp) + (vpass ? st - nK : st) * (kStageF * (BF16 ? 2 : 4));
-    raw[R][0] = *reinterpret_cast<const u32x4_t*>(src);
-    if constexpr (!BF16) raw[R][1] = *reinterpret_cast<const u32x4_t*>(src + 16);
+    const unsigned char* src = (vpass ? vp : kp) + (vpass ? st - nK : st) * (kStageF * elt_size<ET>());
+    if constexpr (ET == kFP8) {
+      const uint2 x = *reinterpret_cast<const uint2*>(src);
+      raw[R][0][0] = x.x;
+      raw[R][0][1] = x.y;
+    } else {
+      raw[R][0] = *reinterpret_cast<const u32x4_t*>(src);
+    }
+    if constexpr (ET == kF32) raw[R][1] = *reinterpret_cast<const u32x4_t*>(src + 16);
   }
 
   template <int R>
   __device__ __forceinline__ double feature(int j) const {
-    if constexpr (BF16) {
+    if constexpr (ET == kFP8) {
+      return static_cast<double>(fp8_byte_to_float(raw[R][0][j >> 2], j & 3));
+    } else if constexpr (ET == kBF16) {
       const uint32_t word = raw[R][0][j >> 1];
       return static_cast<double>(__uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16)));
     } else {
@@ -384,7 +398,7 @@ __device__ __forceinline__ double exp_tab(double x, const double* T) {
   return __builtin_amdgcn_ldexp(T[ni & 255] * p, ni >> 8);
 }
 
-template <bool BF16>
+template <int ET>
 __device__ void gram_tile(const GramLaunch& a, int nthr, lds_byte* smem, double* T) {
   const int P = a.N / 2;
   const bool packed = P < 32 && (32 % P) == 0;   // whole bins per tile
@@ -411,7 +425,7 @@ __device__ void gram_tile(const GramLaunch& a, int nthr, lds_byte* smem, double*
   const int h = unit % a.src.H_kv;
   const bool diag = tr == tc;          // rows and columns are the same points
 
-  GramTile<BF16> t;
+  GramTile<ET> t;
   t.lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   t.wr = w >> 1;
@@ -439,7 +453,7 @@ __device__ void gram_tile(const GramLaunch& a, int nthr, lds_byte* smem, double*
       if (a.err) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       tok = tok < 0 ? 0 : static_cast<int>(a.src.S - 1);
     }
-    const int elt = BF16 ? 2 : 4;
+    const int elt = elt_size<ET>();
     const int64_t row = (static_cast<int64_t>(b) * a.src.S + tok) * a.src.H_kv + h;
     t.kp = static_cast<const unsigned char*>(a.src.k) + (row * a.src.E + 8 * half) * elt;
     t.vp = static_cast<const unsigned char*>(a.src.v) + (row * a.src.D + 8 * half) * elt;
@@ -495,13 +509,13 @@ __device__ void gram_tile(const GramLaunch& a, int nthr, lds_byte* smem, double*
 // b^2 and u into LDS, then wave 0 runs the recursion; with many, each wave
 // takes bins on its own, 4 nthr apart, so the thresholds hold few workgroup
 // slots while the tiles run.
-template <bool BF16>
+template <int ET>
 __global__ __launch_bounds__(256, 4) void pair_gram_kernel(GramLaunch a, int nthr, int thr_per_wave) {
   __shared__ __attribute__((aligned(16))) double smem[2 * kSlots * kStage / sizeof(double) + 256];
   if (static_cast<int>(blockIdx.x) < nthr) {
     if (thr_per_wave) {
       for (int z = 4 * blockIdx.x + (threadIdx.x >> 6); z < a.nbins; z += 4 * nthr)
-        bin_thresholds<BF16>(a, z, nullptr, nullptr);
+        bin_thresholds<ET>(a, z, nullptr, nullptr);
       return;   // the whole workgroup: no barrier in this mode
     }
     const int z = blockIdx.x;
@@ -509,12 +523,12 @@ __global__ __launch_bounds__(256, 4) void pair_gram_kernel(GramLaunch a, int nth
     const int P = a.N / 2;      // b^2 and u of up to kThrCap pairs each fit the tile buffers
     double* s_b2 = smem;
     double* s_u = smem + kThrCap;
-    for (int i = threadIdx.x; i < P; i += 256) pair_b2_u<BF16>(a, z, i, s_b2[i], s_u[i]);
+    for (int i = threadIdx.x; i < P; i += 256) pair_b2_u<ET>(a, z, i, s_b2[i], s_u[i]);
     __syncthreads();
-    if (threadIdx.x < 64) bin_thresholds<BF16>(a, z, s_b2, s_u);
+    if (threadIdx.x < 64) bin_thresholds<ET>(a, z, s_b2, s_u);
     return;
   }
-  gram_tile<BF16>(a, nthr, (lds_byte*)smem, smem + 2 * kSlots * kStage / sizeof(double));
+  gram_tile<ET>(a, nthr, (lds_byte*)smem, smem + 2 * kSlots * kStage / sizeof(double));
 }
 
 // ---------------------------------------------------------------------------
@@ -862,17 +876,24 @@ __global__ void philox_words_kernel(const uint64_t* ctr, int64_t n, uint64_t see
 constexpr int kSmallN = 16;   // points per tile (and largest bin of the fused path)
 
 
-// Eight features of one point kept raw (bf16: one 16-byte load, fp32: two)
-// until their MFMAs, then widened one at a time.
-template <bool BF16>
+// Eight features of one point kept raw (fp8: one 8-byte load, bf16: one
+// 16-byte load, fp32: two) until their MFMAs, then widened one at a time.
+template <int ET>
 struct SmallRaw {
-  u32x4_t w[BF16 ? 1 : 2];
+  u32x4_t w[ET == kF32 ? 2 : 1];
   __device__ __forceinline__ void load(const unsigned char* p) {
-    w[0] = *reinterpret_cast<const u32x4_t*>(p);
-    if constexpr (!BF16) w[1] = *reinterpret_cast<const u32x4_t*>(p + 16);
+    if constexpr (ET == kFP8) {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      w[0][0] = x.x;
+      w[0][1] = x.y;
+    } else {
+      w[0] = *reinterpret_cast<const u32x4_t*>(p);
+    }
+    if constexpr (ET == kF32) w[1] = *reinterpret_cast<const u32x4_t*>(p + 16);
   }
   __device__ __forceinline__ double operator[](int f) const {
-    if constexpr (BF16) return static_cast<double>(__uint_as_float((f & 1) ? (w[0][f >> 1] & 0xffff0000u) : (w[0][f >> 1] << 16)));
+    if constexpr (ET == kFP8) return static_cast<double>(fp8_byte_to_float(w[0][f >> 2], f & 3));
+    else if constexpr (ET == kBF16) return static_cast<double>(__uint_as_float((f & 1) ? (w[0][f >> 1] & 0xffff0000u) : (w[0][f >> 1] << 16)));
     else return static_cast<double>(__uint_as_float(w[f >> 2][f & 3]));
   }
 };
@@ -883,15 +904,15 @@ constexpr int kSmallBatch = 8;   // loads of eight features in flight per lane
 // multiple of 32; the four lanes of a point read 64 contiguous bytes).
 // Loads go out kSmallBatch at a time before their MFMAs, and four
 // accumulators keep four MFMAs in flight.
-template <bool BF16>
+template <int ET>
 __device__ __forceinline__ f64x4_t small_gram(const unsigned char* row, int F) {
   const int quarter = (threadIdx.x & 63) >> 4;
-  const int elt = BF16 ? 2 : 4;
+  const int elt = elt_size<ET>();
   const unsigned char* p = row + quarter * 8 * elt;   // lane quarter q: feature blocks 4 g + q of 8
   const int groups = F / 32;   // loads of eight features per lane
   f64x4_t acc[4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
   for (int g0 = 0; g0 < groups; g0 += kSmallBatch) {
-    SmallRaw<BF16> x[kSmallBatch];
+    SmallRaw<ET> x[kSmallBatch];
 #pragma unroll
     for (int j = 0; j < kSmallBatch; ++j) x[j].load(p + min(g0 + j, groups - 1) * 32 * elt);   // (repeats are not used)
 #pragma unroll
@@ -913,17 +934,17 @@ __device__ __forceinline__ f64x4_t small_gram(const unsigned char* row, int F) {
 // block b with A = B = that register is the 4 x 4 Gram of quad b (d0), and
 // with B = the point of quad b ^ 1 (PAIR) the products of quads b and b ^ 1
 // (d1).  Nothing is formed across bins.
-template <bool BF16, bool PAIR>
+template <int ET, bool PAIR>
 __device__ __forceinline__ void small_gram44(const unsigned char* row, const unsigned char* prow, int F, double& d0,
                                              double& d1) {
   const int quarter = (threadIdx.x & 63) >> 4;
-  const int elt = BF16 ? 2 : 4;
+  const int elt = elt_size<ET>();
   const int off = quarter * 8 * elt;   // feature blocks 4 g + quarter of 8, as in small_gram
   const int groups = F / 32;
   constexpr int BATCH = PAIR ? kSmallBatch / 2 : kSmallBatch;
   double a0[2] = {0.0, 0.0}, a1[2] = {0.0, 0.0};
   for (int g0 = 0; g0 < groups; g0 += BATCH) {
-    SmallRaw<BF16> x[BATCH], y[BATCH];
+    SmallRaw<ET> x[BATCH], y[BATCH];
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int gj = min(g0 + j, groups - 1);   // (repeats are not used)
@@ -945,7 +966,7 @@ __device__ __forceinline__ void small_gram44(const unsigned char* row, const uns
   d1 = a1[0] + a1[1];
 }
 
-template <bool BF16>
+template <int ET>
 __global__ __launch_bounds__(256) void small_halving_kernel(GramLaunch g, SweepLaunch a) {
   __shared__ double s_kap[4][kSmallN][kSmallN + 1];   // kappa of the tile's point pairs, per wave
   const int N = g.N, P = N / 2;
@@ -959,7 +980,7 @@ __global__ __launch_bounds__(256) void small_halving_kernel(GramLaunch g, SweepL
   const int b = unit / g.src.H_kv, h = unit % g.src.H_kv;
 
   // the row of point pt of the tile (points past the tile's bins read its first point)
-  const int elt = BF16 ? 2 : 4;
+  const int elt = elt_size<ET>();
   auto point_row = [&](int pt) -> int64_t {
     const int pb = pt / N;
     const bool ok = pb < bpt && bin0 + pb < g.bins_per_unit;
@@ -975,17 +996,17 @@ __global__ __launch_bounds__(256) void small_halving_kernel(GramLaunch g, SweepL
     double kd0, kd1, vd0, vd1;
     if (N == 8) {
       const int64_t prow = point_row((lane & 15) ^ 4);
-      small_gram44<BF16, true>(K + row * g.src.E * elt, K + prow * g.src.E * elt, g.src.E, kd0, kd1);
-      small_gram44<BF16, true>(V + row * g.src.D * elt, V + prow * g.src.D * elt, g.src.D, vd0, vd1);
+      small_gram44<ET, true>(K + row * g.src.E * elt, K + prow * g.src.E * elt, g.src.E, kd0, kd1);
+      small_gram44<ET, true>(V + row * g.src.D * elt, V + prow * g.src.D * elt, g.src.D, vd0, vd1);
       s_kap[w][4 * qb + m][4 * (qb ^ 1) + n] = exp_f64(g.scale * kd1) * (vd1 + 1.0);
     } else {
-      small_gram44<BF16, false>(K + row * g.src.E * elt, nullptr, g.src.E, kd0, kd1);
-      small_gram44<BF16, false>(V + row * g.src.D * elt, nullptr, g.src.D, vd0, vd1);
+      small_gram44<ET, false>(K + row * g.src.E * elt, nullptr, g.src.E, kd0, kd1);
+      small_gram44<ET, false>(V + row * g.src.D * elt, nullptr, g.src.D, vd0, vd1);
     }
     s_kap[w][4 * qb + m][4 * qb + n] = exp_f64(g.scale * kd0) * (vd0 + 1.0);
   } else {        // 16x16x4: every point pair of the tile
-    const f64x4_t kd = small_gram<BF16>(K + row * g.src.E * elt, g.src.E);
-    const f64x4_t vd = small_gram<BF16>(V + row * g.src.D * elt, g.src.D);
+    const f64x4_t kd = small_gram<ET>(K + row * g.src.E * elt, g.src.E);
+    const f64x4_t vd = small_gram<ET>(V + row * g.src.D * elt, g.src.D);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_kap[w][(lane >> 4) + 4 * i][lane & 15] = exp_f64(g.scale * kd[i]) * (vd[i] + 1.0);
   }
@@ -1056,10 +1077,19 @@ __global__ __launch_bounds__(256) void small_halving_kernel(GramLaunch g, SweepL
 constexpr int kMediumN = 32;   // (64-point bins ran faster on the tiles)
 
 // Eight features at p (LDS), widened.
-template <bool BF16>
+template <int ET>
 __device__ __forceinline__ void medium_features(const lds_byte* p, double x[8]) {
   typedef __attribute__((address_space(3))) const u32x4_t lds_u4;
-  if constexpr (BF16) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) const u32x2_t lds_u2;
+  if constexpr (ET == kFP8) {
+    const u32x2_t w = *reinterpret_cast<lds_u2*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = static_cast<double>(fp8_byte_to_float(w[0], j));
+      x[4 + j] = static_cast<double>(fp8_byte_to_float(w[1], j));
+    }
+  } else if constexpr (ET == kBF16) {
     const u32x4_t w = *reinterpret_cast<lds_u4*>(p);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1076,7 +1106,7 @@ __device__ __forceinline__ void medium_features(const lds_byte* p, double x[8]) 
   }
 }
 
-template <bool BF16>
+template <int ET>
 __global__ __launch_bounds__(256) void medium_halving_kernel(GramLaunch g, SweepLaunch a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char s_rows[];
   __shared__ double s_kap[kMediumN][kMediumN + 1];
@@ -1084,7 +1114,7 @@ __global__ __launch_bounds__(256) void medium_halving_kernel(GramLaunch g, Sweep
   const int z = blockIdx.x;
   const int unit = z / g.bins_per_unit, lb = z % g.bins_per_unit;
   const int b = unit / g.src.H_kv, h = unit % g.src.H_kv;
-  const int elt = BF16 ? 2 : 4;
+  const int elt = elt_size<ET>();
   const int KP = g.src.E * elt / 16, VP = g.src.D * elt / 16;   // 16-byte pieces of a K / V row
   const int RS = (KP + VP + 1) * 16;                            // staged row stride (bytes)
   lds_byte* rows = (lds_byte*)s_rows;
@@ -1134,15 +1164,15 @@ __global__ __launch_bounds__(256) void medium_halving_kernel(GramLaunch g, Sweep
       double kd[2] = {0.0, 0.0}, vd[2] = {0.0, 0.0};
       for (int t = 0; t < g.src.E / 32; ++t) {
         double xa[8], xb[8];
-        medium_features<BF16>(pa + t * 32 * elt, xa);
-        medium_features<BF16>(pb + t * 32 * elt, xb);
+        medium_features<ET>(pa + t * 32 * elt, xa);
+        medium_features<ET>(pb + t * 32 * elt, xb);
 #pragma unroll
         for (int f = 0; f < 8; ++f) kd[f & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(xa[f], xb[f], kd[f & 1], 0, 0, 0);
       }
       for (int t = 0; t < g.src.D / 32; ++t) {
         double xa[8], xb[8];
-        medium_features<BF16>(pa + KP * 16 + t * 32 * elt, xa);
-        medium_features<BF16>(pb + KP * 16 + t * 32 * elt, xb);
+        medium_features<ET>(pa + KP * 16 + t * 32 * elt, xa);
+        medium_features<ET>(pb + KP * 16 + t * 32 * elt, xb);
 #pragma unroll
         for (int f = 0; f < 8; ++f) vd[f & 1] = __builtin_amdgcn_mfma_f64_4x4x4f64(xa[f], xb[f], vd[f & 1], 0, 0, 0);
       }
@@ -1212,10 +1242,12 @@ hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s) {
   int nthr = 0;
   if (P > 64) nthr = per_wave ? std::min((a.nbins + 31) / 32 * 8, 64) : (a.nbins + 7) / 8 * 8;
   dim3 grid(static_cast<unsigned>(blocks + nthr));
-  if (a.src.bf16)
-    hipLaunchKernelGGL(pair_gram_kernel<true>, grid, dim3(256), 0, s, a, nthr, per_wave);
+  if (a.src.dtype == kFP8)
+    hipLaunchKernelGGL(pair_gram_kernel<kFP8>, grid, dim3(256), 0, s, a, nthr, per_wave);
+  else if (a.src.dtype == kBF16)
+    hipLaunchKernelGGL(pair_gram_kernel<kBF16>, grid, dim3(256), 0, s, a, nthr, per_wave);
   else
-    hipLaunchKernelGGL(pair_gram_kernel<false>, grid, dim3(256), 0, s, a, nthr, per_wave);
+    hipLaunchKernelGGL(pair_gram_kernel<kF32>, grid, dim3(256), 0, s, a, nthr, per_wave);
   return hipGetLastError();
 }
 
@@ -1252,45 +1284,50 @@ hipError_t launch_small_halving(const GramLaunch& g, const SweepLaunch& a, hipSt
   const int bpt = kSmallN / g.N;
   const int64_t waves = static_cast<int64_t>(g.nbins / g.bins_per_unit) * ((g.bins_per_unit + bpt - 1) / bpt);
   const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
-  if (g.src.bf16)
-    hipLaunchKernelGGL(small_halving_kernel<true>, grid, dim3(256), 0, s, g, a);
+  if (g.src.dtype == kFP8)
+    hipLaunchKernelGGL(small_halving_kernel<kFP8>, grid, dim3(256), 0, s, g, a);
+  else if (g.src.dtype == kBF16)
+    hipLaunchKernelGGL(small_halving_kernel<kBF16>, grid, dim3(256), 0, s, g, a);
   else
-    hipLaunchKernelGGL(small_halving_kernel<false>, grid, dim3(256), 0, s, g, a);
+    hipLaunchKernelGGL(small_halving_kernel<kF32>, grid, dim3(256), 0, s, g, a);
   return hipGetLastError();
 }
 
-static size_t medium_rows_lds(int N, int E, int D, int bf16) {
-  const int elt = bf16 ? 2 : 4;
+static size_t medium_rows_lds(int N, int E, int D, int dtype) {
+  const int elt = dtype == kF32 ? 4 : (dtype == kBF16 ? 2 : 1);
   return static_cast<size_t>(N) * ((E + D) * elt + 16);
 }
 
-bool medium_halving_supported(int N, int E, int D, int bf16) {
+bool medium_halving_supported(int N, int E, int D, int dtype) {
   return N > kSmallN && N <= kMediumN && N % 4 == 0 && E % 32 == 0 && D % 32 == 0 &&
-         medium_rows_lds(N, E, D, bf16) <= 96 * 1024;
+         medium_rows_lds(N, E, D, dtype) <= 96 * 1024;
 }
 
 hipError_t launch_medium_halving(const GramLaunch& g, const SweepLaunch& a, hipStream_t s) {
-  if (!medium_halving_supported(g.N, g.src.E, g.src.D, g.src.bf16) || g.N != a.N || g.nbins != a.nbins ||
+  if (!medium_halving_supported(g.N, g.src.E, g.src.D, g.src.dtype) || g.N != a.N || g.nbins != a.nbins ||
       g.bins_per_unit != a.bins_per_unit)
     return hipErrorInvalidValue;
   if (g.nbins == 0) return hipSuccess;
-  const size_t lds = medium_rows_lds(g.N, g.src.E, g.src.D, g.src.bf16);
+  const size_t lds = medium_rows_lds(g.N, g.src.E, g.src.D, g.src.dtype);
+  const void* fn = g.src.dtype == kFP8 ? reinterpret_cast<const void*>(medium_halving_kernel<kFP8>)
+                   : g.src.dtype == kBF16 ? reinterpret_cast<const void*>(medium_halving_kernel<kBF16>)
+                                          : reinterpret_cast<const void*>(medium_halving_kernel<kF32>);
   if (lds > 64 * 1024) {
-    static bool set[64][2];   // once per device and element type (for the largest size)
+    static bool set[64][3];   // once per device and element type (for the largest size)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (!set[dev][g.src.bf16 ? 1 : 0]) {
-      const void* fn = g.src.bf16 ? reinterpret_cast<const void*>(medium_halving_kernel<true>)
-                                  : reinterpret_cast<const void*>(medium_halving_kernel<false>);
+    if (!set[dev][g.src.dtype]) {
       const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
       if (e != hipSuccess) return e;
-      set[dev][g.src.bf16 ? 1 : 0] = true;
+      set[dev][g.src.dtype] = true;
     }
   }
-  if (g.src.bf16)
-    hipLaunchKernelGGL(medium_halving_kernel<true>, dim3(g.nbins), dim3(256), lds, s, g, a);
+  if (g.src.dtype == kFP8)
+    hipLaunchKernelGGL(medium_halving_kernel<kFP8>, dim3(g.nbins), dim3(256), lds, s, g, a);
+  else if (g.src.dtype == kBF16)
+    hipLaunchKernelGGL(medium_halving_kernel<kBF16>, dim3(g.nbins), dim3(256), lds, s, g, a);
   else
-    hipLaunchKernelGGL(medium_halving_kernel<false>, dim3(g.nbins), dim3(256), lds, s, g, a);
+    hipLaunchKernelGGL(medium_halving_kernel<kF32>, dim3(g.nbins), dim3(256), lds, s, g, a);
   return hipGetLastError();
 }
 

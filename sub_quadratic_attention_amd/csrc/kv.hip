@@ -7,9 +7,12 @@
 //   slots [0, 4n)    cache C   (weight m)
 //   slots [4n, 6n)   buffer Bf (weight m / 2, representatives of the batch)
 //   slots [6n, 7n)   raw block (weight 1, tokens of the block being streamed)
+//   slot  7n         the representative of a subsampling group longer than a
+//                    block (m / 2 > n), held from the block that contains it
+//                    until the block that completes the group (not visible)
 //
-// K rows [units][7n][E], V rows [units][7n][D] (input dtype) and the token
-// index of every slot [units][7n] live in the caller's state buffer.  Block
+// K rows [units][7n + 1][E], V rows [units][7n + 1][D] (input dtype) and the
+// token index of every slot [units][7n + 1] live in the caller's state buffer.  Block
 // ingest, batch halving and HALVE move rows between these regions; the
 // halvings themselves run the pair-Gram and walk kernels on slot lists.
 
@@ -81,6 +84,19 @@ __global__ void kv_block_reps_kernel(int units, int n, int64_t t0, int log2r, ui
                                      kTagSubsample, seed);
   const int64_t off = log2r ? static_cast<int64_t>(word >> (64 - log2r)) : 0;
   list[i] = static_cast<int32_t>(6 * n + ((g << log2r) + off - t0));
+}
+
+// The representative of group g (r = 2^log2r tokens): token g r + floor(u r),
+// u from counter (g, log2 r, unit, subsample tag).  list[u] = base + (token -
+// lo) when the token lies in [lo, hi), else fallback.
+__global__ void kv_group_rep_kernel(int units, int64_t g, int log2r, uint64_t seed, int64_t lo, int64_t hi, int64_t base,
+                                    int32_t fallback, int32_t* list) {
+  const int u = static_cast<int>(static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
+  if (u >= units) return;
+  const uint64_t word = philox_word0(static_cast<uint64_t>(g), static_cast<uint64_t>(log2r), static_cast<uint64_t>(u),
+                                     kTagSubsample, seed);
+  const int64_t tok = (g << log2r) + (log2r ? static_cast<int64_t>(word >> (64 - log2r)) : 0);
+  list[u] = (tok >= lo && tok < hi) ? static_cast<int32_t>(base + (tok - lo)) : fallback;
 }
 
 __global__ void kv_fill_kernel(int32_t* out, int64_t n, int32_t value) {
@@ -166,7 +182,7 @@ constexpr int kMergeBytes = 64 * 1024;
 constexpr int kMergeSplits = 64;
 constexpr int kDmaSc1 = 16;   // cache policy of a device-scope coherent load (sc1)
 
-template <bool BF16, int D, int G>
+template <int ET, int D, int G>
 __device__ __forceinline__ void combine_unit(const float* partial, int u, int splits, int H, int H_kv, void* out,
                                              unsigned char* lds) {
   constexpr int PS = D + 4;   // floats per partial row
@@ -224,16 +240,16 @@ __device__ __forceinline__ void combine_unit(const float* partial, int u, int sp
       o = num / den;
     }
     const int64_t off = (static_cast<int64_t>(b) * H + hk * G + gh) * D + d;
-    if constexpr (BF16)
+    if constexpr (ET != kF32)   // bfloat16 output (fp8 inputs too)
       static_cast<uint16_t*>(out)[off] = float_to_bf16_bits(o);
     else
       static_cast<float*>(out)[off] = o;
   }
 }
 
-template <bool BF16, int E, int D, int G, int KPW>
+template <int ET, int E, int D, int G, int KPW>
 __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
-  constexpr int ELT = BF16 ? 2 : 4;
+  constexpr int ELT = elt_size<ET>();
   constexpr int FP = 16 / ELT;                          // features per 16-byte piece
   constexpr int VP = D * ELT / 16;                      // 16-byte pieces per value row
   constexpr int VLOADS = KPW * VP / 256;                // value pieces per thread
@@ -286,7 +302,12 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
   for (int x = tid; x < G * E; x += 256) {
     const int gh = x / E, e = x % E;
     const int64_t off = (static_cast<int64_t>(b) * a.H + hk * G + gh) * E + e;
-    sq[gh][e] = BF16 ? bf16_bits_to_float(static_cast<const uint16_t*>(a.q)[off]) : static_cast<const float*>(a.q)[off];
+    if constexpr (ET == kFP8)
+      sq[gh][e] = fp8_low_to_float(static_cast<const uint8_t*>(a.q)[off]);
+    else if constexpr (ET == kBF16)
+      sq[gh][e] = bf16_bits_to_float(static_cast<const uint16_t*>(a.q)[off]);
+    else
+      sq[gh][e] = static_cast<const float*>(a.q)[off];
   }
 #pragma unroll
   for (int i = 0; i < VLOADS; ++i) reinterpret_cast<uint4*>(sv)[tid + 256 * i] = vr[i];
@@ -302,7 +323,12 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
       const int piece = slice + TPK * i;
       const uint32_t wv[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
       float kv[FP];
-      if constexpr (BF16) {
+      if constexpr (ET == kFP8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) kv[4 * j + bb] = fp8_byte_to_float(wv[j], bb);
+      } else if constexpr (ET == kBF16) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           kv[2 * j] = __uint_as_float(wv[j] << 16);
@@ -364,7 +390,11 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
     for (int j = 0; j < nk; ++j) {
       const float p = sp[gh][j];
       float v0, v1;
-      if constexpr (BF16) {
+      if constexpr (ET == kFP8) {
+        const uint32_t vv = reinterpret_cast<const uint16_t*>(sv + j * D * ELT)[d2];
+        v0 = fp8_byte_to_float(vv, 0);
+        v1 = fp8_byte_to_float(vv, 1);
+      } else if constexpr (ET == kBF16) {
         const uint32_t vv = reinterpret_cast<const uint32_t*>(sv + j * D * ELT)[d2];
         v0 = __uint_as_float(vv << 16);
         v1 = __uint_as_float(vv & 0xffff0000u);
@@ -411,7 +441,7 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(KvDecodeLaunch a) {
   }
   __syncthreads();
   if (!s_last) return;   // the whole workgroup
-  combine_unit<BF16, D, G>(a.partial, u, gridDim.x, a.H, a.H_kv, a.out, sv);
+  combine_unit<ET, D, G>(a.partial, u, gridDim.x, a.H, a.H_kv, a.out, sv);
   if (tid == 0) __hip_atomic_store(&a.cnt[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -427,7 +457,7 @@ int decode_keys_per_wg(int total) {
   return 128;
 }
 
-template <bool BF16, int E, int D, int G>
+template <int ET, int E, int D, int G>
 hipError_t decode_one(const KvDecodeLaunch& a, hipStream_t s) {
   const int total = a.nC + a.nBf + a.nRaw + 1;
   const int kpw = decode_keys_per_wg<D, G>(total);
@@ -435,11 +465,11 @@ hipError_t decode_one(const KvDecodeLaunch& a, hipStream_t s) {
   b.splits = (total + kpw - 1) / kpw;
   const dim3 grid(b.splits, a.units);
   if (kpw == 32)
-    hipLaunchKernelGGL((kv_decode_kernel<BF16, E, D, G, 32>), grid, dim3(256), 0, s, b);
+    hipLaunchKernelGGL((kv_decode_kernel<ET, E, D, G, 32>), grid, dim3(256), 0, s, b);
   else if (kpw == 64)
-    hipLaunchKernelGGL((kv_decode_kernel<BF16, E, D, G, 64>), grid, dim3(256), 0, s, b);
+    hipLaunchKernelGGL((kv_decode_kernel<ET, E, D, G, 64>), grid, dim3(256), 0, s, b);
   else
-    hipLaunchKernelGGL((kv_decode_kernel<BF16, E, D, G, 128>), grid, dim3(256), 0, s, b);
+    hipLaunchKernelGGL((kv_decode_kernel<ET, E, D, G, 128>), grid, dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
@@ -458,6 +488,14 @@ hipError_t launch_kv_rows(const KvRowsLaunch& a, hipStream_t s) {
 hipError_t launch_kv_block_reps(int units, int n, int64_t t0, int log2r, uint64_t seed, int32_t* list, hipStream_t s) {
   const int64_t total = static_cast<int64_t>(units) * (n >> log2r);
   hipLaunchKernelGGL(kv_block_reps_kernel, dim3(grid1d(total, 256)), dim3(256), 0, s, units, n, t0, log2r, seed, list);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_group_rep(int units, int64_t g, int log2r, uint64_t seed, int64_t lo, int64_t hi, int64_t base,
+                               int32_t fallback, int32_t* list, hipStream_t s) {
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_group_rep_kernel, dim3(grid1d(units, 256)), dim3(256), 0, s, units, g, log2r, seed, lo, hi,
+                     base, fallback, list);
   return hipGetLastError();
 }
 
@@ -482,14 +520,15 @@ hipError_t launch_kv_summary(const int32_t* tok, int units, int slots, int n, in
   return hipGetLastError();
 }
 
-bool kv_decode_supported(int bf16, int E, int D, int G) {
+bool kv_decode_supported(int dtype, int E, int D, int G) {
   const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
+  if (dtype == kFP8) return g_ok && E == 128 && D == 128;
   return g_ok && ((E == 128 && D == 128) || (E == 64 && D == 64));
 }
 
-hipError_t launch_kv_decode(const KvDecodeLaunch& a, int bf16, int E, int D, int G, hipStream_t s) {
+hipError_t launch_kv_decode(const KvDecodeLaunch& a, int dtype, int E, int D, int G, hipStream_t s) {
 #define THIN_KV_CASE(BF, EE, DD, GG) \
-  if (bf16 == BF && E == EE && D == DD && G == GG) return decode_one<BF, EE, DD, GG>(a, s);
+  if (dtype == BF && E == EE && D == DD && G == GG) return decode_one<BF, EE, DD, GG>(a, s);
   THIN_KV_CASE(1, 128, 128, 1)
   THIN_KV_CASE(1, 128, 128, 2)
   THIN_KV_CASE(1, 128, 128, 4)
@@ -506,6 +545,10 @@ hipError_t launch_kv_decode(const KvDecodeLaunch& a, int bf16, int E, int D, int
   THIN_KV_CASE(0, 64, 64, 2)
   THIN_KV_CASE(0, 64, 64, 4)
   THIN_KV_CASE(0, 64, 64, 8)
+  THIN_KV_CASE(2, 128, 128, 1)
+  THIN_KV_CASE(2, 128, 128, 2)
+  THIN_KV_CASE(2, 128, 128, 4)
+  THIN_KV_CASE(2, 128, 128, 8)
 #undef THIN_KV_CASE
   return hipErrorInvalidValue;
 }

@@ -33,12 +33,15 @@ struct KvLayout {
   size_t off_k, off_v, off_tok, off_cnt, bytes;
 };
 
-int elt_of(const thin_attn* h) { return h->cfg.dtype == THIN_BF16 ? 2 : 4; }
+int elt_of(const thin_attn* h) { return thinhost::elt_bytes(h->cfg.dtype); }
+
+// Slots per unit: cache 4n, buffer 2n, raw block n, one held representative.
+inline int kv_slots(int64_t n) { return static_cast<int>(7 * n + 1); }
 
 KvLayout kv_layout(const thin_attn* h, int64_t units, int64_t n) {
   KvLayout k{};
   Layout L;
-  const int64_t rows = units * 7 * n;
+  const int64_t rows = units * kv_slots(n);
   k.off_k = L.add(static_cast<size_t>(rows) * h->cfg.E * elt_of(h));
   k.off_v = L.add(static_cast<size_t>(rows) * h->cfg.D * elt_of(h));
   k.off_tok = L.add(static_cast<size_t>(rows) * sizeof(int32_t));
@@ -64,52 +67,31 @@ KvWs kv_ws(const thin_attn* h, int64_t units, int64_t n) {
   return w;
 }
 
-// Decisions an ingest of n_new tokens makes from the counters in kv (per unit).
-int64_t decisions_for(const thin_kv& kv0, int64_t n_new) {
-  thin_kv kv = kv0;
-  const int n = kv.n;
-  int64_t dec = 0;
-  int64_t left = n_new;
-  if (kv.tokens == 0 && n_new >= n) {   // bulk path: the static schedule
-    return thin::express_schedule(n_new, n).decisions;
-  }
-  while (left > 0) {
-    const int64_t take = std::min<int64_t>(left, n - kv.nRaw);
-    kv.nRaw += static_cast<int>(take);
-    left -= take;
-    if (kv.nRaw < n) break;
-    if (kv.m == 1) {
-      kv.nC += n;
-    } else {
-      kv.nBf += static_cast<int>(n / (kv.m / 2));
-      if (kv.nBf == 2 * n) {
-        dec += n;
-        kv.nC += n;
-        kv.nBf = 0;
-      }
-    }
-    if (kv.nC == 4 * n) {
-      dec += 3 * n;
-      kv.nC = n;
-      kv.m *= 4;
-    }
-    kv.nRaw = 0;
-  }
-  return dec;
+// Decisions an ingest of n_new tokens makes (per unit): the schedule is fixed by
+// the token count, so it is the difference of the static schedule's counts over
+// the full blocks before and after.
+int64_t decisions_for(const thin_kv& kv, int64_t n_new) {
+  const int64_t n = kv.n;
+  const int64_t before = (kv.tokens / n) * n, after = ((kv.tokens + n_new) / n) * n;
+  return thin::express_schedule(after, static_cast<int>(n)).decisions -
+         thin::express_schedule(before, static_cast<int>(n)).decisions;
 }
 
-// Every block reached must keep its subsampling groups inside one block.
-bool kv_range_ok(const thin_kv& kv, int64_t n_new) {
-  const int64_t blocks = (kv.tokens + n_new) / kv.n;
-  return causal_schedule_ok(blocks * kv.n, kv.n);
+// Streams stay below 2^30 tokens (32-bit token indices).
+bool kv_range_ok(const thin_kv& kv, int64_t n_new) { return n_new >= 0 && kv.tokens + n_new < (1LL << 30); }
+
+int log2_of(int64_t r) {
+  int l = 0;
+  while ((1LL << l) < r) ++l;
+  return l;
 }
 
 thin::PointSource state_source(const thin_kv& kv) {
   const thin_attn* h = kv.h;
   const KvLayout L = kv_layout(h, kv.units, kv.n);
   // rows of unit u are [u][7n]: present the state as a [units, 7n, 1, *] tensor
-  return thin::PointSource{kv.state + L.off_k, kv.state + L.off_v, 7LL * kv.n, 1, h->cfg.E, h->cfg.D,
-                           h->cfg.dtype == THIN_BF16};
+  return thin::PointSource{kv.state + L.off_k, kv.state + L.off_v, kv_slots(kv.n), 1, h->cfg.E, h->cfg.D,
+                           h->cfg.dtype};
 }
 
 thin::KvRowsLaunch rows_base(const thin_kv& kv) {
@@ -121,7 +103,7 @@ thin::KvRowsLaunch rows_base(const thin_kv& kv) {
   r.state_tok = reinterpret_cast<const int32_t*>(kv.state + L.off_tok);
   r.state_tok_out = reinterpret_cast<int32_t*>(kv.state + L.off_tok);
   r.units = kv.units;
-  r.slots = 7 * kv.n;
+  r.slots = kv_slots(kv.n);
   r.E = h->cfg.E;
   r.D = h->cfg.D;
   r.elt = elt_of(h);
@@ -191,12 +173,23 @@ int ingest_block(thin_kv& kv, char* ws, uint8_t* dec, int64_t dec_per_unit, int6
     kv.nC += n;
   } else {
     const int64_t r = kv.m / 2;
-    int log2r = 0;
-    while ((1LL << log2r) < r) ++log2r;
-    const int per = static_cast<int>(n / r);
-    THIN_HIP(thin::launch_kv_block_reps(kv.units, n, t0, log2r, kv.seed, la, st));
-    if ((rc = move_slots(kv, la, per, per, 4 * n + kv.nBf, st))) return rc;
-    kv.nBf += per;
+    const int log2r = log2_of(r);
+    if (r <= n) {   // the block completes n / r groups: their representatives join the buffer
+      const int per = static_cast<int>(n / r);
+      THIN_HIP(thin::launch_kv_block_reps(kv.units, n, t0, log2r, kv.seed, la, st));
+      if ((rc = move_slots(kv, la, per, per, 4 * n + kv.nBf, st))) return rc;
+      kv.nBf += per;
+    } else {        // the block lies inside one group of r tokens
+      // its representative is held in slot 7n when it falls in this block (else the slot keeps itself) ...
+      THIN_HIP(thin::launch_kv_group_rep(kv.units, t0 >> log2r, log2r, kv.seed, t0, t0 + n, 6 * n, 7 * n, la, st));
+      if ((rc = move_slots(kv, la, 1, 1, 7 * n, st))) return rc;
+      // ... and joins the buffer when this block completes the group
+      if ((t0 + n) % r == 0) {
+        THIN_HIP(thin::launch_kv_iota(la, kv.units, 1, 7 * n, st));
+        if ((rc = move_slots(kv, la, 1, 1, 4 * n + kv.nBf, st))) return rc;
+        kv.nBf += 1;
+      }
+    }
     if (kv.nBf == 2 * n) {
       THIN_HIP(thin::launch_kv_iota(la, kv.units, 2 * n, 4 * n, st));
       if ((rc = halve_slots(kv, la, 2 * n, lb, thin::kTagBatch, static_cast<uint64_t>(kv.nb), dec, dec_per_unit,
@@ -239,7 +232,7 @@ int bulk_ingest(thin_kv& kv, const void* k, const void* v, int64_t n_new, uint8_
   const int n = kv.n;
   const thin_attn_config& c = h->cfg;
   const CausalPlan p = plan_causal(h, kv.B, n_new, n);
-  const thin::PointSource src{k, v, n_new, c.H_kv, c.E, c.D, c.dtype == THIN_BF16};
+  const thin::PointSource src{k, v, n_new, c.H_kv, c.E, c.D, c.dtype};
   thin::ExpressView ev{};
   int rc = express_thin(h, src, kv.units, p, kv.seed, dec, p.sc.decisions, ws, st, ev);
   if (rc) return rc;
@@ -273,6 +266,16 @@ int bulk_ingest(thin_kv& kv, const void* k, const void* v, int64_t n_new, uint8_
     kv.m = m;
     kv.nh = E;
     kv.nb = 3 * (E - 1) + nbc;
+    // a group longer than a block still in progress: hold its representative
+    // if the chunk already contains it (else the block that does captures it)
+    const int64_t r = m / 2, done_tok = static_cast<int64_t>(nblk) * n;
+    if (r > n && done_tok % r != 0) {
+      int32_t* la = reinterpret_cast<int32_t*>(ws + p.off_hin);   // free again after the HALVE chain
+      const int log2r = log2_of(r);
+      THIN_HIP(thin::launch_kv_group_rep(kv.units, done_tok >> log2r, log2r, kv.seed, 0, done_tok, 0,
+                                         static_cast<int32_t>(done_tok - 1), la, st));
+      if ((rc = put_tokens(kv, k, v, n_new, 0, 1, 7 * n, 0, la, 1, st))) return rc;
+    }
   }
   const int tail = static_cast<int>(n_new - static_cast<int64_t>(nblk) * n);
   if (tail > 0 && (rc = put_tokens(kv, k, v, n_new, static_cast<int64_t>(nblk) * n, tail, 6 * n, 0, nullptr, 0, st)))
@@ -338,7 +341,7 @@ int thin_attn_kv_create(thin_attn_t* h, void* state, size_t state_bytes, int64_t
     return fail(h, THIN_ENOTSUP, "n_out = %lld: the halving of a full cache (%lld points) exceeds the walk's LDS",
                 (long long)n_out, (long long)(4 * n_out));
   const int G = h->cfg.H / h->cfg.H_kv;
-  if (!thin::kv_decode_supported(h->cfg.dtype == THIN_BF16, h->cfg.E, h->cfg.D, G))
+  if (!thin::kv_decode_supported(h->cfg.dtype, h->cfg.E, h->cfg.D, G))
     return fail(h, THIN_ENOTSUP, "decode not built for E=%d D=%d and %d query heads per KV head", h->cfg.E, h->cfg.D, G);
   const size_t need = kv_layout(h, B * h->cfg.H_kv, n_out).bytes;
   if (!state || state_bytes < need) return fail(h, THIN_ENOMEM, "state of %zu bytes, need %zu", state_bytes, need);
@@ -388,7 +391,7 @@ int thin_attn_kv_append(thin_kv_t* kv, const void* k, const void* v, int64_t n_n
   if (n_new == 0) return THIN_OK;
   if (!k || !v) return fail(h, THIN_EINVAL, "null k or v");
   if (kv->tokens + n_new >= (1LL << 30)) return fail(h, THIN_ENOTSUP, "stream too long");
-  if (!kv_range_ok(*kv, n_new)) return fail(h, THIN_ENOTSUP, "subsampling groups would exceed a block");
+  if (!kv_range_ok(*kv, n_new)) return fail(h, THIN_ENOTSUP, "stream beyond 2^30 tokens");
   const size_t need = thin_attn_kv_workspace_size(kv, n_new);
   if (!workspace || workspace_bytes < need) return fail(h, THIN_ENOMEM, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(h, THIN_EINVAL, "workspace must be 256-byte aligned");
@@ -416,7 +419,7 @@ int thin_attn_kv_decode(thin_kv_t* kv, const void* q, const void* k1, const void
   if (rc) return rc;
   thin_attn* h = kv->h;
   if (!q || !k1 || !v1 || !out) return fail(h, THIN_EINVAL, "null q, k1, v1 or out");
-  if (!kv_range_ok(*kv, 1)) return fail(h, THIN_ENOTSUP, "subsampling groups would exceed a block");
+  if (!kv_range_ok(*kv, 1)) return fail(h, THIN_ENOTSUP, "stream beyond 2^30 tokens");
   const KvWs W = kv_ws(h, kv->units, kv->n);
   if (!workspace || workspace_bytes < W.bytes) return fail(h, THIN_ENOMEM, "workspace of %zu bytes, need %zu", workspace_bytes, W.bytes);
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(h, THIN_EINVAL, "workspace must be 256-byte aligned");
@@ -433,7 +436,7 @@ int thin_attn_kv_decode(thin_kv_t* kv, const void* q, const void* k1, const void
   a.state_k = kv->state + L.off_k;
   a.state_v = kv->state + L.off_v;
   a.units = kv->units;
-  a.slots = 7 * kv->n;
+  a.slots = kv_slots(kv->n);
   a.n = kv->n;
   a.H = c.H;
   a.H_kv = c.H_kv;
@@ -454,7 +457,7 @@ int thin_attn_kv_decode(thin_kv_t* kv, const void* q, const void* k1, const void
     kv->cnt_ready = true;
   }
   THIN_HIP(timed(h, st, "kv_decode", [&] {
-    return thin::launch_kv_decode(a, c.dtype == THIN_BF16, c.E, c.D, c.H / c.H_kv, st);
+    return thin::launch_kv_decode(a, c.dtype, c.E, c.D, c.H / c.H_kv, st);
   }));
   // 2. the token has joined the raw block; a finished block is ingested
   const int64_t ndec = decisions_for(*kv, 1);
@@ -470,7 +473,7 @@ int thin_attn_kv_coreset(thin_kv_t* kv, int32_t* idx, float* w, int32_t* len, vo
   if (rc) return rc;
   thin_attn* h = kv->h;
   const KvLayout L = kv_layout(h, kv->units, kv->n);
-  THIN_HIP(thin::launch_kv_summary(reinterpret_cast<const int32_t*>(kv->state + L.off_tok), kv->units, 7 * kv->n, kv->n,
+  THIN_HIP(thin::launch_kv_summary(reinterpret_cast<const int32_t*>(kv->state + L.off_tok), kv->units, kv_slots(kv->n), kv->n,
                                    kv->nC, kv->nBf, kv->nRaw, static_cast<float>(kv->m),
                                    static_cast<float>(kv->m >= 2 ? kv->m / 2 : 1), idx, w, len, 7 * kv->n,
                                    as_stream(stream)));

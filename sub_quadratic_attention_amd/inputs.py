@@ -8,8 +8,8 @@ KV-cache compression, long-form decoding) but ship no data; these generators
 stand in for them with the shapes, dtypes and value structure of each
 workload.  Every array is drawn in float64 from NumPy's PCG64 seeded by a
 child of ``SeedSequence(seed)`` (one child per tensor), then rounded to the
-workload dtype (round-to-nearest-even); the returned float32 arrays hold
-values that are exact in that dtype.
+workload dtype (round-to-nearest-even; "fp8" is OCP FP8 E4M3); the returned
+float32 arrays hold values that are exact in that dtype.
 
 Workloads (all sizes overridable for reduced test cases):
 
@@ -50,11 +50,25 @@ def bf16_round(x):
     return out.astype(np.float32)
 
 
+def fp8_round(x):
+    """Round to the nearest OCP FP8 E4M3 value (E4M3FN: 1 sign, 4 exponent bits of bias 7,
+    3 mantissa bits; subnormals down to 2^-9; largest finite 448), ties to even; magnitudes
+    above 448 saturate (the generators draw none so large).  float32 out."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6.0)   # binade; subnormals share 2^-6's
+    q = 2.0 ** (e - 3)                                                  # spacing: 3 mantissa bits
+    r = np.minimum(np.round(a / q) * q, 448.0)                          # np.round: ties to even
+    return (np.sign(x) * r).astype(np.float32)
+
+
 def _cast(x, dtype):
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32)
     if dtype == "bf16":
         return bf16_round(x)
+    if dtype == "fp8":
+        return fp8_round(x)
     raise ValueError(dtype)
 
 
@@ -168,8 +182,20 @@ def selected_keys(seed=0, B=1, H=32, Hkv=8, S=32768, T=1024, L=4096, E=128, D=12
                 dtype=dtype, causal=False)
 
 
+def causal_prefill_fp8(seed=0, **kw):
+    """The causal prefill with its q, k, v rounded to FP8 E4M3."""
+    return causal_prefill(seed=seed, dtype="fp8", **kw)
+
+
+def kv_decode_fp8(seed=0, **kw):
+    """The KV-cache decode stream with keys, values and queries rounded to FP8 E4M3."""
+    return kv_decode(seed=seed, dtype="fp8", **kw)
+
+
 WORKLOADS = {
     "unmasked_small": unmasked_small,
+    "causal_prefill_fp8": causal_prefill_fp8,
+    "kv_decode_fp8": kv_decode_fp8,
     "vit_token_mixing": vit_token_mixing,
     "biggan_self_attention": biggan_self_attention,
     "causal_prefill": causal_prefill,

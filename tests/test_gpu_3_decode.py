@@ -64,8 +64,20 @@ def _check(name, d, n, H, Hkv, E, D, seed=0, chunks=None, greedy=False):
     idx, w, ln = (x.cpu().numpy() for x in st.coreset())
     total = d["k_hist"].shape[1] + d["q_steps"].shape[1]
     for u in range(units):
-        assert w[u, :ln[u]].sum() == total
+        assert w[u, :ln[u]].sum() == total - _in_progress(total, n)
     return out
+
+
+def _in_progress(total, n):
+    """Tokens of a subsampling group longer than a block still in progress after `total`
+    tokens (they join the weights when the group completes); 0 while m / 2 <= n."""
+    beta = total // n
+    if beta < 4:
+        return 0
+    m = 4
+    while m * 4 <= beta:
+        m *= 4
+    return (beta * n) % (m // 2)
 
 
 def _stream(seed, S0, steps, Hkv, H, E=128, D=128, dtype="bf16"):
@@ -174,3 +186,25 @@ def test_decode_cache_size_curve():
     say("[decode] cache size vs error (relative Frobenius against exact): " +
         ", ".join(f"n_out={n}: {e:.4f}" for n, e in zip(sizes, errs)))
     assert errs[2] < errs[1] < errs[0]
+
+
+# ---- subsampling groups longer than a block (m / 2 > n_out) -----------------------------
+
+def test_decode_groups_longer_than_a_block():
+    """n = 16: bulk history of 600 tokens, then 3000 decode steps through the HALVE at token
+    1024 into the epoch m = 64 (groups of 32 tokens, two blocks each) and the next HALVE."""
+    d = _stream(7, 600, 3000, Hkv=2, H=8)
+    _check("n=16 bulk 600 + 3000 steps", d, 16, 8, 2, 128, 128)
+
+
+def test_bulk_ingest_with_a_group_in_progress():
+    """n = 16, bulk history of 4900 tokens: epoch m = 256 (groups of 128 tokens = 8 blocks) with a
+    group in progress at the end of the chunk; 300 decode steps complete it and the next ones."""
+    d = _stream(8, 4900, 300, Hkv=1, H=4)
+    _check("n=16 bulk 4900 + 300 steps", d, 16, 4, 1, 128, 128)
+
+
+def test_chunked_appends_groups_longer_than_a_block():
+    """The same long stream appended in uneven chunks (block by block), then decoded."""
+    d = _stream(9, 2300, 100, Hkv=2, H=4)
+    _check("n=16 chunks", d, 16, 4, 2, 128, 128, chunks=[0, 37, 700, 1500, 2222, 2300])

@@ -81,6 +81,14 @@ def test_causal_exact_long_raw_range():
     assert s["decisions"] == 0
 
 
+def test_causal_forward_groups_longer_than_a_block():
+    """n_out = 16, S = 4105: past token 1024 the subsampling groups (32, then 128 tokens) span
+    several blocks; every output, decision and coreset entry."""
+    d = inputs.causal_prefill(seed=7, H=2, S=4096 + 9)
+    s = run_and_compare("causal n_out=16 S=4105", d, True, 2, 2, 128, 128, n_out=16, block_outputs=True)
+    assert s["decisions"] > 0
+
+
 # ---- token indices outside [0, S): clamped, reported, never read out of bounds --------
 
 def test_out_of_range_key_idx_is_reported():

@@ -81,16 +81,32 @@ def test_large_cache_disables_thinning():
         assert np.max(np.abs(out - fwd.exact(q, k, v, causal=True))) <= 1e-12
 
 
-@pytest.mark.parametrize("S,n", [(512, 8), (500, 8), (67, 4), (2048 + 17, 32)])
+def _pending(t, n):
+    """Tokens of a subsampling group still in progress when query t's block began: with
+    beta = t // n and m = 4^floor(log4 beta) (m = 1 before block 4), r = m / 2 and the
+    group in progress holds (beta n) mod r tokens of the earlier blocks (0 whenever r | n)."""
+    beta = t // n
+    if beta < 4:
+        return 0
+    m = 4
+    while m * 4 <= beta:
+        m *= 4
+    return (beta * n) % (m // 2)
+
+
+@pytest.mark.parametrize("S,n", [(512, 8), (500, 8), (67, 4), (2048 + 17, 32), (2000, 4), (4096 + 9, 16)])
 def test_visible_sets(S, n):
+    """Every token is in the weights a query sees, except those of a group longer than a
+    block that is still in progress (n = 4 from token 64 on, n = 16 from token 1024 on)."""
     K, V = _tiny(3, S)
     vis, final, log = exp.run_unit(K, V, n, 0.5, 0.5, 7, 2)
     for t, (idx, w) in vis.items():
-        assert w.sum() == t + 1                           # every token accounted for
+        assert w.sum() == t + 1 - _pending(t, n)
         assert len(idx) < 6 * n
         assert np.all(np.diff(idx) > 0) and idx[-1] == t
     idx, w = final
-    assert w.sum() == S and np.all(np.diff(idx) > 0)
+    assert w.sum() == S - _pending((S // n) * n, n) and np.all(np.diff(idx) > 0)
+    assert len(idx) < 6 * n + n
     # the trailing partial block stays exact
     tail = S % n
     if tail:
@@ -121,10 +137,36 @@ def test_flat_log_round_trip():
     assert len(flat) == sum(p for _, _, p in exp.schedule(S, 8))
 
 
-def test_groups_longer_than_a_block_are_refused():
-    """Beyond t = 2 n_out^2 a subsampling group would span several blocks: not supported."""
-    with pytest.raises(NotImplementedError):
-        exp.schedule(4 * 64 + 4, 4)
+def test_groups_longer_than_a_block_join_when_complete():
+    """n = 4, epoch m = 16 (blocks 16 .. 63): groups of r = 8 tokens span two blocks.  After
+    block b the buffer holds one representative per group completed so far, each the
+    Philox-chosen member g r + floor(u r) of its group, in order."""
+    n = 4
+    K, V = _tiny(8, 64 * n)
+    c = exp.ExpressCache(n, K, V, 0.5, 0.5, 3, 5)
+    for blk in range(16):
+        c.ingest_block(blk * n)
+    assert c.m == 16 and c.buffer == []
+    start_group = 16 * n // 8
+    for blk in range(16, 24):
+        c.ingest_block(blk * n)
+        done = (blk + 1 - 16) * n // 8                     # groups of 8 completed since block 16
+        expect = [8 * g + philox.uniform_offset(g, 3, 5, philox.TAG_SUBSAMPLE, 3, 8)
+                  for g in range(start_group, start_group + done)]
+        assert c.buffer == expect, blk
+
+
+def test_schedule_counts_groups_longer_than_a_block():
+    """The static schedule past the old 2 n_out^2 limit: n = 4 over 4096 tokens (1024 blocks):
+    HALVEs after 4, 16, 64, 256 blocks (and at 1024), a batch every m n_out tokens."""
+    ev = exp.schedule(4096, 4)
+    halves = [b for t, b, _ in ev if t == philox.TAG_HALVE_FIRST]
+    batches = [b for t, b, _ in ev if t == philox.TAG_BATCH]
+    assert halves == [0, 1, 2, 3, 4]
+    assert batches == list(range(12))                      # three per epoch m = 4, 16, 64, 256
+    K, V = _tiny(9, 4096)
+    _, _, log = exp.run_unit(K, V, 4, 0.5, 0.5, 1, 0, query_positions=[])
+    assert [k for k, _ in log] == [(t, b) for t, b, _ in ev]
 
 
 def test_streaming_decode_equals_prefill():
