@@ -193,6 +193,26 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * thin_attn_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * thin_attn_forward; its scratch is instead a device array of
+ * THIN_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  Sizes whose thin_attn_workspace_size exceeds it return
+ * THIN_ENOMEM before anything is enqueued.  The call allocates nothing (its
+ * device address is looked up once per device, at thin_attn_create for the
+ * current device or at the first call on another) and records no launch
+ * timing.  Every call on one GPU shares that GPU's array and nothing in it
+ * needs clearing between calls; calls whose work overlaps on one GPU (other
+ * streams, other host threads, other handles) race on it: serialise them.
+ */
+#define THIN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int thin_attn_forward_static(thin_attn_t* h, const void* q, const void* k, const void* v,
+                             int64_t B, int64_t T, int64_t S, int causal, uint64_t seed,
+                             void* out, int32_t* coreset_idx, float* coreset_w,
+                             int32_t* coreset_len, uint8_t* decisions, void* stream);
+
+/*
  * Unmasked Thinformer attention over a caller-chosen subset of the keys
  * (thinning after a KV selector: the "Express Language Modeling" explainer
  * on gist.science, "Experimental Results", accelerated KV cache compression,

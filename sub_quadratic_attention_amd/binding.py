@@ -48,6 +48,8 @@ _SIGNATURES = {
     "thin_attn_forward": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3
                           + [ctypes.c_int, ctypes.c_uint64] + [ctypes.c_void_p] * 6
                           + [ctypes.c_size_t, ctypes.c_void_p]),
+    "thin_attn_forward_static": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3
+                                 + [ctypes.c_int, ctypes.c_uint64] + [ctypes.c_void_p] * 5 + [ctypes.c_void_p]),
     "thin_attn_forward_subset": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 4
                                  + [ctypes.c_uint64] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
     "thin_attn_coreset_attention": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 3

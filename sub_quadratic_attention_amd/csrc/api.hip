@@ -1,10 +1,42 @@
 // C ABI of the thin-attention library: validation, workspace layout and the
 // launch sequence of the unmasked (Compress) and causal (Express) paths.
 
+#include <mutex>
+
 #include "host.hpp"
 
 using namespace thinhost;
 
+// ---- thin_attn_forward_static: thin_attn_forward on a library-owned scratch ----
+//
+// The scratch lives in this file's device array (one copy per GPU, resident
+// until the process ends).  Its name is only a host-side stand-in: the device
+// address of each GPU's copy is looked up once per device, with that device
+// current, and only that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = THIN_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device (null: not looked up yet)
+
+int static_scratch(thin_attn* h, void** out) {
+  int dev = -1;
+  THIN_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(h, THIN_ENOTSUP, "device %d beyond the static scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    THIN_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255))
+      return fail(h, THIN_EHIP, "static scratch of device %d has no usable address", dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return THIN_OK;
+}
+}  // namespace
 
 extern "C" {
 
@@ -38,6 +70,10 @@ int thin_attn_create(const thin_attn_config* cfg, thin_attn_t** out) {
     } else {
       (void)hipHostFree(flag);
     }
+  }
+  {  // the static scratch's address on the current device (thin_attn_forward_static)
+    void* sp = nullptr;
+    if (static_scratch(h, &sp) != THIN_OK) h->err.clear();
   }
   (void)hipGetLastError();   // a failed probe above leaves no error behind
   h->delta = c.delta > 0.0 ? c.delta : 0.5;
@@ -258,6 +294,30 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
   return THIN_OK;
 }
 
+
+int thin_attn_forward_static(thin_attn_t* h, const void* q, const void* k, const void* v, int64_t B, int64_t T,
+                             int64_t S, int causal, uint64_t seed, void* out, int32_t* coreset_idx, float* coreset_w,
+                             int32_t* coreset_len, uint8_t* decisions, void* stream) {
+  if (!h) return THIN_EINVAL;
+  h->err.clear();
+  if (causal != 0 && causal != 1) return fail(h, THIN_EINVAL, "causal must be 0 or 1");
+  int rc = check_dims(h, B, T, S, causal);
+  if (rc) return rc;
+  const size_t need = thin_attn_workspace_size(h, B, T, S, causal);
+  if (need > kStaticScratchBytes)
+    return fail(h, THIN_ENOMEM, "these sizes need %zu bytes of scratch; the static scratch holds %zu", need,
+                kStaticScratchBytes);
+  if (B * T == 0) return thin_attn_forward(h, q, k, v, B, T, S, causal, seed, out, coreset_idx, coreset_w,
+                                           coreset_len, decisions, nullptr, 0, stream);
+  void* ws = nullptr;
+  if ((rc = static_scratch(h, &ws))) return rc;
+  const bool timing = h->timing;   // launch timing would create events: off for this call
+  h->timing = false;
+  rc = thin_attn_forward(h, q, k, v, B, T, S, causal, seed, out, coreset_idx, coreset_w, coreset_len, decisions, ws,
+                         kStaticScratchBytes, stream);
+  h->timing = timing;
+  return rc;
+}
 
 int thin_attn_forward_subset(thin_attn_t* h, const void* q, const void* k, const void* v, const int32_t* key_idx,
                              int64_t B, int64_t T, int64_t S, int64_t L, uint64_t seed, void* out,
