@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--workload", default="causal_prefill", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-exact", action="store_true")
+    p.add_argument("--one-stream", action="store_true",
+                   help="run the timed steps with every launch on one stream (as the per-kernel pass does)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     return p.parse_args()
@@ -422,7 +424,11 @@ def main():
     q, k, v = (torch.from_numpy(d[x]).to(tdt).cuda() for x in ("q", "k", "v"))
     B, T = q.shape[:2]
     S = k.shape[1]
-    ta = ThinAttention(E, D, H, Hkv, tdt, **opts)
+    ta = ThinAttention(E, D, H, Hkv, tdt, one_stream=args.one_stream, **opts)
+    # per-kernel launch times come from a handle whose launches all go on one
+    # stream: with the causal path's second stream, kernels overlap and a
+    # launch's event time would include its neighbours'
+    ta1 = ThinAttention(E, D, H, Hkv, tdt, one_stream=True, **opts)
     out = torch.empty((B, T, H, D), dtype=odt, device="cuda")
     stream = torch.cuda.current_stream()
     sel = d.get("key_idx")   # thinning after a selector: the list is the point set (L keys per unit)
@@ -431,14 +437,14 @@ def main():
         L = sel.shape[2]
         ws = ta.workspace(B, T, L, False)
 
-        def step():
-            ta.forward_subset(q, k, v, key_idx, seed=0, workspace=ws, out=out, stream=stream)
+        def step(h=ta):
+            h.forward_subset(q, k, v, key_idx, seed=0, workspace=ws, out=out, stream=stream)
     else:
         L = S
         ws = ta.workspace(B, T, S, causal)
 
-        def step():
-            ta.forward(q, k, v, causal=causal, seed=0, workspace=ws, out=out, stream=stream)
+        def step(h=ta):
+            h.forward(q, k, v, causal=causal, seed=0, workspace=ws, out=out, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -449,13 +455,22 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # the same steps again with events around every launch (per-kernel table, roofline)
-    ta.set_timing(True)
-    for _ in range(args.steps):
-        step()
+    # the same steps again, one stream: untimed per launch (the serial step time), then with
+    # events around every launch (per-kernel table, roofline)
+    for _ in range(2):
+        step(ta1)
     torch.cuda.synchronize()
-    recs = ta.timing_records()
-    ta.set_timing(False)
+    a1 = time.perf_counter()
+    for _ in range(args.steps):
+        step(ta1)
+    torch.cuda.synchronize()
+    ms_one_stream = (time.perf_counter() - a1) * 1e3 / args.steps
+    ta1.set_timing(True)
+    for _ in range(args.steps):
+        step(ta1)
+    torch.cuda.synchronize()
+    recs = ta1.timing_records()
+    ta1.set_timing(False)
 
     wm = work_model(args.workload, B, T, L, H, Hkv, E, D, causal, elt, out_elt=2 if dt == "fp8" else elt,
                     **opts)   # (a selector's list: its L keys)
@@ -573,6 +588,9 @@ def main():
                        **opts),
         "kernels": {l: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                     for l, r in per_kernel.items()},
+        "kernel_timing": "HIP events around every launch, all launches on one stream",
+        "streams": 1 if args.one_stream else 2,
+        "ms_per_step_one_stream": ms_one_stream,
         "roofline": roofline,
         "rooflines": rooflines,
         "exact": exact,

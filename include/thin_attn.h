@@ -75,7 +75,14 @@ enum thin_dtype { THIN_F32 = 0, THIN_BF16 = 1, THIN_FP8_E4M3 = 2 };
  *   (t, 0, unit, 5) under the call's seed.  r = 1 (no Compress level, or s0
  *   without such a divisor) changes nothing.  thin_attn_coreset_size,
  *   thin_attn_decision_count and thin_attn_workspace_size follow the flag. */
-enum thin_flags { THIN_GREEDY_SIGNS = 1u, THIN_SUBSAMPLE_BASE = 2u };
+/* THIN_ONE_STREAM: every launch of a call goes on the caller's stream.  By
+ *   default the causal path (thin_attn_forward with causal = 1 and the bulk
+ *   thin_attn_kv_append) also uses a second stream the handle creates on the
+ *   device current at creation: the batch halvings and the attention of each
+ *   finished epoch run there beside the HALVE chain, and the caller's stream
+ *   waits for all of it before the call's last launch.  Results are the same
+ *   either way; the flag gives serial launches (per-kernel timing). */
+enum thin_flags { THIN_GREEDY_SIGNS = 1u, THIN_SUBSAMPLE_BASE = 2u, THIN_ONE_STREAM = 4u };
 
 enum thin_status {
   THIN_OK = 0,
@@ -98,7 +105,7 @@ typedef struct thin_attn_config {
                       thinning (exact causal attention)                                */
   double delta;    /* kernel-halving failure parameter; <= 0 means 0.5                */
   float scale;     /* softmax scale s; 0 means 1/sqrt(E)                              */
-  uint32_t flags;  /* THIN_GREEDY_SIGNS | THIN_SUBSAMPLE_BASE; other bits rejected      */
+  uint32_t flags;  /* THIN_GREEDY_SIGNS | THIN_SUBSAMPLE_BASE | THIN_ONE_STREAM; others rejected */
 } thin_attn_config;
 
 typedef struct thin_attn thin_attn_t;

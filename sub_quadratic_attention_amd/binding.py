@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libthin_attn.so")
 THIN_F32, THIN_BF16, THIN_FP8_E4M3 = 0, 1, 2
 THIN_GREEDY_SIGNS = 1
 THIN_SUBSAMPLE_BASE = 2
+THIN_ONE_STREAM = 4
 _STATUS = {0: "THIN_OK", -1: "THIN_EINVAL", -2: "THIN_ENOTSUP", -3: "THIN_ENOMEM", -4: "THIN_EHIP"}
 
 
@@ -133,14 +134,15 @@ class ThinAttention:
     """
 
     def __init__(self, E, D, H, H_kv=None, dtype=torch.float32, g=0, n_out=0, delta=0.5, scale=0.0,
-                 greedy=False, subsample_base=False):
+                 greedy=False, subsample_base=False, one_stream=False):
         self.lib = load_library()
         self.E, self.D, self.H = E, D, H
         self.H_kv = H if H_kv is None else H_kv
         self.dtype = dtype
         self.out_dtype = output_dtype(dtype)
         cfg = _Config(_dtype_code(dtype), E, D, H, self.H_kv, g, n_out, delta, scale,
-                      (THIN_GREEDY_SIGNS if greedy else 0) | (THIN_SUBSAMPLE_BASE if subsample_base else 0))
+                      (THIN_GREEDY_SIGNS if greedy else 0) | (THIN_SUBSAMPLE_BASE if subsample_base else 0)
+                      | (THIN_ONE_STREAM if one_stream else 0))
         h = ctypes.c_void_p()
         rc = self.lib.thin_attn_create(ctypes.byref(cfg), ctypes.byref(h))
         if rc != 0:

@@ -50,7 +50,7 @@ int thin_attn_create(const thin_attn_config* cfg, thin_attn_t** out) {
   if (c.g < 0) return fail(nullptr, THIN_EINVAL, "g must be >= 0");
   if (c.n_out < 0 || (c.n_out > 0 && (!pow2(c.n_out) || c.n_out < 2)))
     return fail(nullptr, THIN_EINVAL, "n_out must be 0 or a power of two >= 2");
-  if (c.flags & ~static_cast<uint32_t>(THIN_GREEDY_SIGNS | THIN_SUBSAMPLE_BASE))
+  if (c.flags & ~static_cast<uint32_t>(THIN_GREEDY_SIGNS | THIN_SUBSAMPLE_BASE | THIN_ONE_STREAM))
     return fail(nullptr, THIN_EINVAL, "unknown flags 0x%x", c.flags);
   if (!(c.scale >= 0.0f) || !std::isfinite(c.scale)) return fail(nullptr, THIN_EINVAL, "scale must be finite and >= 0");
   if (!thin::attention_supported(c.dtype, c.E, c.D))
@@ -71,6 +71,24 @@ int thin_attn_create(const thin_attn_config* cfg, thin_attn_t** out) {
       (void)hipHostFree(flag);
     }
   }
+  {  // the side stream of the causal path and its events, on the current device
+    int dev = -1;
+    hipStream_t side = nullptr;
+    if (!(c.flags & THIN_ONE_STREAM) && hipGetDevice(&dev) == hipSuccess &&
+        hipStreamCreateWithFlags(&side, hipStreamNonBlocking) == hipSuccess) {
+      bool ok = true;
+      for (int i = 0; i < thin_attn::kSyncEvents && ok; ++i)
+        ok = hipEventCreateWithFlags(&h->sync_ev[i], hipEventDisableTiming) == hipSuccess;
+      if (ok) {
+        h->side = side;
+        h->dev = dev;
+      } else {
+        for (auto& e : h->sync_ev)
+          if (e) (void)hipEventDestroy(e), e = nullptr;
+        (void)hipStreamDestroy(side);
+      }
+    }
+  }
   {  // the static scratch's address on the current device (thin_attn_forward_static)
     void* sp = nullptr;
     if (static_scratch(h, &sp) != THIN_OK) h->err.clear();
@@ -88,6 +106,12 @@ int thin_attn_destroy(thin_attn_t* h) {
   release_timing(h);
   for (auto e : h->pool) (void)hipEventDestroy(e);
   if (h->err_host) (void)hipHostFree(h->err_host);
+  if (h->side) {   // the side stream's work was joined into the caller's stream by every call
+    (void)hipStreamSynchronize(h->side);
+    (void)hipStreamDestroy(h->side);
+  }
+  for (auto e : h->sync_ev)
+    if (e) (void)hipEventDestroy(e);
   delete h;
   return THIN_OK;
 }
@@ -284,11 +308,9 @@ int thin_attn_forward(thin_attn_t* h, const void* q, const void* k, const void* 
   const CausalPlan p = plan_causal(h, B, S, nn);
   const int n = p.sc.n;
   thin::ExpressView ev{};
-  rc = express_thin(h, src, units, p, seed, decisions, ndec, ws, st, ev);
-  if (rc) return rc;
   al.causal = 1;
-  al.ev = ev;
-  THIN_HIP(timed(h, st, "attention", [&] { return thin::launch_attention(al, dt, c.E, c.D, st); }));
+  rc = express_thin(h, src, units, p, seed, decisions, ndec, ws, st, ev, &al);   // thinning and attention
+  if (rc) return rc;
   THIN_HIP(thin::launch_express_final(ev, units, static_cast<int>(S), coreset_idx, coreset_w, coreset_len, 6LL * n,
                                       st));
   return THIN_OK;

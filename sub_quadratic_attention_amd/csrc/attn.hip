@@ -210,7 +210,7 @@ struct Attn {
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg) {
       const int r = q_row(q0, qg);
-      const bool ok = r < a.T;
+      const bool ok = r < a.t1;
       const int64_t qrow = ((static_cast<int64_t>(b) * a.T + (ok ? r : 0)) * a.H + h) * E;
       if constexpr (FP8) {
         // lane group g: features 32 g .. 32 g + 31 of each 128 (the K operand uses the same slices)
@@ -244,7 +244,7 @@ struct Attn {
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg) {
       qr[qg] = q_row(q0, qg);
-      live[qg] = qr[qg] < a.T;
+      live[qg] = qr[qg] < a.t1;
 #pragma unroll
       for (int d = 0; d < ND; ++d) o[qg][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       osum[qg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -748,10 +748,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_w
   __shared__ Smem<ET, E, D, NB> sm;
   const int64_t tile = xcd_remap(blockIdx.y * static_cast<int64_t>(gridDim.x) + blockIdx.x,
                                  static_cast<int64_t>(gridDim.x) * gridDim.y);
-  const int q0 = static_cast<int>(tile % gridDim.x) * kQ * (NB == 1 ? kTilesOne : 1);
+  const int q0 = a.t0 + static_cast<int>(tile % gridDim.x) * kQ * (NB == 1 ? kTilesOne : 1);
   Attn<ET, E, D, RAW, NB> at(a, sm, q0, static_cast<int>(tile / gridDim.x));
   if constexpr (NB == 1) at.fetch_q(q0 + kQ, at.qn);
-  const int q_last = min(q0 + kQ - 1, a.T - 1);
+  const int q_last = min(q0 + kQ - 1, a.t1 - 1);
   const int n = a.causal ? a.ev.n : 1;
   const int beta_lo = a.causal ? q0 / n : 0, beta_hi = a.causal ? q_last / n : 0;
   for (int beta = beta_lo; beta <= beta_hi; ++beta) {
@@ -777,8 +777,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_w
   }
   at.finish();
   if constexpr (NB == 1) {   // unmasked, one chunk: the next tiles reuse the staged keys
-    for (int t = 1; t < kTilesOne && q0 + t * kQ < a.T; ++t) {
-      at.rerun_single(q0 + t * kQ, t + 1 < kTilesOne ? q0 + (t + 1) * kQ : a.T);
+    for (int t = 1; t < kTilesOne && q0 + t * kQ < a.t1; ++t) {
+      at.rerun_single(q0 + t * kQ, t + 1 < kTilesOne ? q0 + (t + 1) * kQ : a.t1);
       at.finish();
     }
   }
@@ -787,11 +787,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_w
 template <int ET, int E, int D>
 hipError_t launch(const AttnLaunch& a, hipStream_t s) {
   constexpr int kQ = 16 * nqg<ET, E, D>() * kWaves;
-  dim3 grid((a.T + kQ - 1) / kQ, a.B * a.H);
+  const int rows = a.t1 - a.t0;
+  dim3 grid((rows + kQ - 1) / kQ, a.B * a.H);
   if (!a.causal && a.cs_idx == nullptr)   // exact attention: one raw range, nothing staged
     hipLaunchKernelGGL((attn_kernel<ET, E, D, true, 2>), grid, dim3(kThreads), 0, s, a);
   else if (!a.causal && a.cs_n <= kC)     // a coreset of one chunk: one buffer, kTilesOne tiles per workgroup
-    hipLaunchKernelGGL((attn_kernel<ET, E, D, false, 1>), dim3((a.T + kQ * kTilesOne - 1) / (kQ * kTilesOne), a.B * a.H),
+    hipLaunchKernelGGL((attn_kernel<ET, E, D, false, 1>), dim3((rows + kQ * kTilesOne - 1) / (kQ * kTilesOne), a.B * a.H),
                        dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((attn_kernel<ET, E, D, false, 2>), grid, dim3(kThreads), 0, s, a);
@@ -806,8 +807,12 @@ bool attention_supported(int dtype, int E, int D) {
   return (E == 64 && (D == 64 || D == 128)) || (E == 128 && D == 128);
 }
 
-hipError_t launch_attention(const AttnLaunch& a, int dtype, int E, int D, hipStream_t s) {
-  if (a.T == 0 || a.B * a.H == 0) return hipSuccess;
+hipError_t launch_attention(const AttnLaunch& la, int dtype, int E, int D, hipStream_t s) {
+  AttnLaunch a = la;
+  if (a.t1 <= 0) a.t1 = a.T;
+  a.t0 = a.t0 < 0 ? 0 : a.t0;
+  a.t1 = a.t1 > a.T ? a.T : a.t1;
+  if (a.t1 <= a.t0 || a.B * a.H == 0) return hipSuccess;
   if (dtype == kFP8) {
     if (E == 128 && D == 128) return launch<kFP8, 128, 128>(a, s);
   } else if (dtype == kBF16) {

@@ -33,6 +33,14 @@ struct thin_attn {
   // device was present at creation (nothing can be launched then).
   int* err_host = nullptr;
   int* err_dev = nullptr;
+  // A second stream (default priority) on the device current at creation: the
+  // causal path runs its batch halvings and the attention of finished epochs
+  // there, beside the HALVE chain on the caller's stream, joined by events.
+  // Null without a device (then everything runs on the caller's stream).
+  hipStream_t side = nullptr;
+  int dev = -1;
+  static constexpr int kSyncEvents = 4;   // fork, batches done, epochs launch, join
+  hipEvent_t sync_ev[kSyncEvents] = {};
 };
 
 namespace thinhost {
@@ -142,10 +150,12 @@ inline UnmaskedPlan plan_unmasked(const thin_attn* h, int64_t B, int64_t S0) {
 
 struct CausalPlan {
   thin::ExpressSchedule sc;
-  size_t off_reps, off_bout, off_hin, off_hmid, off_hout, off_g;
+  size_t off_reps, off_bout, off_hin, off_hmid, off_hout, off_g, off_gh;
   size_t bytes;
 };
 
+// The batch halvings and the HALVE chain may run at once (on two streams), so
+// each has its own pair-Gram scratch.
 inline CausalPlan plan_causal(const thin_attn* h, int64_t B, int64_t S, int64_t n) {
   CausalPlan p{};
   p.sc = thin::express_schedule(S, static_cast<int>(n));
@@ -156,10 +166,8 @@ inline CausalPlan plan_causal(const thin_attn* h, int64_t B, int64_t S, int64_t 
   p.off_hin = L.add(sizeof(int32_t) * units * 4 * n);
   p.off_hmid = L.add(sizeof(int32_t) * units * 2 * n);
   p.off_hout = L.add(sizeof(int32_t) * units * p.sc.n_halves * n);
-  int64_t g = 0;
-  if (p.sc.n_batches_done) g = units * p.sc.n_batches_done * n * n;
-  if (p.sc.n_halves) g = std::max<int64_t>(g, units * 4 * n * n);
-  p.off_g = L.add(sizeof(double) * g);
+  p.off_g = L.add(sizeof(double) * (p.sc.n_batches_done ? units * p.sc.n_batches_done * n * n : 0));
+  p.off_gh = L.add(sizeof(double) * (p.sc.n_halves ? units * 4 * n * n : 0));
   p.bytes = L.total;
   return p;
 }
@@ -293,11 +301,35 @@ inline void release_timing(thin_attn* h) {
   h->recs.clear();
 }
 
-// Thinning of the causal path over S tokens of every unit (no attention):
-// representatives, all batch halvings at once, then the HALVE chain.  Fills
-// `ev` (lists live in `ws` as laid out by plan_causal).
+// The side stream if this call may use it (created on the current device).
+inline hipStream_t side_stream(const thin_attn* h) {
+  if (!h->side) return nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->dev) return nullptr;
+  return h->side;
+}
+
+// `to` waits for the work enqueued so far on `from` (event k of the handle).
+inline hipError_t stream_wait(thin_attn* h, hipStream_t from, hipStream_t to, int k) {
+  if (from == to) return hipSuccess;
+  hipError_t e = hipEventRecord(h->sync_ev[k], from);
+  if (e == hipSuccess) e = hipStreamWaitEvent(to, h->sync_ev[k], 0);
+  return e;
+}
+
+// Thinning of the causal path over S tokens of every unit: representatives,
+// all batch halvings at once, then the HALVE chain; fills `ev` (lists in `ws`
+// as laid out by plan_causal).  With `al` the attention runs too, an epoch at a
+// time as soon as the state it reads exists: epoch 0 (blocks 0..3, still
+// exact), epoch e >= 1 (blocks 4^e .. 4^(e+1) - 1, which read HALVE e - 1 and
+// the batches of epoch e).  With H HALVEs, epochs 0 .. H-1 form one launch
+// after HALVE H-2 and the last epoch (with the trailing partial block) one
+// after HALVE H-1.  With a side stream the batch halvings and the first of
+// those launches run there, beside the HALVE chain on `st` (which needs no
+// batch before HALVE 1); `st` waits for all of it before the last launch.
 inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, const CausalPlan& p, uint64_t seed,
-                        uint8_t* decisions, int64_t ndec, char* ws, hipStream_t st, thin::ExpressView& ev) {
+                        uint8_t* decisions, int64_t ndec, char* ws, hipStream_t st, thin::ExpressView& ev,
+                        thin::AttnLaunch* al = nullptr) {
   const int n = p.sc.n;
   ev = thin::ExpressView{};
   ev.n = n;
@@ -310,29 +342,56 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
   int32_t* hin = reinterpret_cast<int32_t*>(ws + p.off_hin);
   int32_t* hmid = reinterpret_cast<int32_t*>(ws + p.off_hmid);
   int32_t* hout = reinterpret_cast<int32_t*>(ws + p.off_hout);
-  double* G = reinterpret_cast<double*>(ws + p.off_g);
+  double* Gb = reinterpret_cast<double*>(ws + p.off_g);
+  double* Gh = reinterpret_cast<double*>(ws + p.off_gh);
   ev.reps = reps;
   ev.batch_out = bout;
   ev.halve_out = hout;
+  const hipStream_t sx0 = side_stream(h);
+  const hipStream_t sx = sx0 ? sx0 : st;
+  int k = 0;   // next sync event
+  const int dt = h->cfg.dtype;
+  auto attention = [&](hipStream_t s, int64_t blk0, int64_t blk1) -> int {   // blocks [blk0, blk1) (S rows at the end)
+    if (!al) return THIN_OK;
+    thin::AttnLaunch a = *al;
+    a.causal = 1;
+    a.ev = ev;
+    a.t0 = static_cast<int>(std::min<int64_t>(blk0 * n, a.T));
+    a.t1 = static_cast<int>(std::min<int64_t>(blk1 * n, a.T));
+    if (a.t1 <= a.t0) return THIN_OK;
+    THIN_HIP(timed(h, s, "attention", [&] { return thin::launch_attention(a, dt, h->cfg.E, h->cfg.D, s); }));
+    return THIN_OK;
+  };
+  const int64_t all_blocks = (static_cast<int64_t>(al ? al->T : 0) + n - 1) / n + 1;   // past every query row
   // 1. representatives of every thin-phase batch (data independent)
   THIN_HIP(timed(h, st, "express_reps", [&] { return thin::launch_express_reps(ev, units, seed, reps, st); }));
-  // 2. all batch halvings at once: they read only representatives
+  if (p.sc.n_halves == 0) {   // no HALVE: still exact (or only batch halvings past the last block)
+    return attention(st, 0, all_blocks);
+  }
+  THIN_HIP(stream_wait(h, st, sx, k++));
+  // 2. on the side: all batch halvings (they read only representatives); with a
+  // single HALVE, the exact epoch's attention goes there first
+  int rc = THIN_OK;
+  if (p.sc.n_halves == 1 && (rc = attention(sx, 0, 4))) return rc;
   if (p.sc.n_batches_done > 0) {
     const int N = 2 * n;
     const int nb = p.sc.n_batches_done;
     const int64_t ustride = static_cast<int64_t>(p.sc.n_batches_alloc) * N;
-    thin::SweepLaunch sl = make_sweep(h, G, N, units, nb, reps, ustride, bout, seed, thin::kTagBatch, 0);
-    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
+    thin::SweepLaunch sl = make_sweep(h, Gb, N, units, nb, reps, ustride, bout, seed, thin::kTagBatch, 0);
+    THIN_HIP(timed(h, sx, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), sx); }));
     sl.out_stride = n;
     sl.dec = decisions;
     sl.dec_per_unit = ndec;
     sl.dec_mode = 1;
-    THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, st); }));
+    THIN_HIP(timed(h, sx, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, sx); }));
   }
-  // 3. the HALVE chain: halve twice, 4n -> 2n -> n
+  const int k_batches = k++;   // marks the batch halvings on the side
+  if (sx != st) THIN_HIP(hipEventRecord(h->sync_ev[k_batches], sx));
+  // 3. the HALVE chain on st: halve twice, 4n -> 2n -> n; HALVE e >= 1 reads batches 3(e-1) ..
   for (int e = 0; e < p.sc.n_halves; ++e) {
+    if (e == 1 && sx != st) THIN_HIP(hipStreamWaitEvent(st, h->sync_ev[k_batches], 0));
     THIN_HIP(timed(h, st, "halve_input", [&] { return thin::launch_halve_input(ev, units, e, hin, st); }));
-    thin::SweepLaunch s1 = make_sweep(h, G, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
+    thin::SweepLaunch s1 = make_sweep(h, Gh, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
                                       static_cast<uint64_t>(e));
     THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(s1, src, h->scale64), st); }));
     s1.out_stride = 2 * n;
@@ -340,7 +399,7 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
     s1.dec_per_unit = ndec;
     s1.dec_base = static_cast<int64_t>(6) * n * e;
     THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(s1, st); }));
-    thin::SweepLaunch s2 = make_sweep(h, G, 2 * n, units, 1, hmid, 2 * n, hout + static_cast<int64_t>(e) * n, seed,
+    thin::SweepLaunch s2 = make_sweep(h, Gh, 2 * n, units, 1, hmid, 2 * n, hout + static_cast<int64_t>(e) * n, seed,
                                       thin::kTagHalveSecond, static_cast<uint64_t>(e));
     THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(s2, src, h->scale64), st); }));
     s2.out_stride = static_cast<int64_t>(p.sc.n_halves) * n;   // unit u -> row u of [units][halves][n]
@@ -348,6 +407,18 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
     s2.dec_per_unit = ndec;
     s2.dec_base = static_cast<int64_t>(6) * n * e + 2 * n;
     THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(s2, st); }));
+    // epoch e + 1 reads HALVE e and the batches of its epoch (done on the side before this
+    // point).  Every epoch but the last goes in one launch on the side once the HALVE before
+    // the last is done, beside the last HALVE; the last epoch follows that HALVE on st
+    const int H = p.sc.n_halves;
+    if (e == H - 2 && al) {
+      THIN_HIP(stream_wait(h, st, sx, k++));
+      if ((rc = attention(sx, 0, static_cast<int64_t>(1) << (2 * H)))) return rc;
+    }
+    if (e == H - 1) {   // st takes in the side's work (batches, earlier epochs), then runs the last epoch
+      THIN_HIP(stream_wait(h, sx, st, k++));
+      if ((rc = attention(st, static_cast<int64_t>(1) << (2 * H), all_blocks))) return rc;
+    }
   }
   return THIN_OK;
 }

@@ -107,6 +107,8 @@ struct AttnLaunch {
   // Gathered token indices outside [0, S) are clamped into range (no read
   // leaves the unit's rows) and, when err is set, reported by storing 1 there.
   int* err;
+  // Query rows [t0, t1) of every (b, h) are computed (t1 = 0: all T rows).
+  int t0, t1;
 };
 
 // Row moves into / inside the streaming Express state (see kv.hip).

@@ -4,6 +4,13 @@ python -m sub_quadratic_attention_amd.profiling stats KERNEL_STATS_CSV "COMMAND"
     print a text table of a --kernel-trace --stats run (kernel, calls,
     average / total microseconds, share).
 
+python -m sub_quadratic_attention_amd.profiling counters DIR [DIR ...] --command "COMMAND"
+    per-kernel table of --pmc runs (each DIR a rocprofv3 --output-format csv
+    output holding run_counter_collection.csv): instruction counts, MFMA
+    operations by type, and the MFMA-busy fraction of the SIMD cycles
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE of one XCD times the 1024
+    SIMDs, as rocprofv3's MfmaUtil metric defines it).
+
 python -m sub_quadratic_attention_amd.profiling traffic --kernel LABEL --symbol NAME_FRAGMENT
         --source csrc/FILE.hip --workload NAME --fetch CSV --write CSV
         --copy-fetch CSV --copy-write CSV --copy-bytes N
@@ -65,6 +72,43 @@ def copy_counter(path, counter):
     return max(per.values())
 
 
+def kernel_short_name(full):
+    """pair_gram_kernel from 'void thin::(anonymous namespace)::pair_gram_kernel<1>(thin::GramLaunch, ...)'."""
+    import re
+    names = re.findall(r"::(\w+)(?:<[^>]*>)?\(", full)
+    return names[-1] if names else full
+
+
+def counters_table(dirs, command, xcds=8, simds=1024):
+    """Sum every counter over the dispatches of each kernel, per --pmc run directory."""
+    per = {}        # kernel -> counter -> total
+    grbm = {}       # kernel -> sum over dispatches of GRBM_GUI_ACTIVE / xcds (one pass)
+    dispatches = {}
+    for n, d in enumerate(dirs):
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            k = kernel_short_name(r["Kernel_Name"])
+            c, v = r["Counter_Name"], float(r["Counter_Value"])
+            if c == "GRBM_GUI_ACTIVE":
+                if n == 0:
+                    grbm[k] = grbm.get(k, 0.0) + v / xcds
+                    dispatches[k] = dispatches.get(k, 0) + 1
+                continue
+            per.setdefault(k, {})
+            per[k][c] = per[k].get(c, 0.0) + v
+    out = [f"command: {command}", ""]
+    for k in sorted(per, key=lambda x: -grbm.get(x, 0.0)):
+        c = per[k]
+        g = grbm.get(k, 0.0)
+        out.append(f"{k}: {dispatches.get(k, 0)} dispatches, {g:.4g} GPU cycles (GRBM_GUI_ACTIVE of one XCD)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and g:
+            out.append(f"    MFMA busy: {100.0 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (g * simds):.1f}% of SIMD cycles")
+        for name in sorted(c):
+            if name == "SQ_VALU_MFMA_BUSY_CYCLES":
+                continue
+            out.append(f"    {name:34s} {c[name]:.6g}")
+    return "\n".join(out)
+
+
 def traffic_for(label, workload):
     """Bytes per launch recorded for this kernel and workload, or None if absent or stale."""
     try:
@@ -85,6 +129,9 @@ def main(argv=None):
     a = sub.add_parser("stats")
     a.add_argument("csv")
     a.add_argument("command")
+    cn = sub.add_parser("counters")
+    cn.add_argument("dirs", nargs="+")
+    cn.add_argument("--command", required=True)
     t = sub.add_parser("traffic")
     for name in ("kernel", "symbol", "source", "workload", "fetch", "write", "copy_fetch", "copy_write"):
         t.add_argument("--" + name.replace("_", "-"), required=True)
@@ -92,6 +139,9 @@ def main(argv=None):
     args = p.parse_args(argv)
     if args.cmd == "stats":
         print(stats_table(args.csv, args.command))
+        return 0
+    if args.cmd == "counters":
+        print(counters_table(args.dirs, args.command))
         return 0
     symbol, src = args.symbol, args.source
     f_kib, nf = counter_sum(args.fetch, symbol, "FETCH_SIZE")

@@ -52,7 +52,7 @@ def _create(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), -1), (dict(H=3, H_kv=2), -1), (dict(n_out=3), -1), (dict(g=-1), -1),
-    (dict(flags=4), -1), (dict(flags=0x80000001), -1), (dict(E=96), -2), (dict(dtype=0, E=64, D=256), -2), (dict(E=0), -1),
+    (dict(flags=8), -1), (dict(flags=0x80000001), -1), (dict(E=96), -2), (dict(dtype=0, E=64, D=256), -2), (dict(E=0), -1),
 ])
 def test_create_rejects(kw, code):
     rc, h = _create(**kw)

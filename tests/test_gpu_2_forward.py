@@ -265,3 +265,22 @@ def test_thinning_after_selector(S, L, dtype, sub):
     err = att.max_abs_error(out.float().cpu().numpy().astype(np.float64), ref["out"])
     say(f"[subset] S={S} L={L}: max|gpu - oracle| = {err:.3g}")
     assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("S,n", [(4325, 64), (32768 // 4, 0)])
+def test_causal_two_streams_equal_one_stream(S, n):
+    """The causal path's second stream (batch halvings and finished epochs' attention beside
+    the HALVE chain) gives bit-identical outputs, coreset and decisions to one stream."""
+    from sub_quadratic_attention_amd.binding import ThinAttention
+    d = inputs.causal_prefill(seed=9, H=4, S=S)
+    q, k, v = (to_gpu(d[x], "bf16") for x in ("q", "k", "v"))
+    res = []
+    for one in (False, True):
+        ta = ThinAttention(128, 128, 4, 4, torch.bfloat16, n_out=n, one_stream=one)
+        out, ex = ta.forward(q, k, v, causal=True, seed=3, return_coreset=True, return_decisions=True)
+        torch.cuda.synchronize()
+        res.append((out, ex))
+    (o2, e2), (o1, e1) = res
+    assert torch.equal(o1, o2)
+    for key in ("coreset_idx", "coreset_w", "coreset_len", "decisions"):
+        assert torch.equal(e1[key], e2[key]), key
