@@ -368,10 +368,41 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
   if (p.sc.n_halves == 0) {   // no HALVE: still exact (or only batch halvings past the last block)
     return attention(st, 0, all_blocks);
   }
-  THIN_HIP(stream_wait(h, st, sx, k++));
-  // 2. on the side: all batch halvings (they read only representatives); with a
-  // single HALVE, the exact epoch's attention goes there first
+  // HALVE e halves twice, 4n -> 2n -> n, on st; HALVE e >= 1 reads batches 3(e-1) ..
+  auto halve_first_gram = [&](int e) -> int {
+    THIN_HIP(timed(h, st, "halve_input", [&] { return thin::launch_halve_input(ev, units, e, hin, st); }));
+    thin::SweepLaunch s1 = make_sweep(h, Gh, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
+                                      static_cast<uint64_t>(e));
+    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(s1, src, h->scale64), st); }));
+    return THIN_OK;
+  };
+  auto halve_rest = [&](int e) -> int {
+    thin::SweepLaunch s1 = make_sweep(h, Gh, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
+                                      static_cast<uint64_t>(e));
+    s1.out_stride = 2 * n;
+    s1.dec = decisions;
+    s1.dec_per_unit = ndec;
+    s1.dec_base = static_cast<int64_t>(6) * n * e;
+    THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(s1, st); }));
+    thin::SweepLaunch s2 = make_sweep(h, Gh, 2 * n, units, 1, hmid, 2 * n, hout + static_cast<int64_t>(e) * n, seed,
+                                      thin::kTagHalveSecond, static_cast<uint64_t>(e));
+    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(s2, src, h->scale64), st); }));
+    s2.out_stride = static_cast<int64_t>(p.sc.n_halves) * n;   // unit u -> row u of [units][halves][n]
+    s2.dec = decisions;
+    s2.dec_per_unit = ndec;
+    s2.dec_base = static_cast<int64_t>(6) * n * e + 2 * n;
+    THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(s2, st); }));
+    return THIN_OK;
+  };
   int rc = THIN_OK;
+  // 2. HALVE 0's first Gram, then the fork: the side takes every batch halving
+  // (they read only representatives).  Forking after that Gram rather than
+  // before it keeps the batch Gram from crowding the small walks of HALVE 0
+  // out of the compute units (a walk launched while a large Gram holds every
+  // unit waits for it to drain); with a single HALVE, the exact epoch's
+  // attention goes to the side first
+  if ((rc = halve_first_gram(0))) return rc;
+  THIN_HIP(stream_wait(h, st, sx, k++));
   if (p.sc.n_halves == 1 && (rc = attention(sx, 0, 4))) return rc;
   if (p.sc.n_batches_done > 0) {
     const int N = 2 * n;
@@ -387,37 +418,22 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
   }
   const int k_batches = k++;   // marks the batch halvings on the side
   if (sx != st) THIN_HIP(hipEventRecord(h->sync_ev[k_batches], sx));
-  // 3. the HALVE chain on st: halve twice, 4n -> 2n -> n; HALVE e >= 1 reads batches 3(e-1) ..
-  for (int e = 0; e < p.sc.n_halves; ++e) {
+  // 3. the HALVE chain on st
+  const int H = p.sc.n_halves;
+  for (int e = 0; e < H; ++e) {
     if (e == 1 && sx != st) THIN_HIP(hipStreamWaitEvent(st, h->sync_ev[k_batches], 0));
-    THIN_HIP(timed(h, st, "halve_input", [&] { return thin::launch_halve_input(ev, units, e, hin, st); }));
-    thin::SweepLaunch s1 = make_sweep(h, Gh, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
-                                      static_cast<uint64_t>(e));
-    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(s1, src, h->scale64), st); }));
-    s1.out_stride = 2 * n;
-    s1.dec = decisions;
-    s1.dec_per_unit = ndec;
-    s1.dec_base = static_cast<int64_t>(6) * n * e;
-    THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(s1, st); }));
-    thin::SweepLaunch s2 = make_sweep(h, Gh, 2 * n, units, 1, hmid, 2 * n, hout + static_cast<int64_t>(e) * n, seed,
-                                      thin::kTagHalveSecond, static_cast<uint64_t>(e));
-    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(s2, src, h->scale64), st); }));
-    s2.out_stride = static_cast<int64_t>(p.sc.n_halves) * n;   // unit u -> row u of [units][halves][n]
-    s2.dec = decisions;
-    s2.dec_per_unit = ndec;
-    s2.dec_base = static_cast<int64_t>(6) * n * e + 2 * n;
-    THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(s2, st); }));
+    if (e > 0 && (rc = halve_first_gram(e))) return rc;
+    if ((rc = halve_rest(e))) return rc;
     // epoch e + 1 reads HALVE e and the batches of its epoch (done on the side before this
     // point).  Every epoch but the last goes in one launch on the side once the HALVE before
     // the last is done, beside the last HALVE; the last epoch follows that HALVE on st
-    const int H = p.sc.n_halves;
     if (e == H - 2 && al) {
       THIN_HIP(stream_wait(h, st, sx, k++));
       if ((rc = attention(sx, 0, static_cast<int64_t>(1) << (2 * H)))) return rc;
     }
-    if (e == H - 1) {   // st takes in the side's work (batches, earlier epochs), then runs the last epoch
-      THIN_HIP(stream_wait(h, sx, st, k++));
+    if (e == H - 1) {   // the last epoch on st (beside the side's tail), then st takes in the side's work
       if ((rc = attention(st, static_cast<int64_t>(1) << (2 * H), all_blocks))) return rc;
+      THIN_HIP(stream_wait(h, sx, st, k++));
     }
   }
   return THIN_OK;
