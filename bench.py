@@ -494,7 +494,7 @@ def main():
             per_launch_bytes = w["bytes"] / r["launches_per_step"]
             gbs = per_launch_bytes / (r["avg_ms"] * 1e-3) / 1e9
             return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK["hbm_GBs"], "unit": "GB/s",
-                    "frac": round(gbs / PEAK["hbm_GBs"], 4), "traffic": None, "kernel": label,
+                    "frac": round(gbs / PEAK["hbm_GBs"], 4), "traffic": _traffic(label, args.workload), "kernel": label,
                     "work_per_launch_bytes": per_launch_bytes, "avg_launch_ms": r["avg_ms"]}
         per_launch_flops = w["flops"] / r["launches_per_step"]
         peak_key = "f64" if label in ("pair_gram", "medium_halving") else dt
@@ -505,7 +505,7 @@ def main():
             peak_key = "fp8 (Q K^T) + bf16 (P V)"
         achieved = per_launch_flops / (r["avg_ms"] * 1e-3) / 1e12
         res = {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1), "unit": "TFLOP/s",
-               "frac": round(achieved / peak, 4), "traffic": None, "kernel": label,
+               "frac": round(achieved / peak, 4), "traffic": _traffic(label, args.workload), "kernel": label,
                "work_per_launch_flops": per_launch_flops, "avg_launch_ms": r["avg_ms"],
                "dtype": peak_key}
         if w.get("bytes"):
@@ -515,8 +515,6 @@ def main():
         return res
 
     roofline = roof(dom) if wm.get(dom) else None
-    if roofline:
-        roofline["traffic"] = _traffic(dom, args.workload)
     rooflines = {l: roof(l) for l in per_kernel if wm.get(l)}
 
     # exact comparators on the same GPU
