@@ -49,6 +49,32 @@ ELT = {"f32": 4, "bf16": 2, "fp8": 1}
 FLAGS = {"vit_token_mixing_subsampled": dict(subsample_base=True)}   # ThinAttention options per workload
 
 
+def _dense_exact_ms(q, k, v, scale, n_ex, cap_bytes=8 << 30):
+    """Exact attention as dense products (q [.., T, E], k [.., S, E], v [.., S, D], the same
+    leading dims): scores q k^T, softmax in fp32, then P v.  Every operand of a product is a
+    contiguous tensor (K is transposed into a copy first).  None when the fp32 scores would
+    exceed cap_bytes."""
+    import torch
+    S = k.shape[-2]
+    if q.numel() // q.shape[-1] * S * 4 > cap_bytes:
+        return None
+    kT = k.transpose(-1, -2).contiguous()
+
+    def run():
+        sc = torch.matmul(q, kT).float() * scale
+        return torch.matmul(torch.softmax(sc, dim=-1).to(v.dtype), v)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    a = time.perf_counter()
+    for _ in range(n_ex):
+        run()
+    torch.cuda.synchronize()
+    del kT
+    return (time.perf_counter() - a) * 1e3 / n_ex
+
+
 def _traffic(label, workload):
     """HBM bytes per launch from the committed counter runs, None if absent or the kernel changed since."""
     from sub_quadratic_attention_amd.profiling import traffic_for
@@ -354,7 +380,16 @@ def decode_main(args):
         torch.cuda.synchronize()
         exact["sdpa_decode_step_us"] = (time.perf_counter() - a) * 1e6 / 50
         exact["decode_speedup_vs_sdpa"] = exact["sdpa_decode_step_us"] / decode_us
-        del kt, vt
+        # the same step as dense products over the KV heads: [G, E] x [E, S] scores per KV head
+        G = H // Hkv
+        kg = torch.cat([kh, ks], dim=1).to(sdt).permute(0, 2, 1, 3).contiguous()   # [B, Hkv, S, E]
+        vg = torch.cat([vh, vs], dim=1).to(sdt).permute(0, 2, 1, 3).contiguous()   # [B, Hkv, S, D]
+        qg = qs[:, -1].to(sdt).reshape(B, Hkv, G, E).contiguous()
+        dense = _dense_exact_ms(qg, kg, vg, scale=1.0 / math.sqrt(E), n_ex=50)
+        if dense is not None:
+            exact["dense_matmul_decode_step_us"] = dense * 1e3
+            exact["decode_speedup_vs_dense_matmul"] = dense * 1e3 / decode_us
+        del kt, vt, kg, vg
         # this library's attention kernel with thinning disabled: the last step's 32 query
         # heads (one token each) against all S0 + steps keys (unmasked over the whole cache is
         # exactly the causal decode of the last token)
@@ -539,6 +574,11 @@ def main():
             f(qt, kt, vt, is_causal=causal)
         torch.cuda.synchronize()
         exact["sdpa_ms"] = (time.perf_counter() - a) * 1e3 / n_ex
+        if not causal:
+            dense = _dense_exact_ms(qt, kt, vt, scale=1.0 / math.sqrt(E), n_ex=n_ex)
+            if dense is not None:
+                exact["dense_matmul_ms"] = dense
+                exact["speedup_vs_dense_matmul"] = dense / ms_per_step
         del qt, kt, vt
         # this library's own kernels with thinning disabled: the unmasked coreset attention
         # over every key (over the selected keys for a selector's list), and the causal forward
