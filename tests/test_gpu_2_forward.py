@@ -267,10 +267,12 @@ def test_thinning_after_selector(S, L, dtype, sub):
     assert err <= TOL[dtype]
 
 
-@pytest.mark.parametrize("S,n", [(4325, 64), (32768 // 4, 0)])
+@pytest.mark.parametrize("S,n", [(200, 64), (600, 64), (2000, 64), (4325, 64), (32768 // 4, 0)])
 def test_causal_two_streams_equal_one_stream(S, n):
     """The causal path's second stream (batch halvings and finished epochs' attention beside
-    the HALVE chain) gives bit-identical outputs, coreset and decisions to one stream."""
+    the HALVE chain) gives bit-identical outputs, coreset and decisions to one stream: no
+    HALVE (S = 200 at n = 64), one (600: the exact epoch's attention goes to the side), two
+    (2000) and three (4325; 8192 at the default n_out of 128)."""
     from sub_quadratic_attention_amd.binding import ThinAttention
     d = inputs.causal_prefill(seed=9, H=4, S=S)
     q, k, v = (to_gpu(d[x], "bf16") for x in ("q", "k", "v"))
