@@ -432,6 +432,9 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
       if ((rc = attention(sx, 0, static_cast<int64_t>(1) << (2 * H)))) return rc;
     }
     if (e == H - 1) {   // the last epoch on st (beside the side's tail), then st takes in the side's work
+      // the last epoch reads the batches of its own epoch: with a single HALVE
+      // st has not waited for them yet (with more, HALVE 1 did)
+      if (H == 1 && sx != st) THIN_HIP(hipStreamWaitEvent(st, h->sync_ev[k_batches], 0));
       if ((rc = attention(st, static_cast<int64_t>(1) << (2 * H), all_blocks))) return rc;
       THIN_HIP(stream_wait(h, sx, st, k++));
     }
