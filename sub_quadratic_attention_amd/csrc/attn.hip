@@ -173,7 +173,6 @@ struct Attn {
   f32x4_t osum[NQG];   // bf16: row sums of P (all four elements equal)
   float m_run[NQG], l_run[NQG];
 
-  float r_w;   // weighted coreset: weight of the key this thread describes in the next chunk
   uint4 vreg[VGPT > 0 ? VGPT : 1];   // fp8: V pieces of the next chunk, in flight
 
   // the stream: G gathered keys, then raw.count raw ones; current window [w0, w0 + wl)
@@ -355,19 +354,21 @@ struct Attn {
   }
 
   // Per-key visibility and log2-weight of chunk c into buffer buf (threads < kC).
-  // A weighted coreset's entry weight was fetched one chunk earlier (r_w), and
-  // the next one is fetched here, so no load is waited for on the spot.
+  // A weighted coreset's entry weight is loaded and used here; callers take
+  // meta before the chunk's copy, so that waiting for that load never waits
+  // for the copy (memory loads complete in order for the wait counter).
+  // Nothing of it is carried from chunk to chunk: a value loaded one chunk
+  // ahead and kept in a register made the compiler wait for every load in
+  // flight, the next chunk's copy included, before the chunk's reads.
   __device__ __forceinline__ void meta(int c, int nch, int buf) {
+    (void)nch;
     const int tid = threadIdx.x;
     if (tid < kC) {
       const int r = kC * c + tid;
       const int pos = w0 + r;   // position in the stream
       float lg = gs.lnw2 - (pos < gs.cnt[0] + gs.cnt[1] ? 0.f : 1.f);
       if constexpr (!RAW) {
-        if (gs.w != nullptr) {
-          lg = log2f(r_w);
-          if (c + 1 < nch) r_w = entry_weight(c + 1);
-        }
+        if (gs.w != nullptr) lg = log2f(entry_weight(c));
       }
       const bool gathered = pos < G;
       int posc = gathered ? INT_MIN : (raw.causal ? raw.start + (pos - G) : INT_MIN);
@@ -595,11 +596,8 @@ struct Attn {
       __syncthreads();
     }
     const int nch = (wl + kC - 1) / kC;
-    copy(0, (lds_byte*)&sm.k[0][0], (lds_byte*)&sm.v[0][0]);
-    if constexpr (!RAW) {
-      if (gs.w != nullptr && threadIdx.x < kC) r_w = entry_weight(0);
-    }
     meta(0, nch, 0);
+    copy(0, (lds_byte*)&sm.k[0][0], (lds_byte*)&sm.v[0][0]);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     store_v((lds_byte*)&sm.v[0][0]);
     if (kC > wl) {
@@ -637,8 +635,8 @@ struct Attn {
                                           const lds_byte* __restrict__ vc, lds_byte* __restrict__ kn,
                                           lds_byte* __restrict__ vn) {
     if (c + 1 < nch) {
-      copy(c + 1, kn, vn);
       meta(c + 1, nch, (c + 1) & 1);
+      copy(c + 1, kn, vn);
     }
     consume(c, c & 1, kc, vc);
   }
