@@ -28,7 +28,8 @@ import time
 import numpy as np
 
 METRIC = "thinned-attention queries·keys/sec & ms/call vs exact attn; HBM GB/s, MFMA %"
-PEAK = {"hbm_GBs": 8000.0, "f32": 157.3, "bf16": 2500.0, "fp8": 5000.0, "f64": 78.6}   # MI355X: HBM GB/s, dense TFLOP/s
+PEAK = {"hbm_GBs": 8000.0, "f32": 157.3, "bf16": 2500.0, "fp8": 5000.0, "f64": 78.6,
+        "i8": 5000.0}   # MI355X: HBM GB/s, dense TFLOP/s (int8: TOP/s)
 
 WORKLOADS = {
     # name: (generator kwargs, causal, H, H_kv, E, D)
@@ -133,6 +134,28 @@ def express_visible_total(S, n):
     return total
 
 
+def express_halvings(S, n):
+    """(bins per unit, points per bin) of every halving launch of the causal path, per unit."""
+    nblk = S // n
+    halves = 0
+    while 4 ** (halves + 1) <= nblk:
+        halves += 1
+    done = 0
+    e = 1
+    while 4 ** e < nblk:
+        for j in range(3):
+            if 4 ** e * (2 + j) <= nblk:
+                done += 1
+        e += 1
+    return ([(done, 2 * n)] if done else []) + [(1, 4 * n), (1, 2 * n)] * halves
+
+
+def gram8_runs(dt, E, D, N, fp64_gram=False):
+    """Does the library take the exact integer Gram (int8 digit products) for bins of N points?"""
+    return (not fp64_gram and dt in ("bf16", "fp8") and E % 64 == 0 and D % 64 == 0 and 64 <= E <= 256
+            and 64 <= D <= 256 and N >= 256)
+
+
 def express_gram_entries(S, n):
     """Point-Gram entries N(N+1)/2 of every halving (batch and both HALVE passes), per unit."""
     nblk = S // n
@@ -150,9 +173,13 @@ def express_gram_entries(S, n):
     return halves * (tri(4 * n) + tri(2 * n)) + done * tri(2 * n)
 
 
-def work_model(name, B, T, S, H, Hkv, E, D, causal, elt, subsample_base=False, out_elt=None):
-    """Per-forward algorithmic flops / bytes of each kernel label."""
+def work_model(name, B, T, S, H, Hkv, E, D, causal, elt, subsample_base=False, out_elt=None, dt="bf16"):
+    """Per-forward algorithmic flops / bytes of each kernel label.  Pair-Gram launches of bf16 /
+    fp8 bins of >= 256 points run as exact integer dot products on the int8 MFMA (nd^2 digit
+    products per multiply-add of the definition, nd = 4 for bf16 and 3 for fp8) after a digit
+    pass that reads every point once and writes its digits."""
     units = B * Hkv
+    nd = 3 if dt == "fp8" else 4
     if not causal:
         S_full = S
         S = S // base_stride(S) if subsample_base else S   # the list the Compress runs on
@@ -166,6 +193,7 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt, subsample_base=False, o
         medium = lambda N: 16 < N <= 32 and N % 4 == 0 and E % 32 == 0 and D % 32 == 0 and \
             N * ((E + D) * elt + 16) <= 96 * 1024
         levels = [(S // (s0 * 4 ** l), s0 * 2 ** (l + 1)) for l in range(1, j + 1)]   # (bins, N) per unit
+        tiles = [(bins, N) for bins, N in levels if not small(N) and not medium(N)]
         gram_entries = sum(bins * N * (N + 1) // 2 for bins, N in levels if not small(N) and not medium(N))
         medium_entries = sum(bins * N * (N + 1) // 2 for bins, N in levels if medium(N))
         small_bytes = units * sum(bins * N * (E + D) * elt + bins * (N // 2) * 5 for bins, N in levels if small(N))
@@ -178,17 +206,27 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt, subsample_base=False, o
         while n_out * n_out < S:
             n_out *= 2
         gram_entries = express_gram_entries(S, n_out)
+        tiles = express_halvings(S, n_out)
         small_bytes = 0
         medium_entries = 0
         pairs_eff = B * H * T * (T + 1) // 2
         visible = B * H * express_visible_total(S, n_out)
         attn_bytes = (B * T * H * E + units * S * (E + D)) * elt + B * T * H * D * (out_elt or elt)
+    i8 = [(bins, N) for bins, N in tiles if gram8_runs(dt, E, D, N)]
+    i8_entries = sum(bins * N * (N + 1) // 2 for bins, N in i8)
+    i8_points = units * sum(bins * N for bins, N in i8)
+    pair_gram = None
+    if gram_entries:
+        pair_gram = dict(flops=2.0 * (E + D) * gram_entries * units, bytes=None)
+        if i8_entries == gram_entries:   # every tile launch on the int8 MFMA
+            pair_gram.update(int8_ops=nd * nd * pair_gram["flops"], nd=nd)
     return dict(
         n_out=n_out,
+        gram_digits=dict(flops=None, bytes=i8_points * ((E + D) * (elt + nd) + 10)) if i8_points else None,
         pairs_eff=pairs_eff,
         attention=dict(flops=2.0 * visible * (E + D), bytes=attn_bytes, qk_flops=2.0 * visible * E,
                        pv_flops=2.0 * visible * D),
-        pair_gram=dict(flops=2.0 * (E + D) * gram_entries * units, bytes=None) if gram_entries else None,
+        pair_gram=pair_gram,
         small_halving=dict(flops=None, bytes=small_bytes) if small_bytes else None,
         medium_halving=dict(flops=2.0 * (E + D) * medium_entries * units, bytes=None) if medium_entries else None,
     )
@@ -507,7 +545,7 @@ def main():
     recs = ta1.timing_records()
     ta1.set_timing(False)
 
-    wm = work_model(args.workload, B, T, L, H, Hkv, E, D, causal, elt, out_elt=2 if dt == "fp8" else elt,
+    wm = work_model(args.workload, B, T, L, H, Hkv, E, D, causal, elt, out_elt=2 if dt == "fp8" else elt, dt=dt,
                     **opts)   # (a selector's list: its L keys)
     per_kernel = {}
     for label, ms in recs:
@@ -532,6 +570,18 @@ def main():
                     "frac": round(gbs / PEAK["hbm_GBs"], 4), "traffic": _traffic(label, args.workload), "kernel": label,
                     "work_per_launch_bytes": per_launch_bytes, "avg_launch_ms": r["avg_ms"]}
         per_launch_flops = w["flops"] / r["launches_per_step"]
+        if w.get("int8_ops"):
+            # exact dot products as int8 digit products: against the int8 MFMA peak, with the
+            # definition's fp64 multiply-adds per second beside it (what an fp64 Gram would need)
+            ops = w["int8_ops"] / r["launches_per_step"]
+            achieved = ops / (r["avg_ms"] * 1e-3) / 1e12
+            f64 = per_launch_flops / (r["avg_ms"] * 1e-3) / 1e12
+            return {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK["i8"], "unit": "TOP/s",
+                    "frac": round(achieved / PEAK["i8"], 4), "traffic": _traffic(label, args.workload),
+                    "kernel": label, "work_per_launch_ops": ops, "avg_launch_ms": r["avg_ms"],
+                    "dtype": f"i8 (exact digit products, {w['nd']} digits per feature)",
+                    "fp64_equivalent": {"flops_per_launch": per_launch_flops, "achieved": round(f64, 3),
+                                        "peak": PEAK["f64"], "unit": "TFLOP/s", "frac": round(f64 / PEAK["f64"], 4)}}
         peak_key = "f64" if label in ("pair_gram", "medium_halving") else dt
         peak = PEAK[peak_key]
         if label == "attention" and dt == "fp8":

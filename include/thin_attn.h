@@ -82,7 +82,18 @@ enum thin_dtype { THIN_F32 = 0, THIN_BF16 = 1, THIN_FP8_E4M3 = 2 };
  *   finished epoch run there beside the HALVE chain, and the caller's stream
  *   waits for all of it before the call's last launch.  Results are the same
  *   either way; the flag gives serial launches (per-kernel timing). */
-enum thin_flags { THIN_GREEDY_SIGNS = 1u, THIN_SUBSAMPLE_BASE = 2u, THIN_ONE_STREAM = 4u };
+/* THIN_FP64_GRAM: every pair Gram of the kernel-halving walks runs on the
+ *   fp64 matrix cores.  By default the Grams of bf16 and fp8 inputs (E and D
+ *   multiples of 64, bins of at least 256 points) take their dot products on
+ *   the int8 matrix cores instead: each row is scaled by a power of two into
+ *   integers, split into balanced base-256 digits, and the digit products are
+ *   summed exactly, so every dot product is the exact one rounded once to
+ *   fp64; rows whose features span more than the digits hold (bf16 features
+ *   more than 22 binades below the row's largest) have their pairs'
+ *   Gram entries recomputed in fp64.  Decisions agree with the fp64 Gram up
+ *   to the rounding of its dot products (near ties).  The workspace sizes
+ *   include the integer Gram's scratch unless the flag is set. */
+enum thin_flags { THIN_GREEDY_SIGNS = 1u, THIN_SUBSAMPLE_BASE = 2u, THIN_ONE_STREAM = 4u, THIN_FP64_GRAM = 8u };
 
 enum thin_status {
   THIN_OK = 0,
@@ -105,7 +116,8 @@ typedef struct thin_attn_config {
                       thinning (exact causal attention)                                */
   double delta;    /* kernel-halving failure parameter; <= 0 means 0.5                */
   float scale;     /* softmax scale s; 0 means 1/sqrt(E)                              */
-  uint32_t flags;  /* THIN_GREEDY_SIGNS | THIN_SUBSAMPLE_BASE | THIN_ONE_STREAM; others rejected */
+  uint32_t flags;  /* THIN_GREEDY_SIGNS | THIN_SUBSAMPLE_BASE | THIN_ONE_STREAM | THIN_FP64_GRAM;
+                      others rejected */
 } thin_attn_config;
 
 typedef struct thin_attn thin_attn_t;
@@ -266,11 +278,20 @@ int thin_attn_coreset_attention(thin_attn_t* h, const void* q, const void* k, co
  * float64 receives the pair Gram G_ij = <h_i, h_j>, h_i = kappa(x_2i, .) -
  * kappa(x_2i+1, .) (upper triangle G[i][j], j >= i; the rest is left
  * unspecified) and is also the kernel's scratch.  points outside [0, S) are
- * clamped into range and reported (conventions above).
+ * clamped into range and reported (conventions above).  workspace (device,
+ * 256-byte aligned, thin_attn_halving_workspace_size bytes, or NULL) is the
+ * scratch of the exact integer Gram (THIN_FP64_GRAM); with NULL, or a size
+ * of 0, the fp64 Gram runs.  A non-NULL workspace of fewer bytes is
+ * THIN_ENOMEM.
  */
 int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, int64_t S,
                       const int32_t* points, int64_t N, uint64_t seed, uint32_t tag, uint64_t bin,
-                      int32_t* kept, uint8_t* decisions, double* gram, void* stream);
+                      int32_t* kept, uint8_t* decisions, double* gram, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of thin_attn_halving over B batch entries with lists of N
+ * points (0: its Gram runs in fp64 and needs none). */
+size_t thin_attn_halving_workspace_size(const thin_attn_t* h, int64_t B, int64_t N);
 
 /* Philox4x64-10 block for n counters (device arrays, 4 words each) under key
  * (seed, 0); out receives 4 words per counter.  Exposes the generator the

@@ -17,6 +17,7 @@ THIN_F32, THIN_BF16, THIN_FP8_E4M3 = 0, 1, 2
 THIN_GREEDY_SIGNS = 1
 THIN_SUBSAMPLE_BASE = 2
 THIN_ONE_STREAM = 4
+THIN_FP64_GRAM = 8
 _STATUS = {0: "THIN_OK", -1: "THIN_EINVAL", -2: "THIN_ENOTSUP", -3: "THIN_ENOMEM", -4: "THIN_EHIP"}
 
 
@@ -58,7 +59,8 @@ _SIGNATURES = {
                                                               ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     "thin_attn_halving": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 2 + [ctypes.c_int64] * 2
                           + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64]
-                          + [ctypes.c_void_p] * 4),
+                          + [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "thin_attn_halving_workspace_size": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64]),
     "thin_attn_philox": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p,
                                         ctypes.c_void_p]),
     "thin_attn_kv_state_size": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64]),
@@ -134,7 +136,7 @@ class ThinAttention:
     """
 
     def __init__(self, E, D, H, H_kv=None, dtype=torch.float32, g=0, n_out=0, delta=0.5, scale=0.0,
-                 greedy=False, subsample_base=False, one_stream=False):
+                 greedy=False, subsample_base=False, one_stream=False, fp64_gram=False):
         self.lib = load_library()
         self.E, self.D, self.H = E, D, H
         self.H_kv = H if H_kv is None else H_kv
@@ -142,7 +144,7 @@ class ThinAttention:
         self.out_dtype = output_dtype(dtype)
         cfg = _Config(_dtype_code(dtype), E, D, H, self.H_kv, g, n_out, delta, scale,
                       (THIN_GREEDY_SIGNS if greedy else 0) | (THIN_SUBSAMPLE_BASE if subsample_base else 0)
-                      | (THIN_ONE_STREAM if one_stream else 0))
+                      | (THIN_ONE_STREAM if one_stream else 0) | (THIN_FP64_GRAM if fp64_gram else 0))
         h = ctypes.c_void_p()
         rc = self.lib.thin_attn_create(ctypes.byref(cfg), ctypes.byref(h))
         if rc != 0:
@@ -294,8 +296,9 @@ class ThinAttention:
         self._check(rc)
         return out
 
-    def halving(self, k, v, points, seed=0, tag=0, bin_id=0, stream=None):
-        """One kernel halving per unit on points [units, N]; returns (kept, decisions, gram)."""
+    def halving(self, k, v, points, seed=0, tag=0, bin_id=0, stream=None, workspace=True):
+        """One kernel halving per unit on points [units, N]; returns (kept, decisions, gram).
+        workspace=False runs the fp64 Gram (no integer-Gram scratch)."""
         if not (k.is_cuda and v.is_cuda) or k.dtype != self.dtype or v.dtype != self.dtype:
             raise ValueError("k and v must be GPU tensors of the handle dtype")
         k, v = k.contiguous(), v.contiguous()
@@ -306,9 +309,11 @@ class ThinAttention:
         kept = torch.empty((units, P), dtype=torch.int32, device=k.device)
         dec = torch.empty((units, P), dtype=torch.uint8, device=k.device)
         gram = torch.zeros((units, P, P), dtype=torch.float64, device=k.device)
+        nws = int(self.lib.thin_attn_halving_workspace_size(self.h, B, N)) if workspace else 0
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=k.device)
         rc = self.lib.thin_attn_halving(self.h, _ptr(k), _ptr(v), B, S, _ptr(points), N, ctypes.c_uint64(seed),
                                         tag, ctypes.c_uint64(bin_id), _ptr(kept), _ptr(dec), _ptr(gram),
-                                        _stream(stream))
+                                        _ptr(ws) if nws else None, nws, _stream(stream))
         self._check(rc)
         return kept, dec, gram
 

@@ -50,7 +50,7 @@ int thin_attn_create(const thin_attn_config* cfg, thin_attn_t** out) {
   if (c.g < 0) return fail(nullptr, THIN_EINVAL, "g must be >= 0");
   if (c.n_out < 0 || (c.n_out > 0 && (!pow2(c.n_out) || c.n_out < 2)))
     return fail(nullptr, THIN_EINVAL, "n_out must be 0 or a power of two >= 2");
-  if (c.flags & ~static_cast<uint32_t>(THIN_GREEDY_SIGNS | THIN_SUBSAMPLE_BASE | THIN_ONE_STREAM))
+  if (c.flags & ~static_cast<uint32_t>(THIN_GREEDY_SIGNS | THIN_SUBSAMPLE_BASE | THIN_ONE_STREAM | THIN_FP64_GRAM))
     return fail(nullptr, THIN_EINVAL, "unknown flags 0x%x", c.flags);
   if (!(c.scale >= 0.0f) || !std::isfinite(c.scale)) return fail(nullptr, THIN_EINVAL, "scale must be finite and >= 0");
   if (!thin::attention_supported(c.dtype, c.E, c.D))
@@ -213,6 +213,7 @@ static int unmasked_path(thin_attn_t* h, const thin::PointSource& src, thin::Att
     int32_t* a = reinterpret_cast<int32_t*>(ws + p.off_a);
     int32_t* b = reinterpret_cast<int32_t*>(ws + p.off_b);
     double* G = reinterpret_cast<double*>(ws + p.off_g);
+    unsigned char* dig = p.off_dig ? reinterpret_cast<unsigned char*>(ws + p.off_dig) : nullptr;
     const int32_t* in = keys;
     if (!keys) {
       THIN_HIP(timed(h, st, "iota", [&] { return thin::launch_iota(a, units, L, L, st); }));
@@ -238,7 +239,7 @@ static int unmasked_path(thin_attn_t* h, const thin::PointSource& src, thin::Att
         THIN_HIP(timed(h, st, "medium_halving",
                        [&] { return thin::launch_medium_halving(gram_for(sl, src, h->scale64), sl, st); }));
       } else {
-        THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
+        if (const int rg = run_pair_gram(h, st, gram_for(sl, src, h->scale64, dig))) return rg;
         THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, st); }));
       }
       dec_base += static_cast<int64_t>(bins) * (N / 2);
@@ -420,9 +421,14 @@ int thin_attn_coreset_attention(thin_attn_t* h, const void* q, const void* k, co
   return THIN_OK;
 }
 
+size_t thin_attn_halving_workspace_size(const thin_attn_t* h, int64_t B, int64_t N) {
+  if (!h || B < 0 || N < 2 || N > 2048) return 0;
+  return gram8_bytes(h, N, B * h->cfg.H_kv * N);
+}
+
 int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, int64_t S, const int32_t* points,
                       int64_t N, uint64_t seed, uint32_t tag, uint64_t bin, int32_t* kept, uint8_t* decisions,
-                      double* gram, void* stream) {
+                      double* gram, void* workspace, size_t workspace_bytes, void* stream) {
   if (!h) return THIN_EINVAL;
   h->err.clear();
   if (B < 0 || S <= 0) return fail(h, THIN_EINVAL, "bad B or S");
@@ -438,9 +444,14 @@ int thin_attn_halving(thin_attn_t* h, const void* k, const void* v, int64_t B, i
   thin::PointSource src{k, v, S, c.H_kv, c.E, c.D, c.dtype};
   const int n = static_cast<int>(N);
   thin::SweepLaunch sl = make_sweep(h, gram, n, units, 1, points, n, kept, seed, tag, bin);
-  thin::GramLaunch gl = gram_for(sl, src, h->scale64);
+  const size_t need = thin_attn_halving_workspace_size(h, B, N);
+  if (workspace && need > 0 && workspace_bytes < need)
+    return fail(h, THIN_ENOMEM, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(h, THIN_EINVAL, "workspace must be 256-byte aligned");
+  thin::GramLaunch gl = gram_for(sl, src, h->scale64, need > 0 ? static_cast<unsigned char*>(workspace) : nullptr);
   gl.err = h->err_dev;   // the caller's points are clamped into [0, S) and reported
-  THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gl, st); }));
+  if (const int rg = run_pair_gram(h, st, gl)) return rg;
   sl.dec = decisions;
   sl.dec_per_unit = n / 2;
   THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, st); }));

@@ -117,7 +117,7 @@ struct UnmaskedPlan {
   int64_t r, L;   // base stratum length and the thinned list's length S / r
   int j;
   int64_t s0, n_out;
-  size_t off_keys, off_list, off_a, off_b, off_g;
+  size_t off_keys, off_list, off_a, off_b, off_g, off_dig;
   size_t bytes;
 };
 
@@ -127,6 +127,16 @@ constexpr size_t kLdsLimit = 160 * 1024;
 // Can the walk of a bin of N points run?  Bins of more than 128 points keep
 // their thresholds, running sums and signs in LDS.
 inline bool walk_fits(int64_t N) { return N <= 128 || thin::sweep_lds_bytes(static_cast<int>(N)) <= kLdsLimit; }
+
+// Scratch of the exact integer pair Gram over npts points in bins of N (0:
+// the fp64 tiles run, for the dtype, the head dims, the bin size or the flag).
+inline size_t gram8_bytes(const thin_attn* h, int64_t N, int64_t npts) {
+  if ((h->cfg.flags & THIN_FP64_GRAM) || N > (1 << 30) ||
+      !thin::gram8_supported(h->cfg.dtype, h->cfg.E, h->cfg.D, static_cast<int>(N)) ||
+      !thin::gram8_fits(h->cfg.dtype, npts, h->cfg.E, h->cfg.D))
+    return 0;
+  return thin::gram8_scratch_bytes(h->cfg.dtype, h->cfg.E, h->cfg.D, npts);
+}
 
 inline UnmaskedPlan plan_unmasked(const thin_attn* h, int64_t B, int64_t S0) {
   UnmaskedPlan p{};
@@ -143,6 +153,9 @@ inline UnmaskedPlan plan_unmasked(const thin_attn* h, int64_t B, int64_t S0) {
     p.off_a = L.add(sizeof(int32_t) * units * S);
     p.off_b = L.add(sizeof(int32_t) * units * S);
     p.off_g = L.add(sizeof(double) * units * S * p.s0);   // every level needs S * s0 per unit
+    size_t dig = 0;   // level l halves bins of s0 2^(l+1) points over the S >> (l-1) points of a unit
+    for (int l = 1; l <= p.j; ++l) dig = std::max(dig, gram8_bytes(h, p.s0 << (l + 1), units * (S >> (l - 1))));
+    if (dig) p.off_dig = L.add(dig);
   }
   p.bytes = L.total;
   return p;
@@ -150,7 +163,8 @@ inline UnmaskedPlan plan_unmasked(const thin_attn* h, int64_t B, int64_t S0) {
 
 struct CausalPlan {
   thin::ExpressSchedule sc;
-  size_t off_reps, off_bout, off_hin, off_hmid, off_hout, off_g, off_gh;
+  size_t off_reps, off_bout, off_hin, off_hmid, off_hout, off_g, off_gh, off_digb, off_digh;
+  bool dig_b, dig_h;   // the integer Gram's scratch of the batch and the HALVE Grams
   size_t bytes;
 };
 
@@ -168,6 +182,12 @@ inline CausalPlan plan_causal(const thin_attn* h, int64_t B, int64_t S, int64_t 
   p.off_hout = L.add(sizeof(int32_t) * units * p.sc.n_halves * n);
   p.off_g = L.add(sizeof(double) * (p.sc.n_batches_done ? units * p.sc.n_batches_done * n * n : 0));
   p.off_gh = L.add(sizeof(double) * (p.sc.n_halves ? units * 4 * n * n : 0));
+  const size_t db = p.sc.n_batches_done ? gram8_bytes(h, 2 * n, units * p.sc.n_batches_done * 2 * n) : 0;
+  const size_t dh = p.sc.n_halves ? gram8_bytes(h, 4 * n, units * 4 * n) : 0;   // covers the 2n pass
+  p.dig_b = db > 0;
+  p.dig_h = dh > 0;
+  if (db) p.off_digb = L.add(db);
+  if (dh) p.off_digh = L.add(dh);
   p.bytes = L.total;
   return p;
 }
@@ -220,8 +240,11 @@ inline int take_index_error(thin_attn* h) {
 
 // The pair Gram of the bins a walk is about to halve, with that walk's
 // Philox parameters (the Gram launch also forms the walk's thresholds).
-inline thin::GramLaunch gram_for(const thin::SweepLaunch& w, const thin::PointSource& src, double scale) {
+// dig: the integer Gram's scratch for these bins, or nullptr (fp64 tiles).
+inline thin::GramLaunch gram_for(const thin::SweepLaunch& w, const thin::PointSource& src, double scale,
+                                 unsigned char* dig = nullptr) {
   thin::GramLaunch g{};
+  g.dig = dig;
   g.src = src;
   g.idx = w.idx_in;
   g.idx_stride = w.in_stride;
@@ -301,6 +324,18 @@ inline void release_timing(thin_attn* h) {
   h->recs.clear();
 }
 
+// The pair Gram of a launch: the integer Gram's digit pass and tiles under
+// their own timing labels, or the fp64 tiles.
+inline int run_pair_gram(thin_attn* h, hipStream_t st, const thin::GramLaunch& g) {
+  if (thin::gram8_runs(g)) {
+    THIN_HIP(timed(h, st, "gram_digits", [&] { return thin::launch_gram8_digits(g, st); }));
+    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_gram8_tiles(g, st); }));
+    return THIN_OK;
+  }
+  THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(g, st); }));
+  return THIN_OK;
+}
+
 // The side stream if this call may use it (created on the current device).
 inline hipStream_t side_stream(const thin_attn* h) {
   if (!h->side) return nullptr;
@@ -344,6 +379,8 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
   int32_t* hout = reinterpret_cast<int32_t*>(ws + p.off_hout);
   double* Gb = reinterpret_cast<double*>(ws + p.off_g);
   double* Gh = reinterpret_cast<double*>(ws + p.off_gh);
+  unsigned char* digb = p.dig_b ? reinterpret_cast<unsigned char*>(ws + p.off_digb) : nullptr;
+  unsigned char* digh = p.dig_h ? reinterpret_cast<unsigned char*>(ws + p.off_digh) : nullptr;
   ev.reps = reps;
   ev.batch_out = bout;
   ev.halve_out = hout;
@@ -373,7 +410,7 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
     THIN_HIP(timed(h, st, "halve_input", [&] { return thin::launch_halve_input(ev, units, e, hin, st); }));
     thin::SweepLaunch s1 = make_sweep(h, Gh, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
                                       static_cast<uint64_t>(e));
-    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(s1, src, h->scale64), st); }));
+    if (const int rg = run_pair_gram(h, st, gram_for(s1, src, h->scale64, digh))) return rg;
     return THIN_OK;
   };
   auto halve_rest = [&](int e) -> int {
@@ -386,7 +423,7 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
     THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(s1, st); }));
     thin::SweepLaunch s2 = make_sweep(h, Gh, 2 * n, units, 1, hmid, 2 * n, hout + static_cast<int64_t>(e) * n, seed,
                                       thin::kTagHalveSecond, static_cast<uint64_t>(e));
-    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(s2, src, h->scale64), st); }));
+    if (const int rg = run_pair_gram(h, st, gram_for(s2, src, h->scale64, digh))) return rg;
     s2.out_stride = static_cast<int64_t>(p.sc.n_halves) * n;   // unit u -> row u of [units][halves][n]
     s2.dec = decisions;
     s2.dec_per_unit = ndec;
@@ -409,7 +446,7 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
     const int nb = p.sc.n_batches_done;
     const int64_t ustride = static_cast<int64_t>(p.sc.n_batches_alloc) * N;
     thin::SweepLaunch sl = make_sweep(h, Gb, N, units, nb, reps, ustride, bout, seed, thin::kTagBatch, 0);
-    THIN_HIP(timed(h, sx, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), sx); }));
+    if (const int rg = run_pair_gram(h, sx, gram_for(sl, src, h->scale64, digb))) return rg;
     sl.out_stride = n;
     sl.dec = decisions;
     sl.dec_per_unit = ndec;

@@ -53,6 +53,9 @@ struct GramLaunch {
   double* G;
   // Point indices outside [0, S) are clamped (and reported through err, when set).
   int* err;
+  // Scratch of the exact integer Gram (gram8_scratch_bytes for nbins * N points),
+  // or nullptr: the fp64 tiles run instead.
+  unsigned char* dig;
 };
 
 // Kernel-halving decisions of many bins at once (one workgroup per bin).
@@ -151,7 +154,20 @@ struct KvDecodeLaunch {
 };
 
 // Launchers (return hipError_t of the launch).
+// The pair Gram: the exact integer kernels when a.dig is set and
+// gram8_supported() holds, else the fp64 tiles.
 hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s);
+// Exact integer pair Gram (bf16 and fp8 rows, E and D multiples of 64 up to
+// 256, bins of at least 256 points) and its scratch for npts points.
+bool gram8_supported(int dtype, int E, int D, int N);
+bool gram8_fits(int dtype, int64_t npts, int E, int D);
+size_t gram8_scratch_bytes(int dtype, int E, int D, int64_t npts);
+hipError_t launch_pair_gram8(const GramLaunch& a, hipStream_t s);
+// Its two launches (the digit pass, then thresholds, fix-ups and tiles), and
+// whether launch_pair_gram takes that path for a.
+hipError_t launch_gram8_digits(const GramLaunch& a, hipStream_t s);
+hipError_t launch_gram8_tiles(const GramLaunch& a, hipStream_t s);
+bool gram8_runs(const GramLaunch& a);
 hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s);
 // Bins of at most 16 points: the pair Gram, thresholds and walk of a
 // GramLaunch / SweepLaunch pair in one kernel (same outputs as the two).

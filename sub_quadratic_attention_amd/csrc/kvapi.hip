@@ -51,7 +51,7 @@ KvLayout kv_layout(const thin_attn* h, int64_t units, int64_t n) {
 }
 
 struct KvWs {
-  size_t off_la, off_lb, off_lc, off_g, off_part, bytes;
+  size_t off_la, off_lb, off_lc, off_g, off_dig, off_part, bytes;
 };
 
 KvWs kv_ws(const thin_attn* h, int64_t units, int64_t n) {
@@ -61,6 +61,8 @@ KvWs kv_ws(const thin_attn* h, int64_t units, int64_t n) {
   w.off_lb = L.add(sizeof(int32_t) * units * 4 * n);
   w.off_lc = L.add(sizeof(int32_t) * units * 4 * n);
   w.off_g = L.add(sizeof(double) * units * 4 * n * n);
+  const size_t dig = thinhost::gram8_bytes(h, 4 * n, units * 4 * n);   // covers the 2n halvings
+  w.off_dig = dig ? L.add(dig) : 0;
   const int G = h->cfg.H / h->cfg.H_kv;
   w.off_part = L.add(sizeof(float) * units * thin::kv_decode_splits(static_cast<int>(n)) * G * (h->cfg.D + 4));
   w.bytes = L.total;
@@ -143,11 +145,11 @@ int put_tokens(thin_kv& kv, const void* k, const void* v, int64_t S_src, int64_t
 
 // One kernel halving per unit over the state slots in `in` ([units][N]); kept slots -> out.
 int halve_slots(thin_kv& kv, const int32_t* in, int N, int32_t* out, uint32_t tag, uint64_t bin, uint8_t* dec,
-                int64_t dec_per_unit, int64_t dec_base, double* G, hipStream_t st) {
+                int64_t dec_per_unit, int64_t dec_base, double* G, unsigned char* dig, hipStream_t st) {
   thin_attn* h = kv.h;
   const thin::PointSource src = state_source(kv);
   thin::SweepLaunch sl = make_sweep(h, G, N, kv.units, 1, in, N, out, kv.seed, tag, bin);
-  THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(gram_for(sl, src, h->scale64), st); }));
+  if (const int rg = run_pair_gram(h, st, gram_for(sl, src, h->scale64, dig))) return rg;
   sl.dec = dec;
   sl.dec_per_unit = dec_per_unit;
   sl.dec_base = dec_base;
@@ -165,6 +167,7 @@ int ingest_block(thin_kv& kv, char* ws, uint8_t* dec, int64_t dec_per_unit, int6
   int32_t* lb = reinterpret_cast<int32_t*>(ws + W.off_lb);
   int32_t* lc = reinterpret_cast<int32_t*>(ws + W.off_lc);
   double* G = reinterpret_cast<double*>(ws + W.off_g);
+  unsigned char* dig = W.off_dig ? reinterpret_cast<unsigned char*>(ws + W.off_dig) : nullptr;
   const int64_t t0 = kv.tokens - n;   // first token of the finished block
   int rc;
   if (kv.m == 1) {
@@ -193,7 +196,7 @@ int ingest_block(thin_kv& kv, char* ws, uint8_t* dec, int64_t dec_per_unit, int6
     if (kv.nBf == 2 * n) {
       THIN_HIP(thin::launch_kv_iota(la, kv.units, 2 * n, 4 * n, st));
       if ((rc = halve_slots(kv, la, 2 * n, lb, thin::kTagBatch, static_cast<uint64_t>(kv.nb), dec, dec_per_unit,
-                            dec_pos, G, st)))
+                            dec_pos, G, dig, st)))
         return rc;
       dec_pos += n;
       if ((rc = move_slots(kv, lb, n, n, kv.nC, st))) return rc;
@@ -205,11 +208,11 @@ int ingest_block(thin_kv& kv, char* ws, uint8_t* dec, int64_t dec_per_unit, int6
   if (kv.nC == 4 * n) {
     THIN_HIP(thin::launch_kv_iota(la, kv.units, 4 * n, 0, st));
     if ((rc = halve_slots(kv, la, 4 * n, lb, thin::kTagHalveFirst, static_cast<uint64_t>(kv.nh), dec, dec_per_unit,
-                          dec_pos, G, st)))
+                          dec_pos, G, dig, st)))
       return rc;
     dec_pos += 2 * n;
     if ((rc = halve_slots(kv, lb, 2 * n, lc, thin::kTagHalveSecond, static_cast<uint64_t>(kv.nh), dec, dec_per_unit,
-                          dec_pos, G, st)))
+                          dec_pos, G, dig, st)))
       return rc;
     dec_pos += n;
     // compact through the (empty) buffer region: kept slots -> [4n, 5n) -> [0, n)

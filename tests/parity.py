@@ -52,7 +52,7 @@ def sample_queries(B, T, H, n, seed=0, always=()):
 
 def run_and_compare(name, d, causal, H, Hkv, E, D, n_out=0, g=0, seed=0, queries=None, scale=0.0,
                     check_error=True, greedy=False, subsample_base=False, block_outputs=False,
-                    error_queries=None):
+                    error_queries=None, fp64_gram=False):
     """Run forward on the GPU and check it against the replayed oracle.  Returns a summary dict.
 
     queries None compares every output (block_outputs: the oracle forms them a
@@ -63,7 +63,7 @@ def run_and_compare(name, d, causal, H, Hkv, E, D, n_out=0, g=0, seed=0, queries
     say(f"[parity] {name}: causal={causal} shapes q{d['q'].shape} k{d['k'].shape} v{d['v'].shape}")
     dt = d["dtype"]
     ta = ThinAttention(E, D, H, Hkv, torch_dtype(dt), g=g, n_out=n_out, scale=scale, greedy=greedy,
-                       subsample_base=subsample_base)
+                       subsample_base=subsample_base, fp64_gram=fp64_gram)
     q, k, v = (to_gpu(d[x], dt) for x in ("q", "k", "v"))
     out, ex = ta.forward(q, k, v, causal=causal, seed=seed, return_coreset=True, return_decisions=True)
     torch.cuda.synchronize()

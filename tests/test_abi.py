@@ -52,7 +52,7 @@ def _create(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), -1), (dict(H=3, H_kv=2), -1), (dict(n_out=3), -1), (dict(g=-1), -1),
-    (dict(flags=8), -1), (dict(flags=0x80000001), -1), (dict(E=96), -2), (dict(dtype=0, E=64, D=256), -2), (dict(E=0), -1),
+    (dict(flags=16), -1), (dict(flags=0x80000001), -1), (dict(E=96), -2), (dict(dtype=0, E=64, D=256), -2), (dict(E=0), -1),
 ])
 def test_create_rejects(kw, code):
     rc, h = _create(**kw)
@@ -152,9 +152,9 @@ def test_forward_argument_errors_before_any_launch():
                                    None, 0, None)
         assert rc == 0
         # halving: N odd / too large
-        rc = lib.thin_attn_halving(h, fake, fake, 1, 16, fake, 7, 0, 0, 0, fake, None, fake, None)
+        rc = lib.thin_attn_halving(h, fake, fake, 1, 16, fake, 7, 0, 0, 0, fake, None, fake, None, 0, None)
         assert rc == -1
-        rc = lib.thin_attn_halving(h, fake, fake, 1, 16, fake, 4096, 0, 0, 0, fake, None, fake, None)
+        rc = lib.thin_attn_halving(h, fake, fake, 1, 16, fake, 4096, 0, 0, 0, fake, None, fake, None, 0, None)
         assert rc == -1
         # coreset attention: idx NULL needs n == S
         rc = lib.thin_attn_coreset_attention(h, fake, fake, fake, 1, 8, 16, None, None, 8, fake, None)
@@ -258,3 +258,30 @@ def test_kv_import_rejects_tampered_counters():
         lib.thin_attn_kv_destroy(kv)
     finally:
         lib.thin_attn_destroy(h)
+
+
+def test_integer_gram_scratch_sizes():
+    """The workspace holds the exact integer Gram's scratch exactly where that Gram runs: bf16 and
+    fp8 handles with bins of >= 256 points; fp32 handles and THIN_FP64_GRAM need none of it."""
+    lib = _lib()
+    sizes = {}
+    for name, kw in [("bf16", dict(dtype=1)), ("bf16_fp64", dict(dtype=1, flags=8)), ("fp8", dict(dtype=2)),
+                     ("f32", dict(dtype=0))]:
+        rc, h = _create(E=128, D=128, H=32, H_kv=32, **kw)
+        assert rc == 0
+        try:
+            sizes[name] = (lib.thin_attn_workspace_size(h, 1, 32768, 32768, 1),
+                           lib.thin_attn_halving_workspace_size(h, 1, 1024),
+                           lib.thin_attn_halving_workspace_size(h, 1, 128))
+        finally:
+            lib.thin_attn_destroy(h)
+    n, units = 256, 32
+    # digits (4 per bf16 feature, 3 per fp8 one) of K and V, two scales and two flags per point
+    halve = lambda nd: (units * 1024 * nd * 256 + 255) // 256 * 256 + units * 1024 * 10
+    assert sizes["bf16"][1] == halve(4) and sizes["fp8"][1] == halve(3)
+    assert sizes["bf16"][2] == sizes["fp8"][2] == 0          # bins below 256 points stay on fp64
+    assert sizes["bf16_fp64"][1] == sizes["f32"][1] == 0
+    # the causal prefill: batch Grams (7 batches of 2n points) and the HALVE Grams (4n) each get one
+    batch = lambda nd: (units * 7 * 2 * n * nd * 256 + 255) // 256 * 256 + units * 7 * 2 * n * 10
+    al = lambda x: (x + 255) // 256 * 256
+    assert sizes["bf16"][0] - sizes["bf16_fp64"][0] == al(batch(4)) + al(halve(4))
