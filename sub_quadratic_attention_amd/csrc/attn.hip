@@ -390,41 +390,73 @@ struct Attn {
   }
 
   // S^T (keys x queries) of the chunk in buffer kbuf: st[qg][kb] holds keys
-  // 16 kb + 4 g + i (i = 0..3) for query lane % 16.
+  // 16 kb + 4 g + i (i = 0..3) for query lane % 16.  bf16 and fp8: the K
+  // fragments of key block kb + 1 are read before the MFMAs of block kb (two
+  // register sets), and scheduling barriers keep the compiler from sinking
+  // the reads next to their use, so an LDS round trip overlaps a block of
+  // MFMAs instead of stalling between them.
+  template <int NF>
+  struct KFrag {
+    typename std::conditional<FP8, i32x8_t, bf16x8_t>::type f[NF];
+  };
+  __device__ __forceinline__ void kread(const lds_byte* kbuf, int kb, KFrag<NQF>& kf) const {
+    const int R = 16 * kb + (lane & 15);
+    if constexpr (FP8) {
+      // lane group g: features 32 g .. 32 g + 31 of each 128, logical pieces 2 g and 2 g + 1
+      typedef __attribute__((address_space(3))) const u32x4v_t lds_u4;
+#pragma unroll
+      for (int kk = 0; kk < NQF; ++kk) {
+        const u32x4v_t lo = *reinterpret_cast<lds_u4*>(kbuf + R * KB + 16 * ((8 * kk + 2 * g) ^ kswz<KB>(R)));
+        const u32x4v_t hi = *reinterpret_cast<lds_u4*>(kbuf + R * KB + 16 * ((8 * kk + 2 * g + 1) ^ kswz<KB>(R)));
+        kf.f[kk] = i32x8_t{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                           static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                           static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+      }
+    } else {
+      typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
+#pragma unroll
+      for (int kk = 0; kk < NQF; ++kk)
+        kf.f[kk] = *reinterpret_cast<lds_bf16x8*>(kbuf + R * KB + 16 * ((4 * kk + g) ^ kswz<KB>(R)));
+    }
+  }
+  __device__ __forceinline__ void kmfma(const KFrag<NQF>& kf, f32x4_t (&acc)[NQG]) const {
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk)
+#pragma unroll
+      for (int qg = 0; qg < NQG; ++qg) {
+        if constexpr (FP8)   // E4M3 operands (format 0), unit block scales (E8M0 127)
+          acc[qg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf.f[kk], qf[qg][kk], acc[qg], 0, 0, 0, 127, 0,
+                                                                    127);
+        else
+          acc[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.f[kk], qf[qg][kk], acc[qg], 0, 0, 0);
+      }
+  }
+
   __device__ __forceinline__ void scores(const lds_byte* kbuf, f32x4_t st[NQG][4]) const {
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) st[qg][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int R0 = lane & 15;
+    if constexpr (BF16) {
+      KFrag<NQF> kf[2];
+      kread(kbuf, 0, kf[0]);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int R = 16 * kb + R0;
-      if constexpr (FP8) {
-        // lane group g: features 32 g .. 32 g + 31 of each 128, logical pieces 2 g and 2 g + 1
-        typedef __attribute__((address_space(3))) const u32x4v_t lds_u4;
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb + 1 < 4) kread(kbuf, kb + 1, kf[(kb + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t acc[NQG];
 #pragma unroll
-        for (int kk = 0; kk < NQF; ++kk) {
-          const u32x4v_t lo = *reinterpret_cast<lds_u4*>(kbuf + R * KB + 16 * ((8 * kk + 2 * g) ^ kswz<KB>(R)));
-          const u32x4v_t hi = *reinterpret_cast<lds_u4*>(kbuf + R * KB + 16 * ((8 * kk + 2 * g + 1) ^ kswz<KB>(R)));
-          const i32x8_t kf = {static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
-                              static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
-                              static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+        for (int qg = 0; qg < NQG; ++qg) acc[qg] = st[qg][kb];
+        kmfma(kf[kb & 1], acc);
 #pragma unroll
-          for (int qg = 0; qg < NQG; ++qg)   // E4M3 operands (format 0), unit block scales (E8M0 127)
-            st[qg][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[qg][kk], st[qg][kb], 0, 0, 0, 127,
-                                                                          0, 127);
-        }
-      } else if constexpr (BF16) {
-        typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
+        for (int qg = 0; qg < NQG; ++qg) st[qg][kb] = acc[qg];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      const int R0 = lane & 15;
 #pragma unroll
-        for (int kk = 0; kk < NQF; ++kk) {
-          const bf16x8_t kf = *reinterpret_cast<lds_bf16x8*>(kbuf + R * KB + 16 * ((4 * kk + g) ^ kswz<KB>(R)));
-#pragma unroll
-          for (int qg = 0; qg < NQG; ++qg)
-            st[qg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qg][kk], st[qg][kb], 0, 0, 0);
-        }
-      } else {
+      for (int kb = 0; kb < 4; ++kb) {
+        const int R = 16 * kb + R0;
         typedef __attribute__((address_space(3))) const f32x4_t lds_f4;
 #pragma unroll
         for (int kq = 0; kq < E / 16; ++kq) {
@@ -517,11 +549,12 @@ struct Attn {
             pb[qg][hh][4 + i] = static_cast<__bf16>(p[qg][2 * hh + 1][i]);
           }
       // O^T += V^T P^T: lane group g's operand slots 0-3 / 4-7 are keys
-      // 32hh + 4g + (0..3) and 32hh + 16 + 4g + (0..3) (the S^T layout)
+      // 32hh + 4g + (0..3) and 32hh + 16 + 4g + (0..3) (the S^T layout).  The
+      // fragments of dimension block d + 1 are read before the MFMAs of block
+      // d (two register sets, scheduling barriers as in scores()).
       const int i16 = lane & 15;
       typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-#pragma unroll
-      for (int d = 0; d < ND; ++d)
+      auto vread = [&](int d, bf16x8_t (&vf)[2]) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           // logical elements 16 d + 4 (i16 % 4) .. + 3: piece 2 d + (i16 % 4) / 2, half i16 % 2
@@ -531,11 +564,22 @@ struct Attn {
               (lds_bf16x4*)(vbuf + R0 * VB + 16 * (q ^ vswz<BF16, VB>(R0)) + 8 * (i16 & 1)));
           const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
               (lds_bf16x4*)(vbuf + R1 * VB + 16 * (q ^ vswz<BF16, VB>(R1)) + 8 * (i16 & 1)));
-          const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          vf[hh] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      };
+      bf16x8_t vf[2][2];
+      vread(0, vf[0]);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        if (d + 1 < ND) vread(d + 1, vf[(d + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int qg = 0; qg < NQG; ++qg)
-            o[qg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qg][hh], o[qg][d], 0, 0, 0);
-        }
+            o[qg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d & 1][hh], pb[qg][hh], o[qg][d], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // a 16-row block of ones: every row of its output is the query's sum of P
       const bf16x8_t ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                              (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
