@@ -232,12 +232,13 @@ __device__ __forceinline__ double exp_tab(double x, const double* T) {
 // walks of the large sweep kernel read the thresholds).  With few bins
 // (per_wave == 0) workgroup w takes bin w: all its waves form b^2 and u into
 // LDS (smem: 2 kThrCap doubles), then wave 0 runs the recursion; with many,
-// each wave takes bins on its own, 4 nthr apart, so the thresholds hold few
-// workgroup slots while the tiles run.
+// each wave takes bins on its own, (waves per workgroup) nthr apart, so the
+// thresholds hold few workgroup slots while the tiles run.
 template <int ET>
 __device__ void threshold_workgroup(const GramLaunch& a, int w, int nthr, int per_wave, double* smem) {
   if (per_wave) {
-    for (int z = 4 * w + (threadIdx.x >> 6); z < a.nbins; z += 4 * nthr) bin_thresholds<ET>(a, z, nullptr, nullptr);
+    const int waves = blockDim.x >> 6;
+    for (int z = waves * w + (threadIdx.x >> 6); z < a.nbins; z += waves * nthr) bin_thresholds<ET>(a, z, nullptr, nullptr);
     return;   // the whole workgroup: no barrier in this mode
   }
   const int z = w;
@@ -245,7 +246,7 @@ __device__ void threshold_workgroup(const GramLaunch& a, int w, int nthr, int pe
   const int P = a.N / 2;      // b^2 and u of up to kThrCap pairs
   double* s_b2 = smem;
   double* s_u = smem + kThrCap;
-  for (int i = threadIdx.x; i < P; i += 256) pair_b2_u<ET>(a, z, i, s_b2[i], s_u[i]);
+  for (int i = threadIdx.x; i < P; i += blockDim.x) pair_b2_u<ET>(a, z, i, s_b2[i], s_u[i]);
   __syncthreads();
   if (threadIdx.x < 64) bin_thresholds<ET>(a, z, s_b2, s_u);
 }
