@@ -285,27 +285,40 @@ struct Attn {
   // w fills 16-byte slots [w KPT 64, (w + 1) KPT 64) of K (and likewise of V):
   // slot s is row s / KP, stored piece s % KP, which holds logical piece
   // (s % KP) ^ kswz(row).  Rows beyond the window copy the unit's first row;
-  // zero_tail() clears them.
+  // zero_tail() clears them.  The tokens of a lane's rows are read from LDS
+  // first, all at once: read between copies, each would wait for its own LDS
+  // round trip (a copy into LDS may, for the compiler, overwrite sm.idx).
+  __device__ __forceinline__ int chunk_token(int r) const {
+    const int t = token(r);   // in bounds for any r; the value is discarded past the window
+    return r < wl ? t : 0;
+  }
   __device__ __forceinline__ void copy(int c, lds_byte* kdst, lds_byte* vdst) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     typedef __attribute__((address_space(1))) const void* gptr;
     typedef __attribute__((address_space(3))) void* lptr;
+    constexpr bool kSameRows = !FP8 && VP == KP && VPT == KPT;   // V slot s is on K slot s's row
+    constexpr int VT = FP8 ? VGPT : VPT;
+    constexpr int VRP = FP8 ? VGP : VP;                          // V pieces per row, as copied
+    int ktok[KPT], vtok[kSameRows ? 1 : VT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) ktok[i] = chunk_token(kC * c + ((w * KPT + i) * 64 + lane) / KP);
+    if constexpr (!kSameRows) {
+#pragma unroll
+      for (int i = 0; i < VT; ++i) vtok[i] = chunk_token(kC * c + ((w * VT + i) * 64 + lane) / VRP);
+    }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int s = (w * KPT + i) * 64 + lane;
       const int R = s / KP, P = s % KP;
-      const int r = kC * c + R;
-      const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), kstride) +
-                           static_cast<uint32_t>(16 * (P ^ kswz<KB>(R)));
+      const uint32_t off = __umul24(static_cast<uint32_t>(ktok[i]), kstride) + static_cast<uint32_t>(16 * (P ^ kswz<KB>(R)));
       __builtin_amdgcn_global_load_lds((gptr)(kbase + off), (lptr)(kdst + (w * KPT + i) * 1024), 16, 0, 0);
     }
     if constexpr (FP8) {   // V through registers: widened to bf16 by store_v once they land
 #pragma unroll
       for (int i = 0; i < VGPT; ++i) {
         const int s = (w * VGPT + i) * 64 + lane;
-        const int R = s / VGP, P = s % VGP;
-        const int r = kC * c + R;
-        const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), vstride) + static_cast<uint32_t>(16 * P);
+        const int P = s % VGP;
+        const uint32_t off = __umul24(static_cast<uint32_t>(vtok[i]), vstride) + static_cast<uint32_t>(16 * P);
         vreg[i] = *reinterpret_cast<const uint4*>(vbase + off);
       }
     } else {
@@ -313,8 +326,8 @@ struct Attn {
       for (int i = 0; i < VPT; ++i) {
         const int s = (w * VPT + i) * 64 + lane;
         const int R = s / VP, P = s % VP;
-        const int r = kC * c + R;
-        const uint32_t off = __umul24(static_cast<uint32_t>(r < wl ? token(r) : 0), vstride) +
+        const int t = kSameRows ? ktok[i] : vtok[kSameRows ? 0 : i];
+        const uint32_t off = __umul24(static_cast<uint32_t>(t), vstride) +
                              static_cast<uint32_t>(16 * (P ^ vswz<BF16, VB>(R)));
         __builtin_amdgcn_global_load_lds((gptr)(vbase + off), (lptr)(vdst + (w * VPT + i) * 1024), 16, 0, 0);
       }
