@@ -132,7 +132,6 @@ struct Smem {
   alignas(16) unsigned char k[NB][kC * KB];   // 16-byte pieces permuted by kswz(row)
   alignas(16) unsigned char v[NB][kC * VB];   // 16-byte pieces permuted by vswz(row)
   float lnw2[NB][kC];
-  int posc[NB][kC];             // key visible to query t iff posc <= t (INT_MIN: always, INT_MAX: never)
   int idx[kIdxCap];
 };
 
@@ -179,10 +178,13 @@ struct Attn {
   Gather gs;
   Raw raw;
   int G, w0, wl;
-  // key visible to query group qg iff its posc < qlim[qg] (qr + 1, or INT_MIN
-  // when the query is not in the stream's block); rows_ok: every query of the
-  // wave is (then only causal keys need the test)
-  int qlim[NQG];
+  // the key at stream position pos is visible to query group qg's query iff
+  // pos <= vlim[qg]: every gathered key and the raw keys up to the query's
+  // token (INT_MAX without the causal mask, -1 when the query is not in the
+  // stream's block); padding keys carry log-weight -inf instead.  rows_ok:
+  // every query of the wave is in the block (then only raw causal keys need
+  // the test)
+  int vlim[NQG];
   bool rows_ok;
 
   __device__ __forceinline__ Attn(const AttnLaunch& la, Smem<ET, E, D, NB>& s, int q0, int bh) : a(la), sm(s) {
@@ -271,7 +273,7 @@ struct Attn {
     start_tile(q0);
     fetch_q(q0_next, qn);
 #pragma unroll
-    for (int qg = 0; qg < NQG; ++qg) qlim[qg] = qr[qg] + 1;
+    for (int qg = 0; qg < NQG; ++qg) vlim[qg] = INT_MAX;
     consume(0, 0, (const lds_byte*)&sm.k[0][0], (const lds_byte*)&sm.v[0][0]);
   }
 
@@ -383,12 +385,8 @@ struct Attn {
       if constexpr (!RAW) {
         if (gs.w != nullptr) lg = log2f(entry_weight(c));
       }
-      const bool gathered = pos < G;
-      int posc = gathered ? INT_MIN : (raw.causal ? raw.start + (pos - G) : INT_MIN);
-      float lw = gathered ? lg : raw.lnw2;
-      posc = r < wl ? posc : INT_MAX;
+      float lw = pos < G ? lg : raw.lnw2;
       lw = r < wl ? lw : -INFINITY;
-      sm.posc[buf][tid] = posc;
       sm.lnw2[buf][tid] = lw;
     }
   }
@@ -492,25 +490,24 @@ struct Attn {
     // the stream's block need the visibility test
     const bool masked = !rows_ok || (raw.causal && w0 + kC * (c + 1) > G);
     const float sc = a.scale * kLog2e;
-    int pc[4][4];
     float lw[4][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const int4 pv = *reinterpret_cast<const int4*>(&sm.posc[buf][kb * 16 + 4 * g]);
       const float4 lv = *reinterpret_cast<const float4*>(&sm.lnw2[buf][kb * 16 + 4 * g]);
-      pc[kb][0] = pv.x, pc[kb][1] = pv.y, pc[kb][2] = pv.z, pc[kb][3] = pv.w;
       lw[kb][0] = lv.x, lw[kb][1] = lv.y, lw[kb][2] = lv.z, lw[kb][3] = lv.w;
     }
     // online softmax; p[qg][kb][i] is the weight of key 16 kb + 4 g + i
     float p[NQG][4][4];
     if (masked) {   // two copies of the logit loop, so the common one carries no test
 #pragma unroll
-      for (int qg = 0; qg < NQG; ++qg)
+      for (int qg = 0; qg < NQG; ++qg) {
+        const int t = vlim[qg] - (w0 + kC * c) - 4 * g;   // key 16 kb + 4 g + i visible iff 16 kb + i <= t
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            p[qg][kb][i] = pc[kb][i] < qlim[qg] ? fmaf(st[qg][kb][i], sc, lw[kb][i]) : -INFINITY;
+            p[qg][kb][i] = 16 * kb + i <= t ? fmaf(st[qg][kb][i], sc, lw[kb][i]) : -INFINITY;
+      }
     } else {
 #pragma unroll
       for (int qg = 0; qg < NQG; ++qg)
@@ -702,14 +699,14 @@ struct Attn {
   __device__ __forceinline__ void run_stream(const Gather& gather, const Raw& r, const bool row_ok[NQG]) {
     gs = gather;
     raw = r;
+    G = gs.cnt[0] + gs.cnt[1] + gs.cnt[2];
     bool all = true;
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg) {
-      qlim[qg] = row_ok[qg] ? qr[qg] + 1 : INT_MIN;
+      vlim[qg] = row_ok[qg] ? (raw.causal ? qr[qg] - raw.start + G : INT_MAX) : -1;
       all = all && row_ok[qg];
     }
     rows_ok = __ballot(!all) == 0;
-    G = gs.cnt[0] + gs.cnt[1] + gs.cnt[2];
     const int L = G + raw.count;
     const int cap = RAW ? L : kIdxCap;
     for (w0 = 0; w0 < L; w0 += cap) {
