@@ -82,6 +82,21 @@ __host__ __device__ inline Scratch8 scratch8(unsigned char* base, int nd_, int E
   return s;
 }
 
+// Points of the digit scratch, and the scratch row of point pt of the launch
+// (another launch's point when its digit pass serves this one).
+__host__ __device__ inline int64_t dig_points(const GramLaunch& a) {
+  return a.dig_map ? a.dig_npts : static_cast<int64_t>(a.nbins) * a.N;
+}
+__device__ __forceinline__ int64_t drow(const GramLaunch& a, int64_t pt) { return a.dig_map ? a.dig_map[pt] : pt; }
+
+// Fit flags of pair c of the launch (points 2c, 2c + 1; K and V): nonzero when
+// any of the four rows does not fit.
+__device__ __forceinline__ uint32_t pair_flags(const GramLaunch& a, const uint8_t* flag, int64_t c) {
+  if (!a.dig_map) return reinterpret_cast<const uint32_t*>(flag)[c];
+  const uint16_t* f2 = reinterpret_cast<const uint16_t*>(flag);
+  return static_cast<uint32_t>(f2[a.dig_map[2 * c]]) | static_cast<uint32_t>(f2[a.dig_map[2 * c + 1]]);
+}
+
 // Token of point q of bin z, clamped into [0, S) (an index outside is reported).
 __device__ __forceinline__ int64_t point_row(const GramLaunch& a, int z, int q) {
   const int unit = z / a.bins_per_unit, lb = z % a.bins_per_unit;
@@ -224,7 +239,7 @@ struct Tile8 {
       const int o = ((w * per + i) * 64 + lane) * 16;   // this lane's LDS byte
       const int s = o >> 8;
       const int lp = ((o >> 4) & 15) ^ dswz(s);          // logical piece
-      goff[i] = i < per ? static_cast<uint32_t>((pt0 + slot_pos(s)) * sc.pbytes + 16 * (lp < 4 * ND ? lp : 0)) : 0u;
+      goff[i] = i < per ? static_cast<uint32_t>(drow(a, pt0 + slot_pos(s)) * sc.pbytes + 16 * (lp < 4 * ND ? lp : 0)) : 0u;
     }
   }
 
@@ -346,7 +361,7 @@ template <int ET>
 __device__ void gram8_tile(const GramLaunch& a, int tile, int ntiles, lds_byte* smem, double* T, int* s_scale,
                            int* s_flag) {
   constexpr int ND = nd<ET>();
-  Tile8<ET> t(a, scratch8(a.dig, ND, a.src.E, a.src.D, static_cast<int64_t>(a.nbins) * a.N));
+  Tile8<ET> t(a, scratch8(a.dig, ND, a.src.E, a.src.D, dig_points(a)));
   t.P = a.N / 2;
   const int nt = (t.P + 31) / 32;
   const int tiles = nt * (nt + 1) / 2;
@@ -370,7 +385,7 @@ __device__ void gram8_tile(const GramLaunch& a, int tile, int ntiles, lds_byte* 
   t.active = c0 + 15 >= r0 && r0 < t.P && c0 < t.P;
 
   if (static_cast<int>(threadIdx.x) < t.nslots) {
-    const int64_t pt = t.pt0 + t.slot_pos(threadIdx.x);
+    const int64_t pt = drow(a, t.pt0 + t.slot_pos(threadIdx.x));
     s_scale[2 * threadIdx.x] = t.sc.scale[2 * pt];
     s_scale[2 * threadIdx.x + 1] = t.sc.scale[2 * pt + 1];
     s_flag[threadIdx.x] = t.sc.flag[2 * pt] | t.sc.flag[2 * pt + 1];
@@ -458,7 +473,7 @@ __device__ void fix_pair(const GramLaunch& a, const uint8_t* flag, int z, int i,
     double* G = a.G + static_cast<int64_t>(z) * P * P;
     if (j >= i) {
       G[static_cast<int64_t>(i) * P + j] = gv;
-    } else if (reinterpret_cast<const uint32_t*>(flag)[pt0 / 2 + j] == 0) {   // K and V flags of both points
+    } else if (pair_flags(a, flag, pt0 / 2 + j) == 0) {   // K and V flags of both points
       G[static_cast<int64_t>(j) * P + i] = gv;
     }
   }
@@ -468,7 +483,7 @@ __device__ void fix_pair(const GramLaunch& a, const uint8_t* flag, int z, int i,
 template <int ET>
 __device__ void gram8_fixup(const GramLaunch& a, int f, double* smem) {
   const int64_t npts = static_cast<int64_t>(a.nbins) * a.N;
-  const Scratch8 sc = scratch8(a.dig, nd<ET>(), a.src.E, a.src.D, npts);
+  const Scratch8 sc = scratch8(a.dig, nd<ET>(), a.src.E, a.src.D, dig_points(a));
   const int P = a.N / 2;
   const int64_t total = npts / 2;   // pairs of the launch: pair c holds points 2c, 2c + 1
   int* list = reinterpret_cast<int*>(smem + 2 * (a.src.E + a.src.D));
@@ -477,7 +492,7 @@ __device__ void gram8_fixup(const GramLaunch& a, int f, double* smem) {
     if (threadIdx.x == 0) *cnt = 0;
     __syncthreads();
     const int64_t c = c0 + threadIdx.x;
-    if (c < total && reinterpret_cast<const uint32_t*>(sc.flag)[c] != 0) list[atomicAdd(cnt, 1)] = threadIdx.x;
+    if (c < total && pair_flags(a, sc.flag, c) != 0) list[atomicAdd(cnt, 1)] = threadIdx.x;
     __syncthreads();
     const int n = *cnt;
     for (int k = 0; k < n; ++k) {
@@ -527,11 +542,11 @@ size_t gram8_scratch_bytes(int dtype, int E, int D, int64_t npts) {
 // Launch geometry of the integer Gram over a.
 static bool gram8_launch_ok(const GramLaunch& a) {
   return a.dig && gram8_supported(a.src.dtype, a.src.E, a.src.D, a.N) &&
-         gram8_fits(a.src.dtype, static_cast<int64_t>(a.nbins) * a.N, a.src.E, a.src.D);
+         gram8_fits(a.src.dtype, dig_points(a), a.src.E, a.src.D);
 }
 
 hipError_t launch_gram8_digits(const GramLaunch& a, hipStream_t s) {
-  if (!gram8_launch_ok(a)) return hipErrorInvalidValue;
+  if (!gram8_launch_ok(a) || a.dig_map) return hipErrorInvalidValue;
   const int64_t npts = static_cast<int64_t>(a.nbins) * a.N;
   if (npts == 0) return hipSuccess;
   const int64_t blocks_k = (npts * (a.src.E / 8) + 255) / 256, blocks_v = (npts * (a.src.D / 8) + 255) / 256;
@@ -561,7 +576,7 @@ hipError_t launch_gram8_tiles(const GramLaunch& a, hipStream_t s) {
 }
 
 hipError_t launch_pair_gram8(const GramLaunch& a, hipStream_t s) {
-  const hipError_t e = launch_gram8_digits(a, s);
+  const hipError_t e = a.dig_map ? hipSuccess : launch_gram8_digits(a, s);
   return e != hipSuccess ? e : launch_gram8_tiles(a, s);
 }
 

@@ -163,7 +163,7 @@ inline UnmaskedPlan plan_unmasked(const thin_attn* h, int64_t B, int64_t S0) {
 
 struct CausalPlan {
   thin::ExpressSchedule sc;
-  size_t off_reps, off_bout, off_hin, off_hmid, off_hout, off_g, off_gh, off_digb, off_digh;
+  size_t off_reps, off_bout, off_hin, off_hmid, off_hpos, off_hout, off_g, off_gh, off_digb, off_digh;
   bool dig_b, dig_h;   // the integer Gram's scratch of the batch and the HALVE Grams
   size_t bytes;
 };
@@ -179,11 +179,13 @@ inline CausalPlan plan_causal(const thin_attn* h, int64_t B, int64_t S, int64_t 
   p.off_bout = L.add(sizeof(int32_t) * units * p.sc.n_batches_done * n);
   p.off_hin = L.add(sizeof(int32_t) * units * 4 * n);
   p.off_hmid = L.add(sizeof(int32_t) * units * 2 * n);
+  p.off_hpos = L.add(sizeof(int32_t) * units * 2 * n);
   p.off_hout = L.add(sizeof(int32_t) * units * p.sc.n_halves * n);
   p.off_g = L.add(sizeof(double) * (p.sc.n_batches_done ? units * p.sc.n_batches_done * n * n : 0));
   p.off_gh = L.add(sizeof(double) * (p.sc.n_halves ? units * 4 * n * n : 0));
   const size_t db = p.sc.n_batches_done ? gram8_bytes(h, 2 * n, units * p.sc.n_batches_done * 2 * n) : 0;
-  const size_t dh = p.sc.n_halves ? gram8_bytes(h, 4 * n, units * 4 * n) : 0;   // covers the 2n pass
+  // the 2n pass reads the 4n pass's digits
+  const size_t dh = p.sc.n_halves ? gram8_bytes(h, 4 * n, units * 4 * n) : 0;
   p.dig_b = db > 0;
   p.dig_h = dh > 0;
   if (db) p.off_digb = L.add(db);
@@ -328,7 +330,7 @@ inline void release_timing(thin_attn* h) {
 // their own timing labels, or the fp64 tiles.
 inline int run_pair_gram(thin_attn* h, hipStream_t st, const thin::GramLaunch& g) {
   if (thin::gram8_runs(g)) {
-    THIN_HIP(timed(h, st, "gram_digits", [&] { return thin::launch_gram8_digits(g, st); }));
+    if (!g.dig_map) THIN_HIP(timed(h, st, "gram_digits", [&] { return thin::launch_gram8_digits(g, st); }));
     THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_gram8_tiles(g, st); }));
     return THIN_OK;
   }
@@ -376,6 +378,7 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
   int32_t* bout = reinterpret_cast<int32_t*>(ws + p.off_bout);
   int32_t* hin = reinterpret_cast<int32_t*>(ws + p.off_hin);
   int32_t* hmid = reinterpret_cast<int32_t*>(ws + p.off_hmid);
+  int32_t* hpos = reinterpret_cast<int32_t*>(ws + p.off_hpos);
   int32_t* hout = reinterpret_cast<int32_t*>(ws + p.off_hout);
   double* Gb = reinterpret_cast<double*>(ws + p.off_g);
   double* Gh = reinterpret_cast<double*>(ws + p.off_gh);
@@ -416,14 +419,23 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
   auto halve_rest = [&](int e) -> int {
     thin::SweepLaunch s1 = make_sweep(h, Gh, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
                                       static_cast<uint64_t>(e));
+    // the second halving's points are among the first's: with the integer
+    // Gram, the first's digits serve it (through the kept points' numbers)
+    const bool reuse = digh && thin::gram8_runs(gram_for(s1, src, h->scale64, digh));
     s1.out_stride = 2 * n;
+    s1.pos_out = reuse ? hpos : nullptr;
     s1.dec = decisions;
     s1.dec_per_unit = ndec;
     s1.dec_base = static_cast<int64_t>(6) * n * e;
     THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(s1, st); }));
     thin::SweepLaunch s2 = make_sweep(h, Gh, 2 * n, units, 1, hmid, 2 * n, hout + static_cast<int64_t>(e) * n, seed,
                                       thin::kTagHalveSecond, static_cast<uint64_t>(e));
-    if (const int rg = run_pair_gram(h, st, gram_for(s2, src, h->scale64, digh))) return rg;
+    thin::GramLaunch g2 = gram_for(s2, src, h->scale64, digh);
+    if (reuse) {
+      g2.dig_map = hpos;
+      g2.dig_npts = static_cast<int64_t>(units) * 4 * n;
+    }
+    if (const int rg = run_pair_gram(h, st, g2)) return rg;
     s2.out_stride = static_cast<int64_t>(p.sc.n_halves) * n;   // unit u -> row u of [units][halves][n]
     s2.dec = decisions;
     s2.dec_per_unit = ndec;

@@ -56,6 +56,12 @@ struct GramLaunch {
   // Scratch of the exact integer Gram (gram8_scratch_bytes for nbins * N points),
   // or nullptr: the fp64 tiles run instead.
   unsigned char* dig;
+  // Optional: the digit pass of an earlier launch over dig_npts points (in
+  // the same scratch) serves this one.  Point pt = bin * N + q takes the
+  // digits, scales and fit flags of that launch's point dig_map[pt]; no digit
+  // pass runs.
+  const int32_t* dig_map;
+  int64_t dig_npts;
 };
 
 // Kernel-halving decisions of many bins at once (one workgroup per bin).
@@ -69,6 +75,7 @@ struct SweepLaunch {
   int64_t in_unit_stride;
   int32_t* idx_out;         // kept token indices, P per bin
   int64_t out_stride;
+  int32_t* pos_out;         // optional: the kept points' numbers in the launch (bin * N + position), as idx_out
   uint8_t* dec;             // optional decision log (1 = first point kept)
   int64_t dec_per_unit;
   int64_t dec_base;         // offset of this launch's first bin inside a unit's log

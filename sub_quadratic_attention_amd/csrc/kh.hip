@@ -377,6 +377,7 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
 
   const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
   int32_t* out = a.idx_out + static_cast<int64_t>(z) * a.out_stride;
+  int32_t* pout = a.pos_out ? a.pos_out + static_cast<int64_t>(z) * a.out_stride : nullptr;
   uint8_t* dec = a.dec ? a.dec + static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) : nullptr;
   for (int p = 0; p < np; ++p) {
     const int p0 = 64 * p;
@@ -401,6 +402,7 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
         const bool first = (bits >> lane) & 1ull;
         s_eta[i] = first ? 1.0 : -1.0;
         out[i] = in[2 * i + (first ? 0 : 1)];
+        if (pout) pout[i] = z * a.N + 2 * i + (first ? 0 : 1);
         if (dec) dec[i] = first ? 1 : 0;
       }
     } else if (w <= 2 && p + 1 < np) {
@@ -468,6 +470,7 @@ __global__ __launch_bounds__(256) void halving_sweep_small_kernel(SweepLaunch a)
     const bool first = (bits >> lane) & 1ull;
     const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
     a.idx_out[static_cast<int64_t>(z) * a.out_stride + lane] = in[2 * lane + (first ? 0 : 1)];
+    if (a.pos_out) a.pos_out[static_cast<int64_t>(z) * a.out_stride + lane] = z * a.N + 2 * lane + (first ? 0 : 1);
     if (a.dec) a.dec[static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) + lane] = first ? 1 : 0;
   }
 }
@@ -835,6 +838,7 @@ __global__ __launch_bounds__(256) void small_halving_kernel(GramLaunch g, SweepL
     const int z = unit * g.bins_per_unit + lb;
     const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
     a.idx_out[static_cast<int64_t>(z) * a.out_stride + i] = in[2 * i + (first ? 0 : 1)];
+    if (a.pos_out) a.pos_out[static_cast<int64_t>(z) * a.out_stride + i] = z * a.N + 2 * i + (first ? 0 : 1);
     if (a.dec) a.dec[static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) + i] = first ? 1 : 0;
   }
 }
@@ -990,6 +994,7 @@ __global__ __launch_bounds__(256) void medium_halving_kernel(GramLaunch g, Sweep
     const bool first = (bits >> lane) & 1ull;
     const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
     a.idx_out[static_cast<int64_t>(z) * a.out_stride + lane] = in[2 * lane + (first ? 0 : 1)];
+    if (a.pos_out) a.pos_out[static_cast<int64_t>(z) * a.out_stride + lane] = z * a.N + 2 * lane + (first ? 0 : 1);
     if (a.dec) a.dec[static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) + lane] = first ? 1 : 0;
   }
 }
