@@ -389,13 +389,18 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
       double g[64];   // g[cc] = G[p0 + cc][p0 + lane]: the upper triangle holds it for cc < lane
 #pragma unroll
       for (int cc = 0; cc < 64; ++cc) g[cc] = blk[cc * 65 + lane];
+      // decision j is lane j's: its sign eta_j = +1 (keep the first point)
+      // or -1 comes to every lane as the high word of a double through
+      // readlane, and alpha += eta_j g[j] is one fma with that scalar operand
+      // (exact product, the same rounding as the add); the decision bits come
+      // from the same compare's lane mask, off the dependent chain
       uint64_t bits = 0;
 #pragma unroll
       for (int j = 0; j < 64; ++j) {
-        const uint64_t m = __ballot(alpha < thr);
-        const bool first = (m >> j) & 1ull;
-        bits |= static_cast<uint64_t>(first) << j;
-        alpha += first ? g[j] : -g[j];
+        const bool lt = alpha < thr;
+        bits |= __ballot(lt) & (1ull << j);
+        const uint32_t hj = __builtin_amdgcn_readlane(lt ? 0x3FF00000u : 0xBFF00000u, j);
+        alpha = fma(__hiloint2double(static_cast<int>(hj), 0), g[j], alpha);
       }
       if (lane < rows) {
         const int i = p0 + lane;
