@@ -83,15 +83,29 @@ def test_integer_gram_matches_oracle(dt, E, D, N, misfit):
         assert np.array_equal(kept[u], pts[u][khm.kept_positions(keep)])
 
 
-def test_causal_with_misfit_rows():
+@pytest.mark.parametrize("n,nk,nv", [(64, 60, 40), (128, 400, 300)])
+def test_causal_with_misfit_rows(n, nk, nv):
     """A causal forward (batch halvings and HALVEs on the integer Gram) whose keys and values
-    hold rows that do not fit the digits: every output and decision against the oracle."""
+    hold rows that do not fit the digits: every output and decision against the oracle.  At
+    n_out = 128 both halvings of a HALVE take the integer Gram, the second on the first's
+    digits, so its fix-up workgroups find the planted rows through the kept points' numbers;
+    the forward also equals the fp64 Gram's decision for decision."""
+    from sub_quadratic_attention_amd.binding import ThinAttention
     d = inputs.causal_prefill(seed=11, H=2, S=4096 + 64 * 3 + 37)
     rng = np.random.default_rng(5)
     S = d["k"].shape[1]
-    d["k"] = plant_misfits(d["k"], [(int(t), int(h)) for t, h in zip(rng.integers(0, S, 60), rng.integers(0, 2, 60))], rng)
-    d["v"] = plant_misfits(d["v"], [(int(t), int(h)) for t, h in zip(rng.integers(0, S, 40), rng.integers(0, 2, 40))], rng)
-    run_and_compare("causal misfit rows S=4325 n=64", d, True, 2, 2, 128, 128, n_out=64)
+    d["k"] = plant_misfits(d["k"], [(int(t), int(h)) for t, h in zip(rng.integers(0, S, nk), rng.integers(0, 2, nk))], rng)
+    d["v"] = plant_misfits(d["v"], [(int(t), int(h)) for t, h in zip(rng.integers(0, S, nv), rng.integers(0, 2, nv))], rng)
+    r = run_and_compare(f"causal misfit rows S=4325 n={n}", d, True, 2, 2, 128, 128, n_out=n)
+    q, k, v = (to_gpu(d[x], "bf16") for x in ("q", "k", "v"))
+    ta = ThinAttention(128, 128, 2, 2, torch.bfloat16, n_out=n, fp64_gram=True)
+    _, ex = ta.forward(q, k, v, causal=True, seed=0, return_coreset=True, return_decisions=True)
+    torch.cuda.synchronize()
+    dec64 = ex["decisions"].cpu().numpy()
+    ndiff = int((r["dec"] != dec64).sum())
+    say(f"[gram8] causal misfit n={n}: {ndiff} of {dec64.size} decisions differ from the fp64 Gram's")
+    assert ndiff == 0
+    assert np.array_equal(r["idx"], ex["coreset_idx"].cpu().numpy())
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp8"])
