@@ -800,7 +800,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_w
   __shared__ Smem<ET, E, D, NB> sm;
   const int64_t tile = xcd_remap(blockIdx.y * static_cast<int64_t>(gridDim.x) + blockIdx.x,
                                  static_cast<int64_t>(gridDim.x) * gridDim.y);
-  const int q0 = a.t0 + static_cast<int>(tile % gridDim.x) * kQ * (NB == 1 ? kTilesOne : 1);
+  // causal: a head's query tiles in reverse, so that the later blocks, whose
+  // states hold more keys, start first and the last workgroups are short
+  const int qt = static_cast<int>(tile % gridDim.x);
+  const int q0 = a.t0 + (a.causal ? static_cast<int>(gridDim.x) - 1 - qt : qt) * kQ * (NB == 1 ? kTilesOne : 1);
   Attn<ET, E, D, RAW, NB> at(a, sm, q0, static_cast<int>(tile / gridDim.x));
   if constexpr (NB == 1) at.fetch_q(q0 + kQ, at.qn);
   const int q_last = min(q0 + kQ - 1, a.t1 - 1);
