@@ -216,9 +216,13 @@ def work_model(name, B, T, S, H, Hkv, E, D, causal, elt, subsample_base=False, o
     i8_entries = sum(bins * N * (N + 1) // 2 for bins, N in i8)
     i8_points = units * sum(bins * N for bins, N in i8)
     if causal and gram8_runs(dt, E, D, 4 * n_out):
-        # a HALVE's second halving reads the digits of its first (its points are among them)
+        # a HALVE's second halving reads the digits of its first (its points are among them);
+        # when the batches take the integer Gram too, HALVEs after the first read the digits of
+        # HALVE 0's points and of the batch points (every later HALVE point is one of them)
         halves = sum(1 for bins, N in tiles if N == 4 * n_out)
         i8_points -= units * halves * 2 * n_out
+        if halves and len(tiles) > 2 * halves and gram8_runs(dt, E, D, 2 * n_out):
+            i8_points -= units * (halves - 1) * 4 * n_out
     pair_gram = None
     if gram_entries:
         pair_gram = dict(flops=2.0 * (E + D) * gram_entries * units, bytes=None)

@@ -85,16 +85,17 @@ __host__ __device__ inline Scratch8 scratch8(unsigned char* base, int nd_, int E
 // Points of the digit scratch, and the scratch row of point pt of the launch
 // (another launch's point when its digit pass serves this one).
 __host__ __device__ inline int64_t dig_points(const GramLaunch& a) {
-  return a.dig_map ? a.dig_npts : static_cast<int64_t>(a.nbins) * a.N;
+  return a.dig_npts ? a.dig_npts : static_cast<int64_t>(a.nbins) * a.N;
 }
-__device__ __forceinline__ int64_t drow(const GramLaunch& a, int64_t pt) { return a.dig_map ? a.dig_map[pt] : pt; }
+__device__ __forceinline__ int64_t drow(const GramLaunch& a, int64_t pt) {
+  return a.dig_map ? a.dig_map[pt] : a.dig_row0 + pt;
+}
 
 // Fit flags of pair c of the launch (points 2c, 2c + 1; K and V): nonzero when
 // any of the four rows does not fit.
 __device__ __forceinline__ uint32_t pair_flags(const GramLaunch& a, const uint8_t* flag, int64_t c) {
-  if (!a.dig_map) return reinterpret_cast<const uint32_t*>(flag)[c];
   const uint16_t* f2 = reinterpret_cast<const uint16_t*>(flag);
-  return static_cast<uint32_t>(f2[a.dig_map[2 * c]]) | static_cast<uint32_t>(f2[a.dig_map[2 * c + 1]]);
+  return static_cast<uint32_t>(f2[drow(a, 2 * c)]) | static_cast<uint32_t>(f2[drow(a, 2 * c + 1)]);
 }
 
 // Token of point q of bin z, clamped into [0, S) (an index outside is reported).
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256) void gram8_digits_kernel(GramLaunch a, int blo
   const int64_t pt = t / gl;
   const int j = static_cast<int>(t % gl);
   if (pt >= npts) return;   // whole groups (gl divides 256)
-  const Scratch8 sc = scratch8(a.dig, ND, a.src.E, a.src.D, npts);
+  const Scratch8 sc = scratch8(a.dig, ND, a.src.E, a.src.D, dig_points(a));
   const int64_t row = point_row(a, static_cast<int>(pt / a.N), static_cast<int>(pt % a.N));
   const unsigned char* src = static_cast<const unsigned char*>(part ? a.src.v : a.src.k) +
                              (row * F + 8 * j) * elt_size<ET>();
@@ -177,15 +178,16 @@ __global__ __launch_bounds__(256) void gram8_digits_kernel(GramLaunch a, int blo
     }
   }
   const int f0 = 8 * j;
-  unsigned char* o = sc.dig + pt * sc.pbytes + (part ? ND * a.src.E : 0) + 64 * ND * (f0 / 64) + (f0 % 64);
+  const int64_t dr = a.dig_row0 + pt;   // this point's scratch row
+  unsigned char* o = sc.dig + dr * sc.pbytes + (part ? ND * a.src.E : 0) + 64 * ND * (f0 / 64) + (f0 % 64);
 #pragma unroll
   for (int d = 0; d < ND; ++d) *reinterpret_cast<uint2*>(o + 64 * d) = uint2{dg[d][0], dg[d][1]};
   // the row fits when every lane of its group fits
   int bad = ok ? 0 : 1;
   for (int off = gl / 2; off >= 1; off >>= 1) bad |= __shfl_xor(bad, off, 64);
   if (j == 0) {
-    sc.scale[2 * pt + part] = s;
-    sc.flag[2 * pt + part] = static_cast<uint8_t>(bad);
+    sc.scale[2 * dr + part] = s;
+    sc.flag[2 * dr + part] = static_cast<uint8_t>(bad);
   }
 }
 
@@ -542,7 +544,8 @@ size_t gram8_scratch_bytes(int dtype, int E, int D, int64_t npts) {
 // Launch geometry of the integer Gram over a.
 static bool gram8_launch_ok(const GramLaunch& a) {
   return a.dig && gram8_supported(a.src.dtype, a.src.E, a.src.D, a.N) &&
-         gram8_fits(a.src.dtype, dig_points(a), a.src.E, a.src.D);
+         gram8_fits(a.src.dtype, dig_points(a), a.src.E, a.src.D) &&
+         (a.dig_map || a.dig_row0 + static_cast<int64_t>(a.nbins) * a.N <= dig_points(a));
 }
 
 hipError_t launch_gram8_digits(const GramLaunch& a, hipStream_t s) {

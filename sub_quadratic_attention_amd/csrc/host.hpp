@@ -164,12 +164,21 @@ inline UnmaskedPlan plan_unmasked(const thin_attn* h, int64_t B, int64_t S0) {
 struct CausalPlan {
   thin::ExpressSchedule sc;
   size_t off_reps, off_bout, off_hin, off_hmid, off_hpos, off_hout, off_g, off_gh, off_digb, off_digh;
+  size_t off_brow, off_hinrow, off_hrow;
   bool dig_b, dig_h;   // the integer Gram's scratch of the batch and the HALVE Grams
+  bool dig_shared;     // one scratch: HALVE 0's points, then the batch points
+  int64_t dig_rows;    // its rows
   size_t bytes;
 };
 
-// The batch halvings and the HALVE chain may run at once (on two streams), so
-// each has its own pair-Gram scratch.
+// The batch halvings and the HALVE chain may run at once (on two streams).
+// When both take the integer Gram they share one digit scratch: rows
+// [0, units 4n) hold HALVE 0's points (the first 4n tokens of every unit),
+// the batch points follow, each written by its own digit pass, and every
+// later HALVE point is one of these (a HALVE's input is the last HALVE's
+// output and three batch outputs), so the later HALVEs read their rows through
+// the walks' row lists and run no digit pass.  Otherwise each keeps its own
+// scratch and a HALVE's second halving reads its first's digits.
 inline CausalPlan plan_causal(const thin_attn* h, int64_t B, int64_t S, int64_t n) {
   CausalPlan p{};
   p.sc = thin::express_schedule(S, static_cast<int>(n));
@@ -183,13 +192,24 @@ inline CausalPlan plan_causal(const thin_attn* h, int64_t B, int64_t S, int64_t 
   p.off_hout = L.add(sizeof(int32_t) * units * p.sc.n_halves * n);
   p.off_g = L.add(sizeof(double) * (p.sc.n_batches_done ? units * p.sc.n_batches_done * n * n : 0));
   p.off_gh = L.add(sizeof(double) * (p.sc.n_halves ? units * 4 * n * n : 0));
-  const size_t db = p.sc.n_batches_done ? gram8_bytes(h, 2 * n, units * p.sc.n_batches_done * 2 * n) : 0;
-  // the 2n pass reads the 4n pass's digits
-  const size_t dh = p.sc.n_halves ? gram8_bytes(h, 4 * n, units * 4 * n) : 0;
-  p.dig_b = db > 0;
-  p.dig_h = dh > 0;
-  if (db) p.off_digb = L.add(db);
-  if (dh) p.off_digh = L.add(dh);
+  const int64_t hrows = units * 4 * n, brows = units * p.sc.n_batches_done * 2 * n;
+  const size_t ds = p.sc.n_batches_done && p.sc.n_halves ? gram8_bytes(h, 2 * n, hrows + brows) : 0;
+  if (ds && gram8_bytes(h, 4 * n, hrows + brows)) {
+    p.dig_shared = p.dig_b = p.dig_h = true;
+    p.dig_rows = hrows + brows;
+    p.off_digh = p.off_digb = L.add(ds);
+    p.off_brow = L.add(sizeof(int32_t) * units * p.sc.n_batches_done * n);
+    p.off_hinrow = L.add(sizeof(int32_t) * units * 4 * n);
+    p.off_hrow = L.add(sizeof(int32_t) * units * p.sc.n_halves * n);
+  } else {
+    const size_t db = p.sc.n_batches_done ? gram8_bytes(h, 2 * n, brows) : 0;
+    const size_t dh = p.sc.n_halves ? gram8_bytes(h, 4 * n, hrows) : 0;
+    p.dig_b = db > 0;
+    p.dig_h = dh > 0;
+    p.dig_rows = hrows;
+    if (db) p.off_digb = L.add(db);
+    if (dh) p.off_digh = L.add(dh);
+  }
   p.bytes = L.total;
   return p;
 }
@@ -384,6 +404,19 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
   double* Gh = reinterpret_cast<double*>(ws + p.off_gh);
   unsigned char* digb = p.dig_b ? reinterpret_cast<unsigned char*>(ws + p.off_digb) : nullptr;
   unsigned char* digh = p.dig_h ? reinterpret_cast<unsigned char*>(ws + p.off_digh) : nullptr;
+  // digit-scratch rows of the batch outputs, a HALVE's input and the HALVE outputs (shared scratch)
+  int32_t* brow = p.dig_shared ? reinterpret_cast<int32_t*>(ws + p.off_brow) : nullptr;
+  int32_t* hinrow = p.dig_shared ? reinterpret_cast<int32_t*>(ws + p.off_hinrow) : nullptr;
+  int32_t* hrow = p.dig_shared ? reinterpret_cast<int32_t*>(ws + p.off_hrow) : nullptr;
+  // the integer Gram's launch of a HALVE's first halving: HALVE 0 (and every
+  // HALVE without a shared scratch) writes rows [0, units 4n); the others read
+  // their points' rows
+  auto first_gram = [&](const thin::SweepLaunch& s1, int e) {
+    thin::GramLaunch g = gram_for(s1, src, h->scale64, digh);
+    g.dig_npts = p.dig_rows;
+    if (p.dig_shared && e > 0) g.dig_map = hinrow;
+    return g;
+  };
   ev.reps = reps;
   ev.batch_out = bout;
   ev.halve_out = hout;
@@ -410,20 +443,23 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
   }
   // HALVE e halves twice, 4n -> 2n -> n, on st; HALVE e >= 1 reads batches 3(e-1) ..
   auto halve_first_gram = [&](int e) -> int {
-    THIN_HIP(timed(h, st, "halve_input", [&] { return thin::launch_halve_input(ev, units, e, hin, st); }));
+    const thin::HalveRows rows{hrow, brow, e > 0 ? hinrow : nullptr};
+    THIN_HIP(timed(h, st, "halve_input", [&] { return thin::launch_halve_input(ev, units, e, hin, st, rows); }));
     thin::SweepLaunch s1 = make_sweep(h, Gh, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
                                       static_cast<uint64_t>(e));
-    if (const int rg = run_pair_gram(h, st, gram_for(s1, src, h->scale64, digh))) return rg;
+    if (const int rg = run_pair_gram(h, st, first_gram(s1, e))) return rg;
     return THIN_OK;
   };
   auto halve_rest = [&](int e) -> int {
     thin::SweepLaunch s1 = make_sweep(h, Gh, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
                                       static_cast<uint64_t>(e));
     // the second halving's points are among the first's: with the integer
-    // Gram, the first's digits serve it (through the kept points' numbers)
-    const bool reuse = digh && thin::gram8_runs(gram_for(s1, src, h->scale64, digh));
+    // Gram, it reads their digit rows, which the first walk lists
+    const thin::GramLaunch g1 = first_gram(s1, e);
+    const bool reuse = digh && thin::gram8_runs(g1);
     s1.out_stride = 2 * n;
-    s1.pos_out = reuse ? hpos : nullptr;
+    s1.row_out = reuse ? hpos : nullptr;
+    s1.row_map = g1.dig_map;
     s1.dec = decisions;
     s1.dec_per_unit = ndec;
     s1.dec_base = static_cast<int64_t>(6) * n * e;
@@ -433,10 +469,14 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
     thin::GramLaunch g2 = gram_for(s2, src, h->scale64, digh);
     if (reuse) {
       g2.dig_map = hpos;
-      g2.dig_npts = static_cast<int64_t>(units) * 4 * n;
+      g2.dig_npts = p.dig_rows;
     }
     if (const int rg = run_pair_gram(h, st, g2)) return rg;
     s2.out_stride = static_cast<int64_t>(p.sc.n_halves) * n;   // unit u -> row u of [units][halves][n]
+    if (p.dig_shared) {   // the HALVE output's rows, for the next HALVE's input
+      s2.row_out = hrow + static_cast<int64_t>(e) * n;
+      s2.row_map = hpos;
+    }
     s2.dec = decisions;
     s2.dec_per_unit = ndec;
     s2.dec_base = static_cast<int64_t>(6) * n * e + 2 * n;
@@ -458,7 +498,14 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
     const int nb = p.sc.n_batches_done;
     const int64_t ustride = static_cast<int64_t>(p.sc.n_batches_alloc) * N;
     thin::SweepLaunch sl = make_sweep(h, Gb, N, units, nb, reps, ustride, bout, seed, thin::kTagBatch, 0);
-    if (const int rg = run_pair_gram(h, sx, gram_for(sl, src, h->scale64, digb))) return rg;
+    thin::GramLaunch gb = gram_for(sl, src, h->scale64, digb);
+    if (p.dig_shared) {   // the batch points' rows follow HALVE 0's
+      gb.dig_npts = p.dig_rows;
+      gb.dig_row0 = static_cast<int64_t>(units) * 4 * n;
+      sl.row_out = brow;
+      sl.row0 = gb.dig_row0;
+    }
+    if (const int rg = run_pair_gram(h, sx, gb)) return rg;
     sl.out_stride = n;
     sl.dec = decisions;
     sl.dec_per_unit = ndec;

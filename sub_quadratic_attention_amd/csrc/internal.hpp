@@ -56,12 +56,13 @@ struct GramLaunch {
   // Scratch of the exact integer Gram (gram8_scratch_bytes for nbins * N points),
   // or nullptr: the fp64 tiles run instead.
   unsigned char* dig;
-  // Optional: the digit pass of an earlier launch over dig_npts points (in
-  // the same scratch) serves this one.  Point pt = bin * N + q takes the
-  // digits, scales and fit flags of that launch's point dig_map[pt]; no digit
-  // pass runs.
+  // Rows of the digit scratch (digits, scales, fit flags per point row):
+  // dig_npts rows (0: nbins * N).  Point pt = bin * N + q of this launch is
+  // row dig_row0 + pt, which its digit pass writes; or, with dig_map, row
+  // dig_map[pt], written by earlier launches, and no digit pass runs.
   const int32_t* dig_map;
   int64_t dig_npts;
+  int64_t dig_row0;
 };
 
 // Kernel-halving decisions of many bins at once (one workgroup per bin).
@@ -75,7 +76,11 @@ struct SweepLaunch {
   int64_t in_unit_stride;
   int32_t* idx_out;         // kept token indices, P per bin
   int64_t out_stride;
-  int32_t* pos_out;         // optional: the kept points' numbers in the launch (bin * N + position), as idx_out
+  // optional: the kept points' digit-scratch rows, laid out as idx_out; point
+  // pt = bin * N + q is row row_map[pt], or row0 + pt without a map
+  int32_t* row_out;
+  const int32_t* row_map;
+  int64_t row0;
   uint8_t* dec;             // optional decision log (1 = first point kept)
   int64_t dec_per_unit;
   int64_t dec_base;         // offset of this launch's first bin inside a unit's log
@@ -190,7 +195,16 @@ hipError_t launch_iota(int32_t* out, int64_t units, int64_t n, int64_t stride, h
 hipError_t launch_base_sample(const int32_t* list, int64_t L, int units, int64_t r, uint64_t seed, int32_t* out,
                               hipStream_t s);
 hipError_t launch_express_reps(const ExpressView& ev, int units, uint64_t seed, int32_t* reps, hipStream_t s);
-hipError_t launch_halve_input(const ExpressView& ev, int units, int e, int32_t* halve_in, hipStream_t s);
+// Digit-scratch rows of the HALVE outputs ([units][n_halves][n]) and batch
+// outputs ([units][n_batches_done][n]), and the rows of a HALVE's input (out,
+// [units][4n]; nullptr: not formed).
+struct HalveRows {
+  const int32_t* halve;
+  const int32_t* batch;
+  int32_t* out;
+};
+hipError_t launch_halve_input(const ExpressView& ev, int units, int e, int32_t* halve_in, hipStream_t s,
+                              const HalveRows& rows = HalveRows{nullptr, nullptr, nullptr});
 hipError_t launch_express_final(const ExpressView& ev, int units, int S, int32_t* idx, float* w,
                                 int32_t* len, int64_t cap, hipStream_t s);
 hipError_t launch_fill_coreset(const int32_t* src, int64_t src_stride, int units, int n, float w,

@@ -317,6 +317,12 @@ __global__ __launch_bounds__(256, 4) void pair_gram_kernel(GramLaunch a, int nth
 // then all waves add the panel's contribution sum_j eta_j G[j][i] to the
 // alpha of every later pair (coalesced row segments, many in flight).
 // ---------------------------------------------------------------------------
+// Digit-scratch row of point q of bin z (the integer Gram's rows).
+__device__ __forceinline__ int32_t kept_row(const SweepLaunch& a, int z, int q) {
+  const int64_t pt = static_cast<int64_t>(z) * a.N + q;
+  return static_cast<int32_t>(a.row_map ? a.row_map[pt] : a.row0 + pt);
+}
+
 __device__ __forceinline__ int64_t dec_offset(const SweepLaunch& a, int lb, int P) {
   if (a.dec_mode == 1) {   // Express batch k = lb: HALVE 0, then (3 batches, HALVE) per epoch
     const int64_t n = P;
@@ -377,7 +383,7 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
 
   const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
   int32_t* out = a.idx_out + static_cast<int64_t>(z) * a.out_stride;
-  int32_t* pout = a.pos_out ? a.pos_out + static_cast<int64_t>(z) * a.out_stride : nullptr;
+  int32_t* pout = a.row_out ? a.row_out + static_cast<int64_t>(z) * a.out_stride : nullptr;
   uint8_t* dec = a.dec ? a.dec + static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) : nullptr;
   for (int p = 0; p < np; ++p) {
     const int p0 = 64 * p;
@@ -407,7 +413,7 @@ __global__ __launch_bounds__(256) void halving_sweep_kernel(SweepLaunch a) {
         const bool first = (bits >> lane) & 1ull;
         s_eta[i] = first ? 1.0 : -1.0;
         out[i] = in[2 * i + (first ? 0 : 1)];
-        if (pout) pout[i] = z * a.N + 2 * i + (first ? 0 : 1);
+        if (pout) pout[i] = kept_row(a, z, 2 * i + (first ? 0 : 1));
         if (dec) dec[i] = first ? 1 : 0;
       }
     } else if (w <= 2 && p + 1 < np) {
@@ -475,7 +481,7 @@ __global__ __launch_bounds__(256) void halving_sweep_small_kernel(SweepLaunch a)
     const bool first = (bits >> lane) & 1ull;
     const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
     a.idx_out[static_cast<int64_t>(z) * a.out_stride + lane] = in[2 * lane + (first ? 0 : 1)];
-    if (a.pos_out) a.pos_out[static_cast<int64_t>(z) * a.out_stride + lane] = z * a.N + 2 * lane + (first ? 0 : 1);
+    if (a.row_out) a.row_out[static_cast<int64_t>(z) * a.out_stride + lane] = kept_row(a, z, 2 * lane + (first ? 0 : 1));
     if (a.dec) a.dec[static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) + lane] = first ? 1 : 0;
   }
 }
@@ -527,8 +533,10 @@ __global__ void express_reps_kernel(ExpressView ev, int units, uint64_t seed, in
 }
 
 // Input list of HALVE e: the first 4n tokens (e = 0), else the output of
-// HALVE e-1 followed by the three batches of epoch e.
-__global__ void halve_input_kernel(ExpressView ev, int units, int e, int32_t* halve_in) {
+// HALVE e-1 followed by the three batches of epoch e; with rows.out (e >= 1),
+// also the points' digit-scratch rows, from the same places of rows.halve and
+// rows.batch.
+__global__ void halve_input_kernel(ExpressView ev, int units, int e, int32_t* halve_in, HalveRows rows) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t per = 4LL * ev.n;
   if (i >= per * units) return;
@@ -538,10 +546,13 @@ __global__ void halve_input_kernel(ExpressView ev, int units, int e, int32_t* ha
   if (e == 0) {
     val = j;
   } else if (j < ev.n) {
-    val = ev.halve_out[(static_cast<int64_t>(unit) * ev.n_halves + (e - 1)) * ev.n + j];
+    const int64_t at = (static_cast<int64_t>(unit) * ev.n_halves + (e - 1)) * ev.n + j;
+    val = ev.halve_out[at];
+    if (rows.out) rows.out[i] = rows.halve[at];
   } else {
-    const int64_t base = (static_cast<int64_t>(unit) * ev.n_batches_done + 3 * (e - 1)) * ev.n;
-    val = ev.batch_out[base + (j - ev.n)];
+    const int64_t at = (static_cast<int64_t>(unit) * ev.n_batches_done + 3 * (e - 1)) * ev.n + (j - ev.n);
+    val = ev.batch_out[at];
+    if (rows.out) rows.out[i] = rows.batch[at];
   }
   halve_in[i] = val;
 }
@@ -843,7 +854,7 @@ __global__ __launch_bounds__(256) void small_halving_kernel(GramLaunch g, SweepL
     const int z = unit * g.bins_per_unit + lb;
     const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
     a.idx_out[static_cast<int64_t>(z) * a.out_stride + i] = in[2 * i + (first ? 0 : 1)];
-    if (a.pos_out) a.pos_out[static_cast<int64_t>(z) * a.out_stride + i] = z * a.N + 2 * i + (first ? 0 : 1);
+    if (a.row_out) a.row_out[static_cast<int64_t>(z) * a.out_stride + i] = kept_row(a, z, 2 * i + (first ? 0 : 1));
     if (a.dec) a.dec[static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) + i] = first ? 1 : 0;
   }
 }
@@ -999,7 +1010,7 @@ __global__ __launch_bounds__(256) void medium_halving_kernel(GramLaunch g, Sweep
     const bool first = (bits >> lane) & 1ull;
     const int32_t* in = a.idx_in + static_cast<int64_t>(unit) * a.in_unit_stride + static_cast<int64_t>(lb) * a.in_stride;
     a.idx_out[static_cast<int64_t>(z) * a.out_stride + lane] = in[2 * lane + (first ? 0 : 1)];
-    if (a.pos_out) a.pos_out[static_cast<int64_t>(z) * a.out_stride + lane] = z * a.N + 2 * lane + (first ? 0 : 1);
+    if (a.row_out) a.row_out[static_cast<int64_t>(z) * a.out_stride + lane] = kept_row(a, z, 2 * lane + (first ? 0 : 1));
     if (a.dec) a.dec[static_cast<int64_t>(unit) * a.dec_per_unit + dec_offset(a, lb, P) + lane] = first ? 1 : 0;
   }
 }
@@ -1132,9 +1143,10 @@ hipError_t launch_express_reps(const ExpressView& ev, int units, uint64_t seed, 
   return hipGetLastError();
 }
 
-hipError_t launch_halve_input(const ExpressView& ev, int units, int e, int32_t* halve_in, hipStream_t s) {
+hipError_t launch_halve_input(const ExpressView& ev, int units, int e, int32_t* halve_in, hipStream_t s,
+                              const HalveRows& rows) {
   const int64_t total = static_cast<int64_t>(units) * 4 * ev.n;
-  hipLaunchKernelGGL(halve_input_kernel, dim3(grid1d(total, 256)), dim3(256), 0, s, ev, units, e, halve_in);
+  hipLaunchKernelGGL(halve_input_kernel, dim3(grid1d(total, 256)), dim3(256), 0, s, ev, units, e, halve_in, rows);
   return hipGetLastError();
 }
 

@@ -281,7 +281,11 @@ def test_integer_gram_scratch_sizes():
     assert sizes["bf16"][1] == halve(4) and sizes["fp8"][1] == halve(3)
     assert sizes["bf16"][2] == sizes["fp8"][2] == 0          # bins below 256 points stay on fp64
     assert sizes["bf16_fp64"][1] == sizes["f32"][1] == 0
-    # the causal prefill: batch Grams (7 batches of 2n points) and the HALVE Grams (4n) each get one
-    batch = lambda nd: (units * 7 * 2 * n * nd * 256 + 255) // 256 * 256 + units * 7 * 2 * n * 10
+    # the causal prefill: one scratch for HALVE 0's points (4n per unit) and the batch points (7
+    # batches of 2n), and the digit rows of the batch outputs (7n), a HALVE's input (4n) and the
+    # HALVE outputs (3 HALVEs of n)
+    rows = units * (4 * n + 7 * 2 * n)
+    shared = lambda nd: (rows * nd * 256 + 255) // 256 * 256 + rows * 10
     al = lambda x: (x + 255) // 256 * 256
-    assert sizes["bf16"][0] - sizes["bf16_fp64"][0] == al(batch(4)) + al(halve(4))
+    lists = al(4 * units * 7 * n) + al(4 * units * 4 * n) + al(4 * units * 3 * n)
+    assert sizes["bf16"][0] - sizes["bf16_fp64"][0] == al(shared(4)) + lists
