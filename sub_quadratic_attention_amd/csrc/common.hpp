@@ -1,10 +1,24 @@
 // Shared device helpers of the thin-attention HIP library (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace thin {
+
+// A kernel launch that, given an event, has its own dispatch signal that
+// event on completion (hipExtLaunchKernelGGL's stop event) instead of a
+// separate marker in the stream's queue.
+template <typename F, typename... Args>
+inline void launch_signal(F kernel, const dim3& grid, const dim3& block, uint32_t lds, hipStream_t s,
+                          hipEvent_t done, Args... args) {
+  if (done)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, nullptr, done, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
+
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;

@@ -561,7 +561,7 @@ hipError_t launch_gram8_digits(const GramLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gram8_tiles(const GramLaunch& a, hipStream_t s) {
+hipError_t launch_gram8_tiles(const GramLaunch& a, hipStream_t s, hipEvent_t done) {
   if (!gram8_launch_ok(a)) return hipErrorInvalidValue;
   const int64_t npts = static_cast<int64_t>(a.nbins) * a.N;
   if (npts == 0) return hipSuccess;
@@ -572,9 +572,9 @@ hipError_t launch_gram8_tiles(const GramLaunch& a, hipStream_t s) {
   threshold_groups(a, nthr, per_wave);
   const dim3 g2(static_cast<unsigned>(nthr + kFixGroups + tiles));
   if (a.src.dtype == kFP8)
-    hipLaunchKernelGGL(gram8_kernel<kFP8>, g2, dim3(256), 0, s, a, nthr, per_wave, static_cast<int>(tiles));
+    launch_signal(gram8_kernel<kFP8>, g2, dim3(256), 0, s, done, a, nthr, per_wave, static_cast<int>(tiles));
   else
-    hipLaunchKernelGGL(gram8_kernel<kBF16>, g2, dim3(256), 0, s, a, nthr, per_wave, static_cast<int>(tiles));
+    launch_signal(gram8_kernel<kBF16>, g2, dim3(256), 0, s, done, a, nthr, per_wave, static_cast<int>(tiles));
   return hipGetLastError();
 }
 

@@ -347,14 +347,16 @@ inline void release_timing(thin_attn* h) {
 }
 
 // The pair Gram of a launch: the integer Gram's digit pass and tiles under
-// their own timing labels, or the fp64 tiles.
-inline int run_pair_gram(thin_attn* h, hipStream_t st, const thin::GramLaunch& g) {
+// their own timing labels, or the fp64 tiles; done (optional) is signalled
+// when it completes.
+inline int run_pair_gram(thin_attn* h, hipStream_t st, const thin::GramLaunch& g, hipEvent_t done = nullptr) {
   if (thin::gram8_runs(g)) {
     if (!g.dig_map) THIN_HIP(timed(h, st, "gram_digits", [&] { return thin::launch_gram8_digits(g, st); }));
-    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_gram8_tiles(g, st); }));
+    THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_gram8_tiles(g, st, done); }));
     return THIN_OK;
   }
   THIN_HIP(timed(h, st, "pair_gram", [&] { return thin::launch_pair_gram(g, st); }));
+  if (done) THIN_HIP(hipEventRecord(done, st));
   return THIN_OK;
 }
 
@@ -442,15 +444,15 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
     return attention(st, 0, all_blocks);
   }
   // HALVE e halves twice, 4n -> 2n -> n, on st; HALVE e >= 1 reads batches 3(e-1) ..
-  auto halve_first_gram = [&](int e) -> int {
+  auto halve_first_gram = [&](int e, hipEvent_t done) -> int {
     const thin::HalveRows rows{hrow, brow, e > 0 ? hinrow : nullptr};
     THIN_HIP(timed(h, st, "halve_input", [&] { return thin::launch_halve_input(ev, units, e, hin, st, rows); }));
     thin::SweepLaunch s1 = make_sweep(h, Gh, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
                                       static_cast<uint64_t>(e));
-    if (const int rg = run_pair_gram(h, st, first_gram(s1, e))) return rg;
+    if (const int rg = run_pair_gram(h, st, first_gram(s1, e), done)) return rg;
     return THIN_OK;
   };
-  auto halve_rest = [&](int e) -> int {
+  auto halve_rest = [&](int e, hipEvent_t done) -> int {
     thin::SweepLaunch s1 = make_sweep(h, Gh, 4 * n, units, 1, hin, 4 * n, hmid, seed, thin::kTagHalveFirst,
                                       static_cast<uint64_t>(e));
     // the second halving's points are among the first's: with the integer
@@ -480,9 +482,12 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
     s2.dec = decisions;
     s2.dec_per_unit = ndec;
     s2.dec_base = static_cast<int64_t>(6) * n * e + 2 * n;
-    THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(s2, st); }));
+    THIN_HIP(timed(h, st, "halving_sweep", [&] { return thin::launch_halving_sweep(s2, st, done); }));
     return THIN_OK;
   };
+  // an event for st -> sx dependencies, signalled by the dispatch of the
+  // kernel it follows (a separate marker in st's queue delays st's next kernel)
+  auto fork_event = [&]() -> hipEvent_t { return sx != st ? h->sync_ev[k++] : nullptr; };
   int rc = THIN_OK;
   // 2. HALVE 0's first Gram, then the fork: the side takes every batch halving
   // (they read only representatives).  Forking after that Gram rather than
@@ -490,9 +495,14 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
   // out of the compute units (a walk launched while a large Gram holds every
   // unit waits for it to drain); with a single HALVE, the exact epoch's
   // attention goes to the side first
-  if ((rc = halve_first_gram(0))) return rc;
-  THIN_HIP(stream_wait(h, st, sx, k++));
+  {
+    const hipEvent_t fork = fork_event();
+    if ((rc = halve_first_gram(0, fork))) return rc;
+    if (fork) THIN_HIP(hipStreamWaitEvent(sx, fork, 0));
+  }
   if (p.sc.n_halves == 1 && (rc = attention(sx, 0, 4))) return rc;
+  const int k_batches = k++;   // marks the batch halvings on the side
+  const hipEvent_t batches_done = sx != st ? h->sync_ev[k_batches] : nullptr;
   if (p.sc.n_batches_done > 0) {
     const int N = 2 * n;
     const int nb = p.sc.n_batches_done;
@@ -510,21 +520,22 @@ inline int express_thin(thin_attn* h, const thin::PointSource& src, int units, c
     sl.dec = decisions;
     sl.dec_per_unit = ndec;
     sl.dec_mode = 1;
-    THIN_HIP(timed(h, sx, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, sx); }));
+    THIN_HIP(timed(h, sx, "halving_sweep", [&] { return thin::launch_halving_sweep(sl, sx, batches_done); }));
+  } else if (batches_done) {
+    THIN_HIP(hipEventRecord(batches_done, sx));
   }
-  const int k_batches = k++;   // marks the batch halvings on the side
-  if (sx != st) THIN_HIP(hipEventRecord(h->sync_ev[k_batches], sx));
   // 3. the HALVE chain on st
   const int H = p.sc.n_halves;
   for (int e = 0; e < H; ++e) {
     if (e == 1 && sx != st) THIN_HIP(hipStreamWaitEvent(st, h->sync_ev[k_batches], 0));
-    if (e > 0 && (rc = halve_first_gram(e))) return rc;
-    if ((rc = halve_rest(e))) return rc;
+    if (e > 0 && (rc = halve_first_gram(e, nullptr))) return rc;
     // epoch e + 1 reads HALVE e and the batches of its epoch (done on the side before this
     // point).  Every epoch but the last goes in one launch on the side once the HALVE before
     // the last is done, beside the last HALVE; the last epoch follows that HALVE on st
+    const hipEvent_t epochs = e == H - 2 && al ? fork_event() : nullptr;
+    if ((rc = halve_rest(e, epochs))) return rc;
     if (e == H - 2 && al) {
-      THIN_HIP(stream_wait(h, st, sx, k++));
+      if (epochs) THIN_HIP(hipStreamWaitEvent(sx, epochs, 0));
       if ((rc = attention(sx, 0, static_cast<int64_t>(1) << (2 * H)))) return rc;
     }
     if (e == H - 1) {   // the last epoch on st (beside the side's tail), then st takes in the side's work

@@ -178,9 +178,11 @@ hipError_t launch_pair_gram8(const GramLaunch& a, hipStream_t s);
 // Its two launches (the digit pass, then thresholds, fix-ups and tiles), and
 // whether launch_pair_gram takes that path for a.
 hipError_t launch_gram8_digits(const GramLaunch& a, hipStream_t s);
-hipError_t launch_gram8_tiles(const GramLaunch& a, hipStream_t s);
+// done (optional): an event the launch's own dispatch signals when it completes
+// (no marker of its own in the stream's queue)
+hipError_t launch_gram8_tiles(const GramLaunch& a, hipStream_t s, hipEvent_t done = nullptr);
 bool gram8_runs(const GramLaunch& a);
-hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s);
+hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s, hipEvent_t done = nullptr);
 // Bins of at most 16 points: the pair Gram, thresholds and walk of a
 // GramLaunch / SweepLaunch pair in one kernel (same outputs as the two).
 bool small_halving_supported(int N, int E, int D);

@@ -1044,13 +1044,13 @@ hipError_t launch_pair_gram(const GramLaunch& a, hipStream_t s) {
 
 size_t sweep_lds_bytes(int N) { return (3 * static_cast<size_t>(N / 2) + 2 * 64 * 65) * sizeof(double); }
 
-hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s) {
+hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s, hipEvent_t done) {
   if (a.N / 2 <= 16) {
-    hipLaunchKernelGGL(halving_sweep_small_kernel<16>, dim3((a.nbins + 3) / 4), dim3(256), 0, s, a);
+    launch_signal(halving_sweep_small_kernel<16>, dim3((a.nbins + 3) / 4), dim3(256), 0, s, done, a);
     return hipGetLastError();
   }
   if (a.N / 2 <= 64) {
-    hipLaunchKernelGGL(halving_sweep_small_kernel<64>, dim3((a.nbins + 3) / 4), dim3(256), 0, s, a);
+    launch_signal(halving_sweep_small_kernel<64>, dim3((a.nbins + 3) / 4), dim3(256), 0, s, done, a);
     return hipGetLastError();
   }
   const size_t lds = sweep_lds_bytes(a.N);
@@ -1059,7 +1059,7 @@ hipError_t launch_halving_sweep(const SweepLaunch& a, hipStream_t s) {
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(halving_sweep_kernel, dim3(a.nbins), dim3(256), lds, s, a);
+  launch_signal(halving_sweep_kernel, dim3(a.nbins), dim3(256), static_cast<uint32_t>(lds), s, done, a);
   return hipGetLastError();
 }
 
