@@ -273,8 +273,18 @@ struct Tile8 {
     if (active) consume(cur);
   }
 
-  // all digit products of one step
-  __device__ __forceinline__ void consume(const lds_byte* buf) {
+  // The first V step: its products, then the exponentials of the K part,
+  // which depend only on kx and so can issue while the products run.
+  __device__ __forceinline__ void overlap_exp(int st, int nst, const lds_byte* __restrict__ cur,
+                                              lds_byte* __restrict__ nxt, const double* T) {
+    if (st + 1 < nst) copy(st + 1, nxt);
+    if (active) consume<true>(cur, T);
+  }
+
+  // all digit products of one step; EXP: after the products of each digit d
+  // of the row points, the exponentials of a quarter of kx (K part)
+  template <bool EXP = false>
+  __device__ __forceinline__ void consume(const lds_byte* buf, const double* T = nullptr) {
     const int g = lane >> 4, i16 = lane & 15;
     i32x4_t bo[2][ND];
 #pragma unroll
@@ -293,6 +303,11 @@ struct Tile8 {
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
             acc[rb][cb][d + e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ao[rb], bo[cb][e], acc[rb][cb][d + e], 0, 0, 0);
+      if constexpr (EXP) {
+#pragma unroll
+        for (int x = (16 * d) / ND; x < (16 * (d + 1)) / ND; ++x)
+          kx[x >> 3][(x >> 2) & 1][x & 3] = exp_tab(kx[x >> 3][(x >> 2) & 1][x & 3], T);
+      }
     }
   }
 
@@ -307,7 +322,8 @@ struct Tile8 {
 
   // The exact dot products of one part, rounded once: the digit groups as two
   // integers below 2^53 (lo: groups 0 .. 3, hi: the rest), then one fma.
-  // part 0: kx = e^(s <k, k'>); part 1: kx *= <v, v'> + 1.
+  // part 0: kx = s <k, k'> (its exponential is taken during the next step);
+  // part 1: kx *= <v, v'> + 1.
   template <int PART>
   __device__ __forceinline__ void finish_part(const int* s_scale, const double* T, double scale) {
     constexpr int part = PART;
@@ -331,7 +347,7 @@ struct Tile8 {
           const int rs = 32 * wr + 16 * rb + 4 * g + t;
           const double dot = __builtin_amdgcn_ldexp(tot, -(s_scale[2 * rs + part] + csh));
           if constexpr (PART == 0)
-            kx[rb][cb][t] = exp_tab(scale * dot, T);
+            kx[rb][cb][t] = scale * dot;
           else
             kx[rb][cb][t] *= dot + 1.0;
         }
@@ -401,16 +417,26 @@ __device__ void gram8_tile(const GramLaunch& a, int tile, int ntiles, lds_byte* 
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   t.clear();
-  for (int st = 0; st < nst; ++st) {
+  // K steps; the K part's dot products are joined after the last of them
+  for (int st = 0; st < KS; ++st) {
     t.overlap(st, nst, smem + (st & 1) * kBuf, smem + ((st + 1) & 1) * kBuf);
     if (t.active && st == KS - 1) {
       t.template finish_part<0>(s_scale, T, scale);
       t.clear();
     }
-    if (t.active && st == nst - 1) t.template finish_part<1>(s_scale, T, scale);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // this thread's copies have landed
     __syncthreads();
   }
+  // the first V step takes the K part's exponentials beside its products
+  t.overlap_exp(KS, nst, smem + (KS & 1) * kBuf, smem + ((KS + 1) & 1) * kBuf, T);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int st = KS + 1; st < nst; ++st) {
+    t.overlap(st, nst, smem + (st & 1) * kBuf, smem + ((st + 1) & 1) * kBuf);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+  if (t.active) t.template finish_part<1>(s_scale, T, scale);
   if (t.active) t.store(s_flag);
 }
 
