@@ -28,8 +28,8 @@
 // Everything after the dot products (fp64 exp, the pair combination, the
 // thresholds in the lower triangle, the output layout) is the fp64 tiles'.
 //
-// Two launches: a digit pass (one wave per point of the launch: scales,
-// digits, fit flags) and the Gram launch (threshold workgroups, kFixGroups
+// Two launches: a digit pass (one lane group per point row of the launch:
+// scales, digits, fit flags) and the Gram launch (threshold workgroups, kFixGroups
 // workgroups for the pairs that do not fit, then the tiles).
 
 #include <limits.h>
@@ -112,9 +112,9 @@ __device__ __forceinline__ int64_t point_row(const GramLaunch& a, int z, int q) 
 
 // ---------------------------------------------------------------------------
 // Digit pass.  Items are point rows of one part (all K rows, then all V
-// rows); a row of F features takes F / 8 consecutive lanes (an aligned group
-// of a wave), each with 8 consecutive features: one load, a group maximum of
-// the exponents, and one 8-byte store per digit.
+// rows); a row of F features takes F / 16 consecutive lanes (an aligned group
+// of a wave), each with 16 consecutive features: one or two 16-byte loads, a
+// group maximum of the exponents, and one 16-byte store per digit.
 // ---------------------------------------------------------------------------
 template <int ET>
 __global__ __launch_bounds__(256) void gram8_digits_kernel(GramLaunch a, int blocks_k) {
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void gram8_digits_kernel(GramLaunch a, int blo
   const int64_t npts = static_cast<int64_t>(a.nbins) * a.N;
   const int part = static_cast<int>(blockIdx.x) >= blocks_k ? 1 : 0;
   const int F = part ? a.src.D : a.src.E;
-  const int gl = F / 8;   // lanes per row: 8, 16 or 32
+  const int gl = F / 16;   // lanes per row (16 features each): 4, 8 or 16, a power of two dividing 256
   const int64_t t = (static_cast<int64_t>(blockIdx.x) - (part ? blocks_k : 0)) * 256 + threadIdx.x;
   const int64_t pt = t / gl;
   const int j = static_cast<int>(t % gl);
@@ -130,20 +130,21 @@ __global__ __launch_bounds__(256) void gram8_digits_kernel(GramLaunch a, int blo
   const Scratch8 sc = scratch8(a.dig, ND, a.src.E, a.src.D, dig_points(a));
   const int64_t row = point_row(a, static_cast<int>(pt / a.N), static_cast<int>(pt % a.N));
   const unsigned char* src = static_cast<const unsigned char*>(part ? a.src.v : a.src.k) +
-                             (row * F + 8 * j) * elt_size<ET>();
-  uint32_t w[4];
-  if constexpr (ET == kFP8) {
-    const uint2 x = *reinterpret_cast<const uint2*>(src);
-    w[0] = x.x, w[1] = x.y;
-  } else {
+                             (row * F + 16 * j) * elt_size<ET>();
+  uint32_t w[8];
+  {
     const uint4 x = *reinterpret_cast<const uint4*>(src);
     w[0] = x.x, w[1] = x.y, w[2] = x.z, w[3] = x.w;
   }
-  int sgn[8], sig[8], p[8];
+  if constexpr (ET != kFP8) {
+    const uint4 x = *reinterpret_cast<const uint4*>(src + 16);
+    w[4] = x.x, w[5] = x.y, w[6] = x.z, w[7] = x.w;
+  }
+  int sgn[16], sig[16], p[16];
   int pmax = INT_MIN;
   bool ok = true;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < 16; ++u) {
     if constexpr (ET == kFP8) {
       const uint32_t b = (w[u >> 2] >> (8 * (u & 3))) & 255u;
       const uint32_t e4 = (b >> 3) & 15u, m3 = b & 7u;
@@ -163,9 +164,9 @@ __global__ __launch_bounds__(256) void gram8_digits_kernel(GramLaunch a, int blo
   }
   for (int off = gl / 2; off >= 1; off >>= 1) pmax = max(pmax, __shfl_xor(pmax, off, 64));
   const int s = pmax == INT_MIN ? 0 : top_shift<ET>() - pmax;
-  uint32_t dg[ND][2] = {};
+  uint32_t dg[ND][4] = {};
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < 16; ++u) {
     const int e = p[u] + s;
     if (sig[u] && e + __builtin_ctz(static_cast<unsigned>(sig[u])) < 0) ok = false;
     int X = e >= 0 ? (sig[u] << e) : (e > -31 ? (sig[u] >> -e) : 0);
@@ -177,11 +178,11 @@ __global__ __launch_bounds__(256) void gram8_digits_kernel(GramLaunch a, int blo
       X = (X - lo) >> 8;
     }
   }
-  const int f0 = 8 * j;
+  const int f0 = 16 * j;
   const int64_t dr = a.dig_row0 + pt;   // this point's scratch row
   unsigned char* o = sc.dig + dr * sc.pbytes + (part ? ND * a.src.E : 0) + 64 * ND * (f0 / 64) + (f0 % 64);
 #pragma unroll
-  for (int d = 0; d < ND; ++d) *reinterpret_cast<uint2*>(o + 64 * d) = uint2{dg[d][0], dg[d][1]};
+  for (int d = 0; d < ND; ++d) *reinterpret_cast<uint4*>(o + 64 * d) = uint4{dg[d][0], dg[d][1], dg[d][2], dg[d][3]};
   // the row fits when every lane of its group fits
   int bad = ok ? 0 : 1;
   for (int off = gl / 2; off >= 1; off >>= 1) bad |= __shfl_xor(bad, off, 64);
@@ -552,9 +553,9 @@ __global__ __launch_bounds__(256, 2) void gram8_kernel(GramLaunch a, int nthr, i
 
 }  // namespace
 
-bool gram8_supported(int dtype, int E, int D, int N) {
-  return (dtype == kBF16 || dtype == kFP8) && E % 64 == 0 && D % 64 == 0 && E >= 64 && D >= 64 && E <= 256 &&
-         D <= 256 && N >= 256 && N % 2 == 0;
+bool gram8_supported(int dtype, int E, int D, int N) {   // E, D in {64, 128, 256}: the digit pass's lane groups
+  const auto dim_ok = [](int F) { return F == 64 || F == 128 || F == 256; };
+  return (dtype == kBF16 || dtype == kFP8) && dim_ok(E) && dim_ok(D) && N >= 256 && N % 2 == 0;
 }
 
 bool gram8_fits(int dtype, int64_t npts, int E, int D) {   // the tiles address the digits with 32-bit offsets
@@ -578,7 +579,7 @@ hipError_t launch_gram8_digits(const GramLaunch& a, hipStream_t s) {
   if (!gram8_launch_ok(a) || a.dig_map) return hipErrorInvalidValue;
   const int64_t npts = static_cast<int64_t>(a.nbins) * a.N;
   if (npts == 0) return hipSuccess;
-  const int64_t blocks_k = (npts * (a.src.E / 8) + 255) / 256, blocks_v = (npts * (a.src.D / 8) + 255) / 256;
+  const int64_t blocks_k = (npts * (a.src.E / 16) + 255) / 256, blocks_v = (npts * (a.src.D / 16) + 255) / 256;
   const dim3 g1(static_cast<unsigned>(blocks_k + blocks_v));
   if (a.src.dtype == kFP8)
     hipLaunchKernelGGL(gram8_digits_kernel<kFP8>, g1, dim3(256), 0, s, a, static_cast<int>(blocks_k));
