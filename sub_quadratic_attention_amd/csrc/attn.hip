@@ -483,88 +483,6 @@ struct Attn {
     }
   }
 
-  // One-chunk coresets (bf16 and fp8 P V): the maxima and rescales first, then
-  // the first key half's exponentials, then the P V products of each key half
-  // with the second half's exponentials between the first half's products.
-  // Each accumulator still takes key half 0, then half 1.  Fewer registers
-  // stay live across the products, so the three-wave builds spill less.
-  __device__ __forceinline__ void softmax_pv_split(float (&p)[NQG][4][4], const lds_byte* vbuf) {
-    float m_use[NQG];
-#pragma unroll
-    for (int qg = 0; qg < NQG; ++qg) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, p[qg][kb][i]);
-      mx = group_max(mx);
-      const float m_new = fmaxf(m_run[qg], mx);
-      m_use[qg] = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qg] - m_use[qg]);
-      m_run[qg] = m_new;
-      if (__ballot(alpha != 1.0f)) {   // most chunks leave every maximum where it was
-#pragma unroll
-        for (int d = 0; d < ND; ++d) o[qg][d] *= alpha;
-        osum[qg] *= alpha;   // the row sums come out of the P V MFMAs (a block of ones)
-      }
-    }
-    // P in bf16, key half hh (keys 32 hh .. 32 hh + 31): the first half's
-    // exponentials now, the second's between the first half's P V products
-    bf16x8_t pb[NQG][2];
-    auto expo = [&](int qg, int hh) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[qg][hh][i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(p[qg][2 * hh][i] - m_use[qg]));
-        pb[qg][hh][4 + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(p[qg][2 * hh + 1][i] - m_use[qg]));
-      }
-    };
-#pragma unroll
-    for (int qg = 0; qg < NQG; ++qg) expo(qg, 0);
-    // O^T += V^T P^T: lane group g's operand slots 0-3 / 4-7 are keys
-    // 32hh + 4g + (0..3) and 32hh + 16 + 4g + (0..3) (the S^T layout).  The
-    // fragments of dimension block d + 1 are read before the MFMAs of block
-    // d (two register sets, scheduling barriers as in scores()).  Each
-    // accumulator takes key half 0, then half 1, as before the split.
-    const int i16 = lane & 15;
-    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-    auto vread = [&](int d, int hh, bf16x8_t& vf) {
-      // logical elements 16 d + 4 (i16 % 4) .. + 3: piece 2 d + (i16 % 4) / 2, half i16 % 2
-      const int q = 2 * d + ((i16 & 3) >> 1);
-      const int R0 = 32 * hh + 4 * g + (i16 >> 2), R1 = R0 + 16;
-      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4*)(vbuf + R0 * VB + 16 * (q ^ vswz<BF16, VB>(R0)) + 8 * (i16 & 1)));
-      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (lds_bf16x4*)(vbuf + R1 * VB + 16 * (q ^ vswz<BF16, VB>(R1)) + 8 * (i16 & 1)));
-      vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      bf16x8_t vf[2];
-      vread(0, hh, vf[0]);
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        if (d + 1 < ND) vread(d + 1, hh, vf[(d + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int qg = 0; qg < NQG; ++qg)
-          o[qg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d & 1], pb[qg][hh], o[qg][d], 0, 0, 0);
-        if (hh == 0 && d == ND / 2 - 1) {
-#pragma unroll
-          for (int qg = 0; qg < NQG; ++qg) expo(qg, 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // a 16-row block of ones: every row of its output is the query's sum of P
-    const bf16x8_t ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
-                           (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int qg = 0; qg < NQG; ++qg)
-        osum[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qg][hh], osum[qg], 0, 0, 0);
-  }
-
   __device__ __forceinline__ void consume(int c, int buf, const lds_byte* kbuf, const lds_byte* vbuf) {
     f32x4_t st[NQG][4];
     scores(kbuf, st);
@@ -597,10 +515,6 @@ struct Attn {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) p[qg][kb][i] = fmaf(st[qg][kb][i], sc, lw[kb][i]);
-    }
-    if constexpr (BF16 && NB == 1 && D > 64) {   // (D = 64: the split spills more, not less)
-      softmax_pv_split(p, vbuf);
-      return;
     }
 #pragma unroll
     for (int qg = 0; qg < NQG; ++qg) {
@@ -869,14 +783,16 @@ __device__ __forceinline__ void express_pass(const ExpressView& ev, int unit, in
 
 // Unmasked: one pass (the coreset, or all S keys).  Causal: one pass per
 // block beta met by the workgroup's queries.
-// Waves per SIMD the register budget is set for: three where a one-buffer
-// build fits 168 registers without spilling (bf16, E = 64, D = 64 or 256).
+// Waves per SIMD the register budget is set for: three for the one-buffer
+// bf16 build with E = D = 64 (168 registers, 5 spilled); two elsewhere (the
+// one-buffer D = 256 build spills 41 registers at three and runs faster at two
+// with none).
 // Query tiles per workgroup: a one-chunk coreset is staged once and serves
 // kTilesOne consecutive tiles of its unit.
 constexpr int kTilesOne = 4;
 
 template <int ET, int E, int D, int NB>
-constexpr int attn_waves() { return (NB == 1 && ET == kBF16 && E == 64 && (D == 64 || D == 256)) ? 3 : 2; }
+constexpr int attn_waves() { return (NB == 1 && ET == kBF16 && E == 64 && D == 64) ? 3 : 2; }
 
 template <int ET, int E, int D, bool RAW, int NB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_waves<ET, E, D, NB>()))) void attn_kernel(
